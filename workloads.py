@@ -1,0 +1,161 @@
+"""Seeded synthetic workloads for the Conv3D layers the pages describe.
+
+This module holds shapes and random-number recipes only: none of the
+convolution's arithmetic. The GPU tests, the benchmark, the smoke entry point
+and the oracle checks all draw their inputs here, so both sides of every
+comparison see identical tensors.
+
+Recipe (every draw: numpy PCG64, fp32, then converted to bf16 by PyTorch's
+round-to-nearest-even cast; the second parameter of N(.,.) is the variance):
+  x         ~ N(0, 1)
+  w         ~ N(0, 1/(27*Cin))       (OIDHW, the checkpoint layout)
+  bias      ~ N(0, 0.1), kept fp32
+  residual  ~ N(0, 1)
+  gamma     ~ U(0.5, 1.5)
+Seed: SeedSequence([1000 + family, stream]) with stream x=0, w=1, bias=2,
+residual=3, gamma=4, so each tensor is reproducible on its own.
+
+Layer shapes come from the pages' tables: the MiniMax H3 encoder (FlyDSL
+issue page, "Shapes"), the Wan 2.2 encoder's dominant shapes (same page,
+"Why"), the Qwen-Image T2I 96->96 layer at 1024^2 (FlyDSL PR page, "Test
+shapes") and WAN's base_dim=160 family (cuDNN page, "Overview",
+"Requirements").
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import numpy as np
+
+CAUSAL = dict(pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))
+VALID = dict(pad_lo=(0, 0, 0), pad_hi=(0, 0, 0))
+
+
+@dataclasses.dataclass(frozen=True)
+class Layer:
+    name: str
+    family: int                 # seed family 1..5
+    x_shape: Tuple[int, int, int, int, int]   # NDHWC
+    cout: int
+    stride: Tuple[int, int, int] = (1, 1, 1)
+    pad_lo: Tuple[int, int, int] = (0, 0, 0)
+    pad_hi: Tuple[int, int, int] = (0, 0, 0)
+    bias: bool = False
+    residual: bool = False
+    norm_silu: bool = False
+    live_taps: int = 27         # taps that can see real pixels (T=1 causal: 9)
+
+    @property
+    def cin(self) -> int:
+        return self.x_shape[4]
+
+    def out_dhw(self):
+        _, D, H, W, _ = self.x_shape
+        k = 3
+        return tuple((i + lo + hi - k) // s + 1 for i, lo, hi, s in
+                     zip((D, H, W), self.pad_lo, self.pad_hi, self.stride))
+
+    def out_shape(self):
+        return (self.x_shape[0],) + self.out_dhw() + (self.cout,)
+
+    @property
+    def m(self) -> int:
+        n = self.x_shape[0]
+        d, h, w = self.out_dhw()
+        return n * d * h * w
+
+    def flops(self, live: bool = True) -> float:
+        """2*M*N*K with K = 27*Cin (only the live taps when live=True)."""
+        taps = self.live_taps if live else 27
+        return 2.0 * self.m * self.cout * taps * self.cin
+
+
+LAYERS = {
+    # Tiny causal 64->64.
+    "tiny_causal_64": Layer("tiny_causal_64", 1, (1, 5, 16, 16, 64), 64, bias=True, **CAUSAL),
+    # H3 L5: wide channels on 16x16 frames.
+    "h3_l5_1024": Layer("h3_l5_1024", 2, (1, 5, 16, 16, 1024), 1024, bias=True, **CAUSAL),
+    "h3_l5_512to1024": Layer("h3_l5_512to1024", 2, (1, 5, 16, 16, 512), 1024, bias=True, **CAUSAL),
+    # H3 L0: full-resolution 128->128, and its stride-(1,2,2) downsample.
+    "h3_l0_128": Layer("h3_l0_128", 3, (1, 17, 256, 256, 128), 128, **CAUSAL),
+    "h3_l0_128_s122": Layer("h3_l0_128_s122", 3, (1, 17, 256, 256, 128), 128, stride=(1, 2, 2),
+                            pad_lo=(2, 0, 0), pad_hi=(0, 1, 1)),
+    # Wan encoder's pre-padded valid convs.
+    "wan_valid_96": Layer("wan_valid_96", 4, (1, 6, 354, 642, 96), 96, **VALID),
+    "wan_valid_384": Layer("wan_valid_384", 4, (1, 3, 46, 82, 384), 384, **VALID),
+    # Qwen-Image 96->96 at 1024^2, T=1 causal: only the last temporal slice is live.
+    "qwen_t1_96": Layer("qwen_t1_96", 4, (1, 1, 1024, 1024, 96), 96, live_taps=9, **CAUSAL),
+    # WAN base_dim=160 family, 160->320 with the fused post-operations.
+    "wan_fused_160to320": Layer("wan_fused_160to320", 5, (1, 7, 66, 122, 160), 320, bias=True,
+                                residual=True, norm_silu=True, **VALID),
+}
+
+# The layer the headline throughput is quoted on (H3 L0, ~1 TFLOP per call).
+HEADLINE = "h3_l0_128"
+
+
+def _rng(family: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([1000 + family, stream]))
+
+
+def _to_bf16(a32: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32)).to(torch.bfloat16)
+
+
+def bf16_bits(t) -> np.ndarray:
+    """numpy uint16 view of a CPU bf16 tensor's bit patterns."""
+    import torch
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclasses.dataclass
+class Tensors:
+    x: "object"                 # torch bf16 CPU, NDHWC
+    w: "object"                 # torch bf16 CPU, OIDHW
+    bias: Optional["object"]    # torch fp32 CPU [Co]
+    residual: Optional["object"]  # torch bf16 CPU, NDHWC output shape
+    gamma: Optional["object"]   # torch bf16 CPU [Co]
+
+
+def make_tensors(layer: Layer, x_shape=None, cout=None, family=None) -> Tensors:
+    """Seeded inputs for `layer` (shape overrides allow small parity cases)."""
+    import torch
+    fam = layer.family if family is None else family
+    xs = tuple(layer.x_shape if x_shape is None else x_shape)
+    co = layer.cout if cout is None else cout
+    ci = xs[4]
+    x = _to_bf16(_rng(fam, 0).standard_normal(xs, dtype=np.float32))
+    w = _to_bf16(_rng(fam, 1).standard_normal((co, ci, 3, 3, 3), dtype=np.float32)
+                 * np.float32(np.sqrt(1.0 / (27.0 * ci))))
+    bias = residual = gamma = None
+    if layer.bias:
+        bias = torch.from_numpy(_rng(fam, 2).standard_normal((co,), dtype=np.float32)
+                                * np.float32(np.sqrt(0.1)))
+    if layer.residual or layer.norm_silu:
+        d = tuple((i + lo + hi - 3) // s + 1 for i, lo, hi, s in
+                  zip(xs[1:4], layer.pad_lo, layer.pad_hi, layer.stride))
+        if layer.residual:
+            residual = _to_bf16(_rng(fam, 3).standard_normal((xs[0],) + d + (co,), dtype=np.float32))
+        if layer.norm_silu:
+            gamma = _to_bf16(_rng(fam, 4).uniform(0.5, 1.5, size=(co,)).astype(np.float32))
+    return Tensors(x, w, bias, residual, gamma)
+
+
+def integer_tensors(x_shape, cout, seed=7, bias=False):
+    """Integer-valued inputs: x in {-2..2}, w in {-1,0,1}, integer bias.
+
+    Every partial sum of such a convolution is an integer below 2^24 in
+    magnitude for K <= 27648, so any fp32 summation order gives the same exact
+    result; only the final bf16 rounding remains.
+    """
+    import torch
+    rng = np.random.default_rng(np.random.SeedSequence([2000, seed]))
+    ci = x_shape[4]
+    x = torch.from_numpy(rng.integers(-2, 3, size=x_shape).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.integers(-1, 2, size=(cout, ci, 3, 3, 3)).astype(np.float32)).to(torch.bfloat16)
+    b = None
+    if bias:
+        b = torch.from_numpy(rng.integers(-8, 9, size=(cout,)).astype(np.float32))
+    return x, w, b
