@@ -1,0 +1,203 @@
+"""Benchmark of the MI355X bf16 3x3x3 Conv3D library on the pages' layer shapes.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-layers]
+                    [--no-cpu-baseline]
+
+One step is one conv3d_fwd call on the headline layer (H3 L0: x NDHWC
+[1,17,256,256,128] bf16, w [128,128,3,3,3], causal time pad 2, spatial pad 1,
+about 1 TFLOP) with its inputs already resident in HBM and the weight packed
+once beforehand. The K timed steps run back to back on one stream between
+HIP events, bracketed by device synchronisation. `value` is TFLOP/s at the
+layer's algorithmic FLOP count 2*M*Cout*27*Cin (only live taps for the T=1
+layer). Every other layer shape is timed the same way and reported under
+"per_layer". One JSON line is printed on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-layers", action="store_true", help="time only the headline layer")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def describe(L):
+    return (f"{L.name}: x NDHWC {list(L.x_shape)} bf16, w [{L.cout},{L.cin},3,3,3], "
+            f"stride {list(L.stride)}, pad lo {list(L.pad_lo)} hi {list(L.pad_hi)}, "
+            f"out {list(L.out_shape())}"
+            + (", fp32 bias" if L.bias else "") + (", residual" if L.residual else "")
+            + (", L2-norm*sqrt(C)*gamma+SiLU epilogue" if L.norm_silu else ""))
+
+
+class Case:
+    """Device buffers and a bound launch for one layer."""
+
+    def __init__(self, L, torch, cv, layout=None):
+        from convolution_video_vae_amd.layer import Conv3d
+        import workloads
+        t = workloads.make_tensors(L)
+        self.L = L
+        lay = cv.NDHWC if layout is None else layout
+        x = t.x.cuda()
+        if lay == cv.NCDHW:
+            x = x.permute(0, 4, 1, 2, 3).contiguous()
+        self.x = x
+        self.layer = Conv3d(t.w.cuda(), tuple(x.shape), stride=L.stride, pad_lo=L.pad_lo,
+                            pad_hi=L.pad_hi, layout=lay, bias=t.bias, gamma=t.gamma,
+                            norm_silu=L.norm_silu, residual=L.residual)
+        self.res = None if t.residual is None else t.residual.cuda()
+        if lay == cv.NCDHW and self.res is not None:
+            self.res = self.res.permute(0, 4, 1, 2, 3).contiguous()
+        self.y = self.layer.new_output()
+        self.plan = cv.conv3d_plan_describe(self.layer.desc, None)
+
+    def __call__(self):
+        self.layer(self.x, residual=self.res, y=self.y)
+
+
+def time_case(case, steps, warmup, torch):
+    for _ in range(warmup):
+        case()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        case()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall
+
+
+def cpu_baseline(L, seconds):
+    """The oracle, untuned, on a bounded sample of the same layer's output pixels."""
+    import oracle
+    import workloads
+    t = workloads.make_tensors(L)
+    x, w = workloads.bf16_bits(t.x), workloads.bf16_bits(t.w)
+    per_pixel = 2.0 * L.cout * L.cin * L.live_taps
+    chunk = max(256, int(2e10 / per_pixel))            # ~20 GFLOP per call
+    rng = np.random.default_rng(0)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        start = int(rng.integers(0, max(1, L.m - chunk)))
+        pix = np.arange(start, min(L.m, start + chunk))
+        oracle.conv3d(x, w, stride=L.stride, pad_lo=L.pad_lo, pad_hi=L.pad_hi,
+                      bias=None if t.bias is None else t.bias.numpy(), pixels=pix)
+        done += pix.size
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(done * per_pixel / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {L.m} output pixels (all {L.cout} channels each) of "
+                      f"{L.name}, contiguous runs, {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this "
+              "build (the kernel is measured at one GPU's real shape)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import convolution_video_vae_amd as cv
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cv.lib()
+    head = workloads.LAYERS[args.workload or workloads.HEADLINE]
+
+    case = Case(head, torch, cv)
+    ms, wall = time_case(case, args.steps, args.warmup, torch)
+    flops = head.flops(live=True)
+    tflops = flops / (ms * 1e-3) / 1e12
+    assert torch.isfinite(case.y.float()).all().item()
+    del case
+    torch.cuda.empty_cache()
+
+    per_layer = {}
+    if not args.no_layers:
+        for name, L in workloads.LAYERS.items():
+            variants = [(name, None)]
+            if L.norm_silu:
+                variants.append((name + "_ncdhw", cv.NCDHW))
+            for vname, lay in variants:
+                c = Case(L, torch, cv, layout=lay)
+                lms, _ = time_case(c, max(5, args.steps), 3, torch)
+                lt = L.flops(live=True) / (lms * 1e-3) / 1e12
+                io = (L.m * L.cin * 0 + np.prod(L.x_shape) + L.m * L.cout
+                      + 27 * L.cin * L.cout + (L.m * L.cout if L.residual else 0)) * 2
+                per_layer[vname] = {
+                    "us": round(lms * 1e3, 2), "tflops": round(lt, 2),
+                    "pct_peak": round(100 * lt / PEAK_BF16_TFLOPS, 2),
+                    "algorithmic_gbs": round(io / (lms * 1e-3) / 1e9, 1),
+                    "gflop": round(L.flops(live=True) / 1e9, 3), "plan": c.plan}
+                del c
+                torch.cuda.empty_cache()
+        # boundary transpose on its own (NCDHW -> NDHWC of the fused layer's input)
+        L = workloads.LAYERS["wan_fused_160to320"]
+        n, d, h, w, c = L.x_shape
+        src = torch.zeros((n, c, d, h, w), dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty((n, d, h, w, c), dtype=torch.bfloat16, device="cuda")
+        tcase = lambda: cv.conv3d_transpose(src, cv.NCDHW, dst, n, c, d, h, w)
+        tms, _ = time_case(tcase, max(5, args.steps), 3, torch)
+        per_layer["transpose_ncdhw_to_ndhwc_" + L.name] = {
+            "us": round(tms * 1e3, 2), "gbs": round(2 * src.numel() * 2 / (tms * 1e-3) / 1e9, 1),
+            "pct_hbm": round(100 * 2 * src.numel() * 2 / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head, args.cpu_seconds)
+
+    out = {
+        "metric": "conv3d bf16 TFLOP/s per layer shape and % of MI355X bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": describe(head), "gflop_per_step": round(flops / 1e9, 2),
+                   "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "per_layer": per_layer,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

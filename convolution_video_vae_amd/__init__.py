@@ -1,0 +1,178 @@
+"""Python binding of the MI355X Conv3D library (libconv3d_mi355x.so).
+
+Argument marshalling only: every function below forwards to the C entry
+point of the same name in include/conv3d.h, passing device pointers of
+PyTorch tensors and the current HIP stream. PyTorch supplies device memory
+and streams; all computation runs in the library's HIP kernels. There is no
+fallback: if the shared library is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconv3d_mi355x.so")
+
+NCDHW = 0
+NDHWC = 1
+
+EPI_BIAS = 1
+EPI_RESIDUAL = 2
+EPI_L2NORM_SILU = 4
+EPI_RESIDUAL_OUT = 8
+
+STATUS = {0: "CONV3D_OK", 1: "CONV3D_ERR_NULL", 2: "CONV3D_ERR_SHAPE", 3: "CONV3D_ERR_ALIGN",
+          4: "CONV3D_ERR_OVERLAP", 5: "CONV3D_ERR_WORKSPACE", 6: "CONV3D_ERR_UNSUPPORTED",
+          7: "CONV3D_ERR_HIP"}
+
+EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_dims",
+            "conv3d_workspace_bytes", "conv3d_fwd", "conv3d_transpose", "conv3d_status_str",
+            "conv3d_plan_describe")
+
+
+class Conv3dError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+class conv3d_desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("d", ctypes.c_int), ("h", ctypes.c_int), ("w", ctypes.c_int),
+                ("cin", ctypes.c_int), ("cout", ctypes.c_int),
+                ("stride", ctypes.c_int * 3), ("pad_lo", ctypes.c_int * 3),
+                ("pad_hi", ctypes.c_int * 3), ("layout", ctypes.c_int),
+                ("out_layout", ctypes.c_int), ("split_k", ctypes.c_int)]
+
+
+class conv3d_epilogue(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint), ("bias", ctypes.c_void_p),
+                ("residual", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("residual_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python convolution_video_vae_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        pd, pe = ctypes.POINTER(conv3d_desc), ctypes.POINTER(conv3d_epilogue)
+        L.conv3d_packed_weight_bytes.restype = sz
+        L.conv3d_packed_weight_bytes.argtypes = [i, i]
+        L.conv3d_pack_weight.restype = i
+        L.conv3d_pack_weight.argtypes = [vp, vp, i, i, vp]
+        L.conv3d_output_dims.restype = i
+        L.conv3d_output_dims.argtypes = [pd, ctypes.POINTER(ctypes.c_int * 3)]
+        L.conv3d_workspace_bytes.restype = i
+        L.conv3d_workspace_bytes.argtypes = [pd, pe, ctypes.POINTER(sz)]
+        L.conv3d_fwd.restype = i
+        L.conv3d_fwd.argtypes = [pd, vp, vp, pe, vp, vp, sz, vp]
+        L.conv3d_transpose.restype = i
+        L.conv3d_transpose.argtypes = [vp, i, vp, i, i, i, i, i, vp]
+        L.conv3d_status_str.restype = ctypes.c_char_p
+        L.conv3d_status_str.argtypes = [i]
+        L.conv3d_plan_describe.restype = i
+        L.conv3d_plan_describe.argtypes = [pd, pe, ctypes.c_char_p, sz]
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().conv3d_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise Conv3dError(status, what)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_desc(x_shape: Sequence[int], cout: int, *, stride=(1, 1, 1), pad_lo=(0, 0, 0),
+              pad_hi=(0, 0, 0), layout=NDHWC, out_layout=None, split_k=0) -> conv3d_desc:
+    """Descriptor from the input shape in `layout` (NDHWC or NCDHW)."""
+    if layout == NDHWC:
+        n, d, h, w, cin = x_shape
+    else:
+        n, cin, d, h, w = x_shape
+    return conv3d_desc(n, d, h, w, cin, cout, (ctypes.c_int * 3)(*stride),
+                       (ctypes.c_int * 3)(*pad_lo), (ctypes.c_int * 3)(*pad_hi), layout,
+                       layout if out_layout is None else out_layout, split_k)
+
+
+def make_epilogue(bias=None, residual=None, gamma=None, residual_out=None,
+                  norm_silu=False) -> conv3d_epilogue:
+    flags = 0
+    flags |= EPI_BIAS if bias is not None else 0
+    flags |= EPI_RESIDUAL if residual is not None else 0
+    flags |= EPI_L2NORM_SILU if norm_silu else 0
+    flags |= EPI_RESIDUAL_OUT if residual_out is not None else 0
+    return conv3d_epilogue(flags, _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(residual_out))
+
+
+# --------------------------------------------------------------------------- C entry points
+
+def conv3d_packed_weight_bytes(cout: int, cin: int) -> int:
+    return int(lib().conv3d_packed_weight_bytes(cout, cin))
+
+
+def conv3d_pack_weight(w_oidhw, w_packed, cout: int, cin: int, stream=None) -> None:
+    _check(lib().conv3d_pack_weight(_ptr(w_oidhw), _ptr(w_packed), cout, cin, _stream(stream)),
+           "conv3d_pack_weight")
+
+
+def conv3d_output_dims(desc: conv3d_desc):
+    out = (ctypes.c_int * 3)()
+    _check(lib().conv3d_output_dims(ctypes.byref(desc), ctypes.byref(out)), "conv3d_output_dims")
+    return tuple(out)
+
+
+def conv3d_workspace_bytes(desc: conv3d_desc, epi: Optional[conv3d_epilogue] = None) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().conv3d_workspace_bytes(ctypes.byref(desc), ctypes.byref(epi) if epi else None,
+                                        ctypes.byref(out)), "conv3d_workspace_bytes")
+    return int(out.value)
+
+
+def conv3d_fwd(desc: conv3d_desc, x, w_packed, epi: Optional[conv3d_epilogue], y,
+               workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    if workspace is not None and not workspace_bytes and not isinstance(workspace, int):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().conv3d_fwd(ctypes.byref(desc), _ptr(x), _ptr(w_packed),
+                            ctypes.byref(epi) if epi else None, _ptr(y), _ptr(workspace),
+                            workspace_bytes, _stream(stream)), "conv3d_fwd")
+
+
+def conv3d_transpose(src, src_layout: int, dst, n: int, c: int, d: int, h: int, w: int,
+                     stream=None) -> None:
+    _check(lib().conv3d_transpose(_ptr(src), src_layout, _ptr(dst), n, c, d, h, w,
+                                  _stream(stream)), "conv3d_transpose")
+
+
+def conv3d_plan_describe(desc: conv3d_desc, epi: Optional[conv3d_epilogue] = None) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(lib().conv3d_plan_describe(ctypes.byref(desc), ctypes.byref(epi) if epi else None,
+                                      buf, 512), "conv3d_plan_describe")
+    return buf.value.decode()

@@ -1,0 +1,42 @@
+"""Build the Conv3D HIP library for gfx950 in-tree.
+
+Produces convolution_video_vae_amd/libconv3d_mi355x.so from csrc/ with hipcc
+(cross-compiles without a GPU). Packed-fp32 instructions are disabled for all
+device code.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libconv3d_mi355x.so")
+BUILD = os.path.join(HERE, "_build")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    kobj = os.path.join(BUILD, "conv3d_kernels.o")
+    aobj = os.path.join(BUILD, "conv3d_api.o")
+    _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-c",
+          *DEVICE_FLAGS, "-Wall", os.path.join(CSRC, "conv3d_kernels.hip"), "-o", kobj], verbose)
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-c", "-Wall", "-Wextra",
+          os.path.join(CSRC, "conv3d_api.cpp"), "-o", aobj], verbose)
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", kobj, aobj, "-o", OUT + ".tmp"],
+         verbose)
+    os.replace(OUT + ".tmp", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

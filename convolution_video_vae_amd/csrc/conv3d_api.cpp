@@ -1,0 +1,394 @@
+// C-ABI of the Conv3D library: argument checks, planning and dispatch.
+//
+// Every check here runs on the host before anything is enqueued, so a bad
+// call never launches work or touches an output (cuDNN page,
+// "Requirements": aligned operands, outputs that overlap no operand, no
+// silent fallback for an unsupported case).
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/conv3d.h"
+#include "conv3d_internal.h"
+
+using namespace conv3d;
+
+namespace {
+
+constexpr long long kMaxTensorBytes = (1LL << 31) - 64;  // 32-bit buffer offsets
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+Range range_of(const void* p, long long bytes) {
+  Range r;
+  if (p && bytes > 0) {
+    r.lo = (uintptr_t)p;
+    r.hi = r.lo + (uintptr_t)bytes;
+  }
+  return r;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int out_extent(int in, int s, int lo, int hi) {
+  const int span = in + lo + hi - 3;
+  return span < 0 ? 0 : span / s + 1;
+}
+
+// Everything derived from a descriptor.
+struct Problem {
+  int n, d, h, w, cin, cout;
+  int sd, sh, sw, pd, ph, pw;
+  int Do, Ho, Wo;
+  long long M;
+  long long x_bytes, y_bytes;
+  int layout, out_layout;
+  unsigned flags;
+};
+
+struct Plan {
+  TileCfg cfg;
+  int mode;        // EPI_STORE / EPI_NORM / EPI_PARTIAL
+  int splits;      // >1 or reduce needed -> partial + reduce
+  bool reduce;     // a reduce kernel finishes the epilogue
+  int steps;       // 27 * CC
+  int steps_per_split;
+  int m_tiles, n_tiles;
+  long long grid;
+  // workspace carve (bytes, 256-aligned offsets)
+  size_t off_x, off_y, off_res, off_rout, off_part, total;
+};
+
+conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
+  if (!d) return CONV3D_ERR_NULL;
+  if (d->n <= 0 || d->d <= 0 || d->h <= 0 || d->w <= 0 || d->cin <= 0 || d->cout <= 0)
+    return CONV3D_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i) {
+    if (d->stride[i] <= 0 || d->pad_lo[i] < 0 || d->pad_hi[i] < 0) return CONV3D_ERR_SHAPE;
+  }
+  if (d->layout != CONV3D_NCDHW && d->layout != CONV3D_NDHWC) return CONV3D_ERR_SHAPE;
+  if (d->out_layout != CONV3D_NCDHW && d->out_layout != CONV3D_NDHWC) return CONV3D_ERR_SHAPE;
+  if (d->split_k < 0) return CONV3D_ERR_SHAPE;
+  pr->n = d->n; pr->d = d->d; pr->h = d->h; pr->w = d->w;
+  pr->cin = d->cin; pr->cout = d->cout;
+  pr->sd = d->stride[0]; pr->sh = d->stride[1]; pr->sw = d->stride[2];
+  pr->pd = d->pad_lo[0]; pr->ph = d->pad_lo[1]; pr->pw = d->pad_lo[2];
+  pr->Do = out_extent(d->d, d->stride[0], d->pad_lo[0], d->pad_hi[0]);
+  pr->Ho = out_extent(d->h, d->stride[1], d->pad_lo[1], d->pad_hi[1]);
+  pr->Wo = out_extent(d->w, d->stride[2], d->pad_lo[2], d->pad_hi[2]);
+  if (pr->Do < 1 || pr->Ho < 1 || pr->Wo < 1) return CONV3D_ERR_SHAPE;
+  pr->M = (long long)d->n * pr->Do * pr->Ho * pr->Wo;
+  pr->x_bytes = (long long)d->n * d->d * d->h * d->w * d->cin * 2;
+  pr->y_bytes = pr->M * d->cout * 2;
+  pr->layout = d->layout;
+  pr->out_layout = d->out_layout;
+  if (d->cin % 8 != 0) return CONV3D_ERR_ALIGN;
+  if (d->cout % 16 != 0) return CONV3D_ERR_UNSUPPORTED;
+  if (pr->x_bytes > kMaxTensorBytes || pr->y_bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
+  if (pr->M > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
+  return CONV3D_OK;
+}
+
+conv3d_status check_epi(const conv3d_epilogue* e, Problem* pr) {
+  pr->flags = e ? e->flags : 0u;
+  const unsigned f = pr->flags;
+  if (f & ~(unsigned)(F_BIAS | F_RESIDUAL | F_NORM | F_RESIDUAL_OUT)) return CONV3D_ERR_UNSUPPORTED;
+  if ((f & F_RESIDUAL_OUT) && !(f & F_RESIDUAL)) return CONV3D_ERR_UNSUPPORTED;
+  if ((f & F_BIAS) && !e->bias) return CONV3D_ERR_NULL;
+  if ((f & F_RESIDUAL) && !e->residual) return CONV3D_ERR_NULL;
+  if ((f & F_NORM) && !e->gamma) return CONV3D_ERR_NULL;
+  if ((f & F_RESIDUAL_OUT) && !e->residual_out) return CONV3D_ERR_NULL;
+  if ((f & F_BIAS) && !aligned16(e->bias)) return CONV3D_ERR_ALIGN;
+  if ((f & F_RESIDUAL) && !aligned16(e->residual)) return CONV3D_ERR_ALIGN;
+  if ((f & F_NORM) && !aligned16(e->gamma)) return CONV3D_ERR_ALIGN;
+  if ((f & F_RESIDUAL_OUT) && !aligned16(e->residual_out)) return CONV3D_ERR_ALIGN;
+  if ((f & F_NORM) && pr->cout > 2048) return CONV3D_ERR_UNSUPPORTED;
+  return CONV3D_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Kernel choice. Large-M layers run one work-group per (pixel tile, channel
+// tile); small-M / large-K layers cut K into slices whose fp32 partials a
+// second kernel sums in fixed order.
+void make_plan(const Problem& pr, int split_req, Plan* pl) {
+  const int cc = (pr.cin + 31) / 32;
+  pl->steps = 27 * cc;
+  const bool norm = (pr.flags & F_NORM) != 0;
+  TileCfg store_cfg;
+  if (pr.cout % 128 == 0) store_cfg = {4, 1, 4, 8};
+  else if (pr.cout % 96 == 0) store_cfg = {4, 1, 4, 6};
+  else store_cfg = {4, 1, 4, 4};
+  TileCfg part_cfg = {4, 1, 2, store_cfg.j};
+
+  // Fused-norm kernels hold the whole channel row of a pixel in one group.
+  TileCfg norm_cfg = {0, 0, 0, 0};
+  if (norm) {
+    const TileCfg cands[] = {{2, 2, 2, 10}, {2, 2, 2, 5}, {4, 1, 2, 8}};
+    for (const TileCfg& c : cands)
+      if (c.bn() == pr.cout) norm_cfg = c;
+  }
+
+  const long long m_tiles_store = (pr.M + store_cfg.bm() - 1) / store_cfg.bm();
+  const long long n_tiles_store = (pr.cout + store_cfg.bn() - 1) / store_cfg.bn();
+  int splits = 1;
+  if (split_req > 0) {
+    splits = split_req;
+  } else if (m_tiles_store * n_tiles_store < 256) {
+    // Too few tiles to fill 256 CUs: cut K so there are about two groups
+    // per CU, keeping at least 8 K steps per slice.
+    const long long tiles = ((pr.M + part_cfg.bm() - 1) / part_cfg.bm()) *
+                            ((pr.cout + part_cfg.bn() - 1) / part_cfg.bn());
+    splits = (int)std::max(1LL, std::min<long long>((512 + tiles - 1) / tiles, pl->steps / 8));
+  }
+  splits = std::max(1, std::min(splits, pl->steps));
+  pl->steps_per_split = (pl->steps + splits - 1) / splits;
+  splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
+  pl->splits = splits;
+
+  if (splits > 1 || (norm && norm_cfg.wm == 0)) {
+    pl->cfg = part_cfg;
+    pl->mode = EPI_PARTIAL;
+    pl->reduce = true;
+  } else if (norm) {
+    pl->cfg = norm_cfg;
+    pl->mode = EPI_NORM;
+    pl->reduce = false;
+  } else {
+    pl->cfg = store_cfg;
+    pl->mode = EPI_STORE;
+    pl->reduce = false;
+  }
+  pl->m_tiles = (int)((pr.M + pl->cfg.bm() - 1) / pl->cfg.bm());
+  pl->n_tiles = (pr.cout + pl->cfg.bn() - 1) / pl->cfg.bn();
+  pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;
+
+  // Workspace: NDHWC copies for NCDHW boundaries, then split-K partials.
+  size_t off = 0;
+  pl->off_x = pl->off_y = pl->off_res = pl->off_rout = pl->off_part = 0;
+  if (pr.layout == CONV3D_NCDHW) { pl->off_x = off; off = align256(off + pr.x_bytes); }
+  if (pr.out_layout == CONV3D_NCDHW) {
+    pl->off_y = off; off = align256(off + pr.y_bytes);
+    if (pr.flags & F_RESIDUAL) { pl->off_res = off; off = align256(off + pr.y_bytes); }
+    if (pr.flags & F_RESIDUAL_OUT) { pl->off_rout = off; off = align256(off + pr.y_bytes); }
+  }
+  if (pl->reduce) {
+    pl->off_part = off;
+    off = align256(off + (size_t)pl->splits * pr.M * pr.cout * 4);
+  }
+  pl->total = off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* conv3d_status_str(conv3d_status s) {
+  switch (s) {
+    case CONV3D_OK: return "ok";
+    case CONV3D_ERR_NULL: return "required pointer is NULL";
+    case CONV3D_ERR_SHAPE: return "invalid shape, stride, padding or layout";
+    case CONV3D_ERR_ALIGN: return "pointer not 16-byte aligned or cin not a multiple of 8";
+    case CONV3D_ERR_OVERLAP: return "an output overlaps an operand or another output";
+    case CONV3D_ERR_WORKSPACE: return "workspace missing or too small";
+    case CONV3D_ERR_UNSUPPORTED: return "unsupported configuration (no fallback)";
+    case CONV3D_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t conv3d_packed_weight_bytes(int cout, int cin) {
+  if (cout <= 0 || cin <= 0) return 0;
+  return (size_t)27 * ((cin + 31) / 32) * 32 * (size_t)cout * 2;
+}
+
+conv3d_status conv3d_pack_weight(const void* w_oidhw, void* w_packed, int cout, int cin,
+                                 void* stream) {
+  if (!w_oidhw || !w_packed) return CONV3D_ERR_NULL;
+  if (cout <= 0 || cin <= 0) return CONV3D_ERR_SHAPE;
+  if (!aligned16(w_oidhw) || !aligned16(w_packed)) return CONV3D_ERR_ALIGN;
+  const long long in_bytes = 27LL * cout * cin * 2;
+  if (overlaps(range_of(w_oidhw, in_bytes),
+               range_of(w_packed, (long long)conv3d_packed_weight_bytes(cout, cin))))
+    return CONV3D_ERR_OVERLAP;
+  const int rc = launch_pack_weight((const uint16_t*)w_oidhw, (uint16_t*)w_packed, cout, cin, stream);
+  return rc ? CONV3D_ERR_HIP : CONV3D_OK;
+}
+
+conv3d_status conv3d_output_dims(const conv3d_desc* desc, int out_dhw[3]) {
+  if (!out_dhw) return CONV3D_ERR_NULL;
+  Problem pr;
+  const conv3d_status st = check_desc(desc, &pr);
+  if (st == CONV3D_ERR_NULL || st == CONV3D_ERR_SHAPE) return st;
+  out_dhw[0] = pr.Do; out_dhw[1] = pr.Ho; out_dhw[2] = pr.Wo;
+  return CONV3D_OK;
+}
+
+conv3d_status conv3d_workspace_bytes(const conv3d_desc* desc, const conv3d_epilogue* epi,
+                                     size_t* bytes) {
+  if (!bytes) return CONV3D_ERR_NULL;
+  Problem pr;
+  conv3d_status st = check_desc(desc, &pr);
+  if (st != CONV3D_OK) return st;
+  Problem pe = pr;
+  pe.flags = epi ? epi->flags : 0u;
+  Plan pl;
+  make_plan(pe, desc->split_k, &pl);
+  *bytes = pl.total;
+  return CONV3D_OK;
+}
+
+conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogue* epi,
+                                   char* buf, size_t len) {
+  Problem pr;
+  conv3d_status st = check_desc(desc, &pr);
+  if (st != CONV3D_OK) return st;
+  pr.flags = epi ? epi->flags : 0u;
+  Plan pl;
+  make_plan(pr, desc->split_k, &pl);
+  if (buf && len) {
+    static const char* names[] = {"store", "norm", "partial"};
+    snprintf(buf, len,
+             "igemm wm=%d wn=%d p=%d j=%d bm=%d bn=%d mode=%s splits=%d steps=%d grid=%lld "
+             "reduce=%d workspace=%zu",
+             pl.cfg.wm, pl.cfg.wn, pl.cfg.p, pl.cfg.j, pl.cfg.bm(), pl.cfg.bn(), names[pl.mode],
+             pl.splits, pl.steps, pl.grid, (int)pl.reduce, pl.total);
+  }
+  return CONV3D_OK;
+}
+
+conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_packed,
+                         const conv3d_epilogue* epi, void* y, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Problem pr;
+  conv3d_status st = check_desc(desc, &pr);
+  if (st != CONV3D_OK) return st;
+  if (!x || !w_packed || !y) return CONV3D_ERR_NULL;
+  st = check_epi(epi, &pr);
+  if (st != CONV3D_OK) return st;
+  if (!aligned16(x) || !aligned16(w_packed) || !aligned16(y)) return CONV3D_ERR_ALIGN;
+
+  Plan pl;
+  make_plan(pr, desc->split_k, &pl);
+  if (pl.total > 0) {
+    if (!workspace || workspace_bytes < pl.total) return CONV3D_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CONV3D_ERR_ALIGN;
+  }
+
+  // Outputs (y, residual_out, workspace) must not overlap any operand or
+  // each other.
+  const unsigned f = pr.flags;
+  const Range rx = range_of(x, pr.x_bytes);
+  const Range rw = range_of(w_packed, (long long)conv3d_packed_weight_bytes(pr.cout, pr.cin));
+  const Range ry = range_of(y, pr.y_bytes);
+  const Range rb = (f & F_BIAS) ? range_of(epi->bias, 4LL * pr.cout) : Range();
+  const Range rr = (f & F_RESIDUAL) ? range_of(epi->residual, pr.y_bytes) : Range();
+  const Range rg = (f & F_NORM) ? range_of(epi->gamma, 2LL * pr.cout) : Range();
+  const Range ro = (f & F_RESIDUAL_OUT) ? range_of(epi->residual_out, pr.y_bytes) : Range();
+  const Range rs = range_of(workspace, (long long)pl.total);
+  const Range outs[] = {ry, ro, rs};
+  const Range ins[] = {rx, rw, rb, rr, rg};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
+  if (overlaps(ry, ro) || overlaps(ry, rs) || overlaps(ro, rs)) return CONV3D_ERR_OVERLAP;
+
+  char* ws = (char*)workspace;
+  const uint16_t* xin = (const uint16_t*)x;
+  uint16_t* yout = (uint16_t*)y;
+  const uint16_t* res = (f & F_RESIDUAL) ? (const uint16_t*)epi->residual : nullptr;
+  uint16_t* rout = (f & F_RESIDUAL_OUT) ? (uint16_t*)epi->residual_out : nullptr;
+  const int S = pr.d * pr.h * pr.w;
+  const int So = pr.Do * pr.Ho * pr.Wo;
+
+  if (pr.layout == CONV3D_NCDHW) {
+    uint16_t* xt = (uint16_t*)(ws + pl.off_x);
+    if (launch_transpose(xin, xt, pr.n, pr.cin, S, stream)) return CONV3D_ERR_HIP;
+    xin = xt;
+  }
+  if (pr.out_layout == CONV3D_NCDHW) {
+    yout = (uint16_t*)(ws + pl.off_y);
+    if (res) {
+      uint16_t* rt = (uint16_t*)(ws + pl.off_res);
+      if (launch_transpose(res, rt, pr.n, pr.cout, So, stream)) return CONV3D_ERR_HIP;
+      res = rt;
+    }
+    if (rout) rout = (uint16_t*)(ws + pl.off_rout);
+  }
+
+  IgemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = xin;
+  a.wp = (const uint16_t*)w_packed;
+  a.y = yout;
+  a.partial = pl.reduce ? (float*)(ws + pl.off_part) : nullptr;
+  a.bias = (f & F_BIAS) ? epi->bias : nullptr;
+  a.residual = res;
+  a.gamma = (f & F_NORM) ? (const uint16_t*)epi->gamma : nullptr;
+  a.residual_out = rout;
+  a.N = pr.n; a.D = pr.d; a.H = pr.h; a.W = pr.w; a.Cin = pr.cin; a.Cout = pr.cout;
+  a.Do = pr.Do; a.Ho = pr.Ho; a.Wo = pr.Wo;
+  a.sd = pr.sd; a.sh = pr.sh; a.sw = pr.sw;
+  a.pd = pr.pd; a.ph = pr.ph; a.pw = pr.pw;
+  a.CC = (pr.cin + 31) / 32;
+  a.M = (int)pr.M;
+  a.m_tiles = pl.m_tiles; a.n_tiles = pl.n_tiles; a.splits = pl.splits;
+  a.steps_per_split = pl.steps_per_split;
+  a.flags = pl.reduce ? 0u : f;
+  a.x_bytes = (unsigned)pr.x_bytes;
+  a.sqrt_c = sqrtf((float)pr.cout);
+  if (pl.grid > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
+  const int rc = launch_igemm(pl.cfg, pl.mode, a, (int)pl.grid, stream);
+  if (rc) return rc < 0 ? CONV3D_ERR_UNSUPPORTED : CONV3D_ERR_HIP;
+
+  if (pl.reduce) {
+    ReduceArgs r;
+    r.partial = a.partial;
+    r.y = yout;
+    r.bias = a.bias;
+    r.residual = res;
+    r.gamma = a.gamma;
+    r.residual_out = rout;
+    r.M = (int)pr.M;
+    r.Cout = pr.cout;
+    r.splits = pl.splits;
+    r.flags = f;
+    r.sqrt_c = a.sqrt_c;
+    if (launch_reduce(r, stream)) return CONV3D_ERR_HIP;
+  }
+
+  if (pr.out_layout == CONV3D_NCDHW) {
+    if (launch_transpose(yout, (uint16_t*)y, pr.n, So, pr.cout, stream)) return CONV3D_ERR_HIP;
+    if (rout && launch_transpose(rout, (uint16_t*)epi->residual_out, pr.n, So, pr.cout, stream))
+      return CONV3D_ERR_HIP;
+  }
+  return CONV3D_OK;
+}
+
+conv3d_status conv3d_transpose(const void* src, int src_layout, void* dst, int n, int c, int d,
+                               int h, int w, void* stream) {
+  if (!src || !dst) return CONV3D_ERR_NULL;
+  if (n <= 0 || c <= 0 || d <= 0 || h <= 0 || w <= 0) return CONV3D_ERR_SHAPE;
+  if (src_layout != CONV3D_NCDHW && src_layout != CONV3D_NDHWC) return CONV3D_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return CONV3D_ERR_ALIGN;
+  const long long s = (long long)d * h * w;
+  const long long bytes = (long long)n * c * s * 2;
+  if (s > 0x7fffffffLL || bytes > (1LL << 40)) return CONV3D_ERR_UNSUPPORTED;
+  if (overlaps(range_of(src, bytes), range_of(dst, bytes))) return CONV3D_ERR_OVERLAP;
+  const int rc = (src_layout == CONV3D_NCDHW)
+                     ? launch_transpose((const uint16_t*)src, (uint16_t*)dst, n, c, (int)s, stream)
+                     : launch_transpose((const uint16_t*)src, (uint16_t*)dst, n, (int)s, c, stream);
+  return rc ? CONV3D_ERR_HIP : CONV3D_OK;
+}
+
+}  // extern "C"

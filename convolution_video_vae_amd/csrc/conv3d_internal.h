@@ -1,0 +1,74 @@
+// Internal interface between the C-ABI layer (argument checks, planning,
+// workspace carving) and the HIP kernels. Not installed; the public surface
+// is include/conv3d.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace conv3d {
+
+// Epilogue modes of the implicit-GEMM kernel.
+enum EpiMode : int {
+  EPI_STORE = 0,    // bf16 out = value (bias / residual / residual_out per flags)
+  EPI_NORM = 1,     // bf16 out = full contract with channel-row L2 norm + SiLU
+  EPI_PARTIAL = 2,  // fp32 partial sums of one K slice (split-K)
+};
+
+// Epilogue flag bits (same values as the public CONV3D_EPI_* flags).
+enum : unsigned { F_BIAS = 1u, F_RESIDUAL = 2u, F_NORM = 4u, F_RESIDUAL_OUT = 8u };
+
+// Everything one implicit-GEMM launch needs; passed by value as the kernel
+// argument. All tensors NDHWC.
+struct IgemmArgs {
+  const uint16_t* x;        // [N][D][H][W][Cin]
+  const uint16_t* wp;       // packed [27][CC][Cout][32]
+  uint16_t* y;              // [M][Cout]
+  float* partial;           // [splits][M][Cout] (EPI_PARTIAL)
+  const float* bias;        // [Cout]
+  const uint16_t* residual; // [M][Cout]
+  const uint16_t* gamma;    // [Cout]
+  uint16_t* residual_out;   // [M][Cout]
+  int N, D, H, W, Cin, Cout;
+  int Do, Ho, Wo;
+  int sd, sh, sw;           // stride
+  int pd, ph, pw;           // leading zero pad
+  int CC;                   // 32-channel K steps per tap = ceil(Cin / 32)
+  int M;                    // output pixels
+  int m_tiles, n_tiles, splits;
+  int steps_per_split;      // K steps (of 32 channels) per split
+  unsigned flags;
+  unsigned x_bytes;         // size of x, for the buffer range check
+  float sqrt_c;             // sqrtf((float)Cout)
+};
+
+struct ReduceArgs {
+  const float* partial;     // [splits][M][Cout]
+  uint16_t* y;
+  const float* bias;
+  const uint16_t* residual;
+  const uint16_t* gamma;
+  uint16_t* residual_out;
+  int M, Cout, splits;
+  unsigned flags;
+  float sqrt_c;
+};
+
+// A kernel configuration: WM x WN waves, each wave P pixel blocks x J
+// channel blocks of 16 (so BM = 16*P*WM pixels, BN = 16*J*WN channels).
+struct TileCfg {
+  int wm, wn, p, j;
+  int bm() const { return 16 * p * wm; }
+  int bn() const { return 16 * j * wn; }
+};
+
+// Launchers (conv3d_kernels.hip). Each returns 0 on success or the HIP
+// error code of the launch. `stream` is a hipStream_t.
+int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, void* stream);
+int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int a, int b, void* stream);
+// Returns -1 if no kernel is compiled for (cfg, mode).
+int launch_igemm(const TileCfg& cfg, int mode, const IgemmArgs& args, int grid, void* stream);
+bool igemm_has_config(const TileCfg& cfg, int mode);
+int launch_reduce(const ReduceArgs& args, void* stream);
+
+}  // namespace conv3d

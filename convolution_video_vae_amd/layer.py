@@ -1,0 +1,81 @@
+"""Pack-once / execute-many wrapper around the C entry points.
+
+The cuDNN page ("Requirements", "Weight Packing") describes the usage this
+mirrors: pack a checkpoint weight once, keep the packed copy, and execute
+with preallocated buffers on the caller's stream. PyTorch only allocates
+the device buffers here; every step runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_output_dims, conv3d_pack_weight,
+               conv3d_packed_weight_bytes, conv3d_workspace_bytes, make_desc, make_epilogue)
+
+
+def pack_weight(w_oidhw: torch.Tensor, stream=None) -> torch.Tensor:
+    """OIDHW bf16 [Cout][Cin][3][3][3] on the GPU -> packed weight buffer."""
+    if w_oidhw.dtype != torch.bfloat16 or not w_oidhw.is_cuda or w_oidhw.dim() != 5:
+        raise ValueError("weight must be a 5-D bf16 CUDA tensor")
+    cout, cin = w_oidhw.shape[:2]
+    w = w_oidhw.contiguous()
+    out = torch.empty(conv3d_packed_weight_bytes(cout, cin) // 2, dtype=torch.bfloat16,
+                      device=w.device)
+    conv3d_pack_weight(w, out, cout, cin, stream)
+    return out
+
+
+class Conv3d:
+    """One 3x3x3 bf16 conv layer with a packed weight and fixed shapes."""
+
+    def __init__(self, weight: torch.Tensor, x_shape: Sequence[int], *, stride=(1, 1, 1),
+                 pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), layout: int = NDHWC,
+                 out_layout: Optional[int] = None, split_k: int = 0,
+                 bias: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
+                 norm_silu: bool = False, residual: bool = False, residual_out: bool = False):
+        self.cout, self.cin = int(weight.shape[0]), int(weight.shape[1])
+        self.layout = layout
+        self.out_layout = layout if out_layout is None else out_layout
+        self.x_shape = tuple(int(v) for v in x_shape)
+        self.desc = make_desc(self.x_shape, self.cout, stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
+                              layout=layout, out_layout=self.out_layout, split_k=split_k)
+        self.out_dhw = conv3d_output_dims(self.desc)
+        n = self.x_shape[0]
+        if self.out_layout == NDHWC:
+            self.out_shape = (n,) + self.out_dhw + (self.cout,)
+        else:
+            self.out_shape = (n, self.cout) + self.out_dhw
+        self.device = weight.device
+        self.w_packed = pack_weight(weight)
+        self.bias = None if bias is None else bias.to(device=self.device, dtype=torch.float32).contiguous()
+        self.gamma = None if gamma is None else gamma.to(device=self.device, dtype=torch.bfloat16).contiguous()
+        self.norm_silu = norm_silu
+        self.has_residual = residual
+        self.has_residual_out = residual_out
+        probe = make_epilogue(bias=self.bias, gamma=self.gamma, norm_silu=norm_silu)
+        probe.flags |= (2 if residual else 0) | (8 if residual_out else 0)
+        self.workspace_bytes = conv3d_workspace_bytes(self.desc, probe)
+        self.workspace = (torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+                          if self.workspace_bytes else None)
+
+    def new_output(self) -> torch.Tensor:
+        return torch.empty(self.out_shape, dtype=torch.bfloat16, device=self.device)
+
+    def __call__(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                 y: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+        if tuple(x.shape) != self.x_shape or x.dtype != torch.bfloat16 or not x.is_contiguous():
+            raise ValueError(f"x must be a contiguous bf16 tensor of shape {self.x_shape}")
+        if self.has_residual != (residual is not None):
+            raise ValueError("residual presence differs from construction")
+        if self.has_residual_out != (residual_out is not None):
+            raise ValueError("residual_out presence differs from construction")
+        if y is None:
+            y = self.new_output()
+        epi = make_epilogue(bias=self.bias, residual=residual, gamma=self.gamma,
+                            residual_out=residual_out, norm_silu=self.norm_silu)
+        conv3d_fwd(self.desc, x, self.w_packed, epi if epi.flags else None, y, self.workspace,
+                   self.workspace_bytes, stream)
+        return y

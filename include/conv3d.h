@@ -1,0 +1,164 @@
+/*
+ * conv3d.h — bf16 3x3x3 Conv3D for causal video-VAE layers on AMD Instinct
+ * MI355X (gfx950), channels-last (NDHWC), computed as an implicit GEMM:
+ *
+ *   M = N*Do*Ho*Wo output pixels, N = Cout, K = 27*Cin, fp32 accumulation.
+ *
+ * Sources of the operation (cited by page title and section):
+ *  - "conv3d_implicit — accept and emit NDHWC so chained convs skip the layout
+ *    round-trip" (FlyDSL issue): the layout / out_layout parameters ("Ask") and
+ *    the split-K and non-split epilogues (maintainer reply).
+ *  - "Add Qwen-Image VAE classic conv shapes to conv3d tests" (FlyDSL PR):
+ *    causal padding, time (2 before, 0 after) and H/W (1, 1) ("T=1
+ *    degeneration"); the zero pad (0,1,0,1) before a stride-2 conv ("Test
+ *    shapes", table 2); packing a weight once instead of per call (commit
+ *    "Stop the conv 1D/2D entry points from repacking weights every launch").
+ *  - "Fused Conv3D + Bias + Residual + RMSNorm + SiLU" (cuDNN frontend):
+ *    the post-operation contract and its rounding points ("Operation
+ *    Contract"), operand rules ("Requirements") and weight packing once per
+ *    weight ("Weight Packing").
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to bf16 data (raw 16-bit patterns),
+ *    except `bias`, which is fp32. All must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every entry point
+ *    only enqueues work on `stream` and returns; nothing is synchronised.
+ *  - The caller owns every buffer. The library allocates nothing, keeps no
+ *    pointer after a call returns and holds no mutable global state, so calls
+ *    from several host threads are safe and calls are graph-capturable.
+ *  - Argument checks run before anything is enqueued: on an error the call
+ *    returns a non-zero status and neither launches work nor writes any
+ *    output. A failed launch returns CONV3D_ERR_HIP; faults inside a kernel
+ *    surface asynchronously on `stream`.
+ */
+#ifndef CONV3D_MI355X_H
+#define CONV3D_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CONV3D_OK = 0,
+  CONV3D_ERR_NULL = 1,        /* a required pointer is NULL */
+  CONV3D_ERR_SHAPE = 2,       /* non-positive size, bad stride/pad, empty output */
+  CONV3D_ERR_ALIGN = 3,       /* pointer not 16-byte aligned, or Cin % 8 != 0 */
+  CONV3D_ERR_OVERLAP = 4,     /* an output overlaps an input or another output */
+  CONV3D_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  CONV3D_ERR_UNSUPPORTED = 6, /* a case this build does not implement (no fallback) */
+  CONV3D_ERR_HIP = 7          /* the HIP runtime refused a launch */
+} conv3d_status;
+
+typedef enum { CONV3D_NCDHW = 0, CONV3D_NDHWC = 1 } conv3d_layout;
+
+/* Epilogue flags (cuDNN page, "Operation Contract"). With B() = bf16
+ * round-to-nearest-even and acc the fp32 accumulator:
+ *   conv  = B(acc)
+ *   main  = B(conv + bias)                      if CONV3D_EPI_BIAS, else conv
+ *   value = B(main + residual)                  if CONV3D_EPI_RESIDUAL, else main
+ *   out   = value                               without CONV3D_EPI_L2NORM_SILU
+ * with CONV3D_EPI_L2NORM_SILU, over the full channel row of each pixel:
+ *   den   = max(sqrt(sum_c value_c^2), 1e-12)  (a clamp, not an added eps)
+ *   out   = B(a / (1 + exp(-a))),  a = B(B(B(value/den) * sqrt(Cout)) * gamma)
+ * CONV3D_EPI_RESIDUAL_OUT additionally writes `value` (the pre-norm sum). */
+enum {
+  CONV3D_EPI_BIAS = 1,
+  CONV3D_EPI_RESIDUAL = 2,
+  CONV3D_EPI_L2NORM_SILU = 4,
+  CONV3D_EPI_RESIDUAL_OUT = 8
+};
+
+/* One convolution. The kernel is fixed at 3x3x3, unit dilation, one group.
+ * Input extents n, d, h, w; output extents follow PyTorch:
+ *   Do = (d + pad_lo[0] + pad_hi[0] - 3) / stride[0] + 1   (likewise Ho, Wo).
+ * Padding is zero padding folded into the input gather; nothing padded is
+ * materialised. Causal time padding is pad_lo[0] = 2, pad_hi[0] = 0; a
+ * pre-padded ("valid") input uses zeros everywhere; the stride-2 downsample
+ * uses pad_lo = {2,0,0}, pad_hi = {0,1,1}. Index order is {d, h, w}.
+ * layout is the input's layout; out_layout that of y, residual and
+ * residual_out. NCDHW input or output costs a transpose through the
+ * workspace, so chained layers should stay NDHWC.
+ * split_k = 0 lets the library choose how many slices the K = 27*Cin sum is
+ * cut into; a positive value forces that many (clamped to the number of
+ * 32-channel K steps). Slices are summed in a fixed order, so results are
+ * deterministic for a given split_k. */
+typedef struct {
+  int n, d, h, w;
+  int cin, cout;
+  int stride[3];
+  int pad_lo[3];
+  int pad_hi[3];
+  int layout;      /* conv3d_layout of x */
+  int out_layout;  /* conv3d_layout of y / residual / residual_out */
+  int split_k;
+} conv3d_desc;
+
+/* Optional fused post-operations; pass NULL to conv3d_fwd for a plain conv
+ * (out = B(acc)). Pointers a flag does not use are ignored.
+ *   bias          fp32 [cout]                               (CONV3D_EPI_BIAS)
+ *   residual      bf16, output shape, out_layout            (CONV3D_EPI_RESIDUAL)
+ *   gamma         bf16 [cout]                               (CONV3D_EPI_L2NORM_SILU)
+ *   residual_out  bf16, output shape, out_layout            (CONV3D_EPI_RESIDUAL_OUT,
+ *                 requires CONV3D_EPI_RESIDUAL) */
+typedef struct {
+  unsigned flags;
+  const float* bias;
+  const void* residual;
+  const void* gamma;
+  void* residual_out;
+} conv3d_epilogue;
+
+/* Bytes of the packed weight for (cout, cin). */
+size_t conv3d_packed_weight_bytes(int cout, int cin);
+
+/* Pack an OIDHW checkpoint weight [cout][cin][3][3][3] (bf16) once, outside
+ * the inference loop ("Weight Packing": pack once, reuse, repack after the
+ * weights change). Packed layout, bf16:
+ *   packed[t][c / 32][co][c % 32],  t = kd*9 + kh*3 + kw,  c < roundup(cin, 32)
+ * with the channels c >= cin zero. Each 32-channel K step of one tap is then
+ * one contiguous [cout][32] block. w_oidhw and w_packed must not overlap. */
+conv3d_status conv3d_pack_weight(const void* w_oidhw, void* w_packed, int cout, int cin,
+                                 void* stream);
+
+/* Output extents {Do, Ho, Wo} for desc; CONV3D_ERR_SHAPE if any is < 1. */
+conv3d_status conv3d_output_dims(const conv3d_desc* desc, int out_dhw[3]);
+
+/* Workspace bytes conv3d_fwd needs for (desc, epi); 0 for an NDHWC layer
+ * that runs without split-K. epi may be NULL. */
+conv3d_status conv3d_workspace_bytes(const conv3d_desc* desc, const conv3d_epilogue* epi,
+                                     size_t* bytes);
+
+/* y = conv3d(x, w) followed by the epilogue (see CONV3D_EPI_*).
+ *   x          bf16, [n][d][h][w][cin] (NDHWC) or [n][cin][d][h][w] (NCDHW)
+ *   w_packed   from conv3d_pack_weight for (cout, cin)
+ *   y          bf16, output shape in out_layout
+ *   workspace  device scratch of at least conv3d_workspace_bytes() bytes
+ * y must not overlap x, w_packed, the workspace, residual or residual_out.
+ * Channel requirements: cin % 8 == 0, cout % 16 == 0. */
+conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_packed,
+                         const conv3d_epilogue* epi, void* y, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Layout change at a network boundary, bf16, exact:
+ *   src_layout = CONV3D_NCDHW:  [n][c][d][h][w] -> [n][d][h][w][c]
+ *   src_layout = CONV3D_NDHWC:  [n][d][h][w][c] -> [n][c][d][h][w]
+ * src and dst must not overlap. */
+conv3d_status conv3d_transpose(const void* src, int src_layout, void* dst, int n, int c, int d,
+                               int h, int w, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* conv3d_status_str(conv3d_status status);
+
+/* Describe the kernel choice conv3d_fwd would make for (desc, epi) into buf
+ * (NUL-terminated, truncated to len). Returns the same status conv3d_fwd's
+ * argument checks would for the shapes alone. */
+conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogue* epi,
+                                   char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV3D_MI355X_H */

@@ -111,16 +111,16 @@ int oracle_conv3d(const uint16_t* x, const uint16_t* w, int N, int D, int H, int
   if (pix == NULL) npix = M;
   const int ntap = KD * KH * KW;
 
-  /* The oracle's own copy of the weight, [tap][ci][co] in double, so the
-   * innermost loop runs over independent accumulators (one per co) without
-   * changing what any element sums. */
-  double* wt = (double*)malloc(sizeof(double) * (size_t)ntap * Ci * Co);
+  /* The oracle's own copy of the weight, [tap][ci][co] (bf16 values are
+   * exact in fp32), so the innermost loop runs over independent accumulators
+   * (one per co) without changing what any element sums. */
+  float* wt = (float*)malloc(sizeof(float) * (size_t)ntap * Ci * Co);
   if (!wt) return -2;
   for (int co = 0; co < Co; ++co)
     for (int ci = 0; ci < Ci; ++ci)
       for (int t = 0; t < ntap; ++t)
         wt[((size_t)t * Ci + ci) * Co + co] =
-            (double)oracle_bf16_to_f32(w[((size_t)co * Ci + ci) * ntap + t]);
+            oracle_bf16_to_f32(w[((size_t)co * Ci + ci) * ntap + t]);
 
   const float sqrt_c = sqrtf((float)Co);
   int err = 0;
@@ -154,11 +154,11 @@ int oracle_conv3d(const uint16_t* x, const uint16_t* w, int N, int D, int H, int
             const int ww = wo * stride[2] + kw - pad_lo[2];
             if (ww < 0 || ww >= W) continue;
             const uint16_t* xp = x + ((((int64_t)n * D + d) * H + h) * W + ww) * Ci;
-            const double* wp = wt + (size_t)((kd * KH + kh) * KW + kw) * Ci * Co;
+            const float* wp = wt + (size_t)((kd * KH + kh) * KW + kw) * Ci * Co;
             for (int ci = 0; ci < Ci; ++ci) {
               const double xv = (double)oracle_bf16_to_f32(xp[ci]);
-              const double* wr = wp + (size_t)ci * Co;
-              for (int co = 0; co < Co; ++co) acc[co] += xv * wr[co];
+              const float* wr = wp + (size_t)ci * Co;
+              for (int co = 0; co < Co; ++co) acc[co] += xv * (double)wr[co];
             }
           }
         }

@@ -1,0 +1,74 @@
+"""Parity rule between the GPU output and the oracle (test helper).
+
+Several results are correct: the pages fix an fp32 accumulator and the bf16
+rounding points, not the order of the fp32 sum. Two correct orders can land
+on opposite sides of a bf16 rounding boundary (one ulp), and near zero — or
+after a bias or residual cancels most of the conv value — one ulp of the
+larger intermediate is many ulps of the small result. The rule therefore
+measures the allowed error in bf16 ulps of the largest magnitude the error
+can have been made at:
+
+  ulp(s) = 2^(floor(log2 s) - 7)                       (bf16: 8 significant bits)
+  raw:    |y - r| <= 2 ulp(max(|r|, |conv|, 2^-8 RMS(r)))
+  fused:  |y - r| <= 4 ulp(max(|r|, |affine|, k*max(|conv|,|main|,|value|), 2^-8 RMS(r)))
+          with k = sqrt(C) |gamma_c| / den, which carries a pre-norm error to
+          the output's scale.
+
+2 and 4 ulps are the bounds stated for the raw and the fused path. The
+2^-8 RMS floor covers results within 1/256 of the layer's RMS of zero,
+where a correct fp32 sum of tens of thousands of terms has an absolute
+error comparable to the value itself.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def b2f(bits) -> np.ndarray:
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def ulp_bf16(s: np.ndarray) -> np.ndarray:
+    s = np.maximum(np.abs(s).astype(np.float64), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(s)) - 7)
+
+
+def check(y_bits, ref, *, fused=False, gamma_bits=None, cout=None, what=""):
+    """Assert the rule; return diagnostics. ref: oracle dict (intermediates=True)."""
+    y = b2f(y_bits).astype(np.float64)
+    r = b2f(ref["y"]).astype(np.float64)
+    assert y.shape == r.shape, (y.shape, r.shape)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    floor = 2.0 ** -8 * rms
+    conv = np.abs(b2f(ref["conv"]).astype(np.float64))
+    if fused:
+        C = cout if cout is not None else r.shape[-1]
+        g = np.abs(b2f(gamma_bits).astype(np.float64))
+        den = ref["den"].astype(np.float64).reshape(r.shape[:-1] + (1,))
+        k = np.sqrt(C) * g / den
+        pre = np.maximum(np.maximum(conv, np.abs(b2f(ref["main"]))), np.abs(b2f(ref["value"])))
+        scale = np.maximum.reduce([np.abs(r), np.abs(b2f(ref["affine"]).astype(np.float64)),
+                                   k * pre, np.full_like(r, floor)])
+        nulp = 4.0
+    else:
+        scale = np.maximum.reduce([np.abs(r), conv, np.full_like(r, floor)])
+        nulp = 2.0
+    err = np.abs(y - r)
+    allowed = nulp * ulp_bf16(scale)
+    bad = err > allowed
+    at_r = err / ulp_bf16(np.abs(r))
+    diag = {
+        "n": int(r.size),
+        "bit_identical": float(np.mean(y_bits == ref["y"])) if r.size else 1.0,
+        "max_ulp_rule": float(np.max(err / ulp_bf16(scale))) if r.size else 0.0,
+        "max_ulp_at_r": float(np.max(at_r)) if r.size else 0.0,
+        "mean_signed_ulp": float(np.mean((y - r) / ulp_bf16(np.abs(r)))) if r.size else 0.0,
+    }
+    if np.any(bad):
+        idx = np.argwhere(bad)[:5]
+        detail = [(tuple(int(v) for v in i), float(y[tuple(i)]), float(r[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {r.size} outside the rule; "
+                             f"first {detail}; diag {diag}")
+    return diag

@@ -1,0 +1,175 @@
+"""Host-side tests of the C-ABI library: it loads, exports what include/conv3d.h
+declares, and rejects bad calls before any GPU work.
+
+No test here launches a kernel: every conv3d_fwd / pack / transpose call is
+built to fail an argument check (the checks run on the host before anything
+is enqueued), using fake but aligned addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import convolution_video_vae_amd as cv
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv3d.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv3d_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cv.lib()
+    names = header_functions()
+    assert set(names) == set(cv.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_desc_struct_matches_header_layout():
+    # 6 ints, 3x3 ints, layout, out_layout, split_k = 18 ints
+    assert ctypes.sizeof(cv.conv3d_desc) == 18 * 4
+    assert ctypes.sizeof(cv.conv3d_epilogue) == 8 + 4 * 8
+
+
+def test_status_strings():
+    for code in range(8):
+        assert cv.status_str(code)
+    assert cv.status_str(0) == "ok"
+
+
+def test_packed_weight_bytes():
+    assert cv.conv3d_packed_weight_bytes(128, 128) == 27 * 128 * 128 * 2
+    assert cv.conv3d_packed_weight_bytes(320, 160) == 27 * 160 * 320 * 2
+    assert cv.conv3d_packed_weight_bytes(64, 40) == 27 * 64 * 64 * 2   # cin padded to 64
+    assert cv.conv3d_packed_weight_bytes(0, 8) == 0
+
+
+@pytest.mark.parametrize("name", list(workloads.LAYERS))
+def test_output_dims_match_layer_table(name):
+    L = workloads.LAYERS[name]
+    d = cv.make_desc(L.x_shape, L.cout, stride=L.stride, pad_lo=L.pad_lo, pad_hi=L.pad_hi)
+    assert cv.conv3d_output_dims(d) == L.out_dhw()
+
+
+def test_output_shapes_from_the_pages():
+    # valid conv: [N,T,H,W,Ci] -> [N,T-2,H-2,W-2,Co] (cuDNN page, "Raw Conv3D Variant")
+    d = cv.make_desc((1, 7, 66, 122, 160), 320)
+    assert cv.conv3d_output_dims(d) == (5, 64, 120)
+    # stride-2 downsample after a (0,1,0,1) zero pad: 1024 -> 512 (Qwen-Image PR, table 2)
+    d = cv.make_desc((1, 1, 1024, 1024, 96), 96, stride=(1, 2, 2), pad_lo=(2, 0, 0), pad_hi=(0, 1, 1))
+    assert cv.conv3d_output_dims(d) == (1, 512, 512)
+    # causal conv keeps T, H, W
+    d = cv.make_desc((1, 17, 256, 256, 128), 128, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))
+    assert cv.conv3d_output_dims(d) == (17, 256, 256)
+
+
+def test_workspace_and_plans():
+    big = workloads.LAYERS["h3_l0_128"]
+    d = cv.make_desc(big.x_shape, big.cout, pad_lo=big.pad_lo, pad_hi=big.pad_hi)
+    assert cv.conv3d_workspace_bytes(d) == 0
+    assert "splits=1" in cv.conv3d_plan_describe(d)
+    wide = workloads.LAYERS["h3_l5_1024"]
+    d = cv.make_desc(wide.x_shape, wide.cout, pad_lo=wide.pad_lo, pad_hi=wide.pad_hi)
+    plan = cv.conv3d_plan_describe(d)
+    splits = int(re.search(r"splits=(\d+)", plan).group(1))
+    assert splits > 1
+    assert cv.conv3d_workspace_bytes(d) >= splits * wide.m * wide.cout * 4
+    d.split_k = 1
+    assert cv.conv3d_workspace_bytes(d) == 0
+    # NCDHW in and out need NDHWC staging copies
+    d = cv.make_desc((1, 160, 7, 66, 122), 320, layout=cv.NCDHW)
+    assert cv.conv3d_workspace_bytes(d) >= 1 * 160 * 7 * 66 * 122 * 2 + 5 * 64 * 120 * 320 * 2
+
+
+# ------------------------------------------------------------------ rejected calls
+
+X, W, Y, WS, R, G, B = (0x10000000 * k for k in range(1, 8))   # aligned, never dereferenced
+
+
+def fwd(desc, x=X, w=W, epi=None, y=Y, ws=None, ws_bytes=0):
+    return cv.lib().conv3d_fwd(ctypes.byref(desc), x, w, ctypes.byref(epi) if epi else None, y,
+                               ws, ws_bytes, None)
+
+
+def small_desc(**kw):
+    # split_k=1: no workspace, so each call below fails only on what it probes
+    args = dict(pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=1)
+    args.update(kw)
+    return cv.make_desc((1, 3, 8, 8, 32), 32, **args)
+
+
+def test_null_pointers_rejected():
+    assert fwd(small_desc(), x=None) == 1
+    assert fwd(small_desc(), w=None) == 1
+    assert fwd(small_desc(), y=None) == 1
+    assert cv.lib().conv3d_fwd(None, X, W, None, Y, None, 0, None) == 1
+    assert fwd(small_desc(), epi=cv.conv3d_epilogue(cv.EPI_BIAS, None, None, None, None)) == 1
+    assert fwd(small_desc(), epi=cv.conv3d_epilogue(cv.EPI_L2NORM_SILU, None, None, None, None)) == 1
+    assert cv.lib().conv3d_pack_weight(None, W, 8, 8, None) == 1
+    assert cv.lib().conv3d_transpose(None, 0, Y, 1, 8, 1, 1, 1, None) == 1
+
+
+def test_bad_shapes_rejected():
+    assert fwd(cv.make_desc((1, 2, 8, 8, 32), 32)) == 2        # valid conv needs T >= 3
+    assert fwd(cv.make_desc((0, 3, 8, 8, 32), 32)) == 2
+    assert fwd(small_desc(stride=(0, 1, 1))) == 2
+    assert fwd(small_desc(pad_lo=(-1, 0, 0))) == 2
+    d = small_desc(); d.layout = 7
+    assert fwd(d) == 2
+    assert cv.lib().conv3d_transpose(X, 3, Y, 1, 8, 1, 1, 1, None) == 2
+    out = (ctypes.c_int * 3)()
+    assert cv.lib().conv3d_output_dims(ctypes.byref(cv.make_desc((1, 2, 2, 2, 8), 8)),
+                                       ctypes.byref(out)) == 2
+
+
+def test_alignment_rejected():
+    assert fwd(small_desc(), x=X + 2) == 3
+    assert fwd(small_desc(), w=W + 8) == 3
+    assert fwd(small_desc(), y=Y + 4) == 3
+    assert fwd(cv.make_desc((1, 3, 8, 8, 12), 32, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))) == 3
+    epi = cv.conv3d_epilogue(cv.EPI_BIAS, B + 4, None, None, None)
+    assert fwd(small_desc(), epi=epi) == 3
+    assert cv.lib().conv3d_pack_weight(X + 2, W, 8, 8, None) == 3
+
+
+def test_unsupported_rejected_without_fallback():
+    assert fwd(cv.make_desc((1, 3, 8, 8, 32), 24, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))) == 6
+    epi = cv.conv3d_epilogue(cv.EPI_RESIDUAL_OUT, None, None, None, R)
+    assert fwd(small_desc(), epi=epi) == 6                    # residual_out needs residual
+    epi = cv.conv3d_epilogue(64, None, None, None, None)      # unknown flag
+    assert fwd(small_desc(), epi=epi) == 6
+    huge = cv.make_desc((1, 17, 1024, 1024, 128), 128, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))
+    assert fwd(huge) == 6                                       # > 2 GiB activation
+    wide = cv.make_desc((1, 3, 4, 4, 32), 4096)
+    epi = cv.conv3d_epilogue(cv.EPI_L2NORM_SILU, None, None, G, None)
+    assert fwd(wide, epi=epi) == 6                              # norm row too long
+
+
+def test_overlap_rejected():
+    d = small_desc()
+    assert fwd(d, y=X) == 4                                     # y aliases x
+    assert fwd(d, y=X + 64) == 4                                # y inside x
+    assert fwd(d, y=W) == 4
+    epi = cv.conv3d_epilogue(cv.EPI_RESIDUAL | cv.EPI_RESIDUAL_OUT, None, R, None, Y)
+    assert fwd(d, epi=epi) == 4                                 # residual_out aliases y
+    epi = cv.conv3d_epilogue(cv.EPI_RESIDUAL, None, Y, None, None)
+    assert fwd(d, epi=epi) == 4                                 # residual aliases y
+    assert cv.lib().conv3d_pack_weight(X, X + 16, 8, 8, None) == 4
+    assert cv.lib().conv3d_transpose(X, 0, X + 64, 1, 8, 2, 2, 2, None) == 4
+
+
+def test_workspace_checked():
+    wide = workloads.LAYERS["h3_l5_1024"]
+    d = cv.make_desc(wide.x_shape, wide.cout, pad_lo=wide.pad_lo, pad_hi=wide.pad_hi)
+    need = cv.conv3d_workspace_bytes(d)
+    assert fwd(d) == 5
+    assert fwd(d, ws=WS, ws_bytes=need - 1) == 5
+    assert fwd(d, ws=WS + 8, ws_bytes=need) == 3
+    assert fwd(d, ws=X, ws_bytes=need) == 4                     # workspace aliases x

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Integer-valued data, impulses, packing and transposes must match bit for bit;
+random data must satisfy the ulp rule in tests/parity.py. Small cases span
+several tiles and a ragged tail and are compared element by element; the
+full-size layers are compared on sampled output pixels (all channels of each)
+in the launch configuration the benchmark times, and every output element is
+checked to have been written (outputs are pre-filled with NaN).
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_video_vae_amd as cv
+import oracle
+import workloads
+from parity import b2f, check
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    cv.lib()          # fail loudly if the HIP library is missing
+    yield
+
+
+def bits(t):
+    return workloads.bf16_bits(t.cpu())
+
+
+def from_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def poisoned(shape):
+    return torch.full(shape, NAN_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def run_gpu(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=None,
+            residual=None, gamma=None, norm=False, split_k=0, want_residual_out=False,
+            layout=cv.NDHWC, out_layout=None, label=""):
+    """x (NDHWC or NCDHW per layout), w OIDHW: CPU tensors. Returns CPU outputs."""
+    print(f"[gpu] {label} x={tuple(x.shape)} w={tuple(w.shape)} stride={stride} "
+          f"pad={pad_lo}/{pad_hi} split_k={split_k} norm={norm}", flush=True)
+    out_layout = layout if out_layout is None else out_layout
+    cout, cin = w.shape[:2]
+    xd = x.cuda().contiguous()
+    wd = w.cuda().contiguous()
+    wp = torch.empty(cv.conv3d_packed_weight_bytes(cout, cin) // 2, dtype=torch.bfloat16, device="cuda")
+    cv.conv3d_pack_weight(wd, wp, cout, cin)
+    desc = cv.make_desc(tuple(x.shape), cout, stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
+                        layout=layout, out_layout=out_layout, split_k=split_k)
+    od = cv.conv3d_output_dims(desc)
+    n = x.shape[0]
+    yshape = (n,) + od + (cout,) if out_layout == cv.NDHWC else (n, cout) + od
+    y = poisoned(yshape)
+    bd = bias.cuda() if bias is not None else None
+    rd = residual.cuda().contiguous() if residual is not None else None
+    gd = gamma.cuda() if gamma is not None else None
+    ro = poisoned(yshape) if want_residual_out else None
+    epi = cv.make_epilogue(bias=bd, residual=rd, gamma=gd, residual_out=ro, norm_silu=norm)
+    ws_bytes = cv.conv3d_workspace_bytes(desc, epi)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    cv.conv3d_fwd(desc, xd, wp, epi if epi.flags else None, y, ws, ws_bytes)
+    torch.cuda.synchronize()
+    out = {"y": y.cpu(), "plan": cv.conv3d_plan_describe(desc, epi if epi.flags else None)}
+    if ro is not None:
+        out["residual_out"] = ro.cpu()
+    return out
+
+
+def run_oracle(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=None,
+               residual=None, gamma=None, norm=False, pixels=None):
+    return oracle.conv3d(bits(x), bits(w), stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
+                         bias=None if bias is None else bias.numpy(),
+                         residual=None if residual is None else bits(residual),
+                         gamma=None if gamma is None else bits(gamma), norm_silu=norm,
+                         pixels=pixels, intermediates=True)
+
+
+def geom(layer):
+    return dict(stride=layer.stride, pad_lo=layer.pad_lo, pad_hi=layer.pad_hi)
+
+
+# ------------------------------------------------------------------ pack / transpose
+
+@pytest.mark.parametrize("cout,cin", [(64, 64), (96, 40), (320, 160), (16, 8), (1024, 512)])
+def test_pack_weight_matches_documented_layout(cout, cin):
+    rng = np.random.default_rng(cout * 7 + cin)
+    w = rng.integers(0, 65536, size=(cout, cin, 3, 3, 3), dtype=np.uint16)
+    wd = from_bits(w).cuda()
+    nb = cv.conv3d_packed_weight_bytes(cout, cin)
+    wp = torch.full((nb // 2,), NAN_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    cv.conv3d_pack_weight(wd, wp, cout, cin)
+    got = bits(wp)
+    cc = (cin + 31) // 32
+    # packed[t][c // 32][co][c % 32] = w[co][c][kd][kh][kw], t = kd*9 + kh*3 + kw; 0 for c >= cin
+    want = np.zeros((27, cc * 32, cout), np.uint16)
+    want[:, :cin, :] = w.reshape(cout, cin, 27).transpose(2, 1, 0)
+    want = want.reshape(27, cc, 32, cout).transpose(0, 1, 3, 2)
+    np.testing.assert_array_equal(got, want.ravel())
+
+
+@pytest.mark.parametrize("shape", [(2, 24, 3, 5, 7), (1, 160, 7, 66, 122), (1, 320, 5, 64, 120),
+                                   (3, 8, 1, 1, 1), (1, 72, 2, 9, 13)])
+def test_transpose_round_trip_is_exact(shape):
+    n, c, d, h, w = shape
+    rng = np.random.default_rng(sum(shape))
+    src = from_bits(rng.integers(0, 65536, size=shape, dtype=np.uint16)).cuda()
+    mid = poisoned((n, d, h, w, c))
+    cv.conv3d_transpose(src, cv.NCDHW, mid, n, c, d, h, w)
+    back = poisoned(shape)
+    cv.conv3d_transpose(mid, cv.NDHWC, back, n, c, d, h, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(mid), bits(src.cpu().permute(0, 2, 3, 4, 1).contiguous()))
+    np.testing.assert_array_equal(bits(back), bits(src.cpu()))
+
+
+# ------------------------------------------------------------------ exact cases
+
+INT_CASES = [
+    # label, x shape, cout, stride, pad_lo, pad_hi, bias
+    ("causal64", (1, 5, 16, 16, 64), 64, (1, 1, 1), (2, 1, 1), (0, 1, 1), True),
+    ("causal128_ragged", (2, 3, 9, 21, 128), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1), False),
+    ("s122_pad01", (1, 4, 17, 23, 128), 128, (1, 2, 2), (2, 0, 0), (0, 1, 1), False),
+    ("valid96", (1, 6, 12, 30, 96), 96, (1, 1, 1), (0, 0, 0), (0, 0, 0), False),
+    ("t1_96", (1, 1, 33, 40, 96), 96, (1, 1, 1), (2, 1, 1), (0, 1, 1), False),
+    ("cin40_cout48", (1, 3, 7, 9, 40), 48, (1, 1, 1), (2, 1, 1), (0, 1, 1), True),
+    ("s222", (1, 9, 12, 12, 64), 64, (2, 2, 2), (2, 1, 1), (0, 1, 1), False),
+    ("wide512", (1, 3, 6, 6, 512), 1024, (1, 1, 1), (2, 1, 1), (0, 1, 1), True),
+]
+
+
+@pytest.mark.parametrize("case", INT_CASES, ids=[c[0] for c in INT_CASES])
+@pytest.mark.parametrize("split_k", [0, 1, 3])
+def test_integer_data_bit_exact(case, split_k):
+    label, xs, cout, st, lo, hi, has_bias = case
+    x, w, b = workloads.integer_tensors(xs, cout, seed=len(label), bias=has_bias)
+    g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b, split_k=split_k, label=label)
+    r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
+
+
+def test_integer_fused_epilogue_bit_exact_across_splits():
+    """Same integer conv, fused norm epilogue: the conv value is exact, so any
+    K split must give the same bits as the single-pass fused kernel."""
+    xs, cout = (1, 3, 10, 12, 160), 320
+    x, w, b = workloads.integer_tensors(xs, cout, seed=3, bias=True)
+    rng = np.random.default_rng(3)
+    res = torch.from_numpy(rng.integers(-4, 5, size=(1, 1, 8, 10, cout)).astype(np.float32)).to(torch.bfloat16)
+    gam = torch.from_numpy(rng.uniform(0.5, 1.5, cout).astype(np.float32)).to(torch.bfloat16)
+    outs = [run_gpu(x, w, bias=b, residual=res, gamma=gam, norm=True, split_k=s,
+                    want_residual_out=True, label=f"fused_int_s{s}") for s in (1, 2, 0)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(bits(o["y"]), bits(outs[0]["y"]))
+        np.testing.assert_array_equal(bits(o["residual_out"]), bits(outs[0]["residual_out"]))
+    r = run_oracle(x, w, bias=b, residual=res, gamma=gam, norm=True)
+    np.testing.assert_array_equal(bits(outs[0]["residual_out"]), r["value"])
+    check(bits(outs[0]["y"]), r, fused=True, gamma_bits=bits(gam), what="fused integer")
+
+
+@pytest.mark.parametrize("stride,lo,hi", [((1, 1, 1), (2, 1, 1), (0, 1, 1)),
+                                         ((1, 2, 2), (2, 0, 0), (0, 1, 1)),
+                                         ((1, 1, 1), (0, 0, 0), (0, 0, 0))])
+def test_input_impulses_bit_exact(stride, lo, hi):
+    rng = np.random.default_rng(21)
+    xs = (1, 5, 9, 11, 32)
+    w = torch.from_numpy(rng.standard_normal((32, 32, 3, 3, 3)).astype(np.float32)).to(torch.bfloat16)
+    x = np.zeros(xs, np.float32)
+    for (d, h, ww, ci) in [(0, 0, 0, 0), (4, 8, 10, 31), (2, 3, 1, 5), (1, 0, 10, 17)]:
+        x[0, d, h, ww, ci] = 1.0
+    x = torch.from_numpy(x).to(torch.bfloat16)
+    g = run_gpu(x, w, stride=stride, pad_lo=lo, pad_hi=hi, label="impulse")
+    r = run_oracle(x, w, stride=stride, pad_lo=lo, pad_hi=hi)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"])
+
+
+# ------------------------------------------------------------------ random data, small
+
+SMALL = [
+    # name, layer family it scales down, x shape, cout
+    ("tiny_causal_64", "tiny_causal_64", (1, 5, 16, 16, 64), 64),
+    ("causal_128", "h3_l0_128", (1, 5, 24, 40, 128), 128),
+    ("s122_128", "h3_l0_128_s122", (1, 5, 23, 41, 128), 128),
+    ("valid_96", "wan_valid_96", (1, 6, 20, 42, 96), 96),
+    ("valid_384", "wan_valid_384", (1, 3, 14, 22, 384), 384),
+    ("t1_96", "qwen_t1_96", (1, 1, 64, 72, 96), 96),
+    ("wide_1024", "h3_l5_1024", (1, 3, 8, 8, 1024), 1024),
+    ("wide_512to1024", "h3_l5_512to1024", (1, 5, 8, 8, 512), 1024),
+    ("fused_160to320", "wan_fused_160to320", (1, 5, 14, 22, 160), 320),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_random_small_against_oracle(case):
+    name, fam, xs, cout = case
+    L = workloads.LAYERS[fam]
+    t = workloads.make_tensors(L, x_shape=xs, cout=cout)
+    kw = dict(bias=t.bias, residual=t.residual, gamma=t.gamma, norm=L.norm_silu, **geom(L))
+    g = run_gpu(t.x, t.w, want_residual_out=L.residual, label=name, **kw)
+    r = run_oracle(t.x, t.w, **kw)
+    diag = check(bits(g["y"]), r, fused=L.norm_silu,
+                 gamma_bits=None if t.gamma is None else bits(t.gamma), what=name)
+    print(name, g["plan"], diag)
+    if L.residual:
+        check(bits(g["residual_out"]), dict(r, y=r["value"]), what=name + " residual_out")
+
+
+def test_fused_reduce_path_matches_fused_kernel():
+    """The split-K route (partials + reducing epilogue) and the single-pass
+    fused kernel both satisfy the rule on the same random layer."""
+    L = workloads.LAYERS["wan_fused_160to320"]
+    t = workloads.make_tensors(L, x_shape=(1, 4, 10, 19, 160))
+    kw = dict(bias=t.bias, residual=t.residual, gamma=t.gamma, norm=True)
+    r = run_oracle(t.x, t.w, **kw)
+    for s in (1, 4):
+        g = run_gpu(t.x, t.w, split_k=s, label=f"fused_s{s}", **kw)
+        check(bits(g["y"]), r, fused=True, gamma_bits=bits(t.gamma), what=f"split_k={s}")
+
+
+def test_bias_residual_without_norm():
+    """bias -> residual, stopping at `value` (the cuDNN page's bias/residual
+    variant, without its padding)."""
+    L = workloads.LAYERS["wan_fused_160to320"]
+    t = workloads.make_tensors(L, x_shape=(1, 4, 9, 13, 160))
+    g = run_gpu(t.x, t.w, bias=t.bias, residual=t.residual, want_residual_out=True, label="bias_res")
+    r = run_oracle(t.x, t.w, bias=t.bias, residual=t.residual)
+    check(bits(g["y"]), r, what="bias+residual")
+    np.testing.assert_array_equal(bits(g["residual_out"]), bits(g["y"]))
+
+
+# ------------------------------------------------------------------ full-size layers
+
+def sample_pixels(layer, count, seed):
+    M = layer.m
+    rng = np.random.default_rng(seed)
+    n, d, h, w = (layer.x_shape[0],) + layer.out_dhw()
+    edges = []
+    for dq in sorted({0, 1, d - 1}):
+        for hq in sorted({0, h - 1}):
+            for wq in sorted({0, 1, w - 1}):
+                edges.append(((0 * d + dq) * h + hq) * w + wq)
+    pix = np.concatenate([np.arange(min(64, M)), np.arange(max(0, M - 64), M), np.array(edges),
+                          rng.integers(0, M, size=count)])
+    return np.unique(pix)
+
+
+FULL = list(workloads.LAYERS)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_layer_sampled(name):
+    L = workloads.LAYERS[name]
+    t = workloads.make_tensors(L)
+    kw = dict(bias=t.bias, residual=t.residual, gamma=t.gamma, norm=L.norm_silu, **geom(L))
+    g = run_gpu(t.x, t.w, want_residual_out=L.residual, label=name, **kw)
+    y = bits(g["y"])
+    assert not np.any(y == NAN_BF16), "unwritten output elements"
+    count = 96 if L.cin >= 512 else 1500
+    pix = sample_pixels(L, count, seed=L.family)
+    r = run_oracle(t.x, t.w, pixels=pix, **kw)
+    diag = check(y.reshape(-1, L.cout)[pix], r, fused=L.norm_silu,
+                 gamma_bits=None if t.gamma is None else bits(t.gamma), what=name)
+    print(name, g["plan"], diag)
+    assert diag["bit_identical"] > 0.97
+
+
+def test_fused_layer_ncdhw_boundary_variants_are_bit_identical():
+    """NCDHW input (and NCDHW output with an NCDHW residual) gives exactly the
+    NDHWC result, transposed: a transpose is exact."""
+    L = workloads.LAYERS["wan_fused_160to320"]
+    t = workloads.make_tensors(L)
+    kw = dict(bias=t.bias, gamma=t.gamma, norm=True, **geom(L))
+    ref = run_gpu(t.x, t.w, residual=t.residual, want_residual_out=True, label="ndhwc", **kw)
+    x_ncdhw = t.x.permute(0, 4, 1, 2, 3).contiguous()
+    a = run_gpu(x_ncdhw, t.w, residual=t.residual, want_residual_out=True, layout=cv.NCDHW,
+                out_layout=cv.NDHWC, label="ncdhw_in", **kw)
+    np.testing.assert_array_equal(bits(a["y"]), bits(ref["y"]))
+    res_ncdhw = t.residual.permute(0, 4, 1, 2, 3).contiguous()
+    b = run_gpu(x_ncdhw, t.w, residual=res_ncdhw, want_residual_out=True, layout=cv.NCDHW,
+                label="ncdhw_in_out", **kw)
+    np.testing.assert_array_equal(bits(b["y"]), bits(ref["y"].permute(0, 4, 1, 2, 3).contiguous()))
+    np.testing.assert_array_equal(bits(b["residual_out"]),
+                                  bits(ref["residual_out"].permute(0, 4, 1, 2, 3).contiguous()))
+
+
+@pytest.mark.parametrize("name", ["h3_l5_1024", "tiny_causal_64"])
+def test_run_to_run_deterministic(name):
+    L = workloads.LAYERS[name]
+    t = workloads.make_tensors(L)
+    kw = dict(bias=t.bias, **geom(L))
+    a = run_gpu(t.x, t.w, label=name + "_a", **kw)
+    b = run_gpu(t.x, t.w, label=name + "_b", **kw)
+    np.testing.assert_array_equal(bits(a["y"]), bits(b["y"]))
