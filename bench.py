@@ -69,7 +69,10 @@ class Case:
         if lay == cv.NCDHW and self.res is not None:
             self.res = self.res.permute(0, 4, 1, 2, 3).contiguous()
         self.y = self.layer.new_output()
-        self.plan = cv.conv3d_plan_describe(self.layer.desc, None)
+        probe = cv.make_epilogue(bias=self.layer.bias, gamma=self.layer.gamma,
+                                 norm_silu=L.norm_silu)
+        probe.flags |= cv.EPI_RESIDUAL if L.residual else 0
+        self.plan = cv.conv3d_plan_describe(self.layer.desc, probe if probe.flags else None)
 
     def __call__(self):
         self.layer(self.x, residual=self.res, y=self.y)
@@ -112,8 +115,9 @@ def cpu_baseline(L, seconds):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(done * per_pixel / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} of {L.m} output pixels (all {L.cout} channels each) of "
-                      f"{L.name}, contiguous runs, {dt:.1f} s wall"}
+            "sample": f"{done} output pixels (all {L.cout} channels each) of {L.name} "
+                      f"({L.m} in the layer), in random contiguous runs of {chunk}, "
+                      f"{dt:.1f} s wall"}
 
 
 def main():

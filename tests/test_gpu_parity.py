@@ -241,10 +241,10 @@ def sample_pixels(layer, count, seed):
     rng = np.random.default_rng(seed)
     n, d, h, w = (layer.x_shape[0],) + layer.out_dhw()
     edges = []
-    for dq in sorted({0, 1, d - 1}):
+    for dq in sorted({0, min(1, d - 1), d - 1}):
         for hq in sorted({0, h - 1}):
-            for wq in sorted({0, 1, w - 1}):
-                edges.append(((0 * d + dq) * h + hq) * w + wq)
+            for wq in sorted({0, min(1, w - 1), w - 1}):
+                edges.append((dq * h + hq) * w + wq)
     pix = np.concatenate([np.arange(min(64, M)), np.arange(max(0, M - 64), M), np.array(edges),
                           rng.integers(0, M, size=count)])
     return np.unique(pix)
