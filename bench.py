@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--no-layers", action="store_true", help="time only the headline layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--sweep", default=None,
+                   help="development: time the headline layer under each CONV3D_TILE value in "
+                        "this ';'-separated list and print one line per tile to stderr")
     return p.parse_args()
 
 
@@ -134,6 +137,17 @@ def main():
         sys.exit(1)
     cv.lib()
     head = workloads.LAYERS[args.workload or workloads.HEADLINE]
+
+    if args.sweep:
+        for tile in args.sweep.split(";"):
+            os.environ["CONV3D_TILE"] = tile
+            c = Case(head, torch, cv)
+            sms, _ = time_case(c, args.steps, args.warmup, torch)
+            print(f"sweep {head.name} tile={tile} {c.plan}: {sms * 1e3:.1f} us "
+                  f"{head.flops() / (sms * 1e-3) / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            del c
+        os.environ.pop("CONV3D_TILE", None)
+        torch.cuda.empty_cache()
 
     case = Case(head, torch, cv)
     ms, wall = time_case(case, args.steps, args.warmup, torch)

@@ -26,13 +26,16 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    kobj = os.path.join(BUILD, "conv3d_kernels.o")
+    objs = []
+    for name in ("conv3d_kernels", "conv3d_igemm"):
+        obj = os.path.join(BUILD, name + ".o")
+        _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-c",
+              *DEVICE_FLAGS, "-Wall", os.path.join(CSRC, name + ".hip"), "-o", obj], verbose)
+        objs.append(obj)
     aobj = os.path.join(BUILD, "conv3d_api.o")
-    _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-c",
-          *DEVICE_FLAGS, "-Wall", os.path.join(CSRC, "conv3d_kernels.hip"), "-o", kobj], verbose)
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-c", "-Wall", "-Wextra",
           os.path.join(CSRC, "conv3d_api.cpp"), "-o", aobj], verbose)
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", kobj, aobj, "-o", OUT + ".tmp"],
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, aobj, "-o", OUT + ".tmp"],
          verbose)
     os.replace(OUT + ".tmp", OUT)
     return OUT

@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -93,8 +94,11 @@ conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
   pr->layout = d->layout;
   pr->out_layout = d->out_layout;
   if (d->cin % 8 != 0) return CONV3D_ERR_ALIGN;
+  if (d->cin > 8160) return CONV3D_ERR_UNSUPPORTED;  // K steps are encoded in 8 bits per tap
   if (d->cout % 16 != 0) return CONV3D_ERR_UNSUPPORTED;
   if (pr->x_bytes > kMaxTensorBytes || pr->y_bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
+  if ((long long)conv3d_packed_weight_bytes(d->cout, d->cin) > kMaxTensorBytes)
+    return CONV3D_ERR_UNSUPPORTED;
   if (pr->M > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
   return CONV3D_OK;
 }
@@ -121,42 +125,87 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Kernel choice. Large-M layers run one work-group per (pixel tile, channel
 // tile); small-M / large-K layers cut K into slices whose fp32 partials a
 // second kernel sums in fixed order.
+constexpr int kCUs = 256;
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Channel blocking: the widest tile that divides Cout (each lane's run of
+// channels must stay inside Cout).
+TileCfg channel_cfg(int cout) {
+  if (cout % 128 == 0) return {32, 4, 1, 2, 4, 1, 3};
+  if (cout % 96 == 0) return {32, 4, 1, 2, 3, 1, 3};
+  if (cout % 32 == 0) return {32, 4, 1, 2, 2, 1, 3};
+  return {16, 4, 1, 4, 2, 1, 3};
+}
+
 void make_plan(const Problem& pr, int split_req, Plan* pl) {
   const int cc = (pr.cin + 31) / 32;
   pl->steps = 27 * cc;
   const bool norm = (pr.flags & F_NORM) != 0;
-  TileCfg store_cfg;
-  if (pr.cout % 128 == 0) store_cfg = {4, 1, 4, 8};
-  else if (pr.cout % 96 == 0) store_cfg = {4, 1, 4, 6};
-  else store_cfg = {4, 1, 4, 4};
-  TileCfg part_cfg = {4, 1, 2, store_cfg.j};
+  TileCfg base = channel_cfg(pr.cout);
+  const long long n_tiles = ceil_div(pr.cout, base.bn());
 
-  // Fused-norm kernels hold the whole channel row of a pixel in one group.
-  TileCfg norm_cfg = {0, 0, 0, 0};
-  if (norm) {
-    const TileCfg cands[] = {{2, 2, 2, 10}, {2, 2, 2, 5}, {4, 1, 2, 8}};
-    for (const TileCfg& c : cands)
-      if (c.bn() == pr.cout) norm_cfg = c;
+  // Pixel blocking: among the compiled depths, the one that wastes the least
+  // of the last round of work-groups over the 256 CUs.
+  TileCfg store_cfg = base;
+  if (base.r == 32) {
+    long long best = -1;
+    for (int pb : {2}) {
+      TileCfg c = base;
+      c.pb = pb;
+      if (!igemm_has_config(c, EPI_STORE)) continue;
+      const long long tiles = ceil_div(pr.M, c.bm()) * n_tiles;
+      const long long cost = ceil_div(tiles, kCUs) * pb;   // rounds x time per round
+      if (best < 0 || cost < best) { best = cost; store_cfg = c; }
+    }
+  }
+  TileCfg part_cfg = base;
+  part_cfg.pb = 2;
+  if (base.r == 32 && ceil_div(pr.M, part_cfg.bm()) * n_tiles < 64) {
+    TileCfg c = base;
+    c.pb = 1;
+    if (igemm_has_config(c, EPI_PARTIAL)) part_cfg = c;
   }
 
-  const long long m_tiles_store = (pr.M + store_cfg.bm() - 1) / store_cfg.bm();
-  const long long n_tiles_store = (pr.cout + store_cfg.bn() - 1) / store_cfg.bn();
+  // Fused-norm kernels hold the whole channel row of a pixel in one group.
+  TileCfg norm_cfg = {0, 0, 0, 0, 0, 0, 0};
+  if (norm) {
+    const TileCfg cands[] = {{16, 2, 2, 2, 10, 1, 3}, {16, 4, 1, 2, 10, 1, 3}};
+    for (const TileCfg& c : cands)
+      if (c.bn() == pr.cout && igemm_has_config(c, EPI_NORM)) norm_cfg = c;
+  }
+
+  const long long store_tiles = ceil_div(pr.M, store_cfg.bm()) * n_tiles;
   int splits = 1;
   if (split_req > 0) {
     splits = split_req;
-  } else if (m_tiles_store * n_tiles_store < 256) {
-    // Too few tiles to fill 256 CUs: cut K so there are about two groups
+  } else if (store_tiles < kCUs / 2) {
+    // Too few tiles to fill the CUs: cut K so there are about two groups
     // per CU, keeping at least 8 K steps per slice.
-    const long long tiles = ((pr.M + part_cfg.bm() - 1) / part_cfg.bm()) *
-                            ((pr.cout + part_cfg.bn() - 1) / part_cfg.bn());
-    splits = (int)std::max(1LL, std::min<long long>((512 + tiles - 1) / tiles, pl->steps / 8));
+    const long long tiles = ceil_div(pr.M, part_cfg.bm()) * ceil_div(pr.cout, part_cfg.bn());
+    splits = (int)std::max(1LL, std::min<long long>(ceil_div(2 * kCUs, tiles), pl->steps / 8));
   }
   splits = std::max(1, std::min(splits, pl->steps));
   pl->steps_per_split = (pl->steps + splits - 1) / splits;
   splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
   pl->splits = splits;
 
-  if (splits > 1 || (norm && norm_cfg.wm == 0)) {
+  // Development override of the tile (same kernels, another compiled
+  // configuration): CONV3D_TILE="r,wm,wn,pb,cb,kb,ns".
+  if (const char* env = getenv("CONV3D_TILE")) {
+    TileCfg c;
+    if (sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &c.r, &c.wm, &c.wn, &c.pb, &c.cb, &c.kb, &c.ns) == 7 &&
+        c.bn() > 0 && pr.cout % c.bn() == 0) {
+      const int mode = splits > 1 ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
+      if (igemm_has_config(c, mode)) {
+        if (mode == EPI_PARTIAL) part_cfg = c;
+        else if (mode == EPI_NORM) norm_cfg = c;
+        else store_cfg = c;
+      }
+    }
+  }
+
+  if (splits > 1 || (norm && norm_cfg.r == 0)) {
     pl->cfg = part_cfg;
     pl->mode = EPI_PARTIAL;
     pl->reduce = true;
@@ -169,8 +218,8 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     pl->mode = EPI_STORE;
     pl->reduce = false;
   }
-  pl->m_tiles = (int)((pr.M + pl->cfg.bm() - 1) / pl->cfg.bm());
-  pl->n_tiles = (pr.cout + pl->cfg.bn() - 1) / pl->cfg.bn();
+  pl->m_tiles = (int)ceil_div(pr.M, pl->cfg.bm());
+  pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());
   pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;
 
   // Workspace: NDHWC copies for NCDHW boundaries, then split-K partials.
@@ -259,10 +308,10 @@ conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogu
   if (buf && len) {
     static const char* names[] = {"store", "norm", "partial"};
     snprintf(buf, len,
-             "igemm wm=%d wn=%d p=%d j=%d bm=%d bn=%d mode=%s splits=%d steps=%d grid=%lld "
-             "reduce=%d workspace=%zu",
-             pl.cfg.wm, pl.cfg.wn, pl.cfg.p, pl.cfg.j, pl.cfg.bm(), pl.cfg.bn(), names[pl.mode],
-             pl.splits, pl.steps, pl.grid, (int)pl.reduce, pl.total);
+             "igemm mfma=%d wm=%d wn=%d pb=%d cb=%d kb=%d ns=%d bm=%d bn=%d mode=%s splits=%d "
+             "steps=%d grid=%lld reduce=%d workspace=%zu",
+             pl.cfg.r, pl.cfg.wm, pl.cfg.wn, pl.cfg.pb, pl.cfg.cb, pl.cfg.kb, pl.cfg.ns, pl.cfg.bm(),
+             pl.cfg.bn(), names[pl.mode], pl.splits, pl.steps, pl.grid, (int)pl.reduce, pl.total);
   }
   return CONV3D_OK;
 }

@@ -1,0 +1,607 @@
+// Implicit-GEMM main kernels of the bf16 3x3x3 NDHWC Conv3D on gfx950.
+//
+// The convolution is a GEMM whose activation operand is gathered on the fly
+// (FlyDSL issue "conv3d_implicit — accept and emit NDHWC ...", maintainer
+// reply): D[co][m] = sum_k W[co][k] * X[k][m], m an output pixel and
+// k = (tap, input channel). Causal and spatial zero padding live only in the
+// gather (Qwen-Image PR page, "T=1 degeneration"): a tap outside the input
+// gets an out-of-range offset and the buffer unit's range check returns zeros,
+// so no padded copy of the input exists.
+//
+// One K step is 32 input channels of one tap. The accumulators are
+// D[co][pixel] blocks of v_mfma_f32_32x32x16_bf16 (R = 32) or
+// v_mfma_f32_16x16x32_bf16 (R = 16). Per work-group of WM x WN waves:
+//  * weights: the [BN][32] slice of the packed weight for a K step is fetched
+//    3 steps ahead into a register staging ring, copied into an LDS ring 2
+//    steps ahead, and read into MFMA A-operand registers 1 step ahead, so no
+//    global or LDS latency sits between consecutive steps' MFMAs; one barrier
+//    per step. Weight rows are placed in a permuted order so that each lane's
+//    accumulators are consecutive output channels of one pixel, which makes
+//    the NDHWC stores 16-byte runs.
+//  * activations: each wave gathers its own pixels straight into VGPRs in the
+//    MFMA B-operand layout (16 bytes = 8 channels of one pixel per lane),
+//    2 steps ahead.
+//  * taps that no pixel of the tile can see (the two causal planes at T=1,
+//    frame edges) are skipped; steps are walked as (tap, channel chunk) with a
+//    find-first-set over the live-tap mask, and tap offsets come from the
+//    kernel arguments, so the loop has no integer division.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "conv3d_device.h"
+#include "conv3d_internal.h"
+
+namespace conv3d {
+
+namespace {
+
+constexpr unsigned kOobOffset = 0x80000000u;  // beyond any operand (< 2 GiB)
+
+// 16x16x32: lane l supplies operand row/col (l & 15) and channels
+// 8*(l >> 4) .. +8 of the 32; it holds D rows 4*(l >> 4) + e, col (l & 15).
+struct Mfma16 {
+  static constexpr int R = 16;
+  static constexpr int KS = 1;      // MFMAs per 32-channel K step
+  static constexpr int NACC = 4;    // accumulator floats per lane per block
+  typedef f32x4_t acc_t;
+  __device__ static int row(int lane) { return lane & 15; }
+  __device__ static int grp(int lane) { return lane >> 4; }
+  __device__ static int chunk(int lane, int /*h*/) { return lane >> 4; }
+  __device__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // Wave-local channel that D row r of block cb stands for: a lane of group
+  // g holds channels g*4*CB + 4*cb + e, one run of 4*CB.
+  __device__ static int chan_of(int cb, int r, int CB) { return (r >> 2) * 4 * CB + 4 * cb + (r & 3); }
+  __device__ static void row_of(int c, int CB, int& cb, int& r) {
+    const int g = c / (4 * CB), rem = c % (4 * CB);
+    cb = rem >> 2;
+    r = 4 * g + (rem & 3);
+  }
+};
+
+// 32x32x16: lane l supplies operand row/col (l & 31) and channels
+// 16*h + 8*(l >> 5) .. +8 for K half h; it holds D rows
+// 8*(e >> 2) + 4*(l >> 5) + (e & 3), col (l & 31).
+struct Mfma32 {
+  static constexpr int R = 32;
+  static constexpr int KS = 2;
+  static constexpr int NACC = 16;
+  typedef f32x16_t acc_t;
+  __device__ static int row(int lane) { return lane & 31; }
+  __device__ static int grp(int lane) { return lane >> 5; }
+  __device__ static int chunk(int lane, int h) { return 2 * h + (lane >> 5); }
+  __device__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // A lane of group g holds channels g*16*CB + 16*cb + e.
+  __device__ static int chan_of(int cb, int r, int CB) {
+    return ((r >> 2) & 1) * 16 * CB + 16 * cb + 4 * (r >> 3) + (r & 3);
+  }
+  __device__ static void row_of(int c, int CB, int& cb, int& r) {
+    const int g = c / (16 * CB), rem = c % (16 * CB);
+    cb = rem >> 4;
+    r = 8 * ((rem & 15) >> 2) + 4 * g + (rem & 3);
+  }
+};
+
+// LDS weight tile: rows of four 16-byte chunks (32 channels). The chunk index
+// is XORed with row bits so the 8 or 16 consecutive rows one operand read
+// touches land in distinct bank groups.
+__device__ __forceinline__ int lds_idx(int row, int chunk) {
+  return row * 4 + (chunk ^ (((row >> 1) ^ (row >> 3)) & 3));
+}
+
+// Work-group -> (pixel tile, channel tile, K split). Work-groups are dealt
+// round-robin to the 8 XCDs; give each XCD a contiguous run of tiles so tiles
+// sharing input rows or a weight slice meet in the same L2.
+struct TileCoord {
+  int m0, co0, split;
+};
+__device__ __forceinline__ TileCoord tile_coord(const IgemmArgs& a, int BM, int BN) {
+  int bid = blockIdx.x;
+  const int G8 = gridDim.x & ~7;
+  if (bid < G8) bid = (bid & 7) * (G8 >> 3) + (bid >> 3);
+  const int m_tile = bid % a.m_tiles;
+  const int rest = bid / a.m_tiles;
+  TileCoord t;
+  t.m0 = m_tile * BM;
+  t.co0 = (rest % a.n_tiles) * BN;
+  t.split = rest / a.n_tiles;
+  return t;
+}
+
+// Per-lane geometry of PB pixel blocks: byte offset of tap (0,0,0) and a
+// 27-bit mask of the taps that fall inside the input.
+template <int PB, int R>
+__device__ __forceinline__ unsigned pixel_geometry(const IgemmArgs& a, int m_first,
+                                                   long long (&base)[PB], unsigned (&tapmask)[PB]) {
+  unsigned live = 0;
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const int m = m_first + p * R;
+    tapmask[p] = 0;
+    base[p] = 0;
+    if (m < a.M) {
+      int r = m;
+      const int wo = r % a.Wo; r /= a.Wo;
+      const int ho = r % a.Ho; r /= a.Ho;
+      const int dq = r % a.Do;
+      const int n = r / a.Do;
+      const int d0 = dq * a.sd - a.pd;
+      const int h0 = ho * a.sh - a.ph;
+      const int w0 = wo * a.sw - a.pw;
+      unsigned vd = 0, vh = 0, vw = 0;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        vd |= (unsigned)(d0 + k >= 0 && d0 + k < a.D) << k;
+        vh |= (unsigned)(h0 + k >= 0 && h0 + k < a.H) << k;
+        vw |= (unsigned)(w0 + k >= 0 && w0 + k < a.W) << k;
+      }
+      unsigned tm = 0;
+#pragma unroll
+      for (int t = 0; t < 27; ++t)
+        tm |= ((vd >> (t / 9)) & (vh >> ((t / 3) % 3)) & (vw >> (t % 3)) & 1u) << t;
+      tapmask[p] = tm;
+      base[p] = ((((long long)n * a.D + d0) * a.H + h0) * a.W + w0) * (a.Cin * 2);
+    }
+    live |= tapmask[p];
+  }
+  return live;
+}
+
+__device__ __forceinline__ unsigned wave_or(unsigned v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
+  return v;
+}
+
+template <int I>
+struct SlotC {
+  static constexpr int value = I;
+};
+
+// K steps are encoded e = (tap << 8) | channel chunk; kEnd marks none.
+constexpr int kEnd = 0x7fffffff;
+
+// Gather of K step e into MFMA B-operand fragments. Branch-free: an invalid
+// tap or channel group ORs the top bit into the offset, which the buffer range
+// check turns into zeros.
+// A step of kEnd loads zeros (every offset out of range), so prefetches are
+// issued unconditionally and the wait counts stay static.
+template <class T, int PB>
+__device__ __forceinline__ void gather_x(const IgemmArgs& a, __amdgpu_buffer_rsrc_t rsrc, int e,
+                                         int lane, const long long (&base)[PB],
+                                         const unsigned (&tapmask)[PB], u32x4_t (&dst)[PB][T::KS]) {
+  const bool valid = e != kEnd;
+  const int t = valid ? e >> 8 : 0, cc = valid ? e & 255 : 0;
+  const int kd = t / 9, kh = (t / 3) % 3, kw = t % 3;
+  const long long delta =
+      (((long long)kd * a.H + kh) * a.W + kw) * (long long)(a.Cin * 2) + cc * 64;
+#pragma unroll
+  for (int h = 0; h < T::KS; ++h) {
+    const int ch = T::chunk(lane, h);
+    const unsigned chan_ok = (unsigned)(valid && cc * 32 + ch * 8 < a.Cin);
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const unsigned ok = chan_ok & (tapmask[p] >> t);
+      const unsigned off = (unsigned)(base[p] + delta + ch * 16) | (((ok & 1u) - 1u) & kOobOffset);
+      dst[p][h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const IgemmArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)a.x_bytes, 0x00020000);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const IgemmArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)a.wp, (short)0, (int)(27u * a.CC * a.Cout * 64u),
+                                           0x00020000);
+}
+
+// Epilogue. For pixel block p the lane holds channels cbase .. cbase+RUN-1 of
+// pixel m_first + p*R: run position NACC*cb + e is acc[cb][p][e].
+//   EPI_PARTIAL: fp32 partial sums of this K split.
+//   EPI_STORE:   value = B(B(B(acc) + bias) + residual), each step if enabled.
+//   EPI_NORM:    the whole contract; the work-group holds the pixel's full
+//                channel row (BN == Cout), its WN waves meeting through `red`.
+template <class T, int WM, int WN, int PB, int CB, int EPI>
+__device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (&acc)[CB][PB],
+                                         int m_first, int cbase, int split, int wave_m, int wave_n,
+                                         int lrow, int lgrp, float* red) {
+  constexpr int R = T::R, NACC = T::NACC, RUN = NACC * CB;
+  if (EPI == EPI_PARTIAL) {
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const int m = m_first + p * R;
+      if (m >= a.M || cbase >= a.Cout) continue;
+      f32x4_t* dst =
+          reinterpret_cast<f32x4_t*>(a.partial + ((long long)split * a.M + m) * a.Cout + cbase);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int q = 0; q < NACC / 4; ++q)
+          dst[(NACC * cb) / 4 + q] = f32x4_t{acc[cb][p][4 * q], acc[cb][p][4 * q + 1],
+                                             acc[cb][p][4 * q + 2], acc[cb][p][4 * q + 3]};
+    }
+    return;
+  }
+  if (EPI == EPI_STORE) {
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const int m = m_first + p * R;
+      if (m >= a.M || cbase >= a.Cout) continue;
+      const long long off = (long long)m * a.Cout + cbase;
+#pragma unroll
+      for (int c8 = 0; c8 < RUN; c8 += 8) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = rbf(acc[(c8 + e) / NACC][p][(c8 + e) % NACC]);
+        if (a.flags & F_BIAS) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + a.bias[cbase + c8 + e]);
+        }
+        if (a.flags & F_RESIDUAL) {
+          const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.residual + off + c8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + lane_bf(rv, e));
+        }
+        const u32x4_t ov = {pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+        if (a.flags & F_RESIDUAL_OUT) *reinterpret_cast<u32x4_t*>(a.residual_out + off + c8) = ov;
+        *reinterpret_cast<u32x4_t*>(a.y + off + c8) = ov;
+      }
+    }
+    return;
+  }
+  // EPI_NORM. value is bf16 by construction, so it is kept packed two per
+  // register while the row's sum of squares is formed.
+  unsigned vpk[PB][RUN / 2];
+  float ss[PB];
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const int m = m_first + p * R;
+    const bool ok = m < a.M;
+    const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
+    float t = 0.f;
+#pragma unroll
+    for (int c8 = 0; c8 < RUN; c8 += 8) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = rbf(acc[(c8 + e) / NACC][p][(c8 + e) % NACC]);
+      if (a.flags & F_BIAS) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + a.bias[cbase + c8 + e]);
+      }
+      if ((a.flags & F_RESIDUAL) && ok) {
+        const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.residual + off + c8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + lane_bf(rv, e));
+      }
+      const u32x4_t ov = {pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+      if ((a.flags & F_RESIDUAL_OUT) && ok) *reinterpret_cast<u32x4_t*>(a.residual_out + off + c8) = ov;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vpk[p][c8 / 2 + q] = ov[q];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t += v[e] * v[e];
+    }
+#pragma unroll
+    for (int o = R; o < 64; o <<= 1) t += __shfl_xor(t, o);  // lanes of the same pixel
+    ss[p] = t;
+  }
+  if (WN > 1) {  // ... and the WN waves
+    if (lgrp == 0) {
+#pragma unroll
+      for (int p = 0; p < PB; ++p) red[((wave_n * WM + wave_m) * PB + p) * R + lrow] = ss[p];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      float t = 0.f;
+      for (int wn = 0; wn < WN; ++wn) t += red[((wn * WM + wave_m) * PB + p) * R + lrow];
+      ss[p] = t;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const int m = m_first + p * R;
+    if (m >= a.M) continue;
+    const float den = fmaxf(sqrtf(ss[p]), 1e-12f);
+    const long long off = (long long)m * a.Cout + cbase;
+#pragma unroll
+    for (int c8 = 0; c8 < RUN; c8 += 8) {
+      const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.gamma + cbase + c8);
+      const u32x4_t vv = {vpk[p][c8 / 2], vpk[p][c8 / 2 + 1], vpk[p][c8 / 2 + 2], vpk[p][c8 / 2 + 3]};
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float nrm = rbf(lane_bf(vv, e) / den);
+        const float scl = rbf(nrm * a.sqrt_c);
+        const float aff = rbf(scl * lane_bf(gv, e));
+        o[e] = rbf(aff / (1.0f + expf(-aff)));
+      }
+      const u32x4_t ov = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+      *reinterpret_cast<u32x4_t*>(a.y + off + c8) = ov;
+    }
+  }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// Main kernel. A pipeline step is KB consecutive live K steps (KB*32
+// channels); NS is the depth of every ring (pixel fragments NS-1 steps
+// ahead, weight fetches NS steps ahead, LDS stages 2 ahead, weight fragments
+// 1 ahead).
+// ----------------------------------------------------------------------------
+template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
+  constexpr int R = T::R, KS = T::KS, NACC = T::NACC;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BM = R * PB * WM;
+  constexpr int BN = R * CB * WN;
+  constexpr int CHUNKS = BN * 4;               // 16-byte chunks per weight slice
+  constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread
+  constexpr int RUN = NACC * CB;
+  typedef typename T::acc_t acc_t;
+  static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
+  static_assert(NS == 2 || NS == 3, "ring depth");
+
+  __shared__ u32x4_t wlds[NS][KB][CHUNKS];
+  __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
+  __shared__ unsigned live_sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_m = wave % WM;
+  const int wave_n = wave / WM;
+  const int lrow = T::row(lane);
+  const int lgrp = T::grp(lane);
+  const TileCoord tc = tile_coord(a, BM, BN);
+  const int m_first = tc.m0 + wave_m * PB * R + lrow;
+
+  long long base[PB];
+  unsigned tapmask[PB];
+  unsigned live = wave_or(pixel_geometry<PB, R>(a, m_first, base, tapmask));
+  // Taps no pixel of the tile can see are skipped by the whole work-group.
+  if (tid == 0) live_sh = 0;
+  __syncthreads();
+  if (lane == 0) atomicOr(&live_sh, live);
+  __syncthreads();
+  live = __builtin_amdgcn_readfirstlane(live_sh);
+  const __amdgpu_buffer_rsrc_t xrsrc = x_rsrc(a);
+  const __amdgpu_buffer_rsrc_t wrsrc = w_rsrc(a);
+
+  // K steps of this split, in (tap, chunk) order, live taps only.
+  const int s_begin = tc.split * a.steps_per_split;
+  const int s_end = min(s_begin + a.steps_per_split, 27 * a.CC);
+  auto valid_step = [&](int t, int cc) -> int {
+    return (t < 27 && t * a.CC + cc < s_end) ? ((t << 8) | cc) : kEnd;
+  };
+  auto next_step = [&](int e) -> int {
+    if (e == kEnd) return kEnd;
+    int t = e >> 8, cc = (e & 255) + 1;
+    if (cc == a.CC) {
+      cc = 0;
+      const unsigned rest = live & (~0u << (t + 1));
+      t = rest ? __builtin_ctz(rest) : 27;
+    }
+    return valid_step(t, cc);
+  };
+  auto first_step = [&]() -> int {
+    if (s_begin >= s_end) return kEnd;
+    int t = s_begin / a.CC, cc = s_begin % a.CC;
+    if (!((live >> t) & 1u)) {
+      const unsigned rest = live & (~0u << t);
+      t = rest ? __builtin_ctz(rest) : 27;
+      cc = 0;
+    }
+    return valid_step(t, cc);
+  };
+  // A pipeline step: KB consecutive K steps starting after `prev`.
+  auto next_group = [&](int prev, int (&g)[KB]) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      g[k] = next_step(prev);
+      prev = g[k];
+    }
+  };
+
+  acc_t acc[CB][PB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) acc[cb][p][e] = 0.f;
+
+  // Weight slice chunk c (row c >> 2, 16-byte chunk c & 3) -> LDS row in
+  // MFMA order: wave-column, block cb, D row r.
+  auto lds_row_of = [&](int c) -> int {
+    const int col = c >> 2;
+    int cb, r;
+    T::row_of(col % (R * CB), CB, cb, r);
+    return ((col / (R * CB)) * CB + cb) * R + r;
+  };
+  unsigned woff[CPT];  // this thread's chunks, relative to a step's slice
+  int wdst[CPT];       // and where they go in an LDS slice
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * NT;
+    const bool ok = c < CHUNKS && tc.co0 + (c >> 2) < a.Cout;
+    woff[i] = ok ? (unsigned)((tc.co0 * 4 + c) * 16) : kOobOffset;
+    wdst[i] = (c < CHUNKS) ? lds_idx(lds_row_of(c), c & 3) : 0;
+  }
+  // Every fetch below is unconditional (a step of kEnd reads zeros, a
+  // finished pipeline reads or writes LDS slots no later step uses), so the
+  // compiler's wait counts are exact.
+  auto load_w = [&](const int (&g)[KB], u32x4_t (&dst)[KB][CPT]) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int e = g[k];
+      const unsigned soff =
+          (e == kEnd) ? kOobOffset : (unsigned)((e >> 8) * a.CC + (e & 255)) * (unsigned)a.Cout * 64u;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        dst[k][i] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(woff[i] + soff), 0, 0);
+    }
+  };
+  auto store_w = [&](int stage, const u32x4_t (&src)[KB][CPT]) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (CHUNKS % NT == 0 || tid + i * NT < CHUNKS) wlds[stage][k][wdst[i]] = src[k][i];
+  };
+  auto read_frags = [&](int stage, u32x4_t (&dst)[KB][CB][KS]) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+      for (int h = 0; h < KS; ++h)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          dst[k][cb][h] = wlds[stage][k][lds_idx((wave_n * CB + cb) * R + lrow, T::chunk(lane, h))];
+  };
+  auto gather = [&](const int (&g)[KB], u32x4_t (&dst)[KB][PB][KS]) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) gather_x<T, PB>(a, xrsrc, g[k], lane, base, tapmask, dst[k]);
+  };
+
+  u32x4_t xr[NS][KB][PB][KS];   // pixel fragments
+  u32x4_t wst[NS][KB][CPT];     // weight slices in flight to LDS
+  u32x4_t wfr[NS][KB][CB][KS];  // weight fragments
+
+  // Pipeline steps of iterations i .. i+NS: ev[j] (KB K steps each).
+  int ev[NS + 1][KB];
+  {
+    int prev = first_step();
+    ev[0][0] = prev;
+#pragma unroll
+    for (int k = 1; k < KB; ++k) ev[0][k] = prev = next_step(prev);
+#pragma unroll
+    for (int j = 1; j <= NS; ++j) {
+      next_group(prev, ev[j]);
+      prev = ev[j][KB - 1];
+    }
+  }
+  // Prologue: pixels of steps 0..NS-2, weights of steps 0..NS-1, LDS stages
+  // of steps 0 and 1, fragments of step 0.
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j) gather(ev[j], xr[j]);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) load_w(ev[j], wst[j]);
+  store_w(0, wst[0]);
+  store_w(1, wst[1]);
+  __syncthreads();
+  read_frags(0, wfr[0]);
+
+  // Iteration i (ring slot i % NS) computes step ev[0]. The body is
+  // instantiated once per slot so every ring index is a constant.
+  auto iteration = [&](auto slot_c) -> bool {
+    constexpr int slot = decltype(slot_c)::value;
+    constexpr int s1 = (slot + 1) % NS, s2 = (slot + 2) % NS, sx = (slot + NS - 1) % NS;
+    if (ev[0][0] == kEnd) return false;
+    // Next step's fragments first: their LDS latency overlaps this step's
+    // MFMAs instead of the barrier.
+    read_frags(s1, wfr[s1]);
+    __builtin_amdgcn_sched_barrier(0);
+    gather(ev[NS - 1], xr[sx]);
+    load_w(ev[NS], wst[slot]);
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+      for (int h = 0; h < KS; ++h)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int p = 0; p < PB; ++p)
+            acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wfr[slot][k][cb][h]),
+                                __builtin_bit_cast(bf16x8_t, xr[slot][k][p][h]), acc[cb][p]);
+    // Step i+2's slices into their stage, last read before the previous
+    // barrier.
+    store_w(s2, wst[s2]);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int k = 0; k < KB; ++k) ev[j][k] = ev[j + 1][k];
+    next_group(ev[NS - 1][KB - 1], ev[NS]);
+    return true;
+  };
+  for (;;) {
+    if (!iteration(SlotC<0>{})) break;
+    if (!iteration(SlotC<1>{})) break;
+    if constexpr (NS > 2) {
+      if (!iteration(SlotC<2 % NS>{})) break;
+    }
+  }
+  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, m_first, tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split,
+                                   wave_m, wave_n, lrow, lgrp, red);
+}
+
+// ----------------------------------------------------------------------------
+// Compiled configurations.
+// ----------------------------------------------------------------------------
+namespace {
+
+template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
+int launch_one(const IgemmArgs& args, int grid, void* stream) {
+  hipLaunchKernelGGL((igemm_kernel<T, WM, WN, PB, CB, KB, NS, EPI>), dim3((unsigned)grid),
+                     dim3(64 * WM * WN), 0, (hipStream_t)stream, args);
+  return (int)hipGetLastError();
+}
+
+struct Entry {
+  TileCfg cfg;
+  int mode;
+  int (*fn)(const IgemmArgs&, int, void*);
+};
+
+#define C32(WM, WN, PB, CB, KB, NS, MODE) \
+  {{32, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE>}
+#define C16(WM, WN, PB, CB, KB, NS, MODE) \
+  {{16, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE>}
+const Entry kEntries[] = {
+    // Large-M layers: channel tile 128 / 96 / 64.
+    C32(4, 1, 2, 4, 1, 3, EPI_STORE),
+    C32(4, 1, 2, 4, 2, 3, EPI_STORE),
+    C32(4, 1, 2, 4, 2, 2, EPI_STORE),
+    C32(4, 1, 4, 4, 1, 2, EPI_STORE),
+    C32(4, 1, 2, 3, 1, 3, EPI_STORE),
+    C32(4, 1, 2, 3, 2, 3, EPI_STORE),
+    C32(4, 1, 2, 2, 1, 3, EPI_STORE),
+    // Split-K partials (small M, large K).
+    C32(4, 1, 2, 4, 1, 3, EPI_PARTIAL),
+    C32(4, 1, 1, 4, 1, 3, EPI_PARTIAL),
+    C32(4, 1, 1, 4, 2, 3, EPI_PARTIAL),
+    C32(4, 1, 2, 3, 1, 3, EPI_PARTIAL),
+    C32(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
+    // Fused channel-row norm: the whole row of Cout channels in one group.
+    C16(2, 2, 2, 10, 1, 3, EPI_NORM),  // Cout 320
+    C16(4, 1, 2, 10, 1, 3, EPI_NORM),  // Cout 160
+    // Any Cout % 16 == 0.
+    C16(4, 1, 4, 2, 1, 3, EPI_STORE),
+    C16(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
+};
+#undef C32
+#undef C16
+
+const Entry* find_entry(const TileCfg& c, int mode) {
+  for (const Entry& e : kEntries)
+    if (e.cfg.r == c.r && e.cfg.wm == c.wm && e.cfg.wn == c.wn && e.cfg.pb == c.pb &&
+        e.cfg.cb == c.cb && e.cfg.kb == c.kb && e.cfg.ns == c.ns && e.mode == mode)
+      return &e;
+  return nullptr;
+}
+
+}  // namespace
+
+bool igemm_has_config(const TileCfg& cfg, int mode) { return find_entry(cfg, mode) != nullptr; }
+
+int launch_igemm(const TileCfg& cfg, int mode, const IgemmArgs& args, int grid, void* stream) {
+  const Entry* e = find_entry(cfg, mode);
+  if (!e) return -1;
+  return e->fn(args, grid, stream);
+}
+
+}  // namespace conv3d

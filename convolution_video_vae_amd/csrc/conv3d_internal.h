@@ -54,12 +54,15 @@ struct ReduceArgs {
   float sqrt_c;
 };
 
-// A kernel configuration: WM x WN waves, each wave P pixel blocks x J
-// channel blocks of 16 (so BM = 16*P*WM pixels, BN = 16*J*WN channels).
+// A main-kernel configuration: MFMA block size R (16: v_mfma_f32_16x16x32_bf16,
+// 32: v_mfma_f32_32x32x16_bf16), WM x WN waves, each wave PB pixel blocks x
+// CB channel blocks of R (BM = R*PB*WM pixels, BN = R*CB*WN channels); a
+// pipeline step covers KB K steps of 32 channels and the pipeline rings are
+// NS deep.
 struct TileCfg {
-  int wm, wn, p, j;
-  int bm() const { return 16 * p * wm; }
-  int bn() const { return 16 * j * wn; }
+  int r, wm, wn, pb, cb, kb, ns;
+  int bm() const { return r * pb * wm; }
+  int bn() const { return r * cb * wn; }
 };
 
 // Launchers (conv3d_kernels.hip). Each returns 0 on success or the HIP
