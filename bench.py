@@ -28,6 +28,26 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
+# HBM traffic of the headline layer's main kernel, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch), each divided by what
+# the same counter read per byte for an elementwise kernel that reads and
+# writes a known number of bytes (the --calibrate-copy pass). Valid only for
+# the kernel source it was taken on: reported as null once the source hash
+# differs.
+TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "2566e44e0784386e",
+           "bytes": 1278668662}   # 992.8 MB fetched (FETCH_SIZE x 2.000) + 285.8 MB written
+KERNEL_SOURCES = ("convolution_video_vae_amd/csrc/conv3d_igemm.hip",
+                  "convolution_video_vae_amd/csrc/conv3d_device.h")
+
+
+def kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -38,6 +58,9 @@ def parse():
     p.add_argument("--no-layers", action="store_true", help="time only the headline layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a 1 GiB read + 1 GiB write elementwise kernel 3 times (the "
+                        "byte-counter calibration for rocprofv3 --pmc passes)")
     p.add_argument("--sweep", default=None,
                    help="development: time the headline layer under each CONV3D_TILE value in "
                         "this ';'-separated list and print one line per tile to stderr")
@@ -187,6 +210,21 @@ def main():
             "us": round(tms * 1e3, 2), "gbs": round(2 * src.numel() * 2 / (tms * 1e-3) / 1e9, 1),
             "pct_hbm": round(100 * 2 * src.numel() * 2 / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"calibrate-copy: torch.neg over {src.numel() * 2} bytes read and written, "
+              "3 launches", file=sys.stderr, flush=True)
+        del src, dst
+
+    traffic = None
+    if TRAFFIC is not None and TRAFFIC.get("kernel_hash") == kernel_hash() \
+            and TRAFFIC.get("workload") == head.name:
+        traffic = TRAFFIC["bytes"]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head, args.cpu_seconds)
@@ -209,7 +247,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic, "kernel_hash": kernel_hash(),
+                     "kernel": "conv3d igemm main kernel (one launch per step)"},
         "cpu_baseline": cpu,
         "per_layer": per_layer,
         "wall_s_timed": round(wall, 3),

@@ -130,12 +130,19 @@ constexpr int kCUs = 256;
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 // Channel blocking: the widest tile that divides Cout (each lane's run of
-// channels must stay inside Cout).
+// channels must stay inside Cout). `store` is the measured-fastest direct
+// configuration, the plain one is used for split-K partials.
 TileCfg channel_cfg(int cout) {
   if (cout % 128 == 0) return {32, 4, 1, 2, 4, 1, 3};
   if (cout % 96 == 0) return {32, 4, 1, 2, 3, 1, 3};
   if (cout % 32 == 0) return {32, 4, 1, 2, 2, 1, 3};
   return {16, 4, 1, 4, 2, 1, 3};
+}
+
+TileCfg store_channel_cfg(int cout) {
+  if (cout % 128 == 0) return {32, 4, 1, 2, 4, 2, 0};   // three-stage LDS tile kernel
+  if (cout % 96 == 0) return {32, 4, 1, 2, 3, 1, 4};
+  return channel_cfg(cout);
 }
 
 void make_plan(const Problem& pr, int split_req, Plan* pl) {
@@ -145,20 +152,8 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   TileCfg base = channel_cfg(pr.cout);
   const long long n_tiles = ceil_div(pr.cout, base.bn());
 
-  // Pixel blocking: among the compiled depths, the one that wastes the least
-  // of the last round of work-groups over the 256 CUs.
-  TileCfg store_cfg = base;
-  if (base.r == 32) {
-    long long best = -1;
-    for (int pb : {2}) {
-      TileCfg c = base;
-      c.pb = pb;
-      if (!igemm_has_config(c, EPI_STORE)) continue;
-      const long long tiles = ceil_div(pr.M, c.bm()) * n_tiles;
-      const long long cost = ceil_div(tiles, kCUs) * pb;   // rounds x time per round
-      if (best < 0 || cost < best) { best = cost; store_cfg = c; }
-    }
-  }
+  TileCfg store_cfg = store_channel_cfg(pr.cout);
+  if (!igemm_has_config(store_cfg, EPI_STORE)) store_cfg = base;
   TileCfg part_cfg = base;
   part_cfg.pb = 2;
   if (base.r == 32 && ceil_div(pr.M, part_cfg.bm()) * n_tiles < 64) {
@@ -170,9 +165,10 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   // Fused-norm kernels hold the whole channel row of a pixel in one group.
   TileCfg norm_cfg = {0, 0, 0, 0, 0, 0, 0};
   if (norm) {
-    const TileCfg cands[] = {{16, 2, 2, 2, 10, 1, 3}, {16, 4, 1, 2, 10, 1, 3}};
+    const TileCfg cands[] = {{16, 2, 2, 2, 10, 2, 0}, {16, 2, 2, 2, 10, 1, 3},
+                             {16, 4, 1, 2, 10, 1, 3}};
     for (const TileCfg& c : cands)
-      if (c.bn() == pr.cout && igemm_has_config(c, EPI_NORM)) norm_cfg = c;
+      if (norm_cfg.r == 0 && c.bn() == pr.cout && igemm_has_config(c, EPI_NORM)) norm_cfg = c;
   }
 
   const long long store_tiles = ceil_div(pr.M, store_cfg.bm()) * n_tiles;

@@ -329,7 +329,7 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
 
 // ----------------------------------------------------------------------------
 // Main kernel. A pipeline step is KB consecutive live K steps (KB*32
-// channels); NS is the depth of every ring (pixel fragments NS-1 steps
+// channels); NS is the depth of the rings (pixel fragments NS-1 steps
 // ahead, weight fetches NS steps ahead, LDS stages 2 ahead, weight fragments
 // 1 ahead).
 // ----------------------------------------------------------------------------
@@ -344,7 +344,8 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
   constexpr int RUN = NACC * CB;
   typedef typename T::acc_t acc_t;
   static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
-  static_assert(NS == 2 || NS == 3, "ring depth");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  constexpr int NF = (NS % 2 == 0) ? 2 : NS;  // weight-fragment ring: current + next
 
   __shared__ u32x4_t wlds[NS][KB][CHUNKS];
   __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
 
   u32x4_t xr[NS][KB][PB][KS];   // pixel fragments
   u32x4_t wst[NS][KB][CPT];     // weight slices in flight to LDS
-  u32x4_t wfr[NS][KB][CB][KS];  // weight fragments
+  u32x4_t wfr[NF][KB][CB][KS];  // weight fragments
 
   // Pipeline steps of iterations i .. i+NS: ev[j] (KB K steps each).
   int ev[NS + 1][KB];
@@ -500,10 +501,11 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
   auto iteration = [&](auto slot_c) -> bool {
     constexpr int slot = decltype(slot_c)::value;
     constexpr int s1 = (slot + 1) % NS, s2 = (slot + 2) % NS, sx = (slot + NS - 1) % NS;
+    constexpr int f0 = slot % NF, f1 = (slot + 1) % NF;
     if (ev[0][0] == kEnd) return false;
     // Next step's fragments first: their LDS latency overlaps this step's
     // MFMAs instead of the barrier.
-    read_frags(s1, wfr[s1]);
+    read_frags(s1, wfr[f1]);
     __builtin_amdgcn_sched_barrier(0);
     gather(ev[NS - 1], xr[sx]);
     load_w(ev[NS], wst[slot]);
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int p = 0; p < PB; ++p)
-            acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wfr[slot][k][cb][h]),
+            acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wfr[f0][k][cb][h]),
                                 __builtin_bit_cast(bf16x8_t, xr[slot][k][p][h]), acc[cb][p]);
     // Step i+2's slices into their stage, last read before the previous
     // barrier.
@@ -534,9 +536,257 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
     if constexpr (NS > 2) {
       if (!iteration(SlotC<2 % NS>{})) break;
     }
+    if constexpr (NS > 3) {
+      if (!iteration(SlotC<3 % NS>{})) break;
+    }
   }
   epilogue<T, WM, WN, PB, CB, EPI>(a, acc, m_first, tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split,
                                    wave_m, wave_n, lrow, lgrp, red);
+}
+
+// ----------------------------------------------------------------------------
+// Tile kernel: both operands staged through LDS, as in a GEMM.
+//
+// A pipeline stage covers KB consecutive live K steps. The stage's pixel tile
+// (BM pixels x KB*64 contiguous bytes of one tap each) is loaded with
+// coalesced 16-byte loads, a wave instruction covering 64/(4*KB) whole pixel
+// segments: far fewer cache lines per instruction than gathering straight
+// into the MFMA operand layout, whose 32 lanes each touch a different pixel.
+// The tile is stored in LDS with an XOR swizzle of its 16-byte chunks and read
+// back in the MFMA B-operand layout; the weight slices likewise.
+//
+// Pipeline: three LDS stages. Iteration i computes stage i, stores stage i+2
+// (fetched into registers during iteration i-1) and fetches stage i+3; one
+// barrier. Within a stage the operand fragments of sub-step j+1 (one K half
+// of one K step) are read while the MFMAs of sub-step j run, and the last
+// sub-step reads the first fragments of stage i+1, whose LDS slot was filled
+// before the previous barrier: no LDS latency sits in front of the MFMAs.
+// ----------------------------------------------------------------------------
+template <int XQ>
+__device__ __forceinline__ int xs_idx(int pixel, int chunk) {
+  // XQ 16-byte chunks per pixel row; the swizzle keeps 8- and 16-lane groups
+  // reading one chunk of consecutive pixels in distinct bank groups.
+  if constexpr (XQ == 8) return pixel * 8 + (chunk ^ (((pixel >> 1) ^ (pixel << 2)) & 7));
+  else return pixel * 4 + (chunk ^ (((pixel >> 1) ^ (pixel >> 3)) & 3));
+}
+
+template <class T, int WM, int WN, int PB, int CB, int KB, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void igemm_tile_kernel(IgemmArgs a) {
+  constexpr int R = T::R, KS = T::KS, NACC = T::NACC;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BM = R * PB * WM;
+  constexpr int BN = R * CB * WN;
+  constexpr int XQ = 4 * KB;                   // 16-byte chunks per pixel per stage
+  constexpr int XCH = BM * XQ;                 // pixel-tile chunks per stage
+  constexpr int XPT = XCH / NT;                // ... per thread
+  constexpr int WCH = BN * 4;                  // weight chunks per K step
+  constexpr int WPT = (WCH + NT - 1) / NT;     // ... per thread
+  constexpr int RUN = NACC * CB;
+  constexpr int NSTG = 3;                      // LDS stages
+  constexpr int J = KB * KS;                   // MFMA sub-steps per stage
+  typedef typename T::acc_t acc_t;
+  static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
+  static_assert(XQ == 4 || XQ == 8, "stage of 1 or 2 K steps");
+  static_assert(XCH % NT == 0 && NT % XQ == 0, "pixel tile evenly split over threads");
+
+  __shared__ u32x4_t xs[NSTG][XCH];
+  __shared__ u32x4_t ws[NSTG][KB][WCH];
+  __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
+  __shared__ unsigned live_sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_m = wave % WM;
+  const int wave_n = wave / WM;
+  const int lrow = T::row(lane);
+  const int lgrp = T::grp(lane);
+  const TileCoord tc = tile_coord(a, BM, BN);
+
+  // This thread loads chunk xj of the pixels tid/XQ + i*(NT/XQ) of the tile;
+  // chunk xj belongs to K step xj/4 of the stage, bytes 16*(xj%4).. of it.
+  const int xj = tid % XQ;
+  const int xk = xj >> 2;
+  constexpr int XSTRIDE = NT / XQ;
+  long long base[XPT];
+  unsigned tapmask[XPT];
+  unsigned live = 0;
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    long long b1[1];
+    unsigned t1[1];
+    live |= pixel_geometry<1, 1>(a, tc.m0 + tid / XQ + i * XSTRIDE, b1, t1);
+    base[i] = b1[0] + (xj & 3) * 16;
+    tapmask[i] = t1[0];
+  }
+  live = wave_or(live);
+  if (tid == 0) live_sh = 0;
+  __syncthreads();
+  if (lane == 0) atomicOr(&live_sh, live);
+  __syncthreads();
+  live = __builtin_amdgcn_readfirstlane(live_sh);
+  const __amdgpu_buffer_rsrc_t xrsrc = x_rsrc(a);
+  const __amdgpu_buffer_rsrc_t wrsrc = w_rsrc(a);
+
+  const int s_begin = tc.split * a.steps_per_split;
+  const int s_end = min(s_begin + a.steps_per_split, 27 * a.CC);
+  auto valid_step = [&](int t, int cc) -> int {
+    return (t < 27 && t * a.CC + cc < s_end) ? ((t << 8) | cc) : kEnd;
+  };
+  auto next_step = [&](int e) -> int {
+    if (e == kEnd) return kEnd;
+    int t = e >> 8, cc = (e & 255) + 1;
+    if (cc == a.CC) {
+      cc = 0;
+      const unsigned rest = live & (~0u << (t + 1));
+      t = rest ? __builtin_ctz(rest) : 27;
+    }
+    return valid_step(t, cc);
+  };
+  auto first_step = [&]() -> int {
+    if (s_begin >= s_end) return kEnd;
+    int t = s_begin / a.CC, cc = s_begin % a.CC;
+    if (!((live >> t) & 1u)) {
+      const unsigned rest = live & (~0u << t);
+      t = rest ? __builtin_ctz(rest) : 27;
+      cc = 0;
+    }
+    return valid_step(t, cc);
+  };
+  auto next_group = [&](int prev, int (&g)[KB]) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      g[k] = next_step(prev);
+      prev = g[k];
+    }
+  };
+
+  acc_t acc[CB][PB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) acc[cb][p][e] = 0.f;
+
+  auto lds_row_of = [&](int c) -> int {
+    const int col = c >> 2;
+    int cb, r;
+    T::row_of(col % (R * CB), CB, cb, r);
+    return ((col / (R * CB)) * CB + cb) * R + r;
+  };
+  unsigned woff[WPT];
+  int wdst[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int c = tid + i * NT;
+    const bool ok = c < WCH && tc.co0 + (c >> 2) < a.Cout;
+    woff[i] = ok ? (unsigned)((tc.co0 * 4 + c) * 16) : kOobOffset;
+    wdst[i] = (c < WCH) ? lds_idx(lds_row_of(c), c & 3) : 0;
+  }
+
+  // Staging registers for the stage in flight. Loads are unconditional: a
+  // step of kEnd reads zeros, so the compiler's wait counts stay exact.
+  u32x4_t xst[XPT];
+  u32x4_t wst[KB][WPT];
+  auto load_stage = [&](const int (&g)[KB]) {
+    const int e = g[xk];
+    const bool valid = e != kEnd;
+    const int t = valid ? e >> 8 : 0, cc = valid ? e & 255 : 0;
+    const long long delta =
+        (((long long)(t / 9) * a.H + (t / 3) % 3) * a.W + t % 3) * (long long)(a.Cin * 2) + cc * 64;
+    const unsigned chan_ok = (unsigned)(valid && cc * 32 + (xj & 3) * 8 < a.Cin);
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const unsigned ok = chan_ok & (tapmask[i] >> t);
+      const unsigned off = (unsigned)(base[i] + delta) | (((ok & 1u) - 1u) & kOobOffset);
+      xst[i] = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, (int)off, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int ek = g[k];
+      const unsigned soff =
+          (ek == kEnd) ? kOobOffset : (unsigned)((ek >> 8) * a.CC + (ek & 255)) * (unsigned)a.Cout * 64u;
+#pragma unroll
+      for (int i = 0; i < WPT; ++i)
+        wst[k][i] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(woff[i] + soff), 0, 0);
+    }
+  };
+  auto store_stage = [&](int stg) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) xs[stg][xs_idx<XQ>(tid / XQ + i * XSTRIDE, xj)] = xst[i];
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+      for (int i = 0; i < WPT; ++i)
+        if (WCH % NT == 0 || tid + i * NT < WCH) ws[stg][k][wdst[i]] = wst[k][i];
+  };
+  // Fragments of sub-step jj (K step jj / KS, half jj % KS) of LDS slot stg.
+  auto read_frags = [&](int stg, int jj, u32x4_t (&xf)[PB], u32x4_t (&wf)[CB]) {
+    const int k = jj / KS, h = jj % KS;
+    const int q = 4 * k + T::chunk(lane, h);
+#pragma unroll
+    for (int p = 0; p < PB; ++p) xf[p] = xs[stg][xs_idx<XQ>((wave_m * PB + p) * R + lrow, q)];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      wf[cb] = ws[stg][k][lds_idx((wave_n * CB + cb) * R + lrow, T::chunk(lane, h))];
+  };
+
+  // Stages of iterations i .. i+3.
+  int g0[KB], g1[KB], g2[KB], g3[KB];
+  g0[0] = first_step();
+#pragma unroll
+  for (int k = 1; k < KB; ++k) g0[k] = next_step(g0[k - 1]);
+  next_group(g0[KB - 1], g1);
+  next_group(g1[KB - 1], g2);
+
+  u32x4_t xf[2][PB], wf[2][CB];
+  load_stage(g0);
+  store_stage(0);
+  load_stage(g1);
+  store_stage(1);
+  load_stage(g2);
+  __syncthreads();
+  read_frags(0, 0, xf[0], wf[0]);
+
+  auto iteration = [&](auto slot_c) -> bool {
+    constexpr int slot = decltype(slot_c)::value;
+    constexpr int nxt = (slot + 1) % NSTG, far = (slot + 2) % NSTG;
+    if (g0[0] == kEnd) return false;
+    next_group(g2[KB - 1], g3);
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      // Fragments of the next sub-step (the first of stage i+1 at the end).
+      if (jj + 1 < J) read_frags(slot, jj + 1, xf[(jj + 1) & 1], wf[(jj + 1) & 1]);
+      else read_frags(nxt, 0, xf[(jj + 1) & 1], wf[(jj + 1) & 1]);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+          acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wf[jj & 1][cb]),
+                              __builtin_bit_cast(bf16x8_t, xf[jj & 1][p]), acc[cb][p]);
+    }
+    store_stage(far);
+    load_stage(g3);
+    __syncthreads();
+    // J is even, so sub-step 0 of the next stage is in fragment slot 0.
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      g0[k] = g1[k];
+      g1[k] = g2[k];
+      g2[k] = g3[k];
+    }
+    return true;
+  };
+  static_assert(J % 2 == 0, "fragment double buffer");
+  for (;;) {
+    if (!iteration(SlotC<0>{})) break;
+    if (!iteration(SlotC<1>{})) break;
+    if (!iteration(SlotC<2>{})) break;
+  }
+  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
+                                   tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split, wave_m, wave_n,
+                                   lrow, lgrp, red);
 }
 
 // ----------------------------------------------------------------------------
@@ -546,8 +796,12 @@ namespace {
 
 template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
 int launch_one(const IgemmArgs& args, int grid, void* stream) {
-  hipLaunchKernelGGL((igemm_kernel<T, WM, WN, PB, CB, KB, NS, EPI>), dim3((unsigned)grid),
-                     dim3(64 * WM * WN), 0, (hipStream_t)stream, args);
+  if constexpr (NS == 0)
+    hipLaunchKernelGGL((igemm_tile_kernel<T, WM, WN, PB, CB, KB, EPI>), dim3((unsigned)grid),
+                       dim3(64 * WM * WN), 0, (hipStream_t)stream, args);
+  else
+    hipLaunchKernelGGL((igemm_kernel<T, WM, WN, PB, CB, KB, NS, EPI>), dim3((unsigned)grid),
+                       dim3(64 * WM * WN), 0, (hipStream_t)stream, args);
   return (int)hipGetLastError();
 }
 
@@ -562,13 +816,19 @@ struct Entry {
 #define C16(WM, WN, PB, CB, KB, NS, MODE) \
   {{16, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE>}
 const Entry kEntries[] = {
+    // ns = 0: tile kernel (pixels staged through LDS too).
+    C32(4, 1, 2, 4, 2, 0, EPI_STORE),
+    C32(4, 1, 2, 4, 1, 0, EPI_STORE),
+    C32(4, 1, 2, 3, 2, 0, EPI_STORE),
+    C32(4, 1, 2, 4, 2, 0, EPI_PARTIAL),
+    C16(2, 2, 2, 10, 2, 0, EPI_NORM),
     // Large-M layers: channel tile 128 / 96 / 64.
     C32(4, 1, 2, 4, 1, 3, EPI_STORE),
-    C32(4, 1, 2, 4, 2, 3, EPI_STORE),
-    C32(4, 1, 2, 4, 2, 2, EPI_STORE),
+    C32(4, 1, 2, 4, 1, 4, EPI_STORE),
+    C32(4, 1, 2, 4, 2, 4, EPI_STORE),
     C32(4, 1, 4, 4, 1, 2, EPI_STORE),
     C32(4, 1, 2, 3, 1, 3, EPI_STORE),
-    C32(4, 1, 2, 3, 2, 3, EPI_STORE),
+    C32(4, 1, 2, 3, 1, 4, EPI_STORE),
     C32(4, 1, 2, 2, 1, 3, EPI_STORE),
     // Split-K partials (small M, large K).
     C32(4, 1, 2, 4, 1, 3, EPI_PARTIAL),
