@@ -145,6 +145,18 @@ TileCfg store_channel_cfg(int cout) {
   return channel_cfg(cout);
 }
 
+// The halo kernel stages each input row segment once per (kd, kh, channel
+// chunk) for all three kw taps: stride 1 along W, whole 32-channel chunks,
+// and a 512-pixel tile spanning at most 25 output rows.
+bool halo_ok(const Problem& pr) {
+  const long long nseg = ceil_div(511, pr.Wo) + 1;
+  return pr.sw == 1 && pr.cin % 32 == 0 && nseg <= 25 && (pr.cout % 128 == 0 || pr.cout % 96 == 0);
+}
+
+TileCfg halo_cfg(int cout) {
+  return cout % 128 == 0 ? TileCfg{32, 4, 1, 4, 4, 3, -1} : TileCfg{32, 4, 1, 4, 3, 3, -1};
+}
+
 void make_plan(const Problem& pr, int split_req, Plan* pl) {
   const int cc = (pr.cin + 31) / 32;
   pl->steps = 27 * cc;
@@ -154,6 +166,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
 
   TileCfg store_cfg = store_channel_cfg(pr.cout);
   if (!igemm_has_config(store_cfg, EPI_STORE)) store_cfg = base;
+  if (halo_ok(pr) && igemm_has_config(halo_cfg(pr.cout), EPI_STORE)) store_cfg = halo_cfg(pr.cout);
   TileCfg part_cfg = base;
   part_cfg.pb = 2;
   if (base.r == 32 && ceil_div(pr.M, part_cfg.bm()) * n_tiles < 64) {
@@ -191,7 +204,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   if (const char* env = getenv("CONV3D_TILE")) {
     TileCfg c;
     if (sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &c.r, &c.wm, &c.wn, &c.pb, &c.cb, &c.kb, &c.ns) == 7 &&
-        c.bn() > 0 && pr.cout % c.bn() == 0) {
+        c.bn() > 0 && pr.cout % c.bn() == 0 && (c.ns >= 0 || halo_ok(pr))) {
       const int mode = splits > 1 ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
       if (igemm_has_config(c, mode)) {
         if (mode == EPI_PARTIAL) part_cfg = c;
@@ -213,6 +226,12 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     pl->cfg = store_cfg;
     pl->mode = EPI_STORE;
     pl->reduce = false;
+  }
+  if (pl->cfg.ns < 0) {
+    // Halo kernel: a K stage is one (kd, kh) pair and 32 channels.
+    pl->steps = 9 * cc;
+    pl->steps_per_split = (pl->steps + pl->splits - 1) / pl->splits;
+    pl->splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
   }
   pl->m_tiles = (int)ceil_div(pr.M, pl->cfg.bm());
   pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());

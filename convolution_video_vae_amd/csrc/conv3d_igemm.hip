@@ -790,13 +790,328 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_tile_kernel(IgemmArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Halo kernel: stride 1 along W and Cin % 32 == 0.
+//
+// For one (kd, kh) tap pair and one 32-channel chunk, the three kw taps of an
+// output pixel read three neighbouring input pixels of the same input row.
+// A pipeline stage therefore stages, per row segment that the tile's BM
+// output pixels cover, that segment's input pixels plus the two-pixel halo
+// once, and the kw taps read it at slot offsets 0, 1, 2: a third of the
+// activation traffic of staging every tap separately. Slots are 80 bytes
+// (64 data + 16 pad), so eight consecutive slots start in eight distinct
+// 16-byte bank groups and the kw shift is a constant address offset.
+//
+// Both operands reach LDS by buffer-to-LDS DMA (no staging registers); a
+// padding tap or channel is an out-of-range lane, which writes zeros. Each
+// wave computes 128 pixels x 32*CB channels with v_mfma_f32_32x32x16_bf16
+// (16 accumulator blocks for CB = 4). Two LDS stages: the DMA of stage i+2
+// is issued as soon as every wave has read its last fragments of stage i,
+// right after the one barrier per stage, which is placed before the last
+// sub-step so that sub-step's MFMAs cover the first fragment reads of stage
+// i+1.
+// ----------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, void* lds, unsigned voff,
+                                      unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+template <int CB>
+struct HaloShape {
+  static constexpr int R = 32, PB = 4, WM = 4, NT = 256;
+  static constexpr int BM = R * PB * WM;       // 512 output pixels
+  static constexpr int BN = R * CB;
+  static constexpr int XJ = 11;                // X DMA instructions per wave per stage
+  static constexpr int XU = XJ * 4 * 64;       // 16-byte units per X stage
+  static constexpr int SLOT_UNITS = 5;         // 80-byte slots
+  static constexpr int XSLOTS = XU / SLOT_UNITS;
+  static constexpr int WU = BN * 4;            // 16-byte units per tap
+  static constexpr int WJ = (WU / 64 + 3) / 4; // W DMA instructions per wave per tap
+  // Row segments a tile may span: slot of the last pixel + 2 < XSLOTS.
+  static constexpr int MAXSEG = (XSLOTS - BM - 2) / 2 + 1;
+};
+
+template <int CB, int EPI>
+__global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
+  using T = Mfma32;
+  using S = HaloShape<CB>;
+  constexpr int R = S::R, PB = S::PB, WM = S::WM, NACC = T::NACC, RUN = NACC * CB;
+  constexpr int XU = S::XU, WU = S::WU, XJ = S::XJ, WJ = S::WJ;
+  constexpr int XSTAGE = XU * 16, WTAP = WU * 16, WSTAGE = 3 * WTAP;   // bytes
+  typedef typename T::acc_t acc_t;
+  static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
+
+  // Separate arrays per buffer, so the compiler can tell the DMA into one
+  // buffer from the fragment reads of the other.
+  __shared__ u32x4_t xbuf0[XU], xbuf1[XU];
+  __shared__ u32x4_t wbuf0[3 * WU], wbuf1[3 * WU];
+  __shared__ unsigned live_sh;
+  __shared__ float red[1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31;
+  const int lgrp = lane >> 5;
+  const TileCoord tc = tile_coord(a, S::BM, S::BN);
+
+  // Row segments of the tile: the first starts at output column wo0 of row
+  // row0 and holds len0 pixels; each later one is a whole output row.
+  const int row0 = tc.m0 / a.Wo;
+  const int wo0 = tc.m0 - row0 * a.Wo;
+  const int len0 = min(a.Wo - wo0, S::BM);
+  const int rows_total = a.N * a.Do * a.Ho;
+
+  // X DMA entries of this lane: the input pixel (at kd = kh = 0, channel
+  // chunk c) of one slot unit, and the 9-bit mask of the (kd, kh) pairs for
+  // which that pixel is inside the input.
+  int xbase[XJ];
+  unsigned xmask[XJ];
+  unsigned live = 0;
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int q = (j * 4 + wave) * 64 + lane;
+    const int s = q / S::SLOT_UNITS;
+    const int c = q - s * S::SLOT_UNITS;
+    int k, i;
+    if (s < len0 + 2) {
+      k = 0;
+      i = s;
+    } else {
+      const int rel = s - len0 - 2;
+      k = 1 + rel / (a.Wo + 2);
+      i = rel - (k - 1) * (a.Wo + 2);
+    }
+    const int r = row0 + k;
+    const int w_in = (k == 0 ? wo0 : 0) - a.pw + i;
+    unsigned m = 0;
+    long long off = 0;
+    if (c < 4 && r < rows_total && w_in >= 0 && w_in < a.W) {
+      const int ho = r % a.Ho;
+      const int t2 = r / a.Ho;
+      const int dq = t2 % a.Do;
+      const int n = t2 / a.Do;
+      const int d0 = dq * a.sd - a.pd;
+      const int h0 = ho * a.sh - a.ph;
+#pragma unroll
+      for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+          m |= (unsigned)(d0 + kd >= 0 && d0 + kd < a.D && h0 + kh >= 0 && h0 + kh < a.H)
+               << (kd * 3 + kh);
+      off = ((((long long)n * a.D + d0) * a.H + h0) * a.W + w_in) * (a.Cin * 2) + c * 16;
+    }
+    xbase[j] = m ? (int)off : 0;
+    xmask[j] = m;
+    live |= m;
+  }
+  live = wave_or(live);
+  if (tid == 0) live_sh = 0;
+  __syncthreads();
+  if (lane == 0) atomicOr(&live_sh, live);
+  __syncthreads();
+  live = __builtin_amdgcn_readfirstlane(live_sh);
+
+  // W DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
+  // channel order, 16-byte chunk (q % 4) XOR the row swizzle.
+  unsigned woff[WJ];
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int q = (j * 4 + wave) * 64 + lane;
+    const int row = q >> 2;
+    const int c = (q & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    const int col = T::chan_of((row / R) % CB, row % R, CB);
+    woff[j] = (q < WU) ? (unsigned)((tc.co0 + col) * 64 + c * 16) : 0u;
+  }
+
+  // Fragment addresses (bytes): pixel block p of this wave sits at slot
+  // slot_p; tap kw adds 80*kw, K half h adds 32.
+  int ax[PB];
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const int rel = wave * (PB * R) + p * R + lrow;
+    const int k = rel < len0 ? 0 : 1 + (rel - len0) / a.Wo;
+    ax[p] = (rel + 2 * k) * (S::SLOT_UNITS * 16) + lgrp * 16;
+  }
+  int aw[CB][2];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) aw[cb][h] = lds_idx(cb * R + lrow, 2 * h + lgrp) * 16;
+
+  const __amdgpu_buffer_rsrc_t xrsrc = x_rsrc(a);
+  const __amdgpu_buffer_rsrc_t wrsrc = w_rsrc(a);
+
+  // Stages e = (pair << 8) | cc over the live (kd, kh) pairs.
+  const int s_begin = tc.split * a.steps_per_split;
+  const int s_end = min(s_begin + a.steps_per_split, 9 * a.CC);
+  auto valid_stage = [&](int pr, int cc) -> int {
+    return (pr < 9 && pr * a.CC + cc < s_end) ? ((pr << 8) | cc) : kEnd;
+  };
+  auto next_stage = [&](int e) -> int {
+    if (e == kEnd) return kEnd;
+    int pr = e >> 8, cc = (e & 255) + 1;
+    if (cc == a.CC) {
+      cc = 0;
+      const unsigned rest = live & (~0u << (pr + 1));
+      pr = rest ? __builtin_ctz(rest) : 9;
+    }
+    return valid_stage(pr, cc);
+  };
+  auto first_stage = [&]() -> int {
+    if (s_begin >= s_end) return kEnd;
+    int pr = s_begin / a.CC, cc = s_begin % a.CC;
+    if (!((live >> pr) & 1u)) {
+      const unsigned rest = live & (~0u << pr);
+      pr = rest ? __builtin_ctz(rest) : 9;
+      cc = 0;
+    }
+    return valid_stage(pr, cc);
+  };
+
+  // DMA of stage e into buffer b, in four parts so that it can be spread
+  // between MFMAs: X entries [0,4), [4,8), [8,XJ), then the weights.
+  auto issue_dma = [&](int e, auto buf_c, auto part_c) {
+    constexpr int b = decltype(buf_c)::value;
+    constexpr int part = decltype(part_c)::value;
+    u32x4_t* xdst = b ? xbuf1 : xbuf0;
+    u32x4_t* wdst = b ? wbuf1 : wbuf0;
+    if (e == kEnd) return;
+    const int pr = e >> 8, cc = e & 255;
+    const int kd = pr / 3, kh = pr - kd * 3;
+    if constexpr (part < 3) {
+      const unsigned pbit = 1u << pr;
+      const int delta = (kd * a.H + kh) * a.W * (a.Cin * 2) + cc * 64;
+      constexpr int j0 = 4 * part, j1 = (4 * part + 4 < XJ) ? 4 * part + 4 : XJ;
+#pragma unroll
+      for (int j = j0; j < j1; ++j) {
+        const unsigned off = (xmask[j] & pbit) ? (unsigned)(xbase[j] + delta) : kOobOffset;
+        dma16(xrsrc, &xdst[(j * 4 + wave) * 64], off, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw) {
+        const unsigned soff = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+          if constexpr (WU % 256 == 0) {
+            dma16(wrsrc, &wdst[kw * WU + (j * 4 + wave) * 64], woff[j], soff);
+          } else {
+            if ((j * 4 + wave) * 64 < WU) dma16(wrsrc, &wdst[kw * WU + (j * 4 + wave) * 64], woff[j], soff);
+          }
+        }
+      }
+    }
+  };
+  auto issue_dma_all = [&](int e, auto buf_c) {
+    issue_dma(e, buf_c, SlotC<0>{});
+    issue_dma(e, buf_c, SlotC<1>{});
+    issue_dma(e, buf_c, SlotC<2>{});
+    issue_dma(e, buf_c, SlotC<3>{});
+  };
+
+  acc_t acc[CB][PB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) acc[cb][p][e] = 0.f;
+
+  u32x4_t xf[2][PB], wf[2][CB];
+  // Fragments of sub-step u (tap kw = u / 2, K half h = u % 2) of buffer b.
+  auto read_frags = [&](auto buf_c, int u, u32x4_t (&x)[PB], u32x4_t (&w)[CB]) {
+    constexpr int b = decltype(buf_c)::value;
+    const char* xb = reinterpret_cast<const char*>(b ? xbuf1 : xbuf0);
+    const char* wb = reinterpret_cast<const char*>(b ? wbuf1 : wbuf0);
+    const int kw = u >> 1, h = u & 1;
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+      x[p] = *reinterpret_cast<const u32x4_t*>(xb + ax[p] + kw * (S::SLOT_UNITS * 16) + h * 32);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      w[cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][h] + kw * WTAP);
+  };
+  // MFMAs of channel blocks [cb0, cb1).
+  auto mfmas = [&](const u32x4_t (&x)[PB], const u32x4_t (&w)[CB], int cb0, int cb1) {
+#pragma unroll
+    for (int cb = cb0; cb < cb1; ++cb)
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+        acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, w[cb]), __builtin_bit_cast(bf16x8_t, x[p]),
+                            acc[cb][p]);
+  };
+
+  int e0 = first_stage();
+  int e1 = next_stage(e0);
+  int e2 = next_stage(e1);
+  issue_dma_all(e0, SlotC<0>{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  issue_dma_all(e1, SlotC<1>{});
+  read_frags(SlotC<0>{}, 0, xf[0], wf[0]);
+
+  auto iteration = [&](auto buf_c) -> bool {
+    constexpr int b = decltype(buf_c)::value;
+    if (e0 == kEnd) return false;
+    // Sub-steps 0..4: the next sub-step's fragments are read first, then this
+    // sub-step's MFMAs run while they arrive.
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      read_frags(buf_c, u + 1, xf[(u + 1) & 1], wf[(u + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(xf[u & 1], wf[u & 1], 0, CB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Stage i+1 has landed everywhere and nobody reads buffer b any more.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    read_frags(SlotC<b ^ 1>{}, 0, xf[0], wf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // Sub-step 5, with the DMA of stage i+2 into buffer b spread over it.
+    constexpr int Q = (CB + 3) / 4;
+    mfmas(xf[1], wf[1], 0, Q);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_dma(e2, buf_c, SlotC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(xf[1], wf[1], Q, 2 * Q);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_dma(e2, buf_c, SlotC<1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(xf[1], wf[1], 2 * Q, 3 * Q < CB ? 3 * Q : CB);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_dma(e2, buf_c, SlotC<2>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(xf[1], wf[1], 3 * Q < CB ? 3 * Q : CB, CB);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_dma(e2, buf_c, SlotC<3>{});
+    __builtin_amdgcn_sched_barrier(0);
+    e0 = e1;
+    e1 = e2;
+    e2 = next_stage(e2);
+    return true;
+  };
+  for (;;) {
+    if (!iteration(SlotC<0>{})) break;
+    if (!iteration(SlotC<1>{})) break;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  epilogue<T, WM, 1, PB, CB, EPI>(a, acc, tc.m0 + wave * PB * R + lrow, tc.co0 + lgrp * RUN, tc.split,
+                                  wave, 0, lrow, lgrp, red);
+}
+
+// ----------------------------------------------------------------------------
 // Compiled configurations.
 // ----------------------------------------------------------------------------
 namespace {
 
 template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
 int launch_one(const IgemmArgs& args, int grid, void* stream) {
-  if constexpr (NS == 0)
+  if constexpr (NS < 0)
+    hipLaunchKernelGGL((igemm_halo_kernel<CB, EPI>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, args);
+  else if constexpr (NS == 0)
     hipLaunchKernelGGL((igemm_tile_kernel<T, WM, WN, PB, CB, KB, EPI>), dim3((unsigned)grid),
                        dim3(64 * WM * WN), 0, (hipStream_t)stream, args);
   else
@@ -816,6 +1131,10 @@ struct Entry {
 #define C16(WM, WN, PB, CB, KB, NS, MODE) \
   {{16, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE>}
 const Entry kEntries[] = {
+    // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0).
+    C32(4, 1, 4, 4, 3, -1, EPI_STORE),
+    C32(4, 1, 4, 3, 3, -1, EPI_STORE),
+    C32(4, 1, 4, 4, 3, -1, EPI_PARTIAL),
     // ns = 0: tile kernel (pixels staged through LDS too).
     C32(4, 1, 2, 4, 2, 0, EPI_STORE),
     C32(4, 1, 2, 4, 1, 0, EPI_STORE),

@@ -164,6 +164,42 @@ def test_integer_fused_epilogue_bit_exact_across_splits():
     check(bits(outs[0]["y"]), r, fused=True, gamma_bits=bits(gam), what="fused integer")
 
 
+HALO_CASES = [
+    # label, x shape, cout, stride, pad_lo, pad_hi: stride 1 along W, Cin % 32 == 0,
+    # run without a K split so the row-halo kernel computes them.
+    ("halo_causal128_batch2", (2, 3, 9, 40, 128), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("halo_valid96_wide", (1, 4, 6, 300, 96), 96, (1, 1, 1), (0, 0, 0), (0, 0, 0)),
+    ("halo_cin32_cout256", (1, 3, 5, 64, 32), 256, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("halo_wo22_25rows", (1, 2, 30, 22, 64), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("halo_t1", (1, 1, 17, 50, 64), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("halo_asym_wpad", (1, 3, 7, 33, 96), 96, (1, 1, 1), (2, 1, 0), (0, 1, 2)),
+    ("halo_stride_dh", (1, 7, 13, 45, 64), 128, (2, 2, 1), (2, 1, 1), (0, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", HALO_CASES, ids=[c[0] for c in HALO_CASES])
+def test_halo_kernel_integer_bit_exact(case):
+    label, xs, cout, st, lo, hi = case
+    x, w, b = workloads.integer_tensors(xs, cout, seed=len(label) + 7, bias=True)
+    g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b, split_k=1, label=label)
+    assert "ns=-1" in g["plan"], g["plan"]
+    r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
+
+
+@pytest.mark.parametrize("case", HALO_CASES[:2], ids=[c[0] for c in HALO_CASES[:2]])
+def test_halo_kernel_random_against_oracle(case):
+    label, xs, cout, st, lo, hi = case
+    rng = np.random.default_rng(len(label))
+    x = torch.from_numpy(rng.standard_normal(xs).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((cout, xs[-1], 3, 3, 3)) / np.sqrt(27 * xs[-1]))
+                         .astype(np.float32)).to(torch.bfloat16)
+    g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, split_k=1, label=label + "_random")
+    assert "ns=-1" in g["plan"], g["plan"]
+    r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi)
+    check(bits(g["y"]), r, what=label)
+
+
 @pytest.mark.parametrize("stride,lo,hi", [((1, 1, 1), (2, 1, 1), (0, 1, 1)),
                                          ((1, 2, 2), (2, 0, 0), (0, 1, 1)),
                                          ((1, 1, 1), (0, 0, 0), (0, 0, 0))])
