@@ -145,28 +145,44 @@ TileCfg store_channel_cfg(int cout) {
   return channel_cfg(cout);
 }
 
-// The halo kernel stages each input row segment once per (kd, kh, channel
-// chunk) for all three kw taps: stride 1 along W, whole 32-channel chunks,
-// and a 512-pixel tile spanning at most 25 output rows.
-bool halo_ok(const Problem& pr) {
-  const long long nseg = ceil_div(511, pr.Wo) + 1;
-  return pr.sw == 1 && pr.cin % 32 == 0 && nseg <= 25 && (pr.cout % 128 == 0 || pr.cout % 96 == 0);
+// Halo kernel configurations {32, 4 / WN, WN, 4, CB, XJ, -1}: stride 1 along
+// W and whole 32-channel chunks; kb = XJ, the X DMA instructions per wave and
+// stage, sets how many output-row segments one tile may span.
+int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 5 - c.bm() - 2) / 2 + 1; }
+
+bool halo_ok(const Problem& pr, const TileCfg& c) {
+  if (c.ns >= 0) return true;
+  return pr.sw == 1 && pr.cin % 32 == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
+         ceil_div(c.bm() - 1, pr.Wo) + 1 <= halo_maxseg(c);
 }
 
-TileCfg halo_cfg(int cout) {
-  return cout % 128 == 0 ? TileCfg{32, 4, 1, 4, 4, 3, -1} : TileCfg{32, 4, 1, 4, 3, 3, -1};
+const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 11, -1}, {32, 4, 1, 4, 3, 11, -1}};
+const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 6, -1}, {32, 2, 2, 4, 3, 6, -1},
+                                {32, 4, 1, 4, 4, 11, -1}};
+
+template <int N>
+bool pick_halo(const Problem& pr, const TileCfg (&cands)[N], int mode, TileCfg* out) {
+  for (const TileCfg& c : cands)
+    if (halo_ok(pr, c) && igemm_has_config(c, mode)) {
+      *out = c;
+      return true;
+    }
+  return false;
 }
+
+// K steps a kernel walks: 27 taps x 32-channel chunks, or for the halo
+// kernel 9 (kd, kh) pairs x 32-channel chunks.
+int steps_of(const TileCfg& c, int cc) { return c.ns < 0 ? 9 * cc : 27 * cc; }
 
 void make_plan(const Problem& pr, int split_req, Plan* pl) {
   const int cc = (pr.cin + 31) / 32;
-  pl->steps = 27 * cc;
   const bool norm = (pr.flags & F_NORM) != 0;
   TileCfg base = channel_cfg(pr.cout);
   const long long n_tiles = ceil_div(pr.cout, base.bn());
 
   TileCfg store_cfg = store_channel_cfg(pr.cout);
   if (!igemm_has_config(store_cfg, EPI_STORE)) store_cfg = base;
-  if (halo_ok(pr) && igemm_has_config(halo_cfg(pr.cout), EPI_STORE)) store_cfg = halo_cfg(pr.cout);
+  if (!norm) pick_halo(pr, kHaloStore, EPI_STORE, &store_cfg);
   TileCfg part_cfg = base;
   part_cfg.pb = 2;
   if (base.r == 32 && ceil_div(pr.M, part_cfg.bm()) * n_tiles < 64) {
@@ -174,6 +190,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     c.pb = 1;
     if (igemm_has_config(c, EPI_PARTIAL)) part_cfg = c;
   }
+  pick_halo(pr, kHaloPartial, EPI_PARTIAL, &part_cfg);
 
   // Fused-norm kernels hold the whole channel row of a pixel in one group.
   TileCfg norm_cfg = {0, 0, 0, 0, 0, 0, 0};
@@ -184,28 +201,17 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
       if (norm_cfg.r == 0 && c.bn() == pr.cout && igemm_has_config(c, EPI_NORM)) norm_cfg = c;
   }
 
-  const long long store_tiles = ceil_div(pr.M, store_cfg.bm()) * n_tiles;
-  int splits = 1;
-  if (split_req > 0) {
-    splits = split_req;
-  } else if (store_tiles < kCUs / 2) {
-    // Too few tiles to fill the CUs: cut K so there are about two groups
-    // per CU, keeping at least 8 K steps per slice.
-    const long long tiles = ceil_div(pr.M, part_cfg.bm()) * ceil_div(pr.cout, part_cfg.bn());
-    splits = (int)std::max(1LL, std::min<long long>(ceil_div(2 * kCUs, tiles), pl->steps / 8));
-  }
-  splits = std::max(1, std::min(splits, pl->steps));
-  pl->steps_per_split = (pl->steps + splits - 1) / splits;
-  splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
-  pl->splits = splits;
+  // Too few tiles to fill the CUs: cut K.
+  const long long store_tiles = ceil_div(pr.M, store_cfg.bm()) * ceil_div(pr.cout, store_cfg.bn());
+  const bool split = split_req > 1 || (split_req == 0 && store_tiles < kCUs / 2);
 
   // Development override of the tile (same kernels, another compiled
   // configuration): CONV3D_TILE="r,wm,wn,pb,cb,kb,ns".
   if (const char* env = getenv("CONV3D_TILE")) {
     TileCfg c;
     if (sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &c.r, &c.wm, &c.wn, &c.pb, &c.cb, &c.kb, &c.ns) == 7 &&
-        c.bn() > 0 && pr.cout % c.bn() == 0 && (c.ns >= 0 || halo_ok(pr))) {
-      const int mode = splits > 1 ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
+        c.bn() > 0 && pr.cout % c.bn() == 0 && halo_ok(pr, c)) {
+      const int mode = split ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
       if (igemm_has_config(c, mode)) {
         if (mode == EPI_PARTIAL) part_cfg = c;
         else if (mode == EPI_NORM) norm_cfg = c;
@@ -214,7 +220,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     }
   }
 
-  if (splits > 1 || (norm && norm_cfg.r == 0)) {
+  if (split || (norm && norm_cfg.r == 0)) {
     pl->cfg = part_cfg;
     pl->mode = EPI_PARTIAL;
     pl->reduce = true;
@@ -227,12 +233,21 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     pl->mode = EPI_STORE;
     pl->reduce = false;
   }
-  if (pl->cfg.ns < 0) {
-    // Halo kernel: a K stage is one (kd, kh) pair and 32 channels.
-    pl->steps = 9 * cc;
-    pl->steps_per_split = (pl->steps + pl->splits - 1) / pl->splits;
-    pl->splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
+
+  pl->steps = steps_of(pl->cfg, cc);
+  int splits = 1;
+  if (split_req > 1) {
+    splits = split_req;
+  } else if (split) {
+    const long long tiles = ceil_div(pr.M, pl->cfg.bm()) * ceil_div(pr.cout, pl->cfg.bn());
+    if (pl->cfg.ns < 0)   // one work-group per CU: fill one round
+      splits = (int)std::max(1LL, std::min<long long>(kCUs / tiles, pl->steps / 4));
+    else                  // about two groups per CU, at least 8 K steps each
+      splits = (int)std::max(1LL, std::min<long long>(ceil_div(2 * kCUs, tiles), pl->steps / 8));
   }
+  splits = std::max(1, std::min(splits, pl->steps));
+  pl->steps_per_split = (pl->steps + splits - 1) / splits;
+  pl->splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
   pl->m_tiles = (int)ceil_div(pr.M, pl->cfg.bm());
   pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());
   pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;

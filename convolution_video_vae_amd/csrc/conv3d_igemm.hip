@@ -817,12 +817,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, void* lds, un
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
 }
 
-template <int CB>
+template <int CB, int WN, int XJ>
 struct HaloShape {
-  static constexpr int R = 32, PB = 4, WM = 4, NT = 256;
-  static constexpr int BM = R * PB * WM;       // 512 output pixels
-  static constexpr int BN = R * CB;
-  static constexpr int XJ = 11;                // X DMA instructions per wave per stage
+  static constexpr int R = 32, PB = 4, NT = 256;
+  static constexpr int WM = 4 / WN;
+  static constexpr int BM = R * PB * WM;       // output pixels per tile
+  static constexpr int BN = R * CB * WN;       // output channels per tile
   static constexpr int XU = XJ * 4 * 64;       // 16-byte units per X stage
   static constexpr int SLOT_UNITS = 5;         // 80-byte slots
   static constexpr int XSLOTS = XU / SLOT_UNITS;
@@ -830,15 +830,17 @@ struct HaloShape {
   static constexpr int WJ = (WU / 64 + 3) / 4; // W DMA instructions per wave per tap
   // Row segments a tile may span: slot of the last pixel + 2 < XSLOTS.
   static constexpr int MAXSEG = (XSLOTS - BM - 2) / 2 + 1;
+  static_assert(WN == 1 || WN == 2 || WN == 4, "4 waves");
+  static_assert(XJ <= 12, "the X DMA is issued in three parts of at most 4");
 };
 
-template <int CB, int EPI>
+template <int CB, int WN, int XJ, int EPI>
 __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   using T = Mfma32;
-  using S = HaloShape<CB>;
+  using S = HaloShape<CB, WN, XJ>;
   constexpr int R = S::R, PB = S::PB, WM = S::WM, NACC = T::NACC, RUN = NACC * CB;
-  constexpr int XU = S::XU, WU = S::WU, XJ = S::XJ, WJ = S::WJ;
-  constexpr int XSTAGE = XU * 16, WTAP = WU * 16, WSTAGE = 3 * WTAP;   // bytes
+  constexpr int XU = S::XU, WU = S::WU, WJ = S::WJ;
+  constexpr int WTAP = WU * 16;   // bytes
   typedef typename T::acc_t acc_t;
   static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
 
@@ -847,11 +849,13 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   __shared__ u32x4_t xbuf0[XU], xbuf1[XU];
   __shared__ u32x4_t wbuf0[3 * WU], wbuf1[3 * WU];
   __shared__ unsigned live_sh;
-  __shared__ float red[1];
+  __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave % WM;
+  const int wave_n = wave / WM;
   const int lrow = lane & 31;
   const int lgrp = lane >> 5;
   const TileCoord tc = tile_coord(a, S::BM, S::BN);
@@ -921,7 +925,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     const int q = (j * 4 + wave) * 64 + lane;
     const int row = q >> 2;
     const int c = (q & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
-    const int col = T::chan_of((row / R) % CB, row % R, CB);
+    const int col = (row / (R * CB)) * (R * CB) + T::chan_of((row / R) % CB, row % R, CB);
     woff[j] = (q < WU) ? (unsigned)((tc.co0 + col) * 64 + c * 16) : 0u;
   }
 
@@ -930,7 +934,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   int ax[PB];
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
-    const int rel = wave * (PB * R) + p * R + lrow;
+    const int rel = wave_m * (PB * R) + p * R + lrow;
     const int k = rel < len0 ? 0 : 1 + (rel - len0) / a.Wo;
     ax[p] = (rel + 2 * k) * (S::SLOT_UNITS * 16) + lgrp * 16;
   }
@@ -938,7 +942,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) aw[cb][h] = lds_idx(cb * R + lrow, 2 * h + lgrp) * 16;
+    for (int h = 0; h < 2; ++h) aw[cb][h] = lds_idx((wave_n * CB + cb) * R + lrow, 2 * h + lgrp) * 16;
 
   const __amdgpu_buffer_rsrc_t xrsrc = x_rsrc(a);
   const __amdgpu_buffer_rsrc_t wrsrc = w_rsrc(a);
@@ -1097,8 +1101,9 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     if (!iteration(SlotC<1>{})) break;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  epilogue<T, WM, 1, PB, CB, EPI>(a, acc, tc.m0 + wave * PB * R + lrow, tc.co0 + lgrp * RUN, tc.split,
-                                  wave, 0, lrow, lgrp, red);
+  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
+                                   tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split, wave_m, wave_n,
+                                   lrow, lgrp, red);
 }
 
 // ----------------------------------------------------------------------------
@@ -1109,7 +1114,7 @@ namespace {
 template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
 int launch_one(const IgemmArgs& args, int grid, void* stream) {
   if constexpr (NS < 0)
-    hipLaunchKernelGGL((igemm_halo_kernel<CB, EPI>), dim3((unsigned)grid), dim3(256), 0,
+    hipLaunchKernelGGL((igemm_halo_kernel<CB, WN, KB, EPI>), dim3((unsigned)grid), dim3(256), 0,
                        (hipStream_t)stream, args);
   else if constexpr (NS == 0)
     hipLaunchKernelGGL((igemm_tile_kernel<T, WM, WN, PB, CB, KB, EPI>), dim3((unsigned)grid),
@@ -1131,10 +1136,13 @@ struct Entry {
 #define C16(WM, WN, PB, CB, KB, NS, MODE) \
   {{16, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE>}
 const Entry kEntries[] = {
-    // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0).
-    C32(4, 1, 4, 4, 3, -1, EPI_STORE),
-    C32(4, 1, 4, 3, 3, -1, EPI_STORE),
-    C32(4, 1, 4, 4, 3, -1, EPI_PARTIAL),
+    // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0); kb = X DMA
+    // instructions per wave and stage (the row-segment capacity).
+    C32(4, 1, 4, 4, 11, -1, EPI_STORE),
+    C32(4, 1, 4, 3, 11, -1, EPI_STORE),
+    C32(4, 1, 4, 4, 11, -1, EPI_PARTIAL),
+    C32(2, 2, 4, 4, 6, -1, EPI_PARTIAL),
+    C32(2, 2, 4, 3, 6, -1, EPI_PARTIAL),
     // ns = 0: tile kernel (pixels staged through LDS too).
     C32(4, 1, 2, 4, 2, 0, EPI_STORE),
     C32(4, 1, 2, 4, 1, 0, EPI_STORE),

@@ -187,6 +187,26 @@ def test_halo_kernel_integer_bit_exact(case):
     np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
 
 
+HALO_SPLIT_CASES = [
+    # label, x shape, cout, stride, pad_lo, pad_hi: K-split halo kernel (fp32
+    # partials summed in fixed order by the reduce kernel).
+    ("halo_split_cout256", (1, 3, 6, 40, 64), 256, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("halo_split_cout192_w16", (1, 2, 9, 16, 96), 192, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("halo_split_cout128_valid", (2, 3, 5, 70, 32), 128, (1, 1, 1), (0, 0, 0), (0, 0, 0)),
+]
+
+
+@pytest.mark.parametrize("case", HALO_SPLIT_CASES, ids=[c[0] for c in HALO_SPLIT_CASES])
+@pytest.mark.parametrize("split_k", [2, 5])
+def test_halo_kernel_split_k_integer_bit_exact(case, split_k):
+    label, xs, cout, st, lo, hi = case
+    x, w, b = workloads.integer_tensors(xs, cout, seed=len(label) + 11, bias=True)
+    g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b, split_k=split_k, label=label)
+    assert "ns=-1" in g["plan"] and "mode=partial" in g["plan"], g["plan"]
+    r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
+
+
 @pytest.mark.parametrize("case", HALO_CASES[:2], ids=[c[0] for c in HALO_CASES[:2]])
 def test_halo_kernel_random_against_oracle(case):
     label, xs, cout, st, lo, hi = case
