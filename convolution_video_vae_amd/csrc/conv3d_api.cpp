@@ -148,7 +148,7 @@ TileCfg store_channel_cfg(int cout) {
 // Halo kernel configurations {32, 4 / WN, WN, 4, CB, XJ, -1}: stride 1 along
 // W and whole 32-channel chunks; kb = XJ, the X DMA instructions per wave and
 // stage, sets how many output-row segments one tile may span.
-int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 5 - c.bm() - 2) / 2 + 1; }
+int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1; }
 
 bool halo_ok(const Problem& pr, const TileCfg& c) {
   if (c.ns >= 0) return true;
@@ -156,9 +156,9 @@ bool halo_ok(const Problem& pr, const TileCfg& c) {
          ceil_div(c.bm() - 1, pr.Wo) + 1 <= halo_maxseg(c);
 }
 
-const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 11, -1}, {32, 4, 1, 4, 3, 11, -1}};
-const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 6, -1}, {32, 2, 2, 4, 3, 6, -1},
-                                {32, 4, 1, 4, 4, 11, -1}};
+const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 9, -1}, {32, 4, 1, 4, 3, 9, -1}};
+const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 5, -1}, {32, 2, 2, 4, 3, 5, -1},
+                                {32, 4, 1, 4, 4, 9, -1}};
 
 template <int N>
 bool pick_halo(const Problem& pr, const TileCfg (&cands)[N], int mode, TileCfg* out) {

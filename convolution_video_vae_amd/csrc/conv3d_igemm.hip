@@ -161,6 +161,16 @@ struct SlotC {
   static constexpr int value = I;
 };
 
+// Calls f(SlotC<0>{}) .. f(SlotC<N-1>{}): a loop whose index is a constant
+// expression in the body.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(SlotC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // K steps are encoded e = (tap << 8) | channel chunk; kEnd marks none.
 constexpr int kEnd = 0x7fffffff;
 
@@ -797,18 +807,19 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_tile_kernel(IgemmArgs a) {
 // A pipeline stage therefore stages, per row segment that the tile's BM
 // output pixels cover, that segment's input pixels plus the two-pixel halo
 // once, and the kw taps read it at slot offsets 0, 1, 2: a third of the
-// activation traffic of staging every tap separately. Slots are 80 bytes
-// (64 data + 16 pad), so eight consecutive slots start in eight distinct
-// 16-byte bank groups and the kw shift is a constant address offset.
+// activation traffic of staging every tap separately. A slot is one pixel's
+// 64 bytes; its four 16-byte chunks are XOR-swizzled by (slot / 2) % 4, which
+// puts any eight consecutive slots of one chunk in eight distinct 16-byte
+// bank groups.
 //
 // Both operands reach LDS by buffer-to-LDS DMA (no staging registers); a
-// padding tap or channel is an out-of-range lane, which writes zeros. Each
-// wave computes 128 pixels x 32*CB channels with v_mfma_f32_32x32x16_bf16
-// (16 accumulator blocks for CB = 4). Two LDS stages: the DMA of stage i+2
-// is issued as soon as every wave has read its last fragments of stage i,
-// right after the one barrier per stage, which is placed before the last
-// sub-step so that sub-step's MFMAs cover the first fragment reads of stage
-// i+1.
+// padding tap is an out-of-range lane, which writes zeros. Each wave computes
+// 128 pixels x 32*CB channels with v_mfma_f32_32x32x16_bf16 (16 accumulator
+// blocks for CB = 4). Three activation buffers and two weight buffers: while
+// stage i is computed, the weights of stage i+1 and the activations of stage
+// i+2 are fetched, a few DMA instructions between each group of MFMAs so the
+// address unit is never handed a burst. One barrier per stage, before the
+// last sub-step, whose MFMAs then cover the first fragment reads of stage i+1.
 // ----------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -823,31 +834,35 @@ struct HaloShape {
   static constexpr int WM = 4 / WN;
   static constexpr int BM = R * PB * WM;       // output pixels per tile
   static constexpr int BN = R * CB * WN;       // output channels per tile
-  static constexpr int XU = XJ * 4 * 64;       // 16-byte units per X stage
-  static constexpr int SLOT_UNITS = 5;         // 80-byte slots
-  static constexpr int XSLOTS = XU / SLOT_UNITS;
+  static constexpr int XU = XJ * 4 * 64;       // 16-byte units per activation buffer
+  static constexpr int XSLOTS = XU / 4;        // 64-byte slots
   static constexpr int WU = BN * 4;            // 16-byte units per tap
-  static constexpr int WJ = (WU / 64 + 3) / 4; // W DMA instructions per wave per tap
+  static constexpr int WJ = (WU / 64 + 3) / 4; // weight DMA instructions per wave per tap
+  static constexpr int WUP = WJ * 256;         // tap stride: every lane of every wave has a slot
   // Row segments a tile may span: slot of the last pixel + 2 < XSLOTS.
   static constexpr int MAXSEG = (XSLOTS - BM - 2) / 2 + 1;
   static_assert(WN == 1 || WN == 2 || WN == 4, "4 waves");
-  static_assert(XJ <= 12, "the X DMA is issued in three parts of at most 4");
+  static_assert(XJ >= 3 && XJ <= 12, "activation DMA issued in three parts of 1..4");
 };
+
+__device__ __forceinline__ int xslot_chunk(int slot, int chunk) {
+  return chunk ^ ((slot >> 1) & 3);
+}
 
 template <int CB, int WN, int XJ, int EPI>
 __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   using T = Mfma32;
   using S = HaloShape<CB, WN, XJ>;
   constexpr int R = S::R, PB = S::PB, WM = S::WM, NACC = T::NACC, RUN = NACC * CB;
-  constexpr int XU = S::XU, WU = S::WU, WJ = S::WJ;
-  constexpr int WTAP = WU * 16;   // bytes
+  constexpr int XU = S::XU, WU = S::WU, WJ = S::WJ, WUP = S::WUP;
+  constexpr int WTAP = WUP * 16;  // bytes
   typedef typename T::acc_t acc_t;
   static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
 
-  // Separate arrays per buffer, so the compiler can tell the DMA into one
-  // buffer from the fragment reads of the other.
-  __shared__ u32x4_t xbuf0[XU], xbuf1[XU];
-  __shared__ u32x4_t wbuf0[3 * WU], wbuf1[3 * WU];
+  // One array per buffer, so the compiler can tell the DMA into one buffer
+  // from the fragment reads of another.
+  __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
+  __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
   __shared__ unsigned live_sh;
   __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
 
@@ -861,23 +876,25 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   const TileCoord tc = tile_coord(a, S::BM, S::BN);
 
   // Row segments of the tile: the first starts at output column wo0 of row
-  // row0 and holds len0 pixels; each later one is a whole output row.
+  // row0 and holds len0 pixels; each later one is a whole output row. Slot
+  // of segment k's input column i: i for k = 0, else len0 + 2 + (k-1)(Wo+2) + i.
   const int row0 = tc.m0 / a.Wo;
   const int wo0 = tc.m0 - row0 * a.Wo;
   const int len0 = min(a.Wo - wo0, S::BM);
   const int rows_total = a.N * a.Do * a.Ho;
 
-  // X DMA entries of this lane: the input pixel (at kd = kh = 0, channel
-  // chunk c) of one slot unit, and the 9-bit mask of the (kd, kh) pairs for
-  // which that pixel is inside the input.
+  // Activation DMA entries of this lane: LDS unit q of a buffer holds chunk
+  // xslot_chunk(q / 4, q % 4) of slot q / 4. xbase is that chunk's byte offset
+  // in x at kd = kh = 0 and channel chunk 0; xmask the 9-bit set of (kd, kh)
+  // pairs for which the pixel lies inside the input.
   int xbase[XJ];
   unsigned xmask[XJ];
   unsigned live = 0;
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
     const int q = (j * 4 + wave) * 64 + lane;
-    const int s = q / S::SLOT_UNITS;
-    const int c = q - s * S::SLOT_UNITS;
+    const int s = q >> 2;
+    const int c = xslot_chunk(s, q & 3);
     int k, i;
     if (s < len0 + 2) {
       k = 0;
@@ -891,7 +908,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     const int w_in = (k == 0 ? wo0 : 0) - a.pw + i;
     unsigned m = 0;
     long long off = 0;
-    if (c < 4 && r < rows_total && w_in >= 0 && w_in < a.W) {
+    if (r < rows_total && w_in >= 0 && w_in < a.W) {
       const int ho = r % a.Ho;
       const int t2 = r / a.Ho;
       const int dq = t2 % a.Do;
@@ -917,7 +934,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   __syncthreads();
   live = __builtin_amdgcn_readfirstlane(live_sh);
 
-  // W DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
+  // Weight DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
   // channel order, 16-byte chunk (q % 4) XOR the row swizzle.
   unsigned woff[WJ];
 #pragma unroll
@@ -926,17 +943,20 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     const int row = q >> 2;
     const int c = (q & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
     const int col = (row / (R * CB)) * (R * CB) + T::chan_of((row / R) % CB, row % R, CB);
-    woff[j] = (q < WU) ? (unsigned)((tc.co0 + col) * 64 + c * 16) : 0u;
+    woff[j] = (q < WU) ? (unsigned)((tc.co0 + col) * 64 + c * 16) : kOobOffset;
   }
 
-  // Fragment addresses (bytes): pixel block p of this wave sits at slot
-  // slot_p; tap kw adds 80*kw, K half h adds 32.
-  int ax[PB];
+  // Fragment addresses (bytes within a buffer). Pixel block p of this wave,
+  // tap kw: slot s = slot_p + kw, chunk lgrp for K half 0; K half 1 is chunk
+  // lgrp + 2, i.e. the address XOR 32.
+  int ax[PB][3];
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
     const int rel = wave_m * (PB * R) + p * R + lrow;
     const int k = rel < len0 ? 0 : 1 + (rel - len0) / a.Wo;
-    ax[p] = (rel + 2 * k) * (S::SLOT_UNITS * 16) + lgrp * 16;
+    const int slot = rel + 2 * k;
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw) ax[p][kw] = (slot + kw) * 64 + xslot_chunk(slot + kw, lgrp) * 16;
   }
   int aw[CB][2];
 #pragma unroll
@@ -974,45 +994,48 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     return valid_stage(pr, cc);
   };
 
-  // DMA of stage e into buffer b, in four parts so that it can be spread
-  // between MFMAs: X entries [0,4), [4,8), [8,XJ), then the weights.
-  auto issue_dma = [&](int e, auto buf_c, auto part_c) {
-    constexpr int b = decltype(buf_c)::value;
-    constexpr int part = decltype(part_c)::value;
-    u32x4_t* xdst = b ? xbuf1 : xbuf0;
-    u32x4_t* wdst = b ? wbuf1 : wbuf0;
-    if (e == kEnd) return;
-    const int pr = e >> 8, cc = e & 255;
-    const int kd = pr / 3, kh = pr - kd * 3;
-    if constexpr (part < 3) {
-      const unsigned pbit = 1u << pr;
-      const int delta = (kd * a.H + kh) * a.W * (a.Cin * 2) + cc * 64;
-      constexpr int j0 = 4 * part, j1 = (4 * part + 4 < XJ) ? 4 * part + 4 : XJ;
-#pragma unroll
-      for (int j = j0; j < j1; ++j) {
-        const unsigned off = (xmask[j] & pbit) ? (unsigned)(xbase[j] + delta) : kOobOffset;
-        dma16(xrsrc, &xdst[(j * 4 + wave) * 64], off, 0u);
-      }
-    } else {
-#pragma unroll
-      for (int kw = 0; kw < 3; ++kw) {
-        const unsigned soff = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
-#pragma unroll
-        for (int j = 0; j < WJ; ++j) {
-          if constexpr (WU % 256 == 0) {
-            dma16(wrsrc, &wdst[kw * WU + (j * 4 + wave) * 64], woff[j], soff);
-          } else {
-            if ((j * 4 + wave) * 64 < WU) dma16(wrsrc, &wdst[kw * WU + (j * 4 + wave) * 64], woff[j], soff);
-          }
-        }
-      }
-    }
+  auto xbuf = [&](auto b_c) -> u32x4_t* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? xbuf0 : (b == 1 ? xbuf1 : xbuf2);
   };
-  auto issue_dma_all = [&](int e, auto buf_c) {
-    issue_dma(e, buf_c, SlotC<0>{});
-    issue_dma(e, buf_c, SlotC<1>{});
-    issue_dma(e, buf_c, SlotC<2>{});
-    issue_dma(e, buf_c, SlotC<3>{});
+  auto wbuf = [&](auto b_c) -> u32x4_t* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? wbuf0 : wbuf1;
+  };
+  // One DMA instruction of a stage's fetch. The weights of a stage are
+  // NW = 3 * WJ instructions per wave (tap kw = k / WJ, piece j = k % WJ),
+  // then come the XJ activation instructions. Branch-free: the per-stage
+  // scalars come from stage_dma(), and a stage past the end loads nothing
+  // but out-of-range zeros into a buffer nobody reads.
+  constexpr int NW = 3 * WJ;
+  struct StageDma {
+    unsigned wsoff[3];   // weight byte offset of each kw tap
+    unsigned wor;        // 0, or kOobOffset past the last stage
+    unsigned pbit;       // bit of the (kd, kh) pair, 0 past the last stage
+    int delta;           // activation byte offset of the pair and chunk
+  };
+  auto stage_dma = [&](int e) -> StageDma {
+    StageDma d;
+    const bool ok = e != kEnd;
+    const int pr = ok ? e >> 8 : 0, cc = ok ? e & 255 : 0;
+    const int kd = pr / 3, kh = pr - kd * 3;
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw)
+      d.wsoff[kw] = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
+    d.wor = ok ? 0u : kOobOffset;
+    d.pbit = ok ? 1u << pr : 0u;
+    d.delta = (kd * a.H + kh) * a.W * (a.Cin * 2) + cc * 64;
+    return d;
+  };
+  auto issue_w_one = [&](const StageDma& d, auto b_c, auto k_c) {
+    constexpr int k = decltype(k_c)::value;
+    constexpr int kw = k / WJ, j = k % WJ;
+    dma16(wrsrc, &wbuf(b_c)[kw * WUP + (j * 4 + wave) * 64], woff[j] | d.wor, d.wsoff[kw]);
+  };
+  auto issue_x_one = [&](const StageDma& d, auto b_c, auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    const unsigned off = (xmask[j] & d.pbit) ? (unsigned)(xbase[j] + d.delta) : kOobOffset;
+    dma16(xrsrc, &xbuf(b_c)[(j * 4 + wave) * 64], off, 0u);
   };
 
   acc_t acc[CB][PB];
@@ -1024,15 +1047,14 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
       for (int e = 0; e < NACC; ++e) acc[cb][p][e] = 0.f;
 
   u32x4_t xf[2][PB], wf[2][CB];
-  // Fragments of sub-step u (tap kw = u / 2, K half h = u % 2) of buffer b.
-  auto read_frags = [&](auto buf_c, int u, u32x4_t (&x)[PB], u32x4_t (&w)[CB]) {
-    constexpr int b = decltype(buf_c)::value;
-    const char* xb = reinterpret_cast<const char*>(b ? xbuf1 : xbuf0);
-    const char* wb = reinterpret_cast<const char*>(b ? wbuf1 : wbuf0);
+  // Fragments of sub-step u (tap kw = u / 2, K half h = u % 2).
+  auto read_frags = [&](auto xb_c, auto wb_c, int u, u32x4_t (&x)[PB], u32x4_t (&w)[CB]) {
+    const char* xb = reinterpret_cast<const char*>(xbuf(xb_c));
+    const char* wb = reinterpret_cast<const char*>(wbuf(wb_c));
     const int kw = u >> 1, h = u & 1;
 #pragma unroll
     for (int p = 0; p < PB; ++p)
-      x[p] = *reinterpret_cast<const u32x4_t*>(xb + ax[p] + kw * (S::SLOT_UNITS * 16) + h * 32);
+      x[p] = *reinterpret_cast<const u32x4_t*>(xb + (h ? (ax[p][kw] ^ 32) : ax[p][kw]));
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       w[cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][h] + kw * WTAP);
@@ -1050,46 +1072,54 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   int e0 = first_stage();
   int e1 = next_stage(e0);
   int e2 = next_stage(e1);
-  issue_dma_all(e0, SlotC<0>{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  issue_dma_all(e1, SlotC<1>{});
-  read_frags(SlotC<0>{}, 0, xf[0], wf[0]);
+  {
+    const StageDma d0 = stage_dma(e0), d1 = stage_dma(e1);
+    static_for<NW>([&](auto k) { issue_w_one(d0, SlotC<0>{}, k); });
+    static_for<XJ>([&](auto j) { issue_x_one(d0, SlotC<0>{}, j); });
+    static_for<XJ>([&](auto j) { issue_x_one(d1, SlotC<1>{}, j); });
+  }
+  if (e1 == kEnd) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(XJ) : "memory");
+  read_frags(SlotC<0>{}, SlotC<0>{}, 0, xf[0], wf[0]);
 
-  auto iteration = [&](auto buf_c) -> bool {
-    constexpr int b = decltype(buf_c)::value;
+  // Stage i (activation buffer i % 3, weight buffer i % 2) fetches the
+  // weights of stage i+1 and the activations of stage i+2 during sub-steps
+  // 0-4, DMA instruction k after MFMA group k * NG / ND of those sub-steps.
+  constexpr int GPS = CB;                 // MFMA groups (one channel block) per sub-step
+  constexpr int NG = 5 * GPS, ND = NW + XJ;
+  static_assert(ND <= NG * 4, "DMA must fit in sub-steps 0-4");
+  auto iteration = [&](auto i_c) -> bool {
+    constexpr int I = decltype(i_c)::value;
+    constexpr int XB = I % 3, WB = I % 2;
     if (e0 == kEnd) return false;
-    // Sub-steps 0..4: the next sub-step's fragments are read first, then this
-    // sub-step's MFMAs run while they arrive.
-#pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      read_frags(buf_c, u + 1, xf[(u + 1) & 1], wf[(u + 1) & 1]);
+    const StageDma dw = stage_dma(e1), dx = stage_dma(e2);
+    static_for<5>([&](auto u_c) {
+      constexpr int u = decltype(u_c)::value;
+      read_frags(SlotC<XB>{}, SlotC<WB>{}, u + 1, xf[(u + 1) & 1], wf[(u + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(xf[u & 1], wf[u & 1], 0, CB);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Stage i+1 has landed everywhere and nobody reads buffer b any more.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    read_frags(SlotC<b ^ 1>{}, 0, xf[0], wf[0]);
+      static_for<GPS>([&](auto cb_c) {
+        constexpr int cb = decltype(cb_c)::value;
+        constexpr int g = u * GPS + cb;
+        mfmas(xf[u & 1], wf[u & 1], cb, cb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<ND>([&](auto d_c) {
+          constexpr int d = decltype(d_c)::value;
+          if constexpr (d * NG / ND == g) {
+            if constexpr (d < NW) issue_w_one(dw, SlotC<(I + 1) % 2>{}, SlotC<d>{});
+            else issue_x_one(dx, SlotC<(I + 2) % 3>{}, SlotC<d - NW>{});
+          }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+    // Stage i+1 has landed everywhere (only stage i+2's activations may be
+    // in flight) and no wave reads stage i's buffers any more.
+    if (e2 == kEnd) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // Sub-step 5, with the DMA of stage i+2 into buffer b spread over it.
-    constexpr int Q = (CB + 3) / 4;
-    mfmas(xf[1], wf[1], 0, Q);
+    read_frags(SlotC<(I + 1) % 3>{}, SlotC<(I + 1) % 2>{}, 0, xf[0], wf[0]);
     __builtin_amdgcn_sched_barrier(0);
-    issue_dma(e2, buf_c, SlotC<0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(xf[1], wf[1], Q, 2 * Q);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_dma(e2, buf_c, SlotC<1>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(xf[1], wf[1], 2 * Q, 3 * Q < CB ? 3 * Q : CB);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_dma(e2, buf_c, SlotC<2>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(xf[1], wf[1], 3 * Q < CB ? 3 * Q : CB, CB);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_dma(e2, buf_c, SlotC<3>{});
+    mfmas(xf[1], wf[1], 0, CB);
     __builtin_amdgcn_sched_barrier(0);
     e0 = e1;
     e1 = e2;
@@ -1099,6 +1129,10 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   for (;;) {
     if (!iteration(SlotC<0>{})) break;
     if (!iteration(SlotC<1>{})) break;
+    if (!iteration(SlotC<2>{})) break;
+    if (!iteration(SlotC<3>{})) break;
+    if (!iteration(SlotC<4>{})) break;
+    if (!iteration(SlotC<5>{})) break;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
@@ -1138,11 +1172,11 @@ struct Entry {
 const Entry kEntries[] = {
     // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0); kb = X DMA
     // instructions per wave and stage (the row-segment capacity).
-    C32(4, 1, 4, 4, 11, -1, EPI_STORE),
-    C32(4, 1, 4, 3, 11, -1, EPI_STORE),
-    C32(4, 1, 4, 4, 11, -1, EPI_PARTIAL),
-    C32(2, 2, 4, 4, 6, -1, EPI_PARTIAL),
-    C32(2, 2, 4, 3, 6, -1, EPI_PARTIAL),
+    C32(4, 1, 4, 4, 9, -1, EPI_STORE),
+    C32(4, 1, 4, 3, 9, -1, EPI_STORE),
+    C32(4, 1, 4, 4, 9, -1, EPI_PARTIAL),
+    C32(2, 2, 4, 4, 5, -1, EPI_PARTIAL),
+    C32(2, 2, 4, 3, 5, -1, EPI_PARTIAL),
     // ns = 0: tile kernel (pixels staged through LDS too).
     C32(4, 1, 2, 4, 2, 0, EPI_STORE),
     C32(4, 1, 2, 4, 1, 0, EPI_STORE),
