@@ -1078,8 +1078,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     static_for<XJ>([&](auto j) { issue_x_one(d0, SlotC<0>{}, j); });
     static_for<XJ>([&](auto j) { issue_x_one(d1, SlotC<1>{}, j); });
   }
-  if (e1 == kEnd) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(XJ) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(XJ) : "memory");
   read_frags(SlotC<0>{}, SlotC<0>{}, 0, xf[0], wf[0]);
 
   // Stage i (activation buffer i % 3, weight buffer i % 2) fetches the
@@ -1114,8 +1113,9 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     });
     // Stage i+1 has landed everywhere (only stage i+2's activations may be
     // in flight) and no wave reads stage i's buffers any more.
-    if (e2 == kEnd) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
+    // (The XJ activation instructions of stage i+2 are always the last ones
+    // issued; past the end they load zeros into an idle buffer.)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
     __builtin_amdgcn_sched_barrier(0);
     read_frags(SlotC<(I + 1) % 3>{}, SlotC<(I + 1) % 2>{}, 0, xf[0], wf[0]);
     __builtin_amdgcn_sched_barrier(0);
