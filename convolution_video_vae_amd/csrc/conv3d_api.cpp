@@ -67,7 +67,8 @@ struct Plan {
   int m_tiles, n_tiles;
   long long grid;
   // workspace carve (bytes, 256-aligned offsets)
-  size_t off_x, off_y, off_res, off_rout, off_part, total;
+  bool persistent; // one work-group per CU taking tiles from queues
+  size_t off_x, off_y, off_res, off_rout, off_part, off_queue, total;
 };
 
 conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
@@ -251,10 +252,14 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   pl->m_tiles = (int)ceil_div(pr.M, pl->cfg.bm());
   pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());
   pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;
+  // Halo kernel with more tiles than CUs: persistent work-groups.
+  pl->persistent = pl->cfg.ns < 0 && pl->grid > kCUs && !getenv("CONV3D_NO_PERSIST");
+  if (pl->persistent) pl->grid = kCUs;
 
-  // Workspace: NDHWC copies for NCDHW boundaries, then split-K partials.
+  // Workspace: NDHWC copies for NCDHW boundaries, split-K partials, tile
+  // queues.
   size_t off = 0;
-  pl->off_x = pl->off_y = pl->off_res = pl->off_rout = pl->off_part = 0;
+  pl->off_x = pl->off_y = pl->off_res = pl->off_rout = pl->off_part = pl->off_queue = 0;
   if (pr.layout == CONV3D_NCDHW) { pl->off_x = off; off = align256(off + pr.x_bytes); }
   if (pr.out_layout == CONV3D_NCDHW) {
     pl->off_y = off; off = align256(off + pr.y_bytes);
@@ -264,6 +269,10 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   if (pl->reduce) {
     pl->off_part = off;
     off = align256(off + (size_t)pl->splits * pr.M * pr.cout * 4);
+  }
+  if (pl->persistent) {
+    pl->off_queue = off;
+    off = align256(off + kQueueBytes);
   }
   pl->total = off;
 }
@@ -339,9 +348,10 @@ conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogu
     static const char* names[] = {"store", "norm", "partial"};
     snprintf(buf, len,
              "igemm mfma=%d wm=%d wn=%d pb=%d cb=%d kb=%d ns=%d bm=%d bn=%d mode=%s splits=%d "
-             "steps=%d grid=%lld reduce=%d workspace=%zu",
+             "steps=%d grid=%lld persistent=%d reduce=%d workspace=%zu",
              pl.cfg.r, pl.cfg.wm, pl.cfg.wn, pl.cfg.pb, pl.cfg.cb, pl.cfg.kb, pl.cfg.ns, pl.cfg.bm(),
-             pl.cfg.bn(), names[pl.mode], pl.splits, pl.steps, pl.grid, (int)pl.reduce, pl.total);
+             pl.cfg.bn(), names[pl.mode], pl.splits, pl.steps, pl.grid, (int)pl.persistent,
+             (int)pl.reduce, pl.total);
   }
   return CONV3D_OK;
 }
@@ -427,6 +437,10 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
   a.x_bytes = (unsigned)pr.x_bytes;
   a.sqrt_c = sqrtf((float)pr.cout);
   if (pl.grid > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
+  if (pl.persistent) {
+    a.queue = (unsigned*)(ws + pl.off_queue);
+    if (launch_queue_reset(a.queue, stream)) return CONV3D_ERR_HIP;
+  }
   const int rc = launch_igemm(pl.cfg, pl.mode, a, (int)pl.grid, stream);
   if (rc) return rc < 0 ? CONV3D_ERR_UNSUPPORTED : CONV3D_ERR_HIP;
 

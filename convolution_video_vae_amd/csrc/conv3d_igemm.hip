@@ -239,6 +239,8 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
   if (EPI == EPI_STORE) {
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
+      // One pixel block at a time keeps the converted values' registers few.
+      __builtin_amdgcn_sched_barrier(0);
       const int m = m_first + p * R;
       if (m >= a.M || cbase >= a.Cout) continue;
       const long long off = (long long)m * a.Cout + cbase;
@@ -873,7 +875,35 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   const int wave_n = wave / WM;
   const int lrow = lane & 31;
   const int lgrp = lane >> 5;
-  const TileCoord tc = tile_coord(a, S::BM, S::BN);
+
+  // Tiles: one per work-group, or (a.queue set) a persistent work-group per
+  // CU taking tiles from its XCD's queue. Work-groups are dealt to the 8
+  // XCDs round-robin; XCD x owns chunks x, x+8, ... of kQueueChunk
+  // consecutive tiles, handed out in reverse tile order so that the short
+  // tiles of a causal layer's first frames come last (longest first).
+  __shared__ int tile_sh;
+  const int T_all = a.m_tiles * a.n_tiles * a.splits;
+  auto fetch_tile = [&]() -> int {
+    if (tid == 0) {
+      const int x = blockIdx.x & 7;
+      const int j = (int)atomicAdd(a.queue + x * kQueueStride, 1u);
+      const int i = ((j / kQueueChunk) * 8 + x) * kQueueChunk + j % kQueueChunk;
+      tile_sh = i < T_all ? T_all - 1 - i : -1;
+    }
+    __syncthreads();
+    return tile_sh;
+  };
+  int tile_lin = a.queue ? fetch_tile() : 0;
+  while (tile_lin >= 0) {
+  TileCoord tc;
+  if (a.queue) {
+    tc.m0 = (tile_lin % a.m_tiles) * S::BM;
+    const int rest = tile_lin / a.m_tiles;
+    tc.co0 = (rest % a.n_tiles) * S::BN;
+    tc.split = rest / a.n_tiles;
+  } else {
+    tc = tile_coord(a, S::BM, S::BN);
+  }
 
   // Row segments of the tile: the first starts at output column wo0 of row
   // row0 and holds len0 pixels; each later one is a whole output row. Slot
@@ -1138,6 +1168,11 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
                                    tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split, wave_m, wave_n,
                                    lrow, lgrp, red);
+  if (!a.queue) break;
+  // The barrier in fetch_tile also keeps the next tile's DMA away from
+  // buffers a slower wave may still read.
+  tile_lin = fetch_tile();
+  }
 }
 
 // ----------------------------------------------------------------------------

@@ -40,7 +40,14 @@ struct IgemmArgs {
   unsigned flags;
   unsigned x_bytes;         // size of x, for the buffer range check
   float sqrt_c;             // sqrtf((float)Cout)
+  unsigned* queue;          // persistent tile queues (kQueueBytes, zeroed), or null
 };
+
+// Persistent tile queues: one counter per XCD, kQueueStride words apart;
+// XCD x takes chunks of kQueueChunk consecutive tiles.
+constexpr int kQueueStride = 64;
+constexpr int kQueueChunk = 8;
+constexpr size_t kQueueBytes = 8 * kQueueStride * 4;
 
 struct ReduceArgs {
   const float* partial;     // [splits][M][Cout]
@@ -73,5 +80,6 @@ int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int a, int b, vo
 int launch_igemm(const TileCfg& cfg, int mode, const IgemmArgs& args, int grid, void* stream);
 bool igemm_has_config(const TileCfg& cfg, int mode);
 int launch_reduce(const ReduceArgs& args, void* stream);
+int launch_queue_reset(unsigned* queue, void* stream);
 
 }  // namespace conv3d

@@ -185,6 +185,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
 }
 
 // --------------------------------------------------------------------------
+// Zeroes the persistent tile queues before a launch (a kernel rather than a
+// memset so the sequence can be captured in a graph).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void queue_reset_kernel(unsigned* queue) {
+  for (int i = threadIdx.x; i < (int)(kQueueBytes / 4); i += blockDim.x) queue[i] = 0u;
+}
+
+// --------------------------------------------------------------------------
 // Launchers.
 // --------------------------------------------------------------------------
 int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, void* stream) {
@@ -202,6 +210,11 @@ int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int A, int B, vo
   const long long blocks = (long long)n * ta * tb;
   hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      src, dst, A, B, ta, tb);
+  return (int)hipGetLastError();
+}
+
+int launch_queue_reset(unsigned* queue, void* stream) {
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, queue);
   return (int)hipGetLastError();
 }
 
