@@ -150,6 +150,15 @@ __device__ __forceinline__ unsigned pixel_geometry(const IgemmArgs& a, int m_fir
   return live;
 }
 
+// floor(n / d) for 0 <= n, d < 2^22, from a float reciprocal and one
+// correction each way.
+__device__ __forceinline__ int small_div(int n, int d, float inv_d) {
+  int q = (int)((float)n * inv_d);
+  if ((q + 1) * d <= n) ++q;
+  if (q * d > n) --q;
+  return q;
+}
+
 __device__ __forceinline__ unsigned wave_or(unsigned v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
@@ -556,6 +565,32 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
                                    wave_m, wave_n, lrow, lgrp, red);
 }
 
+// Plain store (no bias, residual or norm): each lane's RUN consecutive
+// channels of its PB pixels, rounded to bf16, as 16-byte buffer stores; a
+// pixel past M gets an out-of-range offset, so the store is dropped.
+template <class T, int PB, int CB>
+__device__ __forceinline__ void store_plain(const IgemmArgs& a, typename T::acc_t (&acc)[CB][PB],
+                                            int m_first, int cbase) {
+  constexpr int R = T::R, NACC = T::NACC, RUN = NACC * CB;
+  const __amdgpu_buffer_rsrc_t yr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
+                                        0x00020000);
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const int m = m_first + p * R;
+    const unsigned off = (m < a.M) ? (unsigned)(m * a.Cout + cbase) * 2u : kOobOffset;
+#pragma unroll
+    for (int c8 = 0; c8 < RUN; c8 += 8) {
+      u32x4_t ov;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        ov[q] = pack2(acc[(c8 + 2 * q) / NACC][p][(c8 + 2 * q) % NACC],
+                      acc[(c8 + 2 * q + 1) / NACC][p][(c8 + 2 * q + 1) % NACC]);
+      __builtin_amdgcn_raw_buffer_store_b128(ov, yr, (int)(off + c8 * 2), 0, 0);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Tile kernel: both operands staged through LDS, as in a GEMM.
 //
@@ -865,16 +900,15 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   // from the fragment reads of another.
   __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
   __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
-  __shared__ unsigned live_sh;
   __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane0 = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave % WM;
   const int wave_n = wave / WM;
-  const int lrow = lane & 31;
-  const int lgrp = lane >> 5;
+  const int lrow = lane0 & 31;
+  const int lgrp = lane0 >> 5;
 
   // Tiles: one per work-group, or (a.queue set) a persistent work-group per
   // CU taking tiles from its XCD's queue. Work-groups are dealt to the 8
@@ -893,8 +927,14 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     __syncthreads();
     return tile_sh;
   };
+  const int rows_total = a.N * a.Do * a.Ho;
+  const float inv_wo = 1.0f / (float)a.Wo, inv_wo2 = 1.0f / (float)(a.Wo + 2);
   int tile_lin = a.queue ? fetch_tile() : 0;
   while (tile_lin >= 0) {
+  // Recomputing the per-lane set-up each tile is cheaper than the registers
+  // (and spills) of keeping it across tiles: hide the lane id's invariance.
+  int lane = lane0;
+  asm volatile("" : "+v"(lane));
   TileCoord tc;
   if (a.queue) {
     tc.m0 = (tile_lin % a.m_tiles) * S::BM;
@@ -911,34 +951,15 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   const int row0 = tc.m0 / a.Wo;
   const int wo0 = tc.m0 - row0 * a.Wo;
   const int len0 = min(a.Wo - wo0, S::BM);
-  const int rows_total = a.N * a.Do * a.Ho;
+  const int nseg = (min(tc.m0 + S::BM, a.M) - 1) / a.Wo - row0 + 1;
 
-  // Activation DMA entries of this lane: LDS unit q of a buffer holds chunk
-  // xslot_chunk(q / 4, q % 4) of slot q / 4. xbase is that chunk's byte offset
-  // in x at kd = kh = 0 and channel chunk 0; xmask the 9-bit set of (kd, kh)
-  // pairs for which the pixel lies inside the input.
-  int xbase[XJ];
-  unsigned xmask[XJ];
-  unsigned live = 0;
-#pragma unroll
-  for (int j = 0; j < XJ; ++j) {
-    const int q = (j * 4 + wave) * 64 + lane;
-    const int s = q >> 2;
-    const int c = xslot_chunk(s, q & 3);
-    int k, i;
-    if (s < len0 + 2) {
-      k = 0;
-      i = s;
-    } else {
-      const int rel = s - len0 - 2;
-      k = 1 + rel / (a.Wo + 2);
-      i = rel - (k - 1) * (a.Wo + 2);
-    }
-    const int r = row0 + k;
-    const int w_in = (k == 0 ? wo0 : 0) - a.pw + i;
-    unsigned m = 0;
-    long long off = 0;
-    if (r < rows_total && w_in >= 0 && w_in < a.W) {
+  // Lane k describes row segment k: the input pixel index of (n, d0, h0, 0)
+  // and the 9-bit set of (kd, kh) pairs that fall inside the input.
+  int rbase = 0;
+  unsigned rmask = 0;
+  {
+    const int r = row0 + lane;
+    if (r < rows_total) {
       const int ho = r % a.Ho;
       const int t2 = r / a.Ho;
       const int dq = t2 % a.Do;
@@ -949,20 +970,43 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
       for (int kd = 0; kd < 3; ++kd)
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh)
-          m |= (unsigned)(d0 + kd >= 0 && d0 + kd < a.D && h0 + kh >= 0 && h0 + kh < a.H)
-               << (kd * 3 + kh);
-      off = ((((long long)n * a.D + d0) * a.H + h0) * a.W + w_in) * (a.Cin * 2) + c * 16;
+          rmask |= (unsigned)(d0 + kd >= 0 && d0 + kd < a.D && h0 + kh >= 0 && h0 + kh < a.H)
+                   << (kd * 3 + kh);
+      rbase = ((n * a.D + d0) * a.H + h0) * a.W;
     }
-    xbase[j] = m ? (int)off : 0;
-    xmask[j] = m;
-    live |= m;
   }
-  live = wave_or(live);
-  if (tid == 0) live_sh = 0;
-  __syncthreads();
-  if (lane == 0) atomicOr(&live_sh, live);
-  __syncthreads();
-  live = __builtin_amdgcn_readfirstlane(live_sh);
+  // Live (kd, kh) pairs of the tile: the same in every wave, no LDS needed.
+  const unsigned live = __builtin_amdgcn_readfirstlane(wave_or(lane < nseg ? rmask : 0u));
+
+  // Activation DMA entries of this lane: LDS unit q of a buffer holds chunk
+  // xslot_chunk(q / 4, q % 4) of slot q / 4. xbase is that chunk's byte offset
+  // in x at kd = kh = 0 and channel chunk 0; xmask the (kd, kh) pairs for
+  // which the pixel lies inside the input.
+  int xbase[XJ];
+  unsigned xmask[XJ];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int q = (j * 4 + wave) * 64 + lane;
+    const int sl = q >> 2;
+    const int c = xslot_chunk(sl, q & 3);
+    int k, i;
+    if (sl < len0 + 2) {
+      k = 0;
+      i = sl;
+    } else {
+      const int rel = sl - len0 - 2;
+      const int kq = small_div(rel, a.Wo + 2, inv_wo2);
+      k = 1 + kq;
+      i = rel - kq * (a.Wo + 2);
+    }
+    const int w_in = (k == 0 ? wo0 : 0) - a.pw + i;
+    const int kk = min(k, 63);
+    const unsigned m = __shfl(rmask, kk);
+    const int rb = __shfl(rbase, kk);
+    const bool wok = w_in >= 0 && w_in < a.W;
+    xmask[j] = wok ? m : 0u;
+    xbase[j] = wok ? (rb + w_in) * (a.Cin * 2) + c * 16 : 0;
+  }
 
   // Weight DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
   // channel order, 16-byte chunk (q % 4) XOR the row swizzle.
@@ -983,7 +1027,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
     const int rel = wave_m * (PB * R) + p * R + lrow;
-    const int k = rel < len0 ? 0 : 1 + (rel - len0) / a.Wo;
+    const int k = rel < len0 ? 0 : 1 + small_div(rel - len0, a.Wo, inv_wo);
     const int slot = rel + 2 * k;
 #pragma unroll
     for (int kw = 0; kw < 3; ++kw) ax[p][kw] = (slot + kw) * 64 + xslot_chunk(slot + kw, lgrp) * 16;
@@ -1165,9 +1209,13 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     if (!iteration(SlotC<5>{})) break;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
-                                   tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split, wave_m, wave_n,
-                                   lrow, lgrp, red);
+  if (EPI == EPI_STORE && a.flags == 0) {
+    store_plain<T, PB, CB>(a, acc, tc.m0 + wave_m * PB * R + lrow, tc.co0 + wave_n * R * CB + lgrp * RUN);
+  } else {
+    epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
+                                     tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split, wave_m, wave_n,
+                                     lrow, lgrp, red);
+  }
   if (!a.queue) break;
   // The barrier in fetch_tile also keeps the next tile's DMA away from
   // buffers a slower wave may still read.
