@@ -153,8 +153,10 @@ int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1
 
 bool halo_ok(const Problem& pr, const TileCfg& c) {
   if (c.ns >= 0) return true;
+  // (Output rows are split with a float-reciprocal division, exact below 2^22.)
   return pr.sw == 1 && pr.cin % 32 == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
-         ceil_div(c.bm() - 1, pr.Wo) + 1 <= halo_maxseg(c);
+         ceil_div(c.bm() - 1, pr.Wo) + 1 <= halo_maxseg(c) &&
+         (long long)pr.n * pr.Do * pr.Ho < (1LL << 22);
 }
 
 const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 9, -1}, {32, 4, 1, 4, 3, 9, -1}};

@@ -150,8 +150,8 @@ __device__ __forceinline__ unsigned pixel_geometry(const IgemmArgs& a, int m_fir
   return live;
 }
 
-// floor(n / d) for 0 <= n, d < 2^22, from a float reciprocal and one
-// correction each way.
+// floor(n / d) for 0 <= n < 2^22 and 0 < d < 2^22, from a float reciprocal
+// and one correction each way.
 __device__ __forceinline__ int small_div(int n, int d, float inv_d) {
   int q = (int)((float)n * inv_d);
   if ((q + 1) * d <= n) ++q;
@@ -929,6 +929,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   };
   const int rows_total = a.N * a.Do * a.Ho;
   const float inv_wo = 1.0f / (float)a.Wo, inv_wo2 = 1.0f / (float)(a.Wo + 2);
+  const float inv_ho = 1.0f / (float)a.Ho, inv_do = 1.0f / (float)a.Do;
   int tile_lin = a.queue ? fetch_tile() : 0;
   while (tile_lin >= 0) {
   // Recomputing the per-lane set-up each tile is cheaper than the registers
@@ -960,10 +961,10 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   {
     const int r = row0 + lane;
     if (r < rows_total) {
-      const int ho = r % a.Ho;
-      const int t2 = r / a.Ho;
-      const int dq = t2 % a.Do;
-      const int n = t2 / a.Do;
+      const int t2 = small_div(r, a.Ho, inv_ho);
+      const int ho = r - t2 * a.Ho;
+      const int n = small_div(t2, a.Do, inv_do);
+      const int dq = t2 - n * a.Do;
       const int d0 = dq * a.sd - a.pd;
       const int h0 = ho * a.sh - a.ph;
 #pragma unroll
@@ -989,17 +990,13 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     const int q = (j * 4 + wave) * 64 + lane;
     const int sl = q >> 2;
     const int c = xslot_chunk(sl, q & 3);
-    int k, i;
-    if (sl < len0 + 2) {
-      k = 0;
-      i = sl;
-    } else {
-      const int rel = sl - len0 - 2;
-      const int kq = small_div(rel, a.Wo + 2, inv_wo2);
-      k = 1 + kq;
-      i = rel - kq * (a.Wo + 2);
-    }
-    const int w_in = (k == 0 ? wo0 : 0) - a.pw + i;
+    // Branch-free, so the lane shuffles below issue back to back.
+    const int rel = sl - len0 - 2;
+    const int kq = small_div(max(rel, 0), a.Wo + 2, inv_wo2);
+    const bool first = rel < 0;
+    const int k = first ? 0 : 1 + kq;
+    const int i = first ? sl : rel - kq * (a.Wo + 2);
+    const int w_in = (first ? wo0 : 0) - a.pw + i;
     const int kk = min(k, 63);
     const unsigned m = __shfl(rmask, kk);
     const int rb = __shfl(rbase, kk);
