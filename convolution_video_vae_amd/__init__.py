@@ -14,7 +14,8 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libconv3d_mi355x.so")
+# CONV3D_LIB selects another build of the same library (A/B timing).
+LIB_PATH = os.environ.get("CONV3D_LIB") or os.path.join(_HERE, "libconv3d_mi355x.so")
 
 NCDHW = 0
 NDHWC = 1
