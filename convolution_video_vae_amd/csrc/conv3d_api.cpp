@@ -151,14 +151,29 @@ TileCfg store_channel_cfg(int cout) {
 // stage, sets how many output-row segments one tile may span.
 int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1; }
 
+// Slot kernel {32, WM, WN, PB, CB, 0, -2}: stride 1 along W and whole
+// 32-channel chunks. Output row r owns Wo + 2 slots and a tile is bm() of
+// them; the bm() + 2 slots staged per stage must span at most 64 output rows
+// (one lane each), and slot indices are split with a float-reciprocal
+// division, exact below 2^22.
+long long slot_rows(const Problem& pr) { return (long long)pr.n * pr.Do * pr.Ho; }
+
+bool slot_ok(const Problem& pr, const TileCfg& c) {
+  const long long wp = pr.Wo + 2;
+  return pr.sw == 1 && pr.cin % 32 == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
+         (c.bm() + 1) / wp + 2 <= 64 && slot_rows(pr) * wp + c.bm() + 2048 < (1LL << 22);
+}
+
 bool halo_ok(const Problem& pr, const TileCfg& c) {
   if (c.ns >= 0) return true;
+  if (c.ns == -2) return slot_ok(pr, c);
   // (Output rows are split with a float-reciprocal division, exact below 2^22.)
   return pr.sw == 1 && pr.cin % 32 == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
          ceil_div(c.bm() - 1, pr.Wo) + 1 <= halo_maxseg(c) &&
          (long long)pr.n * pr.Do * pr.Ho < (1LL << 22);
 }
 
+const TileCfg kSlotStore[] = {{32, 2, 2, 8, 2, 0, -2}, {32, 4, 1, 4, 3, 0, -2}};
 const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 9, -1}, {32, 4, 1, 4, 3, 9, -1}};
 const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 5, -1}, {32, 2, 2, 4, 3, 5, -1},
                                 {32, 4, 1, 4, 4, 9, -1}};
@@ -185,7 +200,8 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
 
   TileCfg store_cfg = store_channel_cfg(pr.cout);
   if (!igemm_has_config(store_cfg, EPI_STORE)) store_cfg = base;
-  if (!norm) pick_halo(pr, kHaloStore, EPI_STORE, &store_cfg);
+  if (!norm && !pick_halo(pr, kSlotStore, EPI_STORE, &store_cfg))
+    pick_halo(pr, kHaloStore, EPI_STORE, &store_cfg);
   TileCfg part_cfg = base;
   part_cfg.pb = 2;
   if (base.r == 32 && ceil_div(pr.M, part_cfg.bm()) * n_tiles < 64) {
@@ -193,7 +209,8 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     c.pb = 1;
     if (igemm_has_config(c, EPI_PARTIAL)) part_cfg = c;
   }
-  pick_halo(pr, kHaloPartial, EPI_PARTIAL, &part_cfg);
+  // (Fragment-order partials of the halo kernel have no norm reduction.)
+  if (!norm) pick_halo(pr, kHaloPartial, EPI_PARTIAL, &part_cfg);
 
   // Fused-norm kernels hold the whole channel row of a pixel in one group.
   TileCfg norm_cfg = {0, 0, 0, 0, 0, 0, 0};
@@ -251,7 +268,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   splits = std::max(1, std::min(splits, pl->steps));
   pl->steps_per_split = (pl->steps + splits - 1) / splits;
   pl->splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
-  pl->m_tiles = (int)ceil_div(pr.M, pl->cfg.bm());
+  pl->m_tiles = (int)ceil_div(pl->cfg.ns == -2 ? slot_rows(pr) * (pr.Wo + 2) : pr.M, pl->cfg.bm());
   pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());
   pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;
   // Halo kernel with more tiles than CUs: persistent work-groups.
@@ -269,8 +286,11 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     if (pr.flags & F_RESIDUAL_OUT) { pl->off_rout = off; off = align256(off + pr.y_bytes); }
   }
   if (pl->reduce) {
+    // Halo-kernel partials are whole tiles in fragment order.
+    const size_t rows = pl->cfg.ns == -1 ? (size_t)pl->m_tiles * pl->cfg.bm() : (size_t)pr.M;
+    const size_t cols = pl->cfg.ns == -1 ? (size_t)pl->n_tiles * pl->cfg.bn() : (size_t)pr.cout;
     pl->off_part = off;
-    off = align256(off + (size_t)pl->splits * pr.M * pr.cout * 4);
+    off = align256(off + (size_t)pl->splits * rows * cols * 4);
   }
   if (pl->persistent) {
     pl->off_queue = off;
@@ -438,6 +458,9 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
   a.flags = pl.reduce ? 0u : f;
   a.x_bytes = (unsigned)pr.x_bytes;
   a.sqrt_c = sqrtf((float)pr.cout);
+  a.inv_ho = 1.0f / (float)pr.Ho;
+  a.inv_do = 1.0f / (float)pr.Do;
+  a.inv_wp = 1.0f / (float)(pr.Wo + 2);
   if (pl.grid > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
   if (pl.persistent) {
     a.queue = (unsigned*)(ws + pl.off_queue);
@@ -459,6 +482,12 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
     r.splits = pl.splits;
     r.flags = f;
     r.sqrt_c = a.sqrt_c;
+    r.frag = pl.cfg.ns == -1;
+    r.m_tiles = pl.m_tiles;
+    r.n_tiles = pl.n_tiles;
+    r.wm = pl.cfg.wm;
+    r.pb = pl.cfg.pb;
+    r.cb = pl.cfg.cb;
     if (launch_reduce(r, stream)) return CONV3D_ERR_HIP;
   }
 

@@ -97,6 +97,7 @@ __device__ __forceinline__ int lds_idx(int row, int chunk) {
 // sharing input rows or a weight slice meet in the same L2.
 struct TileCoord {
   int m0, co0, split;
+  int m_end;  // slot kernel: end of the tile's slot range
 };
 __device__ __forceinline__ TileCoord tile_coord(const IgemmArgs& a, int BM, int BN) {
   int bid = blockIdx.x;
@@ -159,6 +160,23 @@ __device__ __forceinline__ int small_div(int n, int d, float inv_d) {
   return q;
 }
 
+// Lane index of the calling lane, recomputed where it is called (volatile,
+// so not hoisted into a register that lives through a main loop).
+__device__ __forceinline__ int lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// OR of a 9-bit mask over the wave, through ballots (scalar results, no
+// lane-index registers).
+__device__ __forceinline__ unsigned wave_or9(unsigned v) {
+  unsigned r = 0;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) r |= (__builtin_amdgcn_ballot_w64(((v >> b) & 1u) != 0u) != 0 ? 1u : 0u) << b;
+  return r;
+}
+
 __device__ __forceinline__ unsigned wave_or(unsigned v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
@@ -218,22 +236,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const IgemmArgs& a) {
                                            0x00020000);
 }
 
+// Output pixel of each of a lane's pixel blocks: m_first + p*R, or -1 past M.
+template <int PB, int R>
+__device__ __forceinline__ void block_pixels(int m_first, int M, int (&mp)[PB]) {
+#pragma unroll
+  for (int p = 0; p < PB; ++p) mp[p] = (m_first + p * R < M) ? m_first + p * R : -1;
+}
+
 // Epilogue. For pixel block p the lane holds channels cbase .. cbase+RUN-1 of
-// pixel m_first + p*R: run position NACC*cb + e is acc[cb][p][e].
+// output pixel mp[p] (none if negative): run position NACC*cb + e is
+// acc[cb][p][e].
 //   EPI_PARTIAL: fp32 partial sums of this K split.
 //   EPI_STORE:   value = B(B(B(acc) + bias) + residual), each step if enabled.
 //   EPI_NORM:    the whole contract; the work-group holds the pixel's full
 //                channel row (BN == Cout), its WN waves meeting through `red`.
 template <class T, int WM, int WN, int PB, int CB, int EPI>
 __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (&acc)[CB][PB],
-                                         int m_first, int cbase, int split, int wave_m, int wave_n,
+                                         const int (&mp)[PB], int cbase, int split, int wave_m, int wave_n,
                                          int lrow, int lgrp, float* red) {
   constexpr int R = T::R, NACC = T::NACC, RUN = NACC * CB;
   if (EPI == EPI_PARTIAL) {
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
-      const int m = m_first + p * R;
-      if (m >= a.M || cbase >= a.Cout) continue;
+      const int m = mp[p];
+      if (m < 0 || cbase >= a.Cout) continue;
       f32x4_t* dst =
           reinterpret_cast<f32x4_t*>(a.partial + ((long long)split * a.M + m) * a.Cout + cbase);
 #pragma unroll
@@ -250,8 +276,8 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
     for (int p = 0; p < PB; ++p) {
       // One pixel block at a time keeps the converted values' registers few.
       __builtin_amdgcn_sched_barrier(0);
-      const int m = m_first + p * R;
-      if (m >= a.M || cbase >= a.Cout) continue;
+      const int m = mp[p];
+      if (m < 0 || cbase >= a.Cout) continue;
       const long long off = (long long)m * a.Cout + cbase;
 #pragma unroll
       for (int c8 = 0; c8 < RUN; c8 += 8) {
@@ -280,8 +306,8 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
   float ss[PB];
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
-    const int m = m_first + p * R;
-    const bool ok = m < a.M;
+    const int m = mp[p];
+    const bool ok = m >= 0;
     const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
     float t = 0.f;
 #pragma unroll
@@ -324,8 +350,8 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
   }
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
-    const int m = m_first + p * R;
-    if (m >= a.M) continue;
+    const int m = mp[p];
+    if (m < 0) continue;
     const float den = fmaxf(sqrtf(ss[p]), 1e-12f);
     const long long off = (long long)m * a.Cout + cbase;
 #pragma unroll
@@ -561,7 +587,9 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
       if (!iteration(SlotC<3 % NS>{})) break;
     }
   }
-  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, m_first, tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split,
+  int mp[PB];
+  block_pixels<PB, R>(m_first, a.M, mp);
+  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, mp, tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split,
                                    wave_m, wave_n, lrow, lgrp, red);
 }
 
@@ -570,15 +598,15 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
 // pixel past M gets an out-of-range offset, so the store is dropped.
 template <class T, int PB, int CB>
 __device__ __forceinline__ void store_plain(const IgemmArgs& a, typename T::acc_t (&acc)[CB][PB],
-                                            int m_first, int cbase) {
-  constexpr int R = T::R, NACC = T::NACC, RUN = NACC * CB;
+                                            const int (&mp)[PB], int cbase) {
+  constexpr int NACC = T::NACC, RUN = NACC * CB;
   const __amdgpu_buffer_rsrc_t yr =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
                                         0x00020000);
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
-    const int m = m_first + p * R;
-    const unsigned off = (m < a.M) ? (unsigned)(m * a.Cout + cbase) * 2u : kOobOffset;
+    const int m = mp[p];
+    const unsigned off = (m >= 0) ? (unsigned)(m * a.Cout + cbase) * 2u : kOobOffset;
 #pragma unroll
     for (int c8 = 0; c8 < RUN; c8 += 8) {
       u32x4_t ov;
@@ -589,6 +617,28 @@ __device__ __forceinline__ void store_plain(const IgemmArgs& a, typename T::acc_
       __builtin_amdgcn_raw_buffer_store_b128(ov, yr, (int)(off + c8 * 2), 0, 0);
     }
   }
+}
+
+// Split-K partials in fragment order (halo kernel): the partial block of
+// (split, m tile, n tile, wave, p, cb) holds a lane's 16 accumulator floats
+// as four 1 KB rows (float4 q of lanes 0..63), so every store instruction
+// writes 1 KB of consecutive bytes; stores straight into the [M][Cout]
+// layout would scatter 16-byte pieces over 64 rows per instruction.
+// reduce_frag_kernel reads the blocks back in the same order.
+template <int PB, int CB>
+__device__ __forceinline__ void store_partial_frag(const IgemmArgs& a, f32x16_t (&acc)[CB][PB],
+                                                   const TileCoord& tc, int BM, int BN, int wave,
+                                                   int lane) {
+  const long long tile = ((long long)tc.split * a.m_tiles + tc.m0 / BM) * a.n_tiles + tc.co0 / BN;
+  f32x4_t* base = reinterpret_cast<f32x4_t*>(a.partial) + (tile * 4 + wave) * (PB * CB * 4 * 64) + lane;
+#pragma unroll
+  for (int p = 0; p < PB; ++p)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        base[((p * CB + cb) * 4 + q) * 64] =
+            f32x4_t{acc[cb][p][4 * q], acc[cb][p][4 * q + 1], acc[cb][p][4 * q + 2], acc[cb][p][4 * q + 3]};
 }
 
 // ----------------------------------------------------------------------------
@@ -831,9 +881,10 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_tile_kernel(IgemmArgs a) {
     if (!iteration(SlotC<1>{})) break;
     if (!iteration(SlotC<2>{})) break;
   }
-  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
-                                   tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split, wave_m, wave_n,
-                                   lrow, lgrp, red);
+  int mp[PB];
+  block_pixels<PB, R>(tc.m0 + wave_m * PB * R + lrow, a.M, mp);
+  epilogue<T, WM, WN, PB, CB, EPI>(a, acc, mp, tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split,
+                                   wave_m, wave_n, lrow, lgrp, red);
 }
 
 // ----------------------------------------------------------------------------
@@ -859,6 +910,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_tile_kernel(IgemmArgs a) {
 // last sub-step, whose MFMAs then cover the first fragment reads of stage i+1.
 // ----------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, void* lds, unsigned voff,
                                       unsigned soff) {
@@ -1206,10 +1258,14 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     if (!iteration(SlotC<5>{})) break;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int mp[PB];
+  block_pixels<PB, R>(tc.m0 + wave_m * PB * R + lrow, a.M, mp);
   if (EPI == EPI_STORE && a.flags == 0) {
-    store_plain<T, PB, CB>(a, acc, tc.m0 + wave_m * PB * R + lrow, tc.co0 + wave_n * R * CB + lgrp * RUN);
+    store_plain<T, PB, CB>(a, acc, mp, tc.co0 + wave_n * R * CB + lgrp * RUN);
+  } else if (EPI == EPI_PARTIAL) {
+    store_partial_frag<PB, CB>(a, acc, tc, S::BM, S::BN, wave, lane0);
   } else {
-    epilogue<T, WM, WN, PB, CB, EPI>(a, acc, tc.m0 + wave_m * PB * R + lrow,
+    epilogue<T, WM, WN, PB, CB, EPI>(a, acc, mp,
                                      tc.co0 + wave_n * R * CB + lgrp * RUN, tc.split, wave_m, wave_n,
                                      lrow, lgrp, red);
   }
@@ -1221,13 +1277,452 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Slot kernel: stride 1 along W and Cin % 32 == 0.
+//
+// Output pixels are addressed through slots: output row r = (n, do, ho) owns
+// WP = Wo + 2 consecutive slots, slot c < Wo of the row being output column c
+// and the last two unused. A tile is BM consecutive slots. For one (kd, kh)
+// tap pair and one 32-channel chunk, a stage stages BM + 2 slots of input:
+// staged slot j holds the input pixel of row r(s0 + j) at column
+// c(s0 + j) - pw. Output slot s at tap kw then reads staged slot s - s0 + kw
+// for every s, across row ends too (an unused slot's result is dropped), so
+// the three kw taps are plain slot offsets. Column n of a wave's pixel
+// fragment f holds slot n*PB + f (the fragments interleave), so the operand
+// of tap kw for pixel block p is fragment p + kw: PB + 2 fragment reads per
+// K half serve all three taps, against 3*PB when every tap is read on its
+// own. The two unused slots of a row cost 2 / (Wo + 2) of the MFMA work.
+//
+// LDS layout of an activation buffer, PB = 2^SH: staged slot s (64 bytes,
+// four 16-byte chunks) sits at position s ^ ((s >> SH) & 1), its chunks
+// XORed with (s >> (SH + 1)) & 3. A fragment read's lanes step PB slots; any
+// eight consecutive lanes then hit eight distinct 16-byte bank groups of a
+// 128-byte window. The permutation stays inside aligned groups of 16 slots,
+// the span of one DMA instruction.
+//
+// Each wave computes R*PB slots x R*CB channels with v_mfma_f32_32x32x16_bf16.
+// Operands reach LDS by buffer-to-LDS DMA (a padding pixel is an
+// out-of-range lane: zeros). Three activation and two weight buffers; one
+// barrier per stage, after sub-step 3 of the six (K half h = u / 3, tap
+// kw = u % 3). Stage i's activation DMA goes out during its sub-steps 0-3,
+// two stages ahead; its weight DMA during sub-steps 4-5, right after the
+// barrier frees the buffer, also two stages ahead. LDS fragment reads run
+// one to two sub-steps ahead of their MFMAs, every load and DMA spread
+// between single MFMAs.
+// ----------------------------------------------------------------------------
+template <int PB, int CB, int WN>
+struct SlotShape {
+  static constexpr int R = 32;
+  static constexpr int WM = 4 / WN;
+  static constexpr int BM = R * PB * WM;            // slots per tile
+  static constexpr int BN = R * CB * WN;            // output channels per tile
+  static constexpr int XS = BM + 2;                 // slots staged per stage
+  static constexpr int XJ = (XS * 4 + 255) / 256;   // activation DMA instructions per wave
+  static constexpr int XU = XJ * 256;               // 16-byte units per activation buffer
+  static constexpr int NF = PB + 2;                 // pixel fragments per K half
+  static constexpr int WU = BN * 4;                 // weight units per tap
+  static constexpr int WJ = (WU / 64 + 3) / 4;      // weight DMA instructions per wave per tap
+  static constexpr int WUP = WJ * 256;
+  static constexpr int NW = 3 * WJ;                 // weight DMA instructions per wave per stage
+  static constexpr int SH = PB == 4 ? 2 : 3;        // log2(PB)
+  static_assert(PB == 4 || PB == 8, "slot swizzle");
+  static_assert(WN == 1 || WN == 2 || WN == 4, "4 waves");
+  static_assert(XU % 64 == 0, "the slot permutation works on 16-slot groups");
+};
+
+// LDS 16-byte unit of (staged slot s, chunk c).
+template <int SH>
+__device__ __forceinline__ int slot_unit(int s, int c) {
+  return ((s ^ ((s >> SH) & 1)) << 2) | (c ^ ((s >> (SH + 1)) & 3));
+}
+
+template <int PB, int CB, int WN, int EPI>
+__global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
+  using T = Mfma32;
+  using S = SlotShape<PB, CB, WN>;
+  constexpr int R = S::R, WM = S::WM, NACC = T::NACC, RUN = NACC * CB;
+  constexpr int XU = S::XU, XJ = S::XJ, NF = S::NF, WU = S::WU, WJ = S::WJ, WUP = S::WUP;
+  constexpr int NW = S::NW;
+  constexpr int WTAP = WUP * 16;        // bytes
+  constexpr int EPI_VM = PB * RUN / 8;  // stores of the plain epilogue per wave
+  typedef typename T::acc_t acc_t;
+  static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
+  static_assert(EPI != EPI_NORM, "the fused norm runs in the tile kernel");
+  static_assert(NW + XJ + EPI_VM <= 63, "vmcnt range");
+
+  __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
+  __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
+
+  const int tid = threadIdx.x;
+  const int lane0 = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave % WM;
+  const int wave_n = wave / WM;
+  const int lrow = lane0 & 31;
+  const int lgrp = lane0 >> 5;
+
+  // Tiles: one per work-group, or (a.queue set) a persistent work-group per
+  // CU taking tiles from its XCD's queue, as in the halo kernel. The ticket
+  // of the next tile is taken when a tile starts, so its latency is hidden.
+  __shared__ int tile_sh;
+  const int T_all = a.m_tiles * a.n_tiles * a.splits;
+  auto take_ticket = [&]() -> unsigned { return atomicAdd(a.queue + (blockIdx.x & 7) * kQueueStride, 1u); };
+  auto ticket_tile = [&](unsigned t) -> int {
+    const int x = blockIdx.x & 7, j = (int)t;
+    const int i = ((j / kQueueChunk) * 8 + x) * kQueueChunk + j % kQueueChunk;
+    return i < T_all ? T_all - 1 - i : -1;
+  };
+  const int rows_total = a.N * a.Do * a.Ho;
+  const int WP = a.Wo + 2;
+  const float inv_wp = a.inv_wp, inv_ho = a.inv_ho, inv_do = a.inv_do;
+
+  // Fragment addresses (bytes within a buffer): pixel fragment f of K half 0
+  // is staged slot wave_m*R*PB + lrow*PB + f, chunk lgrp; K half 1 is chunk
+  // lgrp + 2, i.e. the address XOR 32.
+  int ax[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) ax[f] = slot_unit<S::SH>(wave_m * (PB * R) + lrow * PB + f, lgrp) * 16;
+  int aw[CB][2];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) aw[cb][h] = lds_idx((wave_n * CB + cb) * R + lrow, 2 * h + lgrp) * 16;
+
+  const __amdgpu_buffer_rsrc_t xrsrc = x_rsrc(a);
+  const __amdgpu_buffer_rsrc_t wrsrc = w_rsrc(a);
+
+  // State of the current tile.
+  TileCoord tc;
+  unsigned live = 0;
+  int xbase[XJ];
+  unsigned xmask[XJ];
+  unsigned woff[WJ];
+  int s_begin = 0, s_end = 0;
+  int e0 = kEnd, e1 = kEnd, e2 = kEnd;
+
+  // Stages e = (pair << 8) | cc over the live (kd, kh) pairs.
+  auto valid_stage = [&](int pr, int cc) -> int {
+    return (pr < 9 && pr * a.CC + cc < s_end) ? ((pr << 8) | cc) : kEnd;
+  };
+  auto next_stage = [&](int e) -> int {
+    if (e == kEnd) return kEnd;
+    int pr = e >> 8, cc = (e & 255) + 1;
+    if (cc == a.CC) {
+      cc = 0;
+      const unsigned rest = live & (~0u << (pr + 1));
+      pr = rest ? __builtin_ctz(rest) : 9;
+    }
+    return valid_stage(pr, cc);
+  };
+  auto first_stage = [&]() -> int {
+    if (s_begin >= s_end) return kEnd;
+    int pr = s_begin / a.CC, cc = s_begin % a.CC;
+    if (!((live >> pr) & 1u)) {
+      const unsigned rest = live & (~0u << pr);
+      pr = rest ? __builtin_ctz(rest) : 9;
+      cc = 0;
+    }
+    return valid_stage(pr, cc);
+  };
+
+  auto xbuf = [&](auto b_c) -> u32x4_t* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? xbuf0 : (b == 1 ? xbuf1 : xbuf2);
+  };
+  auto wbuf = [&](auto b_c) -> u32x4_t* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? wbuf0 : wbuf1;
+  };
+  struct StageDma {
+    unsigned wsoff[3];   // weight byte offset of each kw tap
+    unsigned wor;        // 0, or kOobOffset past the last stage
+    unsigned pbit;       // bit of the (kd, kh) pair, 0 past the last stage
+    int delta;           // activation byte offset of the pair and chunk
+  };
+  auto stage_dma = [&](int e) -> StageDma {
+    StageDma d;
+    const bool ok = e != kEnd;
+    const int pr = ok ? e >> 8 : 0, cc = ok ? e & 255 : 0;
+    const int kd = pr / 3, kh = pr - kd * 3;
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw)
+      d.wsoff[kw] = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
+    d.wor = ok ? 0u : kOobOffset;
+    d.pbit = ok ? 1u << pr : 0u;
+    d.delta = (kd * a.H + kh) * a.W * (a.Cin * 2) + cc * 64;
+    return d;
+  };
+  // Weight DMA instruction k of a stage (tap kw = k / WJ, piece k % WJ).
+  auto issue_w_one = [&](const StageDma& d, auto b_c, auto k_c) {
+    constexpr int k = decltype(k_c)::value;
+    constexpr int kw = k / WJ, j = k % WJ;
+    dma16(wrsrc, &wbuf(b_c)[kw * WUP + (j * 4 + wave) * 64], woff[j] | d.wor, d.wsoff[kw]);
+  };
+  auto issue_x_one = [&](const StageDma& d, auto b_c, auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    const unsigned off = (xmask[j] & d.pbit) ? (unsigned)(xbase[j] + d.delta) : kOobOffset;
+    dma16(xrsrc, &xbuf(b_c)[(j * 4 + wave) * 64], off, 0u);
+  };
+
+  // Set-up of tile t and the DMA of its first two stages.
+  auto start_tile = [&](int t) {
+    // Recomputing the per-lane set-up each tile is cheaper than the registers
+    // of keeping it.
+    const int lane = lane_id();
+    if (a.queue) {
+      tc.m0 = (t % a.m_tiles) * S::BM;
+      const int rest = t / a.m_tiles;
+      tc.co0 = (rest % a.n_tiles) * S::BN;
+      tc.split = rest / a.n_tiles;
+    } else {
+      tc = tile_coord(a, S::BM, S::BN);
+    }
+    tc.m_end = min(tc.m0 + S::BM, rows_total * WP);
+    const int s0 = tc.m0;  // first slot of the tile
+    const int row0 = small_div(s0, WP, inv_wp);
+    const int s_last = tc.m_end - 1;
+    const int nrows = small_div(s_last, WP, inv_wp) - row0 + 1;
+
+    // Lane k describes output row row0 + k: the input pixel index of
+    // (n, d0, h0, 0) and the 9-bit set of (kd, kh) pairs inside the input.
+    int rbase = 0;
+    unsigned rmask = 0;
+    {
+      const int r = row0 + lane;
+      if (r < rows_total) {
+        const int t2 = small_div(r, a.Ho, inv_ho);
+        const int ho = r - t2 * a.Ho;
+        const int n = small_div(t2, a.Do, inv_do);
+        const int dq = t2 - n * a.Do;
+        const int d0 = dq * a.sd - a.pd;
+        const int h0 = ho * a.sh - a.ph;
+#pragma unroll
+        for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+          for (int kh = 0; kh < 3; ++kh)
+            rmask |= (unsigned)(d0 + kd >= 0 && d0 + kd < a.D && h0 + kh >= 0 && h0 + kh < a.H)
+                     << (kd * 3 + kh);
+        rbase = ((n * a.D + d0) * a.H + h0) * a.W;
+      }
+    }
+    // (kd, kh) pairs live for some row with an output in the tile.
+    live = wave_or9(lane < nrows ? rmask : 0u);
+
+    // Activation DMA entries: LDS unit q of a buffer holds chunk c of staged
+    // slot sl (inverse of slot_unit). xbase is that chunk's byte offset in x
+    // at kd = kh = 0 and channel chunk 0; xmask the pairs for which it lies
+    // inside the input (0 for a padding column or a slot past the staged
+    // range).
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int q = (j * 4 + wave) * 64 + lane;
+      const int sp = q >> 2;
+      const int sl = sp ^ ((sp >> S::SH) & 1);
+      const int c = (q & 3) ^ ((sl >> (S::SH + 1)) & 3);
+      const int s = s0 + sl;
+      const int k = small_div(s, WP, inv_wp) - row0;
+      const int w_in = s - (row0 + k) * WP - a.pw;
+      const int kk = min(k, 63);
+      const unsigned m = __shfl(rmask, kk);
+      const int rb = __shfl(rbase, kk);
+      const bool ok = sl < S::XS && w_in >= 0 && w_in < a.W;
+      xmask[j] = ok ? m : 0u;
+      xbase[j] = ok ? (rb + w_in) * (a.Cin * 2) + c * 16 : 0;
+    }
+    // Weight DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
+    // channel order, 16-byte chunk (q % 4) XOR the row swizzle.
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int q = (j * 4 + wave) * 64 + lane;
+      const int row = q >> 2;
+      const int c = (q & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+      const int col = (row / (R * CB)) * (R * CB) + T::chan_of((row / R) % CB, row % R, CB);
+      woff[j] = (q < WU) ? (unsigned)((tc.co0 + col) * 64 + c * 16) : kOobOffset;
+    }
+    s_begin = tc.split * a.steps_per_split;
+    s_end = min(s_begin + a.steps_per_split, 9 * a.CC);
+    e0 = first_stage();
+    e1 = next_stage(e0);
+    e2 = next_stage(e1);
+    const StageDma d0 = stage_dma(e0), d1 = stage_dma(e1);
+    static_for<NW>([&](auto k) { issue_w_one(d0, SlotC<0>{}, k); });
+    static_for<XJ>([&](auto j) { issue_x_one(d0, SlotC<0>{}, j); });
+    static_for<NW>([&](auto k) { issue_w_one(d1, SlotC<1>{}, k); });
+    static_for<XJ>([&](auto j) { issue_x_one(d1, SlotC<1>{}, j); });
+  };
+
+  acc_t acc[CB][PB];
+  // Epilogue of a finished tile (coordinates pt) from acc.
+  auto finish_tile = [&](const TileCoord& pt) {
+    // Lane-dependent values are formed here rather than hoisted into
+    // registers that would have to live through the main loop.
+    const int el = lane_id();
+    const int elrow = el & 31, elgrp = el >> 5;
+    // Output pixel of each pixel block: slot m0 + wave_m*R*PB + lrow*PB + p.
+    int mp[PB];
+    {
+      const int sp0 = pt.m0 + wave_m * (PB * R) + elrow * PB;
+      int r = small_div(sp0, WP, inv_wp);
+      int c = sp0 - r * WP;
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        mp[p] = (sp0 + p < pt.m_end && c < a.Wo) ? r * a.Wo + c : -1;
+        if (++c == WP) {
+          c = 0;
+          ++r;
+        }
+      }
+    }
+    const int cbase = pt.co0 + wave_n * R * CB + elgrp * RUN;
+    if (EPI == EPI_STORE && a.flags == 0)
+      store_plain<T, PB, CB>(a, acc, mp, cbase);
+    else
+      epilogue<T, WM, WN, PB, CB, EPI>(a, acc, mp, cbase, pt.split, wave_m, wave_n, elrow, elgrp,
+                                       nullptr);
+  };
+
+  // Pixel fragments by K half; weight fragments in a ring of three sub-steps
+  // (sub-step t uses ring slot t % 3).
+  u32x4_t xf[2][NF], wf[3][CB];
+  auto read_x = [&](auto b_c, int h, int f) {
+    const char* xb = reinterpret_cast<const char*>(xbuf(b_c));
+    xf[h][f] = *reinterpret_cast<const u32x4_t*>(xb + (h ? (ax[f] ^ 32) : ax[f]));
+  };
+  auto read_w = [&](auto b_c, int t, int cb) {
+    const char* wb = reinterpret_cast<const char*>(wbuf(b_c));
+    wf[t % 3][cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][t / 3] + (t % 3) * WTAP);
+  };
+
+  // Main loop of one tile. Memory operations of sub-step u of a stage, in
+  // issue order:
+  //   urgent pixel reads: u0/u1 fragments PB / PB+1 of half 0 (needed one
+  //     sub-step later); u4/u5 half-0 fragments of the next stage;
+  //   CB weight reads for sub-step u + 2 (u4/u5: the next stage's 0 / 1);
+  //   half-1 pixel reads: fragments [0, PB) over u0-u2, PB and PB+1 in u3;
+  //   activation DMA of stage i+2 over u0-u3, weight DMA over u4-u5.
+  auto iteration = [&](auto i_c) -> bool {
+    constexpr int I = decltype(i_c)::value;
+    constexpr int XB = I % 3, WB = I % 2;
+    if (e0 == kEnd) return false;
+    const StageDma d2 = stage_dma(e2);
+    static_for<6>([&](auto u_c) {
+      constexpr int u = decltype(u_c)::value;
+      constexpr int h = u / 3, kw = u % 3;
+      constexpr int NURG = (u < 2) ? 1 : (u >= 4 ? (u - 3) * PB / 2 - (u - 4) * PB / 2 : 0);
+      constexpr int URG0 = (u == 0) ? PB : (u == 1 ? PB + 1 : (u >= 4 ? (u - 4) * PB / 2 : 0));
+      constexpr int H1LO = (u < 3) ? u * PB / 3 : (u == 3 ? PB : 0);
+      constexpr int H1HI = (u < 3) ? (u + 1) * PB / 3 : (u == 3 ? PB + 2 : 0);
+      constexpr int DXLO = (u < 4) ? u * XJ / 4 : 0, DXHI = (u < 4) ? (u + 1) * XJ / 4 : 0;
+      constexpr int DWLO = (u >= 4) ? (u - 4) * NW / 2 : 0, DWHI = (u >= 4) ? (u - 3) * NW / 2 : 0;
+      constexpr int NOPS = NURG + CB + (H1HI - H1LO) + (DXHI - DXLO) + (DWHI - DWLO);
+      constexpr int NM = CB * PB;
+      if constexpr (u == 4) {
+        // Stage i+1 has landed everywhere (only stage i+2's activations may
+        // be in flight) and no wave reads stage i's buffers any more.
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      static_for<NM>([&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
+        static_for<NOPS>([&](auto o_c) {
+          constexpr int o = decltype(o_c)::value;
+          if constexpr (o * NM / NOPS == g) {
+            if constexpr (o < NURG) {
+              if constexpr (u < 2) read_x(SlotC<XB>{}, 0, URG0 + o);
+              else read_x(SlotC<(I + 1) % 3>{}, 0, URG0 + o);
+            } else if constexpr (o < NURG + CB) {
+              constexpr int cb = o - NURG;
+              if constexpr (u < 4) read_w(SlotC<WB>{}, u + 2, cb);
+              else read_w(SlotC<(I + 1) % 2>{}, u - 4, cb);
+            } else if constexpr (o < NURG + CB + (H1HI - H1LO)) {
+              read_x(SlotC<XB>{}, 1, H1LO + (o - NURG - CB));
+            } else if constexpr (o < NURG + CB + (H1HI - H1LO) + (DXHI - DXLO)) {
+              issue_x_one(d2, SlotC<(I + 2) % 3>{}, SlotC<DXLO + (o - NURG - CB - (H1HI - H1LO))>{});
+            } else {
+              issue_w_one(d2, SlotC<WB>{},
+                          SlotC<DWLO + (o - NURG - CB - (H1HI - H1LO) - (DXHI - DXLO))>{});
+            }
+          }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int cb = g % CB, p = g / CB;
+        acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wf[u % 3][cb]),
+                            __builtin_bit_cast(bf16x8_t, xf[h][p + kw]), acc[cb][p]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+    e0 = e1;
+    e1 = e2;
+    e2 = next_stage(e2);
+    return true;
+  };
+
+  // Tile pipeline: the set-up and first DMA of tile t+1 go out before the
+  // epilogue of tile t, so their latency hides behind its stores.
+  int cur = 0;
+  if (a.queue) {
+    if (tid == 0) tile_sh = ticket_tile(take_ticket());
+    __syncthreads();
+    cur = __builtin_amdgcn_readfirstlane(tile_sh);
+  }
+  TileCoord prev;
+  bool have_prev = false;
+  for (;;) {
+    unsigned next_ticket = 0;
+    if (cur >= 0) {
+      if (a.queue && tid == 0) next_ticket = take_ticket();
+      start_tile(cur);
+    }
+    if (have_prev) finish_tile(prev);
+    if (cur < 0) break;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+#pragma unroll
+        for (int e = 0; e < NACC; ++e) acc[cb][p][e] = 0.f;
+    // Stage 0 of this tile has landed everywhere; the previous tile's plain
+    // stores (issued after this tile's DMA) may still be in flight.
+    if (have_prev && EPI == EPI_STORE && a.flags == 0)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW + XJ + EPI_VM) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW + XJ) : "memory");
+#pragma unroll
+    for (int f = 0; f < PB; ++f) read_x(SlotC<0>{}, 0, f);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      read_w(SlotC<0>{}, 0, cb);
+      read_w(SlotC<0>{}, 1, cb);
+    }
+    for (;;) {
+      if (!iteration(SlotC<0>{})) break;
+      if (!iteration(SlotC<1>{})) break;
+      if (!iteration(SlotC<2>{})) break;
+      if (!iteration(SlotC<3>{})) break;
+      if (!iteration(SlotC<4>{})) break;
+      if (!iteration(SlotC<5>{})) break;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // No wave reads this tile's buffers any more; the next tile's number is
+    // visible to all.
+    if (a.queue && tid == 0) tile_sh = ticket_tile(next_ticket);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    prev = tc;
+    have_prev = true;
+    cur = a.queue ? __builtin_amdgcn_readfirstlane(tile_sh) : -1;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Compiled configurations.
 // ----------------------------------------------------------------------------
 namespace {
 
 template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
 int launch_one(const IgemmArgs& args, int grid, void* stream) {
-  if constexpr (NS < 0)
+  if constexpr (NS == -2)
+    hipLaunchKernelGGL((igemm_slot_kernel<PB, CB, WN, EPI>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, args);
+  else if constexpr (NS < 0)
     hipLaunchKernelGGL((igemm_halo_kernel<CB, WN, KB, EPI>), dim3((unsigned)grid), dim3(256), 0,
                        (hipStream_t)stream, args);
   else if constexpr (NS == 0)
@@ -1250,6 +1745,9 @@ struct Entry {
 #define C16(WM, WN, PB, CB, KB, NS, MODE) \
   {{16, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE>}
 const Entry kEntries[] = {
+    // ns = -2: slot kernel (stride 1 along W, Cin % 32 == 0), 512-slot tiles.
+    C32(2, 2, 8, 2, 0, -2, EPI_STORE),
+    C32(4, 1, 4, 3, 0, -2, EPI_STORE),
     // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0); kb = X DMA
     // instructions per wave and stage (the row-segment capacity).
     C32(4, 1, 4, 4, 9, -1, EPI_STORE),

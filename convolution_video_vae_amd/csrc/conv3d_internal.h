@@ -41,6 +41,9 @@ struct IgemmArgs {
   unsigned x_bytes;         // size of x, for the buffer range check
   float sqrt_c;             // sqrtf((float)Cout)
   unsigned* queue;          // persistent tile queues (kQueueBytes, zeroed), or null
+  // fp32 reciprocals of Ho, Do and Wo + 2 (row splits with one correction
+  // step each way; uniform, so they stay in scalar registers).
+  float inv_ho, inv_do, inv_wp;
 };
 
 // Persistent tile queues: one counter per XCD, kQueueStride words apart;
@@ -59,6 +62,9 @@ struct ReduceArgs {
   int M, Cout, splits;
   unsigned flags;
   float sqrt_c;
+  // Fragment-order partials of the halo kernel (frag != 0): tile grid and
+  // shape (4 waves as wm x 4/wm, each pb x cb blocks of 32 x 32).
+  int frag, m_tiles, n_tiles, wm, pb, cb;
 };
 
 // A main-kernel configuration: MFMA block size R (16: v_mfma_f32_16x16x32_bf16,

@@ -52,6 +52,64 @@ __global__ __launch_bounds__(256) void reduce_store_kernel(ReduceArgs a) {
   }
 }
 
+// Fragment-order variant (partials of the halo kernel): one thread per 8
+// consecutive channels of one pixel, at the position a lane's accumulator
+// block holds them; summed over s = 0..S-1 in that fixed order.
+__global__ __launch_bounds__(256) void reduce_frag_kernel(ReduceArgs a) {
+  const int PB = a.pb, CB = a.cb, WM = a.wm, WN = 4 / WM;
+  const int BM = 32 * PB * WM, BN = 32 * CB * WN;
+  const long long tiles = (long long)a.m_tiles * a.n_tiles;
+  const long long blocks_per_split = tiles * 4 * PB * CB;  // 16-float blocks of 64 lanes
+  const long long tasks = blocks_per_split * 2 * 64;
+  const f32x4_t* part = reinterpret_cast<const f32x4_t*>(a.partial);
+  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < tasks;
+       t += (long long)gridDim.x * blockDim.x) {
+    const int L = (int)(t & 63);
+    long long r = t >> 6;
+    const int qq = (int)(r & 1);
+    r >>= 1;
+    const long long blk = r;  // ((tile * 4 + w) * PB + p) * CB + cb
+    const int cb = (int)(r % CB);
+    r /= CB;
+    const int p = (int)(r % PB);
+    r /= PB;
+    const int w = (int)(r & 3);
+    const long long tile = r >> 2;
+    const int mt = (int)(tile / a.n_tiles), nt = (int)(tile % a.n_tiles);
+    const long long m = (long long)mt * BM + (w % WM) * PB * 32 + p * 32 + (L & 31);
+    if (m >= a.M) continue;
+    const int c0 = nt * BN + (w / WM) * 32 * CB + (L >> 5) * 16 * CB + 16 * cb + 8 * qq;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const f32x4_t* src = part + ((s * blocks_per_split + blk) * 4 + 2 * qq) * 64 + L;
+      const f32x4_t lo = src[0], hi = src[64];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] += lo[e];
+        v[4 + e] += hi[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = rbf(v[e]);
+    if (a.flags & F_BIAS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + a.bias[c0 + e]);
+    }
+    if (a.flags & F_RESIDUAL) {
+      const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.residual + m * a.Cout + c0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + bf2f((uint16_t)(rv[e >> 1] >> (16 * (e & 1)))));
+    }
+    u32x4_t ov;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ov[q] = (unsigned)f2bf(v[2 * q]) | ((unsigned)f2bf(v[2 * q + 1]) << 16);
+    if (a.flags & F_RESIDUAL_OUT) *reinterpret_cast<u32x4_t*>(a.residual_out + m * a.Cout + c0) = ov;
+    *reinterpret_cast<u32x4_t*>(a.y + m * a.Cout + c0) = ov;
+  }
+}
+
 // Norm variant: one wave per pixel, each lane holding up to 4 groups of 8
 // channels (Cout <= 2048).
 __global__ __launch_bounds__(256) void reduce_norm_kernel(ReduceArgs a) {
@@ -219,7 +277,13 @@ int launch_queue_reset(unsigned* queue, void* stream) {
 }
 
 int launch_reduce(const ReduceArgs& args, void* stream) {
-  if (args.flags & F_NORM) {
+  if (args.frag) {
+    const long long tasks = (long long)args.m_tiles * args.n_tiles * 4 * args.pb * args.cb * 128;
+    long long blocks = (tasks + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(reduce_frag_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, args);
+  } else if (args.flags & F_NORM) {
     long long blocks = ((long long)args.M + 3) / 4;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(reduce_norm_kernel, dim3((unsigned)blocks), dim3(256), 0,

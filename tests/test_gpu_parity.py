@@ -177,12 +177,40 @@ HALO_CASES = [
 ]
 
 
+def halo_tile(cout):
+    """Tile override selecting the row-halo kernel (the planner prefers the
+    slot kernel for the same layers)."""
+    return "32,4,1,4,4,9,-1" if cout % 128 == 0 else "32,4,1,4,3,9,-1"
+
+
 @pytest.mark.parametrize("case", HALO_CASES, ids=[c[0] for c in HALO_CASES])
-def test_halo_kernel_integer_bit_exact(case):
+def test_halo_kernel_integer_bit_exact(case, monkeypatch):
     label, xs, cout, st, lo, hi = case
+    monkeypatch.setenv("CONV3D_TILE", halo_tile(cout))
     x, w, b = workloads.integer_tensors(xs, cout, seed=len(label) + 7, bias=True)
     g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b, split_k=1, label=label)
     assert "ns=-1" in g["plan"], g["plan"]
+    r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
+
+
+SLOT_CASES = HALO_CASES + [
+    # label, x shape, cout, stride, pad_lo, pad_hi: slot kernel (stride 1 along
+    # W, Cin % 32 == 0; output rows of Wo + 2 slots, 512-slot tiles).
+    ("slot_wo8_many_rows", (1, 3, 20, 8, 64), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("slot_batch3_valid96", (3, 4, 9, 37, 32), 96, (1, 1, 1), (0, 0, 0), (0, 0, 0)),
+    ("slot_wo254_tile_straddles_rows", (1, 3, 5, 256, 64), 128, (1, 1, 1), (0, 1, 2), (0, 1, 0)),
+]
+
+
+@pytest.mark.parametrize("with_bias", [False, True], ids=["plain_store", "bias_epilogue"])
+@pytest.mark.parametrize("case", SLOT_CASES, ids=[c[0] for c in SLOT_CASES])
+def test_slot_kernel_integer_bit_exact(case, with_bias):
+    label, xs, cout, st, lo, hi = case
+    x, w, b = workloads.integer_tensors(xs, cout, seed=len(label) + 7, bias=True)
+    b = b if with_bias else None
+    g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b, split_k=1, label=label)
+    assert "ns=-2" in g["plan"], g["plan"]
     r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b)
     np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
 
@@ -207,15 +235,18 @@ def test_halo_kernel_split_k_integer_bit_exact(case, split_k):
     np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
 
 
+@pytest.mark.parametrize("kernel", ["halo", "slot"])
 @pytest.mark.parametrize("case", HALO_CASES[:2], ids=[c[0] for c in HALO_CASES[:2]])
-def test_halo_kernel_random_against_oracle(case):
+def test_row_kernels_random_against_oracle(case, kernel, monkeypatch):
     label, xs, cout, st, lo, hi = case
+    if kernel == "halo":
+        monkeypatch.setenv("CONV3D_TILE", halo_tile(cout))
     rng = np.random.default_rng(len(label))
     x = torch.from_numpy(rng.standard_normal(xs).astype(np.float32)).to(torch.bfloat16)
     w = torch.from_numpy((rng.standard_normal((cout, xs[-1], 3, 3, 3)) / np.sqrt(27 * xs[-1]))
                          .astype(np.float32)).to(torch.bfloat16)
     g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, split_k=1, label=label + "_random")
-    assert "ns=-1" in g["plan"], g["plan"]
+    assert ("ns=-1" if kernel == "halo" else "ns=-2") in g["plan"], g["plan"]
     r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi)
     check(bits(g["y"]), r, what=label)
 
