@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # writes a known number of bytes (the --calibrate-copy pass). Valid only for
 # the kernel source it was taken on: reported as null once the source hash
 # differs.
-TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "7e59c950707e2cf4",
-           "bytes": 1670785825}   # 1383.0 MB fetched (FETCH_SIZE x 2.000) + 287.8 MB written
+TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "a01b0e3879ea0e06",
+           "bytes": 1598976843}   # 1313.7 MB fetched (FETCH_SIZE x 2.000) + 285.3 MB written
 KERNEL_SOURCES = ("convolution_video_vae_amd/csrc/conv3d_igemm.hip",
                   "convolution_video_vae_amd/csrc/conv3d_device.h")
 

@@ -153,7 +153,7 @@ int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1
 
 // Slot kernel {32, WM, WN, PB, CB, 0, -2}: stride 1 along W and whole
 // 32-channel chunks. Output row r owns Wo + 2 slots and a tile is bm() of
-// them; the bm() + 2 slots staged per stage must span at most 64 output rows
+// them; the bm() slots staged per stage must span at most 64 output rows
 // (one lane each), and slot indices are split with a float-reciprocal
 // division, exact below 2^22.
 long long slot_rows(const Problem& pr) { return (long long)pr.n * pr.Do * pr.Ho; }
@@ -268,7 +268,9 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   splits = std::max(1, std::min(splits, pl->steps));
   pl->steps_per_split = (pl->steps + splits - 1) / splits;
   pl->splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
-  pl->m_tiles = (int)ceil_div(pl->cfg.ns == -2 ? slot_rows(pr) * (pr.Wo + 2) : pr.M, pl->cfg.bm());
+  // (Slot kernel tiles compute bm() slots and store bm() - 2.)
+  pl->m_tiles = pl->cfg.ns == -2 ? (int)ceil_div(slot_rows(pr) * (pr.Wo + 2), pl->cfg.bm() - 2)
+                                 : (int)ceil_div(pr.M, pl->cfg.bm());
   pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());
   pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;
   // Halo kernel with more tiles than CUs: persistent work-groups.

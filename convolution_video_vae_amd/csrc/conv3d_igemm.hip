@@ -1281,12 +1281,14 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 //
 // Output pixels are addressed through slots: output row r = (n, do, ho) owns
 // WP = Wo + 2 consecutive slots, slot c < Wo of the row being output column c
-// and the last two unused. A tile is BM consecutive slots. For one (kd, kh)
-// tap pair and one 32-channel chunk, a stage stages BM + 2 slots of input:
-// staged slot j holds the input pixel of row r(s0 + j) at column
-// c(s0 + j) - pw. Output slot s at tap kw then reads staged slot s - s0 + kw
-// for every s, across row ends too (an unused slot's result is dropped), so
-// the three kw taps are plain slot offsets. Column n of a wave's pixel
+// and the last two unused. A tile computes BM consecutive slots and stores
+// the first BM - 2 (tiles start BM - 2 apart). For one (kd, kh) tap pair and
+// one 32-channel chunk, a stage stages BM slots of input: staged slot j holds
+// the input pixel of row r(s0 + j) at column c(s0 + j) - pw. Output slot s at
+// tap kw then reads staged slot s - s0 + kw for every stored s, across row
+// ends too (an unused slot's result is dropped), so the three kw taps are
+// plain slot offsets; the two extra computed slots, whose taps would reach
+// past the staged range, are never stored. Column n of a wave's pixel
 // fragment f holds slot n*PB + f (the fragments interleave), so the operand
 // of tap kw for pixel block p is fragment p + kw: PB + 2 fragment reads per
 // K half serve all three taps, against 3*PB when every tap is read on its
@@ -1313,9 +1315,10 @@ template <int PB, int CB, int WN>
 struct SlotShape {
   static constexpr int R = 32;
   static constexpr int WM = 4 / WN;
-  static constexpr int BM = R * PB * WM;            // slots per tile
+  static constexpr int BM = R * PB * WM;            // slots computed per tile
+  static constexpr int TS = BM - 2;                 // slots stored per tile (tile stride)
   static constexpr int BN = R * CB * WN;            // output channels per tile
-  static constexpr int XS = BM + 2;                 // slots staged per stage
+  static constexpr int XS = BM;                     // slots staged per stage
   static constexpr int XJ = (XS * 4 + 255) / 256;   // activation DMA instructions per wave
   static constexpr int XU = XJ * 256;               // 16-byte units per activation buffer
   static constexpr int NF = PB + 2;                 // pixel fragments per K half
@@ -1380,7 +1383,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   // lgrp + 2, i.e. the address XOR 32.
   int ax[NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) ax[f] = slot_unit<S::SH>(wave_m * (PB * R) + lrow * PB + f, lgrp) * 16;
+  for (int f = 0; f < NF; ++f)  // (slots past the staged range feed unstored outputs only)
+    ax[f] = slot_unit<S::SH>(min(wave_m * (PB * R) + lrow * PB + f, S::XS - 1), lgrp) * 16;
   int aw[CB][2];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
@@ -1476,7 +1480,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     } else {
       tc = tile_coord(a, S::BM, S::BN);
     }
-    tc.m_end = min(tc.m0 + S::BM, rows_total * WP);
+    tc.m0 = (tc.m0 / S::BM) * S::TS;
+    tc.m_end = min(tc.m0 + S::TS, rows_total * WP);
     const int s0 = tc.m0;  // first slot of the tile
     const int row0 = small_div(s0, WP, inv_wp);
     const int s_last = tc.m_end - 1;
