@@ -215,10 +215,11 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   // Fused-norm kernels hold the whole channel row of a pixel in one group.
   TileCfg norm_cfg = {0, 0, 0, 0, 0, 0, 0};
   if (norm) {
-    const TileCfg cands[] = {{16, 2, 2, 2, 10, 2, 0}, {16, 2, 2, 2, 10, 1, 3},
-                             {16, 4, 1, 2, 10, 1, 3}};
+    const TileCfg cands[] = {{32, 2, 2, 3, 5, 0, -2}, {16, 2, 2, 2, 10, 2, 0},
+                             {16, 2, 2, 2, 10, 1, 3}, {16, 4, 1, 2, 10, 1, 3}};
     for (const TileCfg& c : cands)
-      if (norm_cfg.r == 0 && c.bn() == pr.cout && igemm_has_config(c, EPI_NORM)) norm_cfg = c;
+      if (norm_cfg.r == 0 && c.bn() == pr.cout && halo_ok(pr, c) && igemm_has_config(c, EPI_NORM))
+        norm_cfg = c;
   }
 
   // Too few tiles to fill the CUs: cut K.

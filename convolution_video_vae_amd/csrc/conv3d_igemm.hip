@@ -1326,16 +1326,35 @@ struct SlotShape {
   static constexpr int WJ = (WU / 64 + 3) / 4;      // weight DMA instructions per wave per tap
   static constexpr int WUP = WJ * 256;
   static constexpr int NW = 3 * WJ;                 // weight DMA instructions per wave per stage
-  static constexpr int SH = PB == 4 ? 2 : 3;        // log2(PB)
-  static_assert(PB == 4 || PB == 8, "slot swizzle");
+  static_assert(PB == 3 || PB == 4 || PB == 8, "slot swizzle");
   static_assert(WN == 1 || WN == 2 || WN == 4, "4 waves");
   static_assert(XU % 64 == 0, "the slot permutation works on 16-slot groups");
 };
 
-// LDS 16-byte unit of (staged slot s, chunk c).
-template <int SH>
+// LDS 16-byte unit of (staged slot s, chunk c), and the inverse: the slot
+// and chunk an LDS unit holds. PB = 3: slot s stays at position s, its chunks
+// XORed by (s / 6) & 3 (slots 3 apart then alternate in parity and step the
+// XOR every other lane).
+template <int PB>
 __device__ __forceinline__ int slot_unit(int s, int c) {
-  return ((s ^ ((s >> SH) & 1)) << 2) | (c ^ ((s >> (SH + 1)) & 3));
+  if constexpr (PB == 3) {
+    return (s << 2) | (c ^ ((s / 6) & 3));
+  } else {
+    constexpr int SH = PB == 4 ? 2 : 3;
+    return ((s ^ ((s >> SH) & 1)) << 2) | (c ^ ((s >> (SH + 1)) & 3));
+  }
+}
+template <int PB>
+__device__ __forceinline__ void unit_slot(int q, int& sl, int& c) {
+  const int sp = q >> 2;
+  if constexpr (PB == 3) {
+    sl = sp;
+    c = (q & 3) ^ ((sl / 6) & 3);
+  } else {
+    constexpr int SH = PB == 4 ? 2 : 3;
+    sl = sp ^ ((sp >> SH) & 1);
+    c = (q & 3) ^ ((sl >> (SH + 1)) & 3);
+  }
 }
 
 template <int PB, int CB, int WN, int EPI>
@@ -1349,11 +1368,13 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   constexpr int EPI_VM = PB * RUN / 8;  // stores of the plain epilogue per wave
   typedef typename T::acc_t acc_t;
   static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
-  static_assert(EPI != EPI_NORM, "the fused norm runs in the tile kernel");
+  static_assert(EPI != EPI_NORM || WM * WN * PB * R * 4 <= 2048, "norm exchange area");
   static_assert(NW + XJ + EPI_VM <= 63, "vmcnt range");
 
   __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
   __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
+  // Fused norm: per-pixel sums of squares of the WN waves sharing a pixel.
+  __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
 
   const int tid = threadIdx.x;
   const int lane0 = tid & 63;
@@ -1384,7 +1405,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   int ax[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f)  // (slots past the staged range feed unstored outputs only)
-    ax[f] = slot_unit<S::SH>(min(wave_m * (PB * R) + lrow * PB + f, S::XS - 1), lgrp) * 16;
+    ax[f] = slot_unit<PB>(min(wave_m * (PB * R) + lrow * PB + f, S::XS - 1), lgrp) * 16;
   int aw[CB][2];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
@@ -1520,9 +1541,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
 #pragma unroll
     for (int j = 0; j < XJ; ++j) {
       const int q = (j * 4 + wave) * 64 + lane;
-      const int sp = q >> 2;
-      const int sl = sp ^ ((sp >> S::SH) & 1);
-      const int c = (q & 3) ^ ((sl >> (S::SH + 1)) & 3);
+      int sl, c;
+      unit_slot<PB>(q, sl, c);
       const int s = s0 + sl;
       const int k = small_div(s, WP, inv_wp) - row0;
       const int w_in = s - (row0 + k) * WP - a.pw;
@@ -1582,7 +1602,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       store_plain<T, PB, CB>(a, acc, mp, cbase);
     else
       epilogue<T, WM, WN, PB, CB, EPI>(a, acc, mp, cbase, pt.split, wave_m, wave_n, elrow, elgrp,
-                                       nullptr);
+                                       red);
   };
 
   // Pixel fragments by K half; weight fragments in a ring of three sub-steps
@@ -1753,6 +1773,7 @@ const Entry kEntries[] = {
     // ns = -2: slot kernel (stride 1 along W, Cin % 32 == 0), 512-slot tiles.
     C32(2, 2, 8, 2, 0, -2, EPI_STORE),
     C32(4, 1, 4, 3, 0, -2, EPI_STORE),
+    C32(2, 2, 3, 5, 0, -2, EPI_NORM),   // fused norm, Cout 320
     // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0); kb = X DMA
     // instructions per wave and stage (the row-segment capacity).
     C32(4, 1, 4, 4, 9, -1, EPI_STORE),
