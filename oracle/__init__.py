@@ -1,7 +1,8 @@
-"""Conv3D oracle — TEST INFRASTRUCTURE ONLY.
+"""Conv3D and GroupNorm oracle — TEST INFRASTRUCTURE ONLY.
 
 A plain CPU direct convolution (C, OpenMP) with the cuDNN page's
-"Operation Contract" post-operations, used to check the GPU library.
+"Operation Contract" post-operations, and a plain channels-last GroupNorm
+(+ SiLU, numpy float64, in groupnorm.py), used to check the GPU library.
 Only tests/, the smoke entry point and the benchmark's CPU-baseline leg may
 import this package. It shares no code with the GPU library; both sides see
 the same seeded inputs and nothing else.
@@ -137,3 +138,9 @@ def conv3d(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=N
     out = {k: (v.reshape(shape) if v.ndim == 2 else v) for k, v in extra.items()}
     out["y"] = y.reshape(shape)
     return out
+
+
+def group_norm(x, groups, gamma, beta, **kw):
+    """Channels-last GroupNorm (+ SiLU); see oracle/groupnorm.py."""
+    from .groupnorm import group_norm as _gn
+    return _gn(x, groups, gamma, beta, **kw)
