@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # writes a known number of bytes (the --calibrate-copy pass). Valid only for
 # the kernel source it was taken on: reported as null once the source hash
 # differs.
-TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "a01b0e3879ea0e06",
-           "bytes": 1598976843}   # 1313.7 MB fetched (FETCH_SIZE x 2.000) + 285.3 MB written
+TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "1050575d271e6cfd",
+           "bytes": 1609586303}   # 1324.3 MB fetched (FETCH_SIZE x 2.000) + 285.3 MB written
 KERNEL_SOURCES = ("convolution_video_vae_amd/csrc/conv3d_igemm.hip",
                   "convolution_video_vae_amd/csrc/conv3d_device.h")
 
@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--workload", default=None)
     p.add_argument("--no-layers", action="store_true", help="time only the headline layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--layers", default=None,
+                   help="comma-separated per_layer entries to time (default: all)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a 1 GiB read + 1 GiB write elementwise kernel 3 times (the "
@@ -182,7 +184,10 @@ def main():
 
     per_layer = {}
     if not args.no_layers:
+        wanted = None if args.layers is None else set(args.layers.split(","))
         for name, L in workloads.LAYERS.items():
+            if wanted is not None and name not in wanted:
+                continue
             variants = [(name, None)]
             if L.norm_silu:
                 variants.append((name + "_ncdhw", cv.NCDHW))
@@ -209,6 +214,28 @@ def main():
         per_layer["transpose_ncdhw_to_ndhwc_" + L.name] = {
             "us": round(tms * 1e3, 2), "gbs": round(2 * src.numel() * 2 / (tms * 1e-3) / 1e9, 1),
             "pct_hbm": round(100 * 2 * src.numel() * 2 / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        del src, dst
+        # channels-last GroupNorm (+ SiLU) between the convs
+        from convolution_video_vae_amd.layer import GroupNorm
+        for name, N in workloads.NORM_LAYERS.items():
+            if wanted is not None and name not in wanted:
+                continue
+            x, gamma, beta = workloads.norm_tensors(N)
+            x = x.cuda()
+            y = torch.empty_like(x)
+            gn = GroupNorm(N.x_shape, N.groups, gamma.cuda(), beta.cuda(), eps=N.eps,
+                           silu=N.silu, t_isolated=N.t_isolated)
+            gms, _ = time_case(lambda: gn(x, y=y), max(5, args.steps), 3, torch)
+            assert torch.isfinite(y.float()).all().item()
+            per_layer[name] = {
+                "us": round(gms * 1e3, 2), "algorithmic_gbs": round(N.bytes / (gms * 1e-3) / 1e9, 1),
+                "pct_hbm": round(100 * N.bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                "algorithmic_mb": round(N.bytes / 1e6, 1),
+                "config": f"x NDHWC {list(N.x_shape)} bf16, {N.groups} groups, "
+                          f"{'per-frame' if N.t_isolated else 'per-sample'} statistics"
+                          f"{', SiLU' if N.silu else ''}"}
+            del x, y, gn
+            torch.cuda.empty_cache()
 
     if args.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")

@@ -31,7 +31,7 @@ STATUS = {0: "CONV3D_OK", 1: "CONV3D_ERR_NULL", 2: "CONV3D_ERR_SHAPE", 3: "CONV3
 
 EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_dims",
             "conv3d_workspace_bytes", "conv3d_fwd", "conv3d_transpose", "conv3d_status_str",
-            "conv3d_plan_describe")
+            "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm")
 
 
 class Conv3dError(RuntimeError):
@@ -52,6 +52,12 @@ class conv3d_epilogue(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint), ("bias", ctypes.c_void_p),
                 ("residual", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
                 ("residual_out", ctypes.c_void_p)]
+
+
+class conv3d_group_norm_desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("d", ctypes.c_int), ("h", ctypes.c_int), ("w", ctypes.c_int),
+                ("c", ctypes.c_int), ("groups", ctypes.c_int), ("t_isolated", ctypes.c_int),
+                ("silu", ctypes.c_int), ("eps", ctypes.c_float)]
 
 
 _lib = None
@@ -83,6 +89,11 @@ def lib():
         L.conv3d_status_str.argtypes = [i]
         L.conv3d_plan_describe.restype = i
         L.conv3d_plan_describe.argtypes = [pd, pe, ctypes.c_char_p, sz]
+        pg = ctypes.POINTER(conv3d_group_norm_desc)
+        L.conv3d_group_norm_workspace_bytes.restype = i
+        L.conv3d_group_norm_workspace_bytes.argtypes = [pg, ctypes.POINTER(sz)]
+        L.conv3d_group_norm.restype = i
+        L.conv3d_group_norm.argtypes = [pg, vp, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -177,3 +188,27 @@ def conv3d_plan_describe(desc: conv3d_desc, epi: Optional[conv3d_epilogue] = Non
     _check(lib().conv3d_plan_describe(ctypes.byref(desc), ctypes.byref(epi) if epi else None,
                                       buf, 512), "conv3d_plan_describe")
     return buf.value.decode()
+
+
+def make_group_norm_desc(x_shape: Sequence[int], groups: int, *, eps: float = 1e-5,
+                         silu: bool = False, t_isolated: bool = True) -> conv3d_group_norm_desc:
+    """GroupNorm descriptor for an NDHWC tensor of shape x_shape."""
+    n, d, h, w, c = x_shape
+    return conv3d_group_norm_desc(n, d, h, w, c, groups, int(bool(t_isolated)), int(bool(silu)),
+                                  eps)
+
+
+def conv3d_group_norm_workspace_bytes(desc: conv3d_group_norm_desc) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().conv3d_group_norm_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)),
+           "conv3d_group_norm_workspace_bytes")
+    return int(out.value)
+
+
+def conv3d_group_norm(desc: conv3d_group_norm_desc, x, gamma, beta, y, workspace=None,
+                      workspace_bytes: int = 0, stream=None) -> None:
+    if workspace is not None and not workspace_bytes and not isinstance(workspace, int):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().conv3d_group_norm(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)),
+           "conv3d_group_norm")

@@ -27,7 +27,7 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    for name in ("conv3d_kernels", "conv3d_igemm"):
+    for name in ("conv3d_kernels", "conv3d_igemm", "conv3d_norm"):
         obj = os.path.join(BUILD, name + ".o")
         _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-c",
               *DEVICE_FLAGS, "-Wall", os.path.join(CSRC, name + ".hip"), "-o", obj], verbose)

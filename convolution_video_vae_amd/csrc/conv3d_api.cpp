@@ -302,6 +302,54 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   pl->total = off;
 }
 
+// GroupNorm planning: units, chunking and the workspace carve.
+struct GnPlan {
+  GroupNormArgs a;
+  long long bytes;        // size of x (and y)
+  size_t off_stats, total;
+};
+
+constexpr int kGnTargetGroups = 2048;   // work-groups per pass, about 8 per CU
+constexpr long long kGnMaxChunk = 1 << 20;
+
+conv3d_status plan_group_norm(const conv3d_group_norm_desc* d, GnPlan* pl) {
+  if (!d) return CONV3D_ERR_NULL;
+  if (d->n <= 0 || d->d <= 0 || d->h <= 0 || d->w <= 0 || d->c <= 0 || d->groups <= 0)
+    return CONV3D_ERR_SHAPE;
+  if (!(d->eps > 0.0f) || !isfinite(d->eps)) return CONV3D_ERR_SHAPE;
+  if (d->c % d->groups) return CONV3D_ERR_SHAPE;
+  if (d->c % 8) return CONV3D_ERR_ALIGN;
+  if (d->c > 2048 || d->groups > 256) return CONV3D_ERR_UNSUPPORTED;
+  const long long units = d->t_isolated ? (long long)d->n * d->d : d->n;
+  const long long P = (d->t_isolated ? 1LL : (long long)d->d) * d->h * d->w;
+  const long long bytes = units * P * d->c * 2;
+  if (bytes > (1LL << 40) || units > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
+  GroupNormArgs& a = pl->a;
+  a = GroupNormArgs{};
+  a.P = P;
+  a.C = d->c;
+  a.G = d->groups;
+  a.cpg = d->c / d->groups;
+  a.V = d->c / 8;
+  a.ppi = 256 / a.V;
+  const long long want = std::max(1LL, (kGnTargetGroups + units - 1) / units);
+  // a chunk stays below 2^31 bytes (32-bit offsets inside the kernels)
+  long long chunk = std::min((P + want - 1) / want, std::min(kGnMaxChunk, (1LL << 30) / d->c));
+  chunk = (chunk + a.ppi - 1) / a.ppi * a.ppi;
+  const long long chunks = (P + chunk - 1) / chunk;
+  if (units * chunks > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
+  a.units = (int)units;
+  a.chunks = (int)chunks;
+  a.chunk_px = (int)chunk;
+  a.eps = d->eps;
+  a.silu = d->silu ? 1 : 0;
+  pl->bytes = bytes;
+  const size_t part = (size_t)units * chunks * a.G * 16;
+  pl->off_stats = (part + 255) / 256 * 256;
+  pl->total = pl->off_stats + ((size_t)units * a.G * 8 + 255) / 256 * 256;
+  return CONV3D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -500,6 +548,45 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
       return CONV3D_ERR_HIP;
   }
   return CONV3D_OK;
+}
+
+conv3d_status conv3d_group_norm_workspace_bytes(const conv3d_group_norm_desc* desc,
+                                                size_t* bytes) {
+  if (!bytes) return CONV3D_ERR_NULL;
+  GnPlan pl;
+  const conv3d_status st = plan_group_norm(desc, &pl);
+  if (st != CONV3D_OK) return st;
+  *bytes = pl.total;
+  return CONV3D_OK;
+}
+
+conv3d_status conv3d_group_norm(const conv3d_group_norm_desc* desc, const void* x,
+                                const float* gamma, const float* beta, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!desc || !x || !gamma || !beta || !y) return CONV3D_ERR_NULL;
+  GnPlan pl;
+  const conv3d_status st = plan_group_norm(desc, &pl);
+  if (st != CONV3D_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta))
+    return CONV3D_ERR_ALIGN;
+  if (!workspace || workspace_bytes < pl.total) return CONV3D_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CONV3D_ERR_ALIGN;
+  const Range rx = range_of(x, pl.bytes), ry = range_of(y, pl.bytes);
+  const Range rg = range_of(gamma, (long long)desc->c * 4), rb = range_of(beta, (long long)desc->c * 4);
+  const Range rw = range_of(workspace, (long long)pl.total);
+  if (x != y && overlaps(rx, ry)) return CONV3D_ERR_OVERLAP;
+  for (const Range& o : {ry, rw})
+    for (const Range& i : {rg, rb})
+      if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
+  if (overlaps(rw, rx) || overlaps(rw, ry)) return CONV3D_ERR_OVERLAP;
+  GroupNormArgs a = pl.a;
+  a.x = (const uint16_t*)x;
+  a.y = (uint16_t*)y;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.partial = (double*)workspace;
+  a.stats = (float*)((char*)workspace + pl.off_stats);
+  return launch_group_norm(a, stream) ? CONV3D_ERR_HIP : CONV3D_OK;
 }
 
 conv3d_status conv3d_transpose(const void* src, int src_layout, void* dst, int n, int c, int d,

@@ -78,7 +78,25 @@ struct TileCfg {
   int bn() const { return r * cb * wn; }
 };
 
-// Launchers (conv3d_kernels.hip). Each returns 0 on success or the HIP
+// Channels-last GroupNorm (conv3d_norm.hip). A unit is one frame (n, d) or
+// one sample n; its P pixels of C channels are contiguous. Chunks of
+// chunk_px pixels (a multiple of ppi) split each unit across work-groups.
+struct GroupNormArgs {
+  const uint16_t* x;        // [units][P][C]
+  uint16_t* y;              // same shape; may be x itself
+  const float* gamma;       // [C]
+  const float* beta;        // [C]
+  double* partial;          // [units][chunks][G][2]: shifted sum, sum of squares
+  float* stats;             // [units][G][2]: mean, 1/sqrt(var + eps)
+  long long P;              // pixels per unit
+  int C, G, cpg;            // channels, groups, channels per group
+  int V, ppi;               // C / 8 vectors per pixel; 256 / V pixels per pass
+  int units, chunks, chunk_px;
+  float eps;
+  int silu;
+};
+
+// Launchers (conv3d_kernels.hip, conv3d_norm.hip). Each returns 0 on success or the HIP
 // error code of the launch. `stream` is a hipStream_t.
 int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, void* stream);
 int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int a, int b, void* stream);
@@ -87,5 +105,6 @@ int launch_igemm(const TileCfg& cfg, int mode, const IgemmArgs& args, int grid, 
 bool igemm_has_config(const TileCfg& cfg, int mode);
 int launch_reduce(const ReduceArgs& args, void* stream);
 int launch_queue_reset(unsigned* queue, void* stream);
+int launch_group_norm(const GroupNormArgs& args, void* stream);
 
 }  // namespace conv3d

@@ -11,8 +11,9 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_output_dims, conv3d_pack_weight,
-               conv3d_packed_weight_bytes, conv3d_workspace_bytes, make_desc, make_epilogue)
+from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_group_norm, conv3d_group_norm_workspace_bytes,
+               conv3d_output_dims, conv3d_pack_weight, conv3d_packed_weight_bytes,
+               conv3d_workspace_bytes, make_desc, make_epilogue, make_group_norm_desc)
 
 
 def pack_weight(w_oidhw: torch.Tensor, stream=None) -> torch.Tensor:
@@ -78,4 +79,32 @@ class Conv3d:
                             residual_out=residual_out, norm_silu=self.norm_silu)
         conv3d_fwd(self.desc, x, self.w_packed, epi if epi.flags else None, y, self.workspace,
                    self.workspace_bytes, stream)
+        return y
+
+
+class GroupNorm:
+    """Channels-last GroupNorm (+ SiLU) of one NDHWC activation shape, with
+    its workspace allocated once; statistics per frame when t_isolated."""
+
+    def __init__(self, x_shape: Sequence[int], groups: int, gamma: torch.Tensor,
+                 beta: torch.Tensor, *, eps: float = 1e-5, silu: bool = False,
+                 t_isolated: bool = True):
+        self.x_shape = tuple(int(v) for v in x_shape)
+        self.desc = make_group_norm_desc(self.x_shape, groups, eps=eps, silu=silu,
+                                         t_isolated=t_isolated)
+        self.device = gamma.device
+        self.gamma = gamma.to(dtype=torch.float32).contiguous()
+        self.beta = beta.to(device=self.device, dtype=torch.float32).contiguous()
+        self.workspace_bytes = conv3d_group_norm_workspace_bytes(self.desc)
+        self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+
+    def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+        """y = GroupNorm(x); pass y=x to normalise in place."""
+        if tuple(x.shape) != self.x_shape or x.dtype != torch.bfloat16 or not x.is_contiguous():
+            raise ValueError(f"x must be a contiguous bf16 tensor of shape {self.x_shape}")
+        if y is None:
+            y = torch.empty_like(x)
+        conv3d_group_norm(self.desc, x, self.gamma, self.beta, y, self.workspace,
+                          self.workspace_bytes, stream)
         return y

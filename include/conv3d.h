@@ -17,10 +17,13 @@
  *    the post-operation contract and its rounding points ("Operation
  *    Contract"), operand rules ("Requirements") and weight packing once per
  *    weight ("Weight Packing").
+ *  - The channels-last GroupNorm (+ SiLU) between the convs: the MiniMax H3
+ *    comment on the FlyDSL issue page (its GroupNorm argument).
  *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers to bf16 data (raw 16-bit patterns),
- *    except `bias`, which is fp32. All must be 16-byte aligned.
+ *    except `bias`, `gamma` and `beta` of the GroupNorm, which are fp32. All
+ *    must be 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream). Every entry point
  *    only enqueues work on `stream` and returns; nothing is synchronised.
  *  - The caller owns every buffer. The library allocates nothing, keeps no
@@ -147,6 +150,45 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
  * src and dst must not overlap. */
 conv3d_status conv3d_transpose(const void* src, int src_layout, void* dst, int n, int c, int d,
                                int h, int w, void* stream);
+
+/* ------------------------------------------------------------- GroupNorm
+ * Channels-last GroupNorm (+ SiLU), the norm between the convs of a causal
+ * video-VAE encoder (FlyDSL issue page, MiniMax H3 comment, the GroupNorm
+ * argument: statistics per frame once time is folded into the batch, which
+ * NDHWC makes a free view; the SiLU after it fused in; a group's c/groups
+ * channels contiguous at every pixel). On x [n][d][h][w][c] with groups of
+ * c/groups consecutive channels, and a unit = one frame (n, d) when
+ * t_isolated, else one sample n (all its frames):
+ *   mean, var = population mean and variance over the unit's pixels and the
+ *               group's channels
+ *   a = B((x - mean) / sqrt(var + eps) * gamma[c] + beta[c])
+ *   y = B(a * sigmoid(a)) with silu, else a
+ * B() rounds fp32 to bf16, to nearest, ties to even. */
+typedef struct {
+  int n, d, h, w, c;  /* NDHWC extents */
+  int groups;         /* 1..256, c % groups == 0 */
+  int t_isolated;     /* 1: statistics per frame; 0: per sample */
+  int silu;           /* 1: SiLU after the affine */
+  float eps;          /* > 0, finite */
+} conv3d_group_norm_desc;
+
+/* Workspace bytes conv3d_group_norm needs for desc (always > 0: per-chunk
+ * partial sums and the per-group statistics). */
+conv3d_status conv3d_group_norm_workspace_bytes(const conv3d_group_norm_desc* desc,
+                                                size_t* bytes);
+
+/* y = GroupNorm(x) (+ SiLU) as above.
+ *   x, y         bf16 NDHWC; y may be x itself (in place), any other overlap
+ *                with x is CONV3D_ERR_OVERLAP
+ *   gamma, beta  fp32 [c]
+ *   workspace    device scratch of at least conv3d_group_norm_workspace_bytes()
+ * Errors: c % 8 != 0 -> CONV3D_ERR_ALIGN; c % groups != 0, a size < 1, eps not
+ * > 0 -> CONV3D_ERR_SHAPE; c > 2048, groups > 256 or a tensor over 2^40 bytes
+ * -> CONV3D_ERR_UNSUPPORTED. The workspace, gamma and beta must not overlap
+ * x or y. */
+conv3d_status conv3d_group_norm(const conv3d_group_norm_desc* desc, const void* x,
+                                const float* gamma, const float* beta, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* conv3d_status_str(conv3d_status status);

@@ -177,3 +177,57 @@ def test_workspace_checked():
     assert fwd(d, ws=WS, ws_bytes=need - 1) == 5
     assert fwd(d, ws=WS + 8, ws_bytes=need) == 3
     assert fwd(d, ws=X, ws_bytes=need) == 4                     # workspace aliases x
+
+
+# ------------------------------------------------------------------ GroupNorm
+
+def gn(desc, x=X, gamma=G, beta=B, y=Y, ws=WS, ws_bytes=1 << 30):
+    return cv.lib().conv3d_group_norm(ctypes.byref(desc) if desc is not None else None, x, gamma,
+                                      beta, y, ws, ws_bytes, None)
+
+
+def gn_desc(shape=(1, 3, 8, 8, 64), groups=32, **kw):
+    return cv.make_group_norm_desc(shape, groups, **kw)
+
+
+def test_group_norm_desc_struct_matches_header_layout():
+    assert ctypes.sizeof(cv.conv3d_group_norm_desc) == 9 * 4
+
+
+def test_group_norm_workspace_covers_partials_and_stats():
+    for name, L in workloads.NORM_LAYERS.items():
+        d = gn_desc(L.x_shape, L.groups)
+        need = cv.conv3d_group_norm_workspace_bytes(d)
+        units = L.x_shape[0] * L.x_shape[1]
+        # at least one chunk partial (two fp64) and one (mean, rstd) pair per group and unit
+        assert need >= units * L.groups * (16 + 8), name
+        assert need < 64 << 20, name
+    # statistics over the whole clip: one unit per sample
+    a = cv.conv3d_group_norm_workspace_bytes(gn_desc((2, 5, 4, 4, 64), t_isolated=False))
+    assert a >= 2 * 32 * 24
+
+
+def test_group_norm_rejected_calls():
+    assert gn(None) == 1
+    assert gn(gn_desc(), x=None) == 1
+    assert gn(gn_desc(), gamma=None) == 1
+    assert gn(gn_desc(), beta=None) == 1
+    assert gn(gn_desc(), y=None) == 1
+    assert gn(gn_desc((0, 3, 8, 8, 64))) == 2
+    assert gn(gn_desc(groups=0)) == 2
+    assert gn(gn_desc(groups=24)) == 2                         # 64 % 24 != 0
+    assert gn(gn_desc(eps=0.0)) == 2
+    assert gn(gn_desc(eps=float("inf"))) == 2
+    assert gn(gn_desc((1, 3, 8, 8, 36), groups=4)) == 3        # c % 8 != 0
+    assert gn(gn_desc(), x=X + 2) == 3
+    assert gn(gn_desc(), gamma=G + 4) == 3
+    assert gn(gn_desc((1, 1, 2, 2, 4096), groups=32)) == 6     # c > 2048
+    assert gn(gn_desc((1, 1, 2, 2, 1024), groups=512)) == 6    # groups > 256
+    need = cv.conv3d_group_norm_workspace_bytes(gn_desc())
+    assert gn(gn_desc(), ws=None) == 5
+    assert gn(gn_desc(), ws_bytes=need - 1) == 5
+    assert gn(gn_desc(), ws=WS + 8, ws_bytes=need) == 3
+    assert gn(gn_desc(), y=X + 64) == 4                        # partial overlap with x
+    assert gn(gn_desc(), ws=X, ws_bytes=need) == 4             # workspace inside x
+    assert gn(gn_desc(), gamma=Y) == 4                         # gamma inside y
+    assert gn(gn_desc(), beta=WS) == 4                         # beta inside the workspace

@@ -1,0 +1,124 @@
+"""GPU parity of the channels-last GroupNorm (+ SiLU) against the oracle.
+
+Every call goes through the C ABI (conv3d_group_norm via the ctypes binding)
+on seeded inputs from workloads.norm_tensors; the oracle runs on the same
+bits. Cases span the kernel's thread mappings (8 to 2048 channels, 1 to 64
+channels per group, a group inside one 16-byte vector or across several),
+many chunks with a ragged last one, one-pixel frames, statistics per frame
+and per clip, in-place calls, a mean far above the spread, constant frames
+and the full-size H3 L0 activation (checked on sampled frames, which the
+per-frame statistics make exact to check one by one).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from convolution_video_vae_amd.layer import GroupNorm
+from parity import check_group_norm
+
+pytestmark = pytest.mark.gpu
+
+BASE = workloads.NORM_LAYERS["gn_h3_l0_128"]
+
+
+def b2f_(b):
+    return oracle.bf16_to_f32(b)
+
+
+def bits(t):
+    return workloads.bf16_bits(t.cpu())
+
+
+def run(x, gamma, beta, groups, *, eps=1e-5, silu=True, t_isolated=True, inplace=False):
+    print(f"[gn] shape={tuple(x.shape)} groups={groups} silu={silu} t_isolated={t_isolated} "
+          f"inplace={inplace}", flush=True)
+    layer = GroupNorm(tuple(x.shape), groups, gamma.cuda(), beta.cuda(), eps=eps, silu=silu,
+                      t_isolated=t_isolated)
+    xd = x.cuda()
+    y = layer(xd, y=xd if inplace else None)
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+def ref(x, gamma, beta, groups, *, eps=1e-5, silu=True, t_isolated=True):
+    return oracle.group_norm(bits(x), groups, gamma.numpy(), beta.numpy(),
+                             eps=float(np.float32(eps)), silu=silu, t_isolated=t_isolated,
+                             intermediates=True)
+
+
+CASES = [
+    # name, x shape (NDHWC), groups, silu, t_isolated
+    ("c64_g32_silu", (1, 3, 10, 14, 64), 32, True, True),
+    ("c96_cpg3", (2, 2, 9, 7, 96), 32, True, True),
+    ("c8_one_vector", (1, 3, 7, 5, 8), 4, False, True),
+    ("c2048_g256", (1, 2, 6, 10, 2048), 256, True, True),
+    ("c64_clip_stats", (2, 4, 6, 7, 64), 32, True, False),
+    ("c128_many_chunks_ragged", (1, 2, 61, 67, 128), 32, True, True),
+    ("one_pixel_frames", (1, 6, 1, 1, 256), 32, True, True),
+    ("group_of_one_channel", (1, 2, 5, 5, 64), 64, True, True),
+    ("one_group", (1, 2, 5, 5, 64), 1, False, True),
+    ("c320_wan", (1, 3, 11, 13, 320), 32, True, True),
+    ("h3_l5_1024_full", workloads.NORM_LAYERS["gn_h3_l5_1024"].x_shape, 32, True, True),
+    ("h3_l5_1024_clip", workloads.NORM_LAYERS["gn_h3_l5_1024"].x_shape, 32, True, False),
+    ("h3_l3_512_full", workloads.NORM_LAYERS["gn_h3_l3_512"].x_shape, 32, True, True),
+]
+
+
+@pytest.mark.parametrize("name,shape,groups,silu,t_iso", CASES, ids=[c[0] for c in CASES])
+def test_group_norm_against_oracle(name, shape, groups, silu, t_iso):
+    x, gamma, beta = workloads.norm_tensors(BASE, x_shape=shape)
+    y = run(x, gamma, beta, groups, silu=silu, t_isolated=t_iso)
+    r = ref(x, gamma, beta, groups, silu=silu, t_isolated=t_iso)
+    diag = check_group_norm(y, r, what=name)
+    assert diag["bit_identical"] > 0.99, diag
+
+
+def test_in_place_matches_out_of_place():
+    x, gamma, beta = workloads.norm_tensors(BASE, x_shape=(1, 3, 20, 24, 128))
+    a = run(x, gamma, beta, 32)
+    b = run(x, gamma, beta, 32, inplace=True)
+    assert np.array_equal(a, b)
+
+
+def test_deterministic():
+    x, gamma, beta = workloads.norm_tensors(BASE, x_shape=(1, 4, 33, 40, 256))
+    assert np.array_equal(run(x, gamma, beta, 32), run(x, gamma, beta, 32))
+
+
+def test_mean_far_above_spread():
+    """x = 8 + 0.5 N(0, 1): a plain sum of squares in fp32 would lose the
+    variance to cancellation; the per-group shift keeps it."""
+    x, gamma, beta = workloads.norm_tensors(BASE, x_shape=(1, 2, 40, 52, 128))
+    x = (x.float() * 0.5 + 8.0).to(torch.bfloat16)
+    y = run(x, gamma, beta, 32, eps=1e-6)
+    check_group_norm(y, ref(x, gamma, beta, 32, eps=1e-6), what="offset")
+
+
+def test_constant_frame_gives_silu_of_beta_exactly():
+    """Zero variance: the norm term is exactly 0 on both sides, so the output
+    is B(silu(B(beta_c))) on every pixel; the SiLU's own rounding is the only
+    difference allowed."""
+    x, gamma, beta = workloads.norm_tensors(BASE, x_shape=(1, 3, 9, 11, 64))
+    x[:, 1] = 0.625
+    y = run(x, gamma, beta, 32)
+    r = ref(x, gamma, beta, 32)
+    check_group_norm(y, r, what="constant frame")
+    step = np.abs(y[:, 1].astype(np.int32) - r["y"][:, 1].astype(np.int32))
+    assert np.max(step) <= 1 and np.array_equal(np.sign(b2f_(y[:, 1])), np.sign(b2f_(r["y"][:, 1])))
+
+
+def test_full_size_h3_l0_sampled_frames():
+    """The bench workload (x [1, 17, 256, 256, 128], 32 groups, per-frame
+    statistics, SiLU) in the launch configuration the bench times; frames
+    are independent, so the oracle checks frames 0, 8 and 16 one by one."""
+    L = BASE
+    x, gamma, beta = workloads.norm_tensors(L)
+    y = run(x, gamma, beta, L.groups, eps=L.eps, silu=L.silu, t_isolated=L.t_isolated)
+    for d in (0, 8, 16):
+        xf = x[:, d:d + 1]
+        r = ref(xf, gamma, beta, L.groups, eps=L.eps, silu=L.silu)
+        diag = check_group_norm(y[:, d:d + 1], r, what=f"frame {d}")
+        print(f"[gn] frame {d}: {diag}", flush=True)
+        assert diag["bit_identical"] > 0.99, diag

@@ -159,3 +159,51 @@ def integer_tensors(x_shape, cout, seed=7, bias=False):
     if bias:
         b = torch.from_numpy(rng.integers(-8, 9, size=(cout,)).astype(np.float32))
     return x, w, b
+
+
+# ---------------------------------------------------------------- GroupNorm
+
+@dataclasses.dataclass(frozen=True)
+class NormLayer:
+    """A GroupNorm (+ SiLU) between the H3 encoder's convs: the activation
+    each ResnetBlock normalises at one level (FlyDSL issue page, H3 comment:
+    "Shapes" for the activations, the GroupNorm argument for the norm)."""
+    name: str
+    family: int
+    x_shape: Tuple[int, int, int, int, int]   # NDHWC
+    groups: int = 32
+    silu: bool = True
+    t_isolated: bool = True
+    eps: float = 1e-5
+
+    @property
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: x read once, y written once (bf16)."""
+        return 2 * 2 * int(np.prod(self.x_shape))
+
+
+NORM_LAYERS = {
+    "gn_h3_l0_128": NormLayer("gn_h3_l0_128", 6, (1, 17, 256, 256, 128)),
+    "gn_h3_l1_256": NormLayer("gn_h3_l1_256", 6, (1, 17, 128, 128, 256)),
+    "gn_h3_l3_512": NormLayer("gn_h3_l3_512", 6, (1, 5, 32, 32, 512)),
+    "gn_h3_l5_1024": NormLayer("gn_h3_l5_1024", 6, (1, 5, 16, 16, 1024)),
+}
+
+
+def norm_tensors(layer: NormLayer, x_shape=None, seed_stream: int = 0):
+    """Seeded GroupNorm inputs: x bf16 NDHWC, gamma and beta fp32 [C].
+
+    x ~ N(0, 1) + o_c with a per-channel offset o_c ~ N(0, 0.25) (a conv
+    output with bias, so group means are not zero); gamma ~ U(0.5, 1.5);
+    beta ~ N(0, 0.01). Seed: SeedSequence([1000 + family, s]) with s = 10 for
+    x (10 + 10 k for draw k of seed_stream), 11 offsets, 12 gamma, 13 beta."""
+    import torch
+    xs = tuple(layer.x_shape if x_shape is None else x_shape)
+    c = xs[4]
+    fam = layer.family
+    off = _rng(fam, 11).standard_normal(c, dtype=np.float32) * np.float32(0.5)
+    x = _rng(fam, 10 + 10 * seed_stream).standard_normal(xs, dtype=np.float32)
+    x += off
+    gamma = torch.from_numpy(_rng(fam, 12).uniform(0.5, 1.5, size=c).astype(np.float32))
+    beta = torch.from_numpy(_rng(fam, 13).standard_normal(c, dtype=np.float32) * np.float32(0.1))
+    return _to_bf16(x), gamma, beta
