@@ -1,8 +1,10 @@
-"""Conv3D and GroupNorm oracle — TEST INFRASTRUCTURE ONLY.
+"""Conv3D, GroupNorm and streaming oracle — TEST INFRASTRUCTURE ONLY.
 
 A plain CPU direct convolution (C, OpenMP) with the cuDNN page's
-"Operation Contract" post-operations, and a plain channels-last GroupNorm
-(+ SiLU, numpy float64, in groupnorm.py), used to check the GPU library.
+"Operation Contract" post-operations, a plain channels-last GroupNorm
+(+ SiLU, numpy float64, in groupnorm.py) and the streaming scheme's padded
+outputs, history planes and caches (numpy, in stream.py), used to check the
+GPU library.
 Only tests/, the smoke entry point and the benchmark's CPU-baseline leg may
 import this package. It shares no code with the GPU library; both sides see
 the same seeded inputs and nothing else.

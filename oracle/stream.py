@@ -1,0 +1,76 @@
+"""Streaming causal conv oracle: padded outputs, history planes and caches —
+TEST INFRASTRUCTURE ONLY.
+
+What it computes. The cuDNN frontend page "Fused Conv3D + Bias + Residual +
+RMSNorm + SiLU" describes how a video VAE runs its causal convs on temporal
+chunks ("Causal Conv3D with Cache", "Normalization and Padding Variant",
+"Spatial Padding Variant"): a layer writes its activations into the interior
+of a larger buffer whose border is zero and whose two leading temporal planes
+hold the previous chunk's last two activated frames (its "history"), and it
+keeps those last frames in a small cache for the next chunk. The next conv
+then runs as a valid conv on that buffer: the history planes stand where the
+causal zero planes would be, the zero border is the spatial padding. The
+first layer packs its raw input chunk (channels-first, 12 channels in the
+page's workload) the same way, with zero channels up to a multiple of 8.
+
+Everything here is data movement on bf16 bit patterns (uint16 arrays), so it
+is exact. The convolutions are oracle.conv3d's.
+
+Only tests/, the smoke entry point and the benchmark's CPU-baseline leg may
+import this module; it shares no code with the GPU library.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def pad_output(y, pad_lo, pad_hi, history=None):
+    """y [N, D, H, W, C] -> [N, D+pt+qt, H+ph+qh, W+pw+qw, C] with y in the
+    interior and zeros elsewhere, except that with history [N, P, H, W, C]
+    (P <= pt) the interiors of planes pt-P .. pt-1 hold the history."""
+    y = np.asarray(y)
+    N, D, H, W, C = y.shape
+    (pt, ph, pw), (qt, qh, qw) = pad_lo, pad_hi
+    out = np.zeros((N, D + pt + qt, H + ph + qh, W + pw + qw, C), dtype=y.dtype)
+    out[:, pt:pt + D, ph:ph + H, pw:pw + W] = y
+    if history is not None and history.shape[1]:
+        P = history.shape[1]
+        if P > pt:
+            raise ValueError("more history frames than leading planes")
+        out[:, pt - P:pt, ph:ph + H, pw:pw + W] = history
+    return out
+
+
+def cache_tail(current, cache_frames, previous=None):
+    """The last cache_frames frames of previous ++ current (along D)."""
+    frames = current if previous is None else np.concatenate([previous, current], axis=1)
+    if cache_frames > frames.shape[1]:
+        raise ValueError("cache longer than the frames seen")
+    return frames[:, frames.shape[1] - cache_frames:].copy()
+
+
+def pack_stream_input(chunk_ncthw, history=None, c_pad=16):
+    """First layer of a streaming causal encoder: a channels-first chunk
+    [N, C, T, H, W] and up to two raw history frames [N, P, H, W, C] (NDHWC)
+    -> (padded [N, T+2, H+2, W+2, c_pad], cache [N, min(2, T+P), H, W, C]).
+
+    padded holds the chunk (channels-last) in planes 2 .. T+1, the history in
+    the P planes before them, zeros in the 2-P missing-history planes, the
+    one-pixel spatial border and channels C .. c_pad-1; cache holds the last
+    raw frames of history ++ chunk."""
+    x = np.ascontiguousarray(np.transpose(np.asarray(chunk_ncthw), (0, 2, 3, 4, 1)))
+    N, T, H, W, C = x.shape
+    if c_pad < C:
+        raise ValueError("c_pad below the channel count")
+    P = 0 if history is None else history.shape[1]
+    if P > 2:
+        raise ValueError("at most two history frames")
+    xc = np.zeros((N, T, H, W, c_pad), dtype=x.dtype)
+    xc[..., :C] = x
+    hc = None
+    if P:
+        hc = np.zeros((N, P, H, W, c_pad), dtype=x.dtype)
+        hc[..., :C] = history
+    padded = pad_output(xc, (2, 1, 1), (0, 1, 1), history=hc)
+    cache = cache_tail(x, min(2, T + P), previous=history if P else None)
+    return padded, cache
