@@ -148,6 +148,77 @@ def cpu_baseline(L, seconds):
                       f"{dt:.1f} s wall"}
 
 
+def stream_cases(args, per_layer, wanted, torch, cv, workloads):
+    """Streaming variants: padded outputs with history and cache, and the
+    first layer's chunk packing (timed together with its conv)."""
+    from convolution_video_vae_amd.layer import Conv3d, stream_pack_input
+    for name, S in workloads.STREAM_LAYERS.items():
+        if wanted is not None and name not in wanted:
+            continue
+        if "video" in S:
+            rng = np.random.default_rng(np.random.SeedSequence([1007, 0]))
+            video = torch.from_numpy(rng.standard_normal(S["video"], dtype=np.float32)).to(
+                torch.bfloat16).cuda()
+            n, c, T, h, w = S["video"]
+            chunk = video[:, :, S["t0"]:S["t0"] + S["t"]]
+            hist = video[:, :, S["t0"] - S["history"]:S["t0"]].permute(0, 2, 3, 4, 1).contiguous()
+            wt = torch.zeros((S["cout"], S["c_pad"], 3, 3, 3), dtype=torch.bfloat16)
+            wt[:, :c] = torch.from_numpy(rng.standard_normal((S["cout"], c, 3, 3, 3), dtype=np.float32)
+                                         * np.float32(np.sqrt(1 / (27 * c)))).to(torch.bfloat16)
+            padded = torch.empty((n, S["t"] + 2, h + 2, w + 2, S["c_pad"]), dtype=torch.bfloat16,
+                                 device="cuda")
+            cache = torch.empty((n, 2, h, w, c), dtype=torch.bfloat16, device="cuda")
+            conv = Conv3d(wt.cuda(), tuple(padded.shape))
+            y = conv.new_output()
+
+            def step():
+                stream_pack_input(chunk, hist, S["c_pad"], padded=padded, cache=cache)
+                conv(padded, y=y)
+            m = n * S["t"] * h * w
+            flops = 2.0 * m * S["cout"] * 27 * c
+            plan = cv.conv3d_plan_describe(conv.desc)
+            config = (f"chunk NCTHW [{n}, {c}, {S['t']}, {h}, {w}] (strided view of a {T}-frame "
+                      f"clip) + {S['history']} history frames -> padded [{n}, {S['t'] + 2}, {h + 2}, "
+                      f"{w + 2}, {S['c_pad']}] -> valid conv to {S['cout']} channels")
+        else:
+            if "layer" in S:
+                L = workloads.LAYERS[S["layer"]]
+                t = workloads.make_tensors(L)
+                xs, cout = L.x_shape, L.cout
+                kw = dict(bias=t.bias, gamma=t.gamma, norm_silu=L.norm_silu, residual=L.residual)
+                res = None if t.residual is None else t.residual.cuda()
+                x, w = t.x.cuda(), t.w.cuda()
+            else:
+                xs, cout = S["x"], S["cout"]
+                L = workloads.Layer(name, 5, xs, cout, bias=True, residual=True)
+                t = workloads.make_tensors(L)
+                kw = dict(bias=t.bias, residual=True)
+                res, x, w = t.residual.cuda(), t.x.cuda(), t.w.cuda()
+            conv = Conv3d(w, xs, out_pad_lo=S["pad_lo"], out_pad_hi=S["pad_hi"],
+                          history_frames=S.get("history", 0), cache_frames=S.get("cache", 0), **kw)
+            y = torch.zeros(conv.out_shape, dtype=torch.bfloat16, device="cuda")
+            cache = (torch.empty(conv.cache_shape, dtype=torch.bfloat16, device="cuda")
+                     if S.get("cache") else None)
+
+            def step():
+                conv(x, residual=res, y=y, cache=cache)
+            flops = L.flops()
+            probe = cv.make_epilogue(bias=conv.bias, gamma=conv.gamma, norm_silu=conv.norm_silu)
+            probe.flags |= cv.EPI_RESIDUAL if conv.has_residual else 0
+            plan = cv.conv3d_plan_describe(conv.desc, probe)
+            config = (f"x NDHWC {list(xs)} -> {cout} channels, output written padded "
+                      f"{list(S['pad_lo'])}/{list(S['pad_hi'])} into {list(conv.out_shape)}"
+                      f"{', history ' + str(S['history']) if S.get('history') else ''}"
+                      f"{', cache ' + str(S['cache']) if S.get('cache') else ''}")
+        sms, _ = time_case(step, max(5, args.steps), 3, torch)
+        assert torch.isfinite(y.float()).all().item()
+        tf = flops / (sms * 1e-3) / 1e12
+        per_layer[name] = {"us": round(sms * 1e3, 2), "tflops": round(tf, 2),
+                           "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                           "gflop": round(flops / 1e9, 3), "config": config, "plan": plan}
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -236,6 +307,9 @@ def main():
                           f"{', SiLU' if N.silu else ''}"}
             del x, y, gn
             torch.cuda.empty_cache()
+
+    if not args.no_layers:
+        stream_cases(args, per_layer, wanted, torch, cv, workloads)
 
     if args.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")

@@ -31,7 +31,8 @@ STATUS = {0: "CONV3D_OK", 1: "CONV3D_ERR_NULL", 2: "CONV3D_ERR_SHAPE", 3: "CONV3
 
 EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_dims",
             "conv3d_workspace_bytes", "conv3d_fwd", "conv3d_transpose", "conv3d_status_str",
-            "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm")
+            "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm",
+            "conv3d_padded_workspace_bytes", "conv3d_fwd_padded", "conv3d_stream_pack_input")
 
 
 class Conv3dError(RuntimeError):
@@ -52,6 +53,12 @@ class conv3d_epilogue(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint), ("bias", ctypes.c_void_p),
                 ("residual", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
                 ("residual_out", ctypes.c_void_p)]
+
+
+class conv3d_out_pad(ctypes.Structure):
+    _fields_ = [("pad_lo", ctypes.c_int * 3), ("pad_hi", ctypes.c_int * 3),
+                ("history_frames", ctypes.c_int), ("cache_frames", ctypes.c_int),
+                ("cache", ctypes.c_void_p)]
 
 
 class conv3d_group_norm_desc(ctypes.Structure):
@@ -89,6 +96,14 @@ def lib():
         L.conv3d_status_str.argtypes = [i]
         L.conv3d_plan_describe.restype = i
         L.conv3d_plan_describe.argtypes = [pd, pe, ctypes.c_char_p, sz]
+        po = ctypes.POINTER(conv3d_out_pad)
+        L.conv3d_padded_workspace_bytes.restype = i
+        L.conv3d_padded_workspace_bytes.argtypes = [pd, pe, po, ctypes.POINTER(sz)]
+        L.conv3d_fwd_padded.restype = i
+        L.conv3d_fwd_padded.argtypes = [pd, vp, vp, pe, po, vp, vp, sz, vp]
+        L.conv3d_stream_pack_input.restype = i
+        L.conv3d_stream_pack_input.argtypes = [vp, ctypes.POINTER(ctypes.c_longlong * 5), i, i, i, i,
+                                               i, vp, i, vp, i, vp, i, vp]
         pg = ctypes.POINTER(conv3d_group_norm_desc)
         L.conv3d_group_norm_workspace_bytes.restype = i
         L.conv3d_group_norm_workspace_bytes.argtypes = [pg, ctypes.POINTER(sz)]
@@ -212,3 +227,42 @@ def conv3d_group_norm(desc: conv3d_group_norm_desc, x, gamma, beta, y, workspace
     _check(lib().conv3d_group_norm(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
                                    _ptr(workspace), workspace_bytes, _stream(stream)),
            "conv3d_group_norm")
+
+
+def make_out_pad(pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), history_frames: int = 0, cache=None,
+                 cache_frames: int = 0) -> conv3d_out_pad:
+    """Padded-output placement for conv3d_fwd_padded."""
+    return conv3d_out_pad((ctypes.c_int * 3)(*pad_lo), (ctypes.c_int * 3)(*pad_hi),
+                          history_frames, cache_frames, _ptr(cache))
+
+
+def conv3d_padded_workspace_bytes(desc: conv3d_desc, epi: Optional[conv3d_epilogue],
+                                  out_pad: Optional[conv3d_out_pad]) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().conv3d_padded_workspace_bytes(ctypes.byref(desc),
+                                               ctypes.byref(epi) if epi else None,
+                                               ctypes.byref(out_pad) if out_pad else None,
+                                               ctypes.byref(out)), "conv3d_padded_workspace_bytes")
+    return int(out.value)
+
+
+def conv3d_fwd_padded(desc: conv3d_desc, x, w_packed, epi: Optional[conv3d_epilogue],
+                      out_pad: Optional[conv3d_out_pad], y, workspace=None,
+                      workspace_bytes: int = 0, stream=None) -> None:
+    if workspace is not None and not workspace_bytes and not isinstance(workspace, int):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().conv3d_fwd_padded(ctypes.byref(desc), _ptr(x), _ptr(w_packed),
+                                   ctypes.byref(epi) if epi else None,
+                                   ctypes.byref(out_pad) if out_pad else None, _ptr(y),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)),
+           "conv3d_fwd_padded")
+
+
+def conv3d_stream_pack_input(chunk, strides: Sequence[int], n: int, c: int, t: int, h: int, w: int,
+                             history, history_frames: int, padded, c_pad: int, cache,
+                             cache_frames: int, stream=None) -> None:
+    st = (ctypes.c_longlong * 5)(*[int(v) for v in strides])
+    _check(lib().conv3d_stream_pack_input(_ptr(chunk), ctypes.byref(st), n, c, t, h, w,
+                                          _ptr(history), history_frames, _ptr(padded), c_pad,
+                                          _ptr(cache), cache_frames, _stream(stream)),
+           "conv3d_stream_pack_input")

@@ -302,6 +302,47 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   pl->total = off;
 }
 
+// Padded-output placement (conv3d_fwd_padded).
+struct PadPlan {
+  bool on = false;
+  long long y_bytes = 0;   // padded y
+  PlaceArgs a{};
+};
+
+conv3d_status check_out_pad(const conv3d_out_pad* op, const Problem& pr, PadPlan* pp) {
+  *pp = PadPlan();
+  if (!op) return CONV3D_OK;
+  for (int i = 0; i < 3; ++i)
+    if (op->pad_lo[i] < 0 || op->pad_hi[i] < 0 || op->pad_lo[i] > 65536 || op->pad_hi[i] > 65536)
+      return CONV3D_ERR_SHAPE;
+  const int hist = op->history_frames;
+  if (hist < 0 || hist > op->pad_lo[0]) return CONV3D_ERR_SHAPE;
+  if (op->cache) {
+    if (op->cache_frames < 1 || op->cache_frames > pr.Do + hist) return CONV3D_ERR_SHAPE;
+    if (!aligned16(op->cache)) return CONV3D_ERR_ALIGN;
+  }
+  const bool padded = op->pad_lo[0] || op->pad_lo[1] || op->pad_lo[2] || op->pad_hi[0] ||
+                      op->pad_hi[1] || op->pad_hi[2];
+  if (!padded && !op->cache) return CONV3D_OK;
+  if (pr.out_layout != CONV3D_NDHWC) return CONV3D_ERR_UNSUPPORTED;
+  PlaceArgs& a = pp->a;
+  a.n = pr.n; a.cout = pr.cout;
+  a.Do = pr.Do; a.Ho = pr.Ho; a.Wo = pr.Wo;
+  a.Dy = pr.Do + op->pad_lo[0] + op->pad_hi[0];
+  a.Hy = pr.Ho + op->pad_lo[1] + op->pad_hi[1];
+  a.Wy = pr.Wo + op->pad_lo[2] + op->pad_hi[2];
+  a.pt = op->pad_lo[0]; a.ph = op->pad_lo[1]; a.pw = op->pad_lo[2];
+  a.hist = hist;
+  a.cache = (uint16_t*)op->cache;
+  a.cache_frames = op->cache ? op->cache_frames : 0;
+  a.cache_k = op->cache ? std::min(op->cache_frames, pr.Do) : 0;
+  pp->y_bytes = (long long)pr.n * a.Dy * a.Hy * a.Wy * pr.cout * 2;
+  if (pp->y_bytes > kMaxTensorBytes || (long long)pr.n * a.Dy * a.Hy > 0x7fffffffLL)
+    return CONV3D_ERR_UNSUPPORTED;
+  pp->on = true;
+  return CONV3D_OK;
+}
+
 // GroupNorm planning: units, chunking and the workspace carve.
 struct GnPlan {
   GroupNormArgs a;
@@ -409,6 +450,23 @@ conv3d_status conv3d_workspace_bytes(const conv3d_desc* desc, const conv3d_epilo
   return CONV3D_OK;
 }
 
+conv3d_status conv3d_padded_workspace_bytes(const conv3d_desc* desc, const conv3d_epilogue* epi,
+                                            const conv3d_out_pad* out_pad, size_t* bytes) {
+  if (!bytes) return CONV3D_ERR_NULL;
+  Problem pr;
+  conv3d_status st = check_desc(desc, &pr);
+  if (st != CONV3D_OK) return st;
+  PadPlan pp;
+  st = check_out_pad(out_pad, pr, &pp);
+  if (st != CONV3D_OK) return st;
+  Problem pe = pr;
+  pe.flags = epi ? epi->flags : 0u;
+  Plan pl;
+  make_plan(pe, desc->split_k, &pl);
+  *bytes = pp.on ? pl.total + align256(pr.y_bytes) : pl.total;
+  return CONV3D_OK;
+}
+
 conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogue* epi,
                                    char* buf, size_t len) {
   Problem pr;
@@ -432,6 +490,12 @@ conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogu
 conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_packed,
                          const conv3d_epilogue* epi, void* y, void* workspace,
                          size_t workspace_bytes, void* stream) {
+  return conv3d_fwd_padded(desc, x, w_packed, epi, nullptr, y, workspace, workspace_bytes, stream);
+}
+
+conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                const conv3d_epilogue* epi, const conv3d_out_pad* op, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   Problem pr;
   conv3d_status st = check_desc(desc, &pr);
   if (st != CONV3D_OK) return st;
@@ -440,10 +504,16 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
   if (st != CONV3D_OK) return st;
   if (!aligned16(x) || !aligned16(w_packed) || !aligned16(y)) return CONV3D_ERR_ALIGN;
 
+  // Output placement: padded y and / or frame cache.
+  PadPlan pp;
+  st = check_out_pad(op, pr, &pp);
+  if (st != CONV3D_OK) return st;
   Plan pl;
   make_plan(pr, desc->split_k, &pl);
-  if (pl.total > 0) {
-    if (!workspace || workspace_bytes < pl.total) return CONV3D_ERR_WORKSPACE;
+  const size_t off_stage = pl.total;                     // staged unpadded output
+  const size_t ws_total = pp.on ? off_stage + align256(pr.y_bytes) : pl.total;
+  if (ws_total > 0) {
+    if (!workspace || workspace_bytes < ws_total) return CONV3D_ERR_WORKSPACE;
     if (!aligned16(workspace)) return CONV3D_ERR_ALIGN;
   }
 
@@ -452,22 +522,27 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
   const unsigned f = pr.flags;
   const Range rx = range_of(x, pr.x_bytes);
   const Range rw = range_of(w_packed, (long long)conv3d_packed_weight_bytes(pr.cout, pr.cin));
-  const Range ry = range_of(y, pr.y_bytes);
+  const Range ry = range_of(y, pp.on ? pp.y_bytes : pr.y_bytes);
+  const Range rcache = pp.a.cache ? range_of(pp.a.cache, (long long)pr.n * pp.a.cache_frames *
+                                                             pr.Ho * pr.Wo * pr.cout * 2)
+                                  : Range();
   const Range rb = (f & F_BIAS) ? range_of(epi->bias, 4LL * pr.cout) : Range();
   const Range rr = (f & F_RESIDUAL) ? range_of(epi->residual, pr.y_bytes) : Range();
   const Range rg = (f & F_NORM) ? range_of(epi->gamma, 2LL * pr.cout) : Range();
   const Range ro = (f & F_RESIDUAL_OUT) ? range_of(epi->residual_out, pr.y_bytes) : Range();
-  const Range rs = range_of(workspace, (long long)pl.total);
-  const Range outs[] = {ry, ro, rs};
+  const Range rs = range_of(workspace, (long long)ws_total);
+  const Range outs[] = {ry, ro, rs, rcache};
   const Range ins[] = {rx, rw, rb, rr, rg};
   for (const Range& o : outs)
     for (const Range& i : ins)
       if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
-  if (overlaps(ry, ro) || overlaps(ry, rs) || overlaps(ro, rs)) return CONV3D_ERR_OVERLAP;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return CONV3D_ERR_OVERLAP;
 
   char* ws = (char*)workspace;
   const uint16_t* xin = (const uint16_t*)x;
-  uint16_t* yout = (uint16_t*)y;
+  uint16_t* yout = pp.on ? (uint16_t*)(ws + off_stage) : (uint16_t*)y;
   const uint16_t* res = (f & F_RESIDUAL) ? (const uint16_t*)epi->residual : nullptr;
   uint16_t* rout = (f & F_RESIDUAL_OUT) ? (uint16_t*)epi->residual_out : nullptr;
   const int S = pr.d * pr.h * pr.w;
@@ -541,6 +616,12 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
     r.cb = pl.cfg.cb;
     if (launch_reduce(r, stream)) return CONV3D_ERR_HIP;
   }
+  if (pp.on) {
+    PlaceArgs pa = pp.a;
+    pa.y0 = yout;
+    pa.y = (uint16_t*)y;
+    if (launch_place(pa, stream)) return CONV3D_ERR_HIP;
+  }
 
   if (pr.out_layout == CONV3D_NCDHW) {
     if (launch_transpose(yout, (uint16_t*)y, pr.n, So, pr.cout, stream)) return CONV3D_ERR_HIP;
@@ -548,6 +629,47 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
       return CONV3D_ERR_HIP;
   }
   return CONV3D_OK;
+}
+
+conv3d_status conv3d_stream_pack_input(const void* chunk, const long long strides[5], int n,
+                                       int c, int t, int h, int w, const void* history,
+                                       int history_frames, void* padded, int c_pad, void* cache,
+                                       int cache_frames, void* stream) {
+  if (!chunk || !strides || !padded) return CONV3D_ERR_NULL;
+  if (history_frames > 0 && !history) return CONV3D_ERR_NULL;
+  if (n <= 0 || c <= 0 || t <= 0 || h <= 0 || w <= 0) return CONV3D_ERR_SHAPE;
+  if (history_frames < 0 || history_frames > 2 || c_pad < c) return CONV3D_ERR_SHAPE;
+  for (int i = 0; i < 5; ++i)
+    if (strides[i] < 0) return CONV3D_ERR_SHAPE;
+  if (cache && (cache_frames < 1 || cache_frames > t + history_frames)) return CONV3D_ERR_SHAPE;
+  if (c_pad % 8) return CONV3D_ERR_ALIGN;
+  if (!aligned16(padded) || ((uintptr_t)chunk & 1) || ((uintptr_t)history & 1) ||
+      ((uintptr_t)cache & 1))
+    return CONV3D_ERR_ALIGN;
+  const long long padded_bytes = (long long)n * (t + 2) * (h + 2) * (w + 2) * c_pad * 2;
+  if (padded_bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
+  const long long dims[5] = {n, c, t, h, w};
+  long long last = 0;
+  for (int i = 0; i < 5; ++i) last += (dims[i] - 1) * strides[i];
+  const Range rchunk = range_of(chunk, (last + 1) * 2);
+  const Range rhist = range_of(history, (long long)n * history_frames * h * w * c * 2);
+  const Range rpad = range_of(padded, padded_bytes);
+  const Range rcache = cache ? range_of(cache, (long long)n * cache_frames * h * w * c * 2) : Range();
+  for (const Range& o : {rpad, rcache})
+    for (const Range& i : {rchunk, rhist})
+      if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
+  if (overlaps(rpad, rcache)) return CONV3D_ERR_OVERLAP;
+  StreamPackArgs a;
+  a.chunk = (const uint16_t*)chunk;
+  a.sn = strides[0]; a.sc = strides[1]; a.st = strides[2]; a.sh = strides[3]; a.sw = strides[4];
+  a.history = (const uint16_t*)history;
+  a.padded = (uint16_t*)padded;
+  a.cache = (uint16_t*)cache;
+  a.n = n; a.c = c; a.t = t; a.h = h; a.w = w;
+  a.P = history_frames;
+  a.c_pad = c_pad;
+  a.cache_frames = cache ? cache_frames : 0;
+  return launch_stream_pack(a, stream) ? CONV3D_ERR_HIP : CONV3D_OK;
 }
 
 conv3d_status conv3d_group_norm_workspace_bytes(const conv3d_group_norm_desc* desc,

@@ -106,5 +106,28 @@ bool igemm_has_config(const TileCfg& cfg, int mode);
 int launch_reduce(const ReduceArgs& args, void* stream);
 int launch_queue_reset(unsigned* queue, void* stream);
 int launch_group_norm(const GroupNormArgs& args, void* stream);
+// Padded outputs: the unpadded output y0 [N][Do][Ho][Wo][Cout] placed into
+// y [N][Dy][Hy][Wy][Cout] at (pt, ph, pw); zeros elsewhere except the
+// interiors of the hist planes before pt; the last cache_k frames also into
+// cache [N][cache_frames][Ho][Wo][Cout] at its last frames (cache may be null).
+struct PlaceArgs {
+  const uint16_t* y0;
+  uint16_t* y;
+  uint16_t* cache;
+  int n, cout, Do, Ho, Wo, Dy, Hy, Wy, pt, ph, pw, hist;
+  int cache_frames, cache_k;
+};
+int launch_place(const PlaceArgs& args, void* stream);
+// First layer of a streaming causal conv: a strided channels-first chunk and
+// up to two raw history frames -> padded NDHWC input and the raw-frame cache.
+struct StreamPackArgs {
+  const uint16_t* chunk;
+  long long sn, sc, st, sh, sw;   // chunk strides in elements
+  const uint16_t* history;        // [N][P][H][W][C] or null
+  uint16_t* padded;               // [N][T+2][H+2][W+2][c_pad]
+  uint16_t* cache;                // [N][cache_frames][H][W][C]
+  int n, c, t, h, w, P, c_pad, cache_frames;
+};
+int launch_stream_pack(const StreamPackArgs& args, void* stream);
 
 }  // namespace conv3d

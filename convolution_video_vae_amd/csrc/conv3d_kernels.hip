@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "conv3d_device.h"
 #include "conv3d_internal.h"
 
@@ -182,6 +184,113 @@ __global__ __launch_bounds__(256) void reduce_norm_kernel(ReduceArgs a) {
       *reinterpret_cast<u32x4_t*>(a.y + m * a.Cout + c0) = ov;
     }
   }
+}
+
+// --------------------------------------------------------------------------
+// Padded outputs: the unpadded output y0 [N][Do][Ho][Wo][Cout] placed into
+// y [N][Dy][Hy][Wy][Cout] at offset (pt, ph, pw), zeros everywhere else
+// except the interiors of the history planes (the caller's), and the last
+// cache_k frames also into the cache tail. One work-group per row (n, t, h)
+// of y: an output row is one contiguous copy plus its two border runs.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void place_kernel(PlaceArgs a) {
+  const long long row = blockIdx.x;
+  const int hh = (int)(row % a.Hy);
+  const long long nt = row / a.Hy;
+  const int t = (int)(nt % a.Dy);
+  const long long n = nt / a.Dy;
+  const int V = a.cout / 8;
+  u32x4_t* yr = reinterpret_cast<u32x4_t*>(a.y + row * a.Wy * a.cout);
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  const int d = t - a.pt, h = hh - a.ph;
+  const bool rowin = h >= 0 && h < a.Ho;
+  if (d >= 0 && d < a.Do && rowin) {
+    const u32x4_t* src =
+        reinterpret_cast<const u32x4_t*>(a.y0 + ((n * a.Do + d) * a.Ho + h) * a.Wo * a.cout);
+    u32x4_t* cr = nullptr;
+    if (a.cache && d >= a.Do - a.cache_k)
+      cr = reinterpret_cast<u32x4_t*>(
+          a.cache + ((n * a.cache_frames + (a.cache_frames - a.Do) + d) * a.Ho + h) * a.Wo * a.cout);
+    const int inner = a.Wo * V;
+    for (int i = threadIdx.x; i < inner; i += blockDim.x) {
+      const u32x4_t v = src[i];
+      yr[a.pw * V + i] = v;
+      if (cr) cr[i] = v;
+    }
+  } else if (d < -a.hist || d >= a.Do || !rowin) {
+    // a zero plane (before the history, or after the output) or a border row
+    for (int i = threadIdx.x; i < a.Wy * V; i += blockDim.x) yr[i] = z;
+    return;
+  }
+  // left and right border columns of an output or history row
+  const int lead = a.pw * V, tail = (a.Wy - a.pw - a.Wo) * V;
+  for (int i = threadIdx.x; i < lead + tail; i += blockDim.x)
+    yr[i < lead ? i : (a.pw + a.Wo) * V + (i - lead)] = z;
+}
+
+int launch_place(const PlaceArgs& a, void* stream) {
+  const long long rows = (long long)a.n * a.Dy * a.Hy;
+  hipLaunchKernelGGL(place_kernel, dim3((unsigned)rows), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Streaming first layer: padded [N][T+2][H+2][W+2][c_pad] from a strided
+// channels-first chunk and P raw history frames (zeros in the border, the
+// 2-P missing planes and channels >= C), then the cache: the last
+// cache_frames frames of history ++ chunk, [N][cache_frames][H][W][C].
+// One thread per padded pixel (16-byte stores of 8 channels), then one per
+// cache pixel.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t stream_src(const StreamPackArgs& a, int nn, int s, int hq,
+                                               int wq, int ch) {
+  // frame s of history ++ chunk
+  if (s < a.P)
+    return a.history[((((long long)nn * a.P + s) * a.h + hq) * a.w + wq) * a.c + ch];
+  return a.chunk[nn * a.sn + ch * a.sc + (long long)(s - a.P) * a.st + hq * a.sh + wq * a.sw];
+}
+
+__global__ __launch_bounds__(256) void stream_pack_kernel(StreamPackArgs a) {
+  const long long np = (long long)a.n * (a.t + 2) * (a.h + 2) * (a.w + 2);
+  const long long nc = (long long)a.n * a.cache_frames * a.h * a.w;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < np + nc;
+       i += (long long)gridDim.x * blockDim.x) {
+    if (i < np) {
+      long long r = i;
+      const int wp = (int)(r % (a.w + 2)); r /= a.w + 2;
+      const int hp = (int)(r % (a.h + 2)); r /= a.h + 2;
+      const int tp = (int)(r % (a.t + 2));
+      const int nn = (int)(r / (a.t + 2));
+      const bool inside = hp >= 1 && hp <= a.h && wp >= 1 && wp <= a.w && tp >= 2 - a.P;
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.padded + i * a.c_pad);
+      for (int c8 = 0; c8 < a.c_pad; c8 += 8) {
+        unsigned q[4] = {0u, 0u, 0u, 0u};
+        if (inside) {
+          for (int e = 0; e < 8 && c8 + e < a.c; ++e)
+            q[e >> 1] |= (unsigned)stream_src(a, nn, tp - 2 + a.P, hp - 1, wp - 1, c8 + e)
+                         << (16 * (e & 1));
+        }
+        dst[c8 / 8] = u32x4_t{q[0], q[1], q[2], q[3]};
+      }
+    } else {
+      long long r = i - np;
+      const int wq = (int)(r % a.w); r /= a.w;
+      const int hq = (int)(r % a.h); r /= a.h;
+      const int f = (int)(r % a.cache_frames);
+      const int nn = (int)(r / a.cache_frames);
+      const int s = a.P + a.t - a.cache_frames + f;
+      uint16_t* dst = a.cache + (i - np) * a.c;
+      for (int ch = 0; ch < a.c; ++ch) dst[ch] = stream_src(a, nn, s, hq, wq, ch);
+    }
+  }
+}
+
+int launch_stream_pack(const StreamPackArgs& a, void* stream) {
+  const long long total = (long long)a.n * (a.t + 2) * (a.h + 2) * (a.w + 2) +
+                          (long long)a.n * a.cache_frames * a.h * a.w;
+  const long long blocks = std::min<long long>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(stream_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
 }
 
 // --------------------------------------------------------------------------

@@ -11,9 +11,10 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_group_norm, conv3d_group_norm_workspace_bytes,
-               conv3d_output_dims, conv3d_pack_weight, conv3d_packed_weight_bytes,
-               conv3d_workspace_bytes, make_desc, make_epilogue, make_group_norm_desc)
+from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_fwd_padded, conv3d_group_norm,
+               conv3d_group_norm_workspace_bytes, conv3d_output_dims, conv3d_pack_weight,
+               conv3d_packed_weight_bytes, conv3d_padded_workspace_bytes, conv3d_stream_pack_input,
+               conv3d_workspace_bytes, make_desc, make_epilogue, make_group_norm_desc, make_out_pad)
 
 
 def pack_weight(w_oidhw: torch.Tensor, stream=None) -> torch.Tensor:
@@ -35,7 +36,13 @@ class Conv3d:
                  pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), layout: int = NDHWC,
                  out_layout: Optional[int] = None, split_k: int = 0,
                  bias: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
-                 norm_silu: bool = False, residual: bool = False, residual_out: bool = False):
+                 norm_silu: bool = False, residual: bool = False, residual_out: bool = False,
+                 out_pad_lo=None, out_pad_hi=(0, 0, 0), history_frames: int = 0,
+                 cache_frames: int = 0):
+        """out_pad_lo / out_pad_hi: write the output into the interior of a
+        zero-bordered buffer (the history_frames planes before it are the
+        caller's); cache_frames > 0: also keep the last output frames in a
+        cache passed to each call."""
         self.cout, self.cin = int(weight.shape[0]), int(weight.shape[1])
         self.layout = layout
         self.out_layout = layout if out_layout is None else out_layout
@@ -48,6 +55,15 @@ class Conv3d:
             self.out_shape = (n,) + self.out_dhw + (self.cout,)
         else:
             self.out_shape = (n, self.cout) + self.out_dhw
+        self.padded = out_pad_lo is not None or cache_frames > 0
+        self.out_pad_lo = tuple(out_pad_lo or (0, 0, 0))
+        self.out_pad_hi = tuple(out_pad_hi)
+        self.history_frames = history_frames
+        self.cache_frames = cache_frames
+        if self.padded:
+            self.out_shape = (n,) + tuple(o + a + b for o, a, b in zip(
+                self.out_dhw, self.out_pad_lo, self.out_pad_hi)) + (self.cout,)
+            self.cache_shape = (n, cache_frames) + self.out_dhw[1:] + (self.cout,)
         self.device = weight.device
         self.w_packed = pack_weight(weight)
         self.bias = None if bias is None else bias.to(device=self.device, dtype=torch.float32).contiguous()
@@ -57,16 +73,26 @@ class Conv3d:
         self.has_residual_out = residual_out
         probe = make_epilogue(bias=self.bias, gamma=self.gamma, norm_silu=norm_silu)
         probe.flags |= (2 if residual else 0) | (8 if residual_out else 0)
-        self.workspace_bytes = conv3d_workspace_bytes(self.desc, probe)
+        if self.padded:
+            self.workspace_bytes = conv3d_padded_workspace_bytes(self.desc, probe,
+                                                                 self._out_pad(None))
+        else:
+            self.workspace_bytes = conv3d_workspace_bytes(self.desc, probe)
         self.workspace = (torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
                           if self.workspace_bytes else None)
+
+    def _out_pad(self, cache):
+        # the probe for the workspace size only needs a non-null cache address
+        c = cache if cache is not None else (16 if self.cache_frames else None)
+        return make_out_pad(self.out_pad_lo, self.out_pad_hi, self.history_frames, c,
+                            self.cache_frames)
 
     def new_output(self) -> torch.Tensor:
         return torch.empty(self.out_shape, dtype=torch.bfloat16, device=self.device)
 
     def __call__(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
                  y: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
-                 stream=None) -> torch.Tensor:
+                 stream=None, cache: Optional[torch.Tensor] = None) -> torch.Tensor:
         if tuple(x.shape) != self.x_shape or x.dtype != torch.bfloat16 or not x.is_contiguous():
             raise ValueError(f"x must be a contiguous bf16 tensor of shape {self.x_shape}")
         if self.has_residual != (residual is not None):
@@ -77,9 +103,36 @@ class Conv3d:
             y = self.new_output()
         epi = make_epilogue(bias=self.bias, residual=residual, gamma=self.gamma,
                             residual_out=residual_out, norm_silu=self.norm_silu)
-        conv3d_fwd(self.desc, x, self.w_packed, epi if epi.flags else None, y, self.workspace,
-                   self.workspace_bytes, stream)
+        if self.padded:
+            if (cache is not None) != (self.cache_frames > 0):
+                raise ValueError("cache presence differs from construction")
+            conv3d_fwd_padded(self.desc, x, self.w_packed, epi if epi.flags else None,
+                              self._out_pad(cache), y, self.workspace, self.workspace_bytes, stream)
+        else:
+            conv3d_fwd(self.desc, x, self.w_packed, epi if epi.flags else None, y, self.workspace,
+                       self.workspace_bytes, stream)
         return y
+
+
+def stream_pack_input(chunk: torch.Tensor, history: Optional[torch.Tensor], c_pad: int,
+                      padded: Optional[torch.Tensor] = None, cache: Optional[torch.Tensor] = None,
+                      cache_frames: int = 2, stream=None):
+    """First layer of a streaming causal encoder: chunk [N, C, T, H, W] (any
+    strides) and history [N, P, H, W, C] -> (padded [N, T+2, H+2, W+2, c_pad],
+    cache [N, min(cache_frames, T+P), H, W, C])."""
+    n, c, t, h, w = (int(v) for v in chunk.shape)
+    P = 0 if history is None else int(history.shape[1])
+    cf = min(cache_frames, t + P)
+    if padded is None:
+        padded = torch.empty((n, t + 2, h + 2, w + 2, c_pad), dtype=torch.bfloat16,
+                             device=chunk.device)
+    if cache is None and cf > 0:
+        cache = torch.empty((n, cf, h, w, c), dtype=torch.bfloat16, device=chunk.device)
+    if history is not None:
+        history = history.contiguous()
+    conv3d_stream_pack_input(chunk, chunk.stride(), n, c, t, h, w, history, P, padded, c_pad,
+                             cache, cf if cache is not None else 0, stream)
+    return padded, cache
 
 
 class GroupNorm:

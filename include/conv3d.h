@@ -19,6 +19,10 @@
  *    weight ("Weight Packing").
  *  - The channels-last GroupNorm (+ SiLU) between the convs: the MiniMax H3
  *    comment on the FlyDSL issue page (its GroupNorm argument).
+ *  - Streaming causal convs on temporal chunks: outputs written into padded
+ *    buffers with history planes and a frame cache, and the first layer's
+ *    chunk packing (cuDNN page: "Causal Conv3D with Cache", "Normalization
+ *    and Padding Variant", "Spatial Padding Variant").
  *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers to bf16 data (raw 16-bit patterns),
@@ -143,6 +147,62 @@ conv3d_status conv3d_workspace_bytes(const conv3d_desc* desc, const conv3d_epilo
 conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_packed,
                          const conv3d_epilogue* epi, void* y, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------- padded outputs
+ * Where conv3d_fwd_padded writes its output (cuDNN page, "Normalization and
+ * Padding Variant" and "Spatial Padding Variant"): y is NDHWC
+ *   [n][Do + pad_lo[0] + pad_hi[0]][Ho + pad_lo[1] + pad_hi[1]][Wo + pad_lo[2] + pad_hi[2]][cout]
+ * with output pixel (d, h, w) at (d + pad_lo[0], h + pad_lo[1], w + pad_lo[2]).
+ * Everything else in y is written with zeros, except the interiors of the
+ * history_frames planes just before the output (pad_lo[0] - history_frames
+ * .. pad_lo[0] - 1), which hold the caller's history (the previous chunk's
+ * last activated frames) and are not touched. A following valid conv on y
+ * then sees the history where a causal conv would see zero planes, and the
+ * zero border as its spatial padding; pad_hi = {0, 1, 1} gives the zero
+ * bottom row and right column a stride-2 conv expects.
+ * With cache != NULL, the last min(cache_frames, Do) output frames of each
+ * sample are also written to the last frames of cache, NDHWC
+ * [n][cache_frames][Ho][Wo][cout]; older cache frames are the caller's. */
+typedef struct {
+  int pad_lo[3];       /* >= 0: time, h, w */
+  int pad_hi[3];       /* >= 0 */
+  int history_frames;  /* 0 .. pad_lo[0] */
+  int cache_frames;    /* 1 .. Do + history_frames when cache != NULL */
+  void* cache;         /* bf16, 16-byte aligned, or NULL */
+} conv3d_out_pad;
+
+/* Workspace bytes conv3d_fwd_padded needs (the conv's own workspace plus a
+ * staged copy of the unpadded output when out_pad pads or caches). */
+conv3d_status conv3d_padded_workspace_bytes(const conv3d_desc* desc, const conv3d_epilogue* epi,
+                                            const conv3d_out_pad* out_pad, size_t* bytes);
+
+/* conv3d_fwd with its output written as out_pad describes (out_layout must
+ * be NDHWC; the epilogue is the same, residual and residual_out keep the
+ * unpadded output shape). y, cache, residual_out and the workspace must not
+ * overlap any operand or each other. out_pad == NULL is conv3d_fwd. */
+conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                const conv3d_epilogue* epi, const conv3d_out_pad* out_pad,
+                                void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* First layer of a streaming causal encoder (cuDNN page, "Causal Conv3D
+ * with Cache"): one temporal chunk, channels-first with arbitrary strides,
+ * chunk[i_n * strides[0] + i_c * strides[1] + i_t * strides[2] + i_h * strides[3]
+ *       + i_w * strides[4]] (elements, bf16, >= 0),
+ * and history_frames (0..2) raw frames before it, NDHWC [n][history_frames][h][w][c]
+ * -> padded NDHWC [n][t + 2][h + 2][w + 2][c_pad]: the chunk in planes 2..t+1
+ * and the history in the planes before, at spatial offset (1, 1); zeros in
+ * the border, the 2 - history_frames missing planes and channels c..c_pad-1.
+ * A valid conv3d_fwd on padded is the chunk's causal conv.
+ * With cache != NULL, cache NDHWC [n][cache_frames][h][w][c] receives the
+ * last cache_frames raw frames of history ++ chunk (1 <= cache_frames <=
+ * t + history_frames; 2 when the next chunk needs two).
+ * c_pad % 8 == 0, c_pad >= c; padded 16-byte aligned; chunk, history and
+ * cache 2-byte aligned; padded and cache must not overlap each other, chunk
+ * or history. */
+conv3d_status conv3d_stream_pack_input(const void* chunk, const long long strides[5], int n,
+                                       int c, int t, int h, int w, const void* history,
+                                       int history_frames, void* padded, int c_pad, void* cache,
+                                       int cache_frames, void* stream);
 
 /* Layout change at a network boundary, bf16, exact:
  *   src_layout = CONV3D_NCDHW:  [n][c][d][h][w] -> [n][d][h][w][c]

@@ -231,3 +231,64 @@ def test_group_norm_rejected_calls():
     assert gn(gn_desc(), ws=X, ws_bytes=need) == 4             # workspace inside x
     assert gn(gn_desc(), gamma=Y) == 4                         # gamma inside y
     assert gn(gn_desc(), beta=WS) == 4                         # beta inside the workspace
+
+
+# ------------------------------------------------------------------ padded outputs, stream packing
+
+def fwd_padded(desc, op, x=X, w=W, epi=None, y=Y, ws=WS, ws_bytes=1 << 30):
+    return cv.lib().conv3d_fwd_padded(ctypes.byref(desc), x, w, ctypes.byref(epi) if epi else None,
+                                      ctypes.byref(op) if op else None, y, ws, ws_bytes, None)
+
+
+def test_out_pad_struct_matches_header_layout():
+    assert ctypes.sizeof(cv.conv3d_out_pad) == 8 * 4 + 8
+
+
+def test_padded_workspace_adds_the_staged_output():
+    d = small_desc()
+    base = cv.conv3d_workspace_bytes(d)
+    op = cv.make_out_pad((2, 1, 1), (0, 1, 1), 1, R, 2)
+    staged = cv.conv3d_padded_workspace_bytes(d, None, op)
+    assert staged >= base + 1 * 3 * 8 * 8 * 32 * 2
+    assert cv.conv3d_padded_workspace_bytes(d, None, None) == base
+    assert cv.conv3d_padded_workspace_bytes(d, None, cv.make_out_pad()) == base
+
+
+def test_padded_rejected_calls():
+    d = small_desc()
+    assert fwd_padded(d, cv.make_out_pad((-1, 0, 0))) == 2
+    assert fwd_padded(d, cv.make_out_pad((1, 1, 1), history_frames=2)) == 2   # history > pad
+    assert fwd_padded(d, cv.make_out_pad((2, 1, 1), cache=R, cache_frames=0)) == 2
+    assert fwd_padded(d, cv.make_out_pad((2, 1, 1), history_frames=1, cache=R,
+                                         cache_frames=5)) == 2                 # > Do + history
+    assert fwd_padded(d, cv.make_out_pad((2, 1, 1), cache=R + 8, cache_frames=1)) == 3
+    dn = small_desc(); dn.out_layout = cv.NCDHW
+    assert fwd_padded(dn, cv.make_out_pad((0, 1, 1), (0, 1, 1))) == 6
+    need = cv.conv3d_padded_workspace_bytes(d, None, cv.make_out_pad((2, 1, 1), (0, 1, 1)))
+    assert fwd_padded(d, cv.make_out_pad((2, 1, 1), (0, 1, 1)), ws=None, ws_bytes=0) == 5
+    assert fwd_padded(d, cv.make_out_pad((2, 1, 1), (0, 1, 1)), ws_bytes=need - 1) == 5
+    assert fwd_padded(d, cv.make_out_pad((2, 1, 1), (0, 1, 1), cache=Y + 256, cache_frames=1)) == 4
+    assert fwd_padded(d, cv.make_out_pad((2, 1, 1), (0, 1, 1)), y=X + 4096) == 4
+
+
+def pack(chunk=X, strides=(12 * 4 * 6 * 6, 4 * 6 * 6, 6 * 6, 6, 1), n=1, c=12, t=4, h=6, w=6,
+         hist=None, P=0, padded=Y, c_pad=16, cache=None, cf=0):
+    st = (ctypes.c_longlong * 5)(*strides)
+    return cv.lib().conv3d_stream_pack_input(chunk, ctypes.byref(st), n, c, t, h, w, hist, P, padded,
+                                             c_pad, cache, cf, None)
+
+
+def test_stream_pack_rejected_calls():
+    assert pack(chunk=None) == 1
+    assert pack(padded=None) == 1
+    assert pack(P=1) == 1                                         # history missing
+    assert pack(t=0) == 2
+    assert pack(hist=R, P=3) == 2
+    assert pack(c_pad=8) == 2                                     # c_pad < c
+    assert pack(c_pad=20) == 3                                    # c_pad % 8
+    assert pack(strides=(-1, 1, 1, 1, 1)) == 2
+    assert pack(cache=G, cf=5) == 2                               # > t + history
+    assert pack(padded=Y + 8) == 3
+    assert pack(chunk=X + 1) == 3
+    assert pack(padded=X + 64) == 4                               # padded inside the chunk
+    assert pack(cache=Y + 64, cf=2) == 4                          # cache inside padded

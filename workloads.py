@@ -207,3 +207,26 @@ def norm_tensors(layer: NormLayer, x_shape=None, seed_stream: int = 0):
     gamma = torch.from_numpy(_rng(fam, 12).uniform(0.5, 1.5, size=c).astype(np.float32))
     beta = torch.from_numpy(_rng(fam, 13).standard_normal(c, dtype=np.float32) * np.float32(0.1))
     return _to_bf16(x), gamma, beta
+
+
+# ---------------------------------------------------------------- streaming
+
+# Streaming variants at the Wan 160-channel level (cuDNN page, "Causal Conv3D
+# with Cache", "Normalization and Padding Variant", "Spatial Padding
+# Variant"): chunks of 5 frames of 64 x 120 with two history frames, so a
+# padded buffer is [1, 7, 66, 122, C] like the fused layer's input.
+STREAM_LAYERS = {
+    # first layer: 12-channel chunk (frames 5..9 of a 17-frame clip, a
+    # strided view), two raw history frames, packed to 32 channels, then a
+    # valid 32 -> 160 conv without bias
+    "wan_stream_in_12to160": dict(video=(1, 12, 17, 64, 120), t0=5, t=5, history=2, c_pad=32,
+                                  cout=160),
+    # fused 160 -> 320 written padded for the next causal conv, two history
+    # frames, two-frame cache
+    "wan_fused_pad_160to320": dict(layer="wan_fused_160to320", pad_lo=(2, 1, 1),
+                                   pad_hi=(0, 1, 1), history=2, cache=2),
+    # bias + residual with a zero bottom row and right column (feeds a
+    # stride-2 conv)
+    "wan_bias_res_pad_160to160": dict(x=(1, 7, 66, 122, 160), cout=160, pad_lo=(0, 0, 0),
+                                      pad_hi=(0, 1, 1)),
+}
