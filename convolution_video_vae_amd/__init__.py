@@ -32,7 +32,8 @@ STATUS = {0: "CONV3D_OK", 1: "CONV3D_ERR_NULL", 2: "CONV3D_ERR_SHAPE", 3: "CONV3
 EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_dims",
             "conv3d_workspace_bytes", "conv3d_fwd", "conv3d_transpose", "conv3d_status_str",
             "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm",
-            "conv3d_padded_workspace_bytes", "conv3d_fwd_padded", "conv3d_stream_pack_input")
+            "conv3d_padded_workspace_bytes", "conv3d_fwd_padded", "conv3d_stream_pack_input",
+            "conv3d_pack_weight_2d")
 
 
 class Conv3dError(RuntimeError):
@@ -84,6 +85,8 @@ def lib():
         L.conv3d_packed_weight_bytes.argtypes = [i, i]
         L.conv3d_pack_weight.restype = i
         L.conv3d_pack_weight.argtypes = [vp, vp, i, i, vp]
+        L.conv3d_pack_weight_2d.restype = i
+        L.conv3d_pack_weight_2d.argtypes = [vp, vp, i, i, vp]
         L.conv3d_output_dims.restype = i
         L.conv3d_output_dims.argtypes = [pd, ctypes.POINTER(ctypes.c_int * 3)]
         L.conv3d_workspace_bytes.restype = i
@@ -168,6 +171,11 @@ def conv3d_packed_weight_bytes(cout: int, cin: int) -> int:
 def conv3d_pack_weight(w_oidhw, w_packed, cout: int, cin: int, stream=None) -> None:
     _check(lib().conv3d_pack_weight(_ptr(w_oidhw), _ptr(w_packed), cout, cin, _stream(stream)),
            "conv3d_pack_weight")
+
+
+def conv3d_pack_weight_2d(w_oihw, w_packed, cout: int, cin: int, stream=None) -> None:
+    _check(lib().conv3d_pack_weight_2d(_ptr(w_oihw), _ptr(w_packed), cout, cin, _stream(stream)),
+           "conv3d_pack_weight_2d")
 
 
 def conv3d_output_dims(desc: conv3d_desc):

@@ -423,7 +423,22 @@ conv3d_status conv3d_pack_weight(const void* w_oidhw, void* w_packed, int cout, 
   if (overlaps(range_of(w_oidhw, in_bytes),
                range_of(w_packed, (long long)conv3d_packed_weight_bytes(cout, cin))))
     return CONV3D_ERR_OVERLAP;
-  const int rc = launch_pack_weight((const uint16_t*)w_oidhw, (uint16_t*)w_packed, cout, cin, stream);
+  const int rc = launch_pack_weight((const uint16_t*)w_oidhw, (uint16_t*)w_packed, cout, cin, 27,
+                                    stream);
+  return rc ? CONV3D_ERR_HIP : CONV3D_OK;
+}
+
+conv3d_status conv3d_pack_weight_2d(const void* w_oihw, void* w_packed, int cout, int cin,
+                                    void* stream) {
+  if (!w_oihw || !w_packed) return CONV3D_ERR_NULL;
+  if (cout <= 0 || cin <= 0) return CONV3D_ERR_SHAPE;
+  if (!aligned16(w_oihw) || !aligned16(w_packed)) return CONV3D_ERR_ALIGN;
+  const long long in_bytes = 9LL * cout * cin * 2;
+  if (overlaps(range_of(w_oihw, in_bytes),
+               range_of(w_packed, (long long)conv3d_packed_weight_bytes(cout, cin))))
+    return CONV3D_ERR_OVERLAP;
+  const int rc = launch_pack_weight((const uint16_t*)w_oihw, (uint16_t*)w_packed, cout, cin, 9,
+                                    stream);
   return rc ? CONV3D_ERR_HIP : CONV3D_OK;
 }
 

@@ -98,7 +98,9 @@ struct GroupNormArgs {
 
 // Launchers (conv3d_kernels.hip, conv3d_norm.hip). Each returns 0 on success or the HIP
 // error code of the launch. `stream` is a hipStream_t.
-int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, void* stream);
+// taps = 27: an OIDHW weight; taps = 9: a [cout][cin][3][3] weight placed in
+// the last temporal slice (kd = 2), the other slices zero.
+int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, int taps, void* stream);
 int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int a, int b, void* stream);
 // Returns -1 if no kernel is compiled for (cfg, mode).
 int launch_igemm(const TileCfg& cfg, int mode, const IgemmArgs& args, int grid, void* stream);

@@ -299,7 +299,7 @@ int launch_stream_pack(const StreamPackArgs& a, void* stream) {
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __restrict__ w,
                                                           uint16_t* __restrict__ wp, int cout,
-                                                          int cin, int cc_n) {
+                                                          int cin, int cc_n, int taps) {
   const long long total = 27LL * cc_n * cout * 4;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (long long)gridDim.x * blockDim.x) {
@@ -315,7 +315,9 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int ci = cc * 32 + q * 8 + 2 * k + h;
-        const unsigned v = (ci < cin) ? w[((long long)co * cin + ci) * 27 + t] : 0u;
+        // a 9-tap (2D) weight fills the last temporal slice, t = 18 .. 26
+        const int ts = t - (27 - taps);
+        const unsigned v = (ci < cin && ts >= 0) ? w[((long long)co * cin + ci) * taps + ts] : 0u;
         v2 |= v << (16 * h);
       }
       out[k] = v2;
@@ -362,13 +364,13 @@ __global__ __launch_bounds__(256) void queue_reset_kernel(unsigned* queue) {
 // --------------------------------------------------------------------------
 // Launchers.
 // --------------------------------------------------------------------------
-int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, void* stream) {
+int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, int taps, void* stream) {
   const int cc_n = (cin + 31) / 32;
   const long long total = 27LL * cc_n * cout * 4;
   long long blocks = (total + 255) / 256;
   if (blocks > 65535) blocks = 65535;
   hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                     (hipStream_t)stream, w, wp, cout, cin, cc_n);
+                     (hipStream_t)stream, w, wp, cout, cin, cc_n, taps);
   return (int)hipGetLastError();
 }
 

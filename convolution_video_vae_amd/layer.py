@@ -13,19 +13,25 @@ import torch
 
 from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_fwd_padded, conv3d_group_norm,
                conv3d_group_norm_workspace_bytes, conv3d_output_dims, conv3d_pack_weight,
-               conv3d_packed_weight_bytes, conv3d_padded_workspace_bytes, conv3d_stream_pack_input,
-               conv3d_workspace_bytes, make_desc, make_epilogue, make_group_norm_desc, make_out_pad)
+               conv3d_pack_weight_2d, conv3d_packed_weight_bytes, conv3d_padded_workspace_bytes,
+               conv3d_stream_pack_input, conv3d_workspace_bytes, make_desc, make_epilogue,
+               make_group_norm_desc, make_out_pad)
 
 
 def pack_weight(w_oidhw: torch.Tensor, stream=None) -> torch.Tensor:
-    """OIDHW bf16 [Cout][Cin][3][3][3] on the GPU -> packed weight buffer."""
-    if w_oidhw.dtype != torch.bfloat16 or not w_oidhw.is_cuda or w_oidhw.dim() != 5:
-        raise ValueError("weight must be a 5-D bf16 CUDA tensor")
+    """OIDHW bf16 [Cout][Cin][3][3][3] on the GPU -> packed weight buffer.
+    A 4-D [Cout][Cin][3][3] weight is packed as the last temporal slice of a
+    3x3x3 weight (for 2D and 1x3x3 layers run on single frames)."""
+    if w_oidhw.dtype != torch.bfloat16 or not w_oidhw.is_cuda or w_oidhw.dim() not in (4, 5):
+        raise ValueError("weight must be a 4-D or 5-D bf16 CUDA tensor")
     cout, cin = w_oidhw.shape[:2]
     w = w_oidhw.contiguous()
     out = torch.empty(conv3d_packed_weight_bytes(cout, cin) // 2, dtype=torch.bfloat16,
                       device=w.device)
-    conv3d_pack_weight(w, out, cout, cin, stream)
+    if w.dim() == 4:
+        conv3d_pack_weight_2d(w, out, cout, cin, stream)
+    else:
+        conv3d_pack_weight(w, out, cout, cin, stream)
     return out
 
 

@@ -129,6 +129,17 @@ size_t conv3d_packed_weight_bytes(int cout, int cin);
 conv3d_status conv3d_pack_weight(const void* w_oidhw, void* w_packed, int cout, int cin,
                                  void* stream);
 
+/* Pack a 2D weight [cout][cin][3][3] (bf16) as the last temporal slice
+ * (kd = 2) of a 3x3x3 weight whose other slices are zero; same packed layout
+ * and size as conv3d_pack_weight. A causal conv3d_fwd (pad_lo[0] = 2,
+ * pad_hi[0] = 0) on single-frame inputs [n][1][h][w][c] with it is the 2D
+ * conv of each image, because such a conv only ever sees its last temporal
+ * tap (Qwen PR, "T=1 degeneration"); the zero slices are dead taps the
+ * kernels skip. A 1x3x3 conv over d frames is the same call on the view
+ * [n*d][1][h][w][c] of an NDHWC tensor (no copy). */
+conv3d_status conv3d_pack_weight_2d(const void* w_oihw, void* w_packed, int cout, int cin,
+                                    void* stream);
+
 /* Output extents {Do, Ho, Wo} for desc; CONV3D_ERR_SHAPE if any is < 1. */
 conv3d_status conv3d_output_dims(const conv3d_desc* desc, int out_dhw[3]);
 

@@ -21,7 +21,7 @@ HEADER = os.path.join(ROOT, "include", "conv3d.h")
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv3d_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(conv3d_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -292,3 +292,10 @@ def test_stream_pack_rejected_calls():
     assert pack(chunk=X + 1) == 3
     assert pack(padded=X + 64) == 4                               # padded inside the chunk
     assert pack(cache=Y + 64, cf=2) == 4                          # cache inside padded
+
+
+def test_pack_weight_2d_rejected_calls():
+    assert cv.lib().conv3d_pack_weight_2d(None, W, 8, 8, None) == 1
+    assert cv.lib().conv3d_pack_weight_2d(X, W, 0, 8, None) == 2
+    assert cv.lib().conv3d_pack_weight_2d(X + 2, W, 8, 8, None) == 3
+    assert cv.lib().conv3d_pack_weight_2d(X, X + 16, 8, 8, None) == 4
