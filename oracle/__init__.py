@@ -1,7 +1,7 @@
 """Conv3D, GroupNorm and streaming oracle — TEST INFRASTRUCTURE ONLY.
 
 A plain CPU direct convolution (C, OpenMP) with the cuDNN page's
-"Operation Contract" post-operations, a plain channels-last GroupNorm
+"Operation Contract" post-operations (zero or reflect spatial padding), a plain channels-last GroupNorm
 (+ SiLU, numpy float64, in groupnorm.py) and the streaming scheme's padded
 outputs, history planes and caches (numpy, in stream.py), used to check the
 GPU library.
@@ -146,3 +146,25 @@ def group_norm(x, groups, gamma, beta, **kw):
     """Channels-last GroupNorm (+ SiLU); see oracle/groupnorm.py."""
     from .groupnorm import group_norm as _gn
     return _gn(x, groups, gamma, beta, **kw)
+
+
+def reflect_pad_hw(x, pad_lo, pad_hi):
+    """Reflect padding of H and W of an NDHWC array (the border row or column
+    itself is not repeated: index -k maps to k, H-1+k to H-1-k), as the H3
+    encoder pads spatially before each conv (FlyDSL issue, H3 comment, the
+    conv call site). pad_lo / pad_hi: (h, w) amounts, each < the extent."""
+    x = np.asarray(x)
+    (ph, pw), (qh, qw) = pad_lo, pad_hi
+    H, W = x.shape[2], x.shape[3]
+    if max(ph, qh) >= H or max(pw, qw) >= W:
+        raise ValueError("reflect padding must be smaller than the extent")
+    rows = [abs(i) if i < 0 else (2 * (H - 1) - i if i >= H else i) for i in range(-ph, H + qh)]
+    cols = [abs(j) if j < 0 else (2 * (W - 1) - j if j >= W else j) for j in range(-pw, W + qw)]
+    return x[:, :, rows][:, :, :, cols]
+
+
+def conv3d_reflect(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), **kw):
+    """conv3d with zero padding in time and reflect padding in H and W: the
+    input reflect-padded first, then the conv with the temporal pad only."""
+    xp = reflect_pad_hw(x, pad_lo[1:], pad_hi[1:])
+    return conv3d(xp, w, stride=stride, pad_lo=(pad_lo[0], 0, 0), pad_hi=(pad_hi[0], 0, 0), **kw)

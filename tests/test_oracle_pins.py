@@ -313,3 +313,42 @@ def test_epilogue_sqrt_c_is_output_channels():
                         norm_silu=True, intermediates=True)
     np.testing.assert_allclose(got["den"], 8.0)
     np.testing.assert_array_equal(b2f(got["y"]), np.float32(0.73046875))
+
+
+# ---------------------------------------------------------------- reflect padding
+
+def test_reflect_pad_matches_torch():
+    rng = np.random.default_rng(51)
+    x = rand_bf16(rng, (2, 3, 5, 6, 8))
+    got = oracle.reflect_pad_hw(x, (1, 1), (1, 0))
+    xt = torch.from_numpy(b2f(x).astype(np.float64)).permute(0, 4, 1, 2, 3)   # N, C, D, H, W
+    want = F.pad(xt, (1, 0, 1, 1, 0, 0), mode="reflect").permute(0, 2, 3, 4, 1).numpy()
+    assert np.array_equal(b2f(got).astype(np.float64), want)
+
+
+def test_reflect_pad_hand_example():
+    x = np.arange(3 * 4, dtype=np.uint16).reshape(1, 1, 3, 4, 1)
+    got = oracle.reflect_pad_hw(x, (1, 1), (1, 1))[0, 0, :, :, 0]
+    want = np.array([[5, 4, 5, 6, 7, 6],
+                     [1, 0, 1, 2, 3, 2],
+                     [5, 4, 5, 6, 7, 6],
+                     [9, 8, 9, 10, 11, 10],
+                     [5, 4, 5, 6, 7, 6]])
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("stride", [(1, 1, 1), (2, 2, 2), (1, 2, 2)])
+def test_reflect_conv_matches_torch(stride):
+    """Causal time pad (zeros) + reflect spatial pad, as the H3 encoder's convs."""
+    rng = np.random.default_rng(52)
+    x = rand_bf16(rng, (1, 5, 6, 7, 8))
+    w = rand_bf16(rng, (16, 8, 3, 3, 3), 0.2)
+    got = oracle.conv3d_reflect(x, w, stride=stride, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1),
+                                intermediates=True)
+    xt = torch.from_numpy(b2f(x).astype(np.float64)).permute(0, 4, 1, 2, 3)
+    xt = F.pad(xt, (1, 1, 1, 1, 0, 0), mode="reflect")
+    xt = F.pad(xt, (0, 0, 0, 0, 2, 0))
+    ref = F.conv3d(xt, torch.from_numpy(b2f(w).astype(np.float64)), stride=stride)
+    assert_acc_matches(got["acc"], ref.permute(0, 2, 3, 4, 1).numpy())
+    with pytest.raises(ValueError):
+        oracle.reflect_pad_hw(rand_bf16(rng, (1, 1, 1, 4, 8)), (1, 1), (1, 1))
