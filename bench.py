@@ -74,7 +74,8 @@ def describe(L):
             f"stride {list(L.stride)}, pad lo {list(L.pad_lo)} hi {list(L.pad_hi)}, "
             f"out {list(L.out_shape())}"
             + (", fp32 bias" if L.bias else "") + (", residual" if L.residual else "")
-            + (", L2-norm*sqrt(C)*gamma+SiLU epilogue" if L.norm_silu else ""))
+            + (", L2-norm*sqrt(C)*gamma+SiLU epilogue" if L.norm_silu else "")
+            + (", reflect spatial padding" if L.reflect else ""))
 
 
 class Case:
@@ -92,7 +93,8 @@ class Case:
         self.x = x
         self.layer = Conv3d(t.w.cuda(), tuple(x.shape), stride=L.stride, pad_lo=L.pad_lo,
                             pad_hi=L.pad_hi, layout=lay, bias=t.bias, gamma=t.gamma,
-                            norm_silu=L.norm_silu, residual=L.residual)
+                            norm_silu=L.norm_silu, residual=L.residual,
+                            pad_mode=cv.PAD_REFLECT if L.reflect else cv.PAD_ZERO)
         self.res = None if t.residual is None else t.residual.cuda()
         if lay == cv.NCDHW and self.res is not None:
             self.res = self.res.permute(0, 4, 1, 2, 3).contiguous()

@@ -20,6 +20,9 @@ LIB_PATH = os.environ.get("CONV3D_LIB") or os.path.join(_HERE, "libconv3d_mi355x
 NCDHW = 0
 NDHWC = 1
 
+PAD_ZERO = 0
+PAD_REFLECT = 1
+
 EPI_BIAS = 1
 EPI_RESIDUAL = 2
 EPI_L2NORM_SILU = 4
@@ -47,7 +50,8 @@ class conv3d_desc(ctypes.Structure):
                 ("cin", ctypes.c_int), ("cout", ctypes.c_int),
                 ("stride", ctypes.c_int * 3), ("pad_lo", ctypes.c_int * 3),
                 ("pad_hi", ctypes.c_int * 3), ("layout", ctypes.c_int),
-                ("out_layout", ctypes.c_int), ("split_k", ctypes.c_int)]
+                ("out_layout", ctypes.c_int), ("split_k", ctypes.c_int),
+                ("pad_mode", ctypes.c_int)]
 
 
 class conv3d_epilogue(ctypes.Structure):
@@ -141,7 +145,8 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_desc(x_shape: Sequence[int], cout: int, *, stride=(1, 1, 1), pad_lo=(0, 0, 0),
-              pad_hi=(0, 0, 0), layout=NDHWC, out_layout=None, split_k=0) -> conv3d_desc:
+              pad_hi=(0, 0, 0), layout=NDHWC, out_layout=None, split_k=0,
+              pad_mode=PAD_ZERO) -> conv3d_desc:
     """Descriptor from the input shape in `layout` (NDHWC or NCDHW)."""
     if layout == NDHWC:
         n, d, h, w, cin = x_shape
@@ -149,7 +154,7 @@ def make_desc(x_shape: Sequence[int], cout: int, *, stride=(1, 1, 1), pad_lo=(0,
         n, cin, d, h, w = x_shape
     return conv3d_desc(n, d, h, w, cin, cout, (ctypes.c_int * 3)(*stride),
                        (ctypes.c_int * 3)(*pad_lo), (ctypes.c_int * 3)(*pad_hi), layout,
-                       layout if out_layout is None else out_layout, split_k)
+                       layout if out_layout is None else out_layout, split_k, pad_mode)
 
 
 def make_epilogue(bias=None, residual=None, gamma=None, residual_out=None,

@@ -55,6 +55,7 @@ struct Problem {
   long long x_bytes, y_bytes;
   int layout, out_layout;
   unsigned flags;
+  bool reflect;    // spatial reflect padding
 };
 
 struct Plan {
@@ -81,6 +82,13 @@ conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
   if (d->layout != CONV3D_NCDHW && d->layout != CONV3D_NDHWC) return CONV3D_ERR_SHAPE;
   if (d->out_layout != CONV3D_NCDHW && d->out_layout != CONV3D_NDHWC) return CONV3D_ERR_SHAPE;
   if (d->split_k < 0) return CONV3D_ERR_SHAPE;
+  if (d->pad_mode != CONV3D_PAD_ZERO && d->pad_mode != CONV3D_PAD_REFLECT) return CONV3D_ERR_SHAPE;
+  pr->reflect = d->pad_mode == CONV3D_PAD_REFLECT;
+  if (pr->reflect) {
+    if (d->h < 2 || d->w < 2) return CONV3D_ERR_SHAPE;
+    for (int i = 1; i < 3; ++i)
+      if (d->pad_lo[i] > 1 || d->pad_hi[i] > 1) return CONV3D_ERR_UNSUPPORTED;
+  }
   pr->n = d->n; pr->d = d->d; pr->h = d->h; pr->w = d->w;
   pr->cin = d->cin; pr->cout = d->cout;
   pr->sd = d->stride[0]; pr->sh = d->stride[1]; pr->sw = d->stride[2];
@@ -181,7 +189,7 @@ const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 5, -1}, {32, 2, 2, 4, 3, 5, -1}
 template <int N>
 bool pick_halo(const Problem& pr, const TileCfg (&cands)[N], int mode, TileCfg* out) {
   for (const TileCfg& c : cands)
-    if (halo_ok(pr, c) && igemm_has_config(c, mode)) {
+    if (halo_ok(pr, c) && igemm_has_config(c, mode, pr.reflect)) {
       *out = c;
       return true;
     }
@@ -199,7 +207,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   const long long n_tiles = ceil_div(pr.cout, base.bn());
 
   TileCfg store_cfg = store_channel_cfg(pr.cout);
-  if (!igemm_has_config(store_cfg, EPI_STORE)) store_cfg = base;
+  if (!igemm_has_config(store_cfg, EPI_STORE, pr.reflect)) store_cfg = base;
   if (!norm && !pick_halo(pr, kSlotStore, EPI_STORE, &store_cfg))
     pick_halo(pr, kHaloStore, EPI_STORE, &store_cfg);
   TileCfg part_cfg = base;
@@ -207,7 +215,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   if (base.r == 32 && ceil_div(pr.M, part_cfg.bm()) * n_tiles < 64) {
     TileCfg c = base;
     c.pb = 1;
-    if (igemm_has_config(c, EPI_PARTIAL)) part_cfg = c;
+    if (igemm_has_config(c, EPI_PARTIAL, pr.reflect)) part_cfg = c;
   }
   // (Fragment-order partials of the halo kernel have no norm reduction.)
   if (!norm) pick_halo(pr, kHaloPartial, EPI_PARTIAL, &part_cfg);
@@ -218,7 +226,8 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     const TileCfg cands[] = {{32, 2, 2, 3, 5, 0, -2}, {16, 2, 2, 2, 10, 2, 0},
                              {16, 2, 2, 2, 10, 1, 3}, {16, 4, 1, 2, 10, 1, 3}};
     for (const TileCfg& c : cands)
-      if (norm_cfg.r == 0 && c.bn() == pr.cout && halo_ok(pr, c) && igemm_has_config(c, EPI_NORM))
+      if (norm_cfg.r == 0 && c.bn() == pr.cout && halo_ok(pr, c) &&
+          igemm_has_config(c, EPI_NORM, pr.reflect))
         norm_cfg = c;
   }
 
@@ -233,7 +242,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     if (sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &c.r, &c.wm, &c.wn, &c.pb, &c.cb, &c.kb, &c.ns) == 7 &&
         c.bn() > 0 && pr.cout % c.bn() == 0 && halo_ok(pr, c)) {
       const int mode = split ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
-      if (igemm_has_config(c, mode)) {
+      if (igemm_has_config(c, mode, pr.reflect)) {
         if (mode == EPI_PARTIAL) part_cfg = c;
         else if (mode == EPI_NORM) norm_cfg = c;
         else store_cfg = c;
@@ -607,7 +616,7 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
     a.queue = (unsigned*)(ws + pl.off_queue);
     if (launch_queue_reset(a.queue, stream)) return CONV3D_ERR_HIP;
   }
-  const int rc = launch_igemm(pl.cfg, pl.mode, a, (int)pl.grid, stream);
+  const int rc = launch_igemm(pl.cfg, pl.mode, pr.reflect, a, (int)pl.grid, stream);
   if (rc) return rc < 0 ? CONV3D_ERR_UNSUPPORTED : CONV3D_ERR_HIP;
 
   if (pl.reduce) {

@@ -113,8 +113,10 @@ __device__ __forceinline__ TileCoord tile_coord(const IgemmArgs& a, int BM, int 
 }
 
 // Per-lane geometry of PB pixel blocks: byte offset of tap (0,0,0) and a
-// 27-bit mask of the taps that fall inside the input.
-template <int PB, int R>
+// 27-bit mask of the taps that fall inside the input. With reflect padding
+// every spatial tap reads real input and bits 27-30 flag the pixels whose
+// first row / last row / first column / last column tap is reflected.
+template <int PB, int R, bool REF = false>
 __device__ __forceinline__ unsigned pixel_geometry(const IgemmArgs& a, int m_first,
                                                    long long (&base)[PB], unsigned (&tapmask)[PB]) {
   unsigned live = 0;
@@ -136,19 +138,22 @@ __device__ __forceinline__ unsigned pixel_geometry(const IgemmArgs& a, int m_fir
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         vd |= (unsigned)(d0 + k >= 0 && d0 + k < a.D) << k;
-        vh |= (unsigned)(h0 + k >= 0 && h0 + k < a.H) << k;
-        vw |= (unsigned)(w0 + k >= 0 && w0 + k < a.W) << k;
+        vh |= (unsigned)(REF || (h0 + k >= 0 && h0 + k < a.H)) << k;
+        vw |= (unsigned)(REF || (w0 + k >= 0 && w0 + k < a.W)) << k;
       }
       unsigned tm = 0;
 #pragma unroll
       for (int t = 0; t < 27; ++t)
         tm |= ((vd >> (t / 9)) & (vh >> ((t / 3) % 3)) & (vw >> (t % 3)) & 1u) << t;
+      if (REF)
+        tm |= ((unsigned)(h0 < 0) << 27) | ((unsigned)(h0 + 2 >= a.H) << 28) |
+              ((unsigned)(w0 < 0) << 29) | ((unsigned)(w0 + 2 >= a.W) << 30);
       tapmask[p] = tm;
       base[p] = ((((long long)n * a.D + d0) * a.H + h0) * a.W + w0) * (a.Cin * 2);
     }
     live |= tapmask[p];
   }
-  return live;
+  return live & ((1u << 27) - 1u);
 }
 
 // floor(n / d) for 0 <= n < 2^22 and 0 < d < 2^22, from a float reciprocal
@@ -158,6 +163,31 @@ __device__ __forceinline__ int small_div(int n, int d, float inv_d) {
   if ((q + 1) * d <= n) ++q;
   if (q * d > n) --q;
   return q;
+}
+
+// Reflect padding (the H3 encoder's spatial pad): index -1 reads 1 and index
+// n reads n - 2 (pads of at most one, extents of at least two).
+__device__ __forceinline__ int reflect_index(int i, int n) {
+  return i < 0 ? -i : (i >= n ? 2 * n - 2 - i : i);
+}
+
+// (kd, kh) pairs of an output row whose input rows start at (d0, h0): bit
+// kd * 3 + kh set when the pair reads real input. Time is always zero
+// padded; with reflect padding every kh reads a real row, and bit 9 (h0 = -1:
+// tap kh = 0 reads row 1, two rows down) and bit 10 (h0 + 2 = H: tap kh = 2
+// reads row H - 2, two rows up) tell the gathers where to move.
+template <bool REF>
+__device__ __forceinline__ unsigned row_mask(const IgemmArgs& a, int d0, int h0) {
+  unsigned m = 0;
+#pragma unroll
+  for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+    for (int kh = 0; kh < 3; ++kh) {
+      const bool hv = REF || (h0 + kh >= 0 && h0 + kh < a.H);
+      m |= (unsigned)(d0 + kd >= 0 && d0 + kd < a.D && hv) << (kd * 3 + kh);
+    }
+  if (REF) m |= ((unsigned)(h0 < 0) << 9) | ((unsigned)(h0 + 2 >= a.H) << 10);
+  return m;
 }
 
 // Lane index of the calling lane, recomputed where it is called (volatile,
@@ -206,7 +236,7 @@ constexpr int kEnd = 0x7fffffff;
 // check turns into zeros.
 // A step of kEnd loads zeros (every offset out of range), so prefetches are
 // issued unconditionally and the wait counts stay static.
-template <class T, int PB>
+template <class T, int PB, bool REF = false>
 __device__ __forceinline__ void gather_x(const IgemmArgs& a, __amdgpu_buffer_rsrc_t rsrc, int e,
                                          int lane, const long long (&base)[PB],
                                          const unsigned (&tapmask)[PB], u32x4_t (&dst)[PB][T::KS]) {
@@ -222,7 +252,17 @@ __device__ __forceinline__ void gather_x(const IgemmArgs& a, __amdgpu_buffer_rsr
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
       const unsigned ok = chan_ok & (tapmask[p] >> t);
-      const unsigned off = (unsigned)(base[p] + delta + ch * 16) | (((ok & 1u) - 1u) & kOobOffset);
+      long long adj = 0;
+      if (REF) {  // reflected taps: two rows / columns back inside
+        const unsigned f = tapmask[p];
+        const int rowb = a.W * a.Cin * 2, colb = a.Cin * 2;
+        if (kh == 0 && ((f >> 27) & 1u)) adj += 2 * rowb;
+        if (kh == 2 && ((f >> 28) & 1u)) adj -= 2 * rowb;
+        if (kw == 0 && ((f >> 29) & 1u)) adj += 2 * colb;
+        if (kw == 2 && ((f >> 30) & 1u)) adj -= 2 * colb;
+      }
+      const unsigned off =
+          (unsigned)(base[p] + delta + adj + ch * 16) | (((ok & 1u) - 1u) & kOobOffset);
       dst[p][h] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
     }
   }
@@ -380,7 +420,7 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
 // ahead, weight fetches NS steps ahead, LDS stages 2 ahead, weight fragments
 // 1 ahead).
 // ----------------------------------------------------------------------------
-template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
+template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI, bool REF = false>
 __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
   constexpr int R = T::R, KS = T::KS, NACC = T::NACC;
   constexpr int NT = 64 * WM * WN;
@@ -410,7 +450,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
 
   long long base[PB];
   unsigned tapmask[PB];
-  unsigned live = wave_or(pixel_geometry<PB, R>(a, m_first, base, tapmask));
+  unsigned live = wave_or(pixel_geometry<PB, R, REF>(a, m_first, base, tapmask));
   // Taps no pixel of the tile can see are skipped by the whole work-group.
   if (tid == 0) live_sh = 0;
   __syncthreads();
@@ -512,7 +552,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
   };
   auto gather = [&](const int (&g)[KB], u32x4_t (&dst)[KB][PB][KS]) {
 #pragma unroll
-    for (int k = 0; k < KB; ++k) gather_x<T, PB>(a, xrsrc, g[k], lane, base, tapmask, dst[k]);
+    for (int k = 0; k < KB; ++k) gather_x<T, PB, REF>(a, xrsrc, g[k], lane, base, tapmask, dst[k]);
   };
 
   u32x4_t xr[NS][KB][PB][KS];   // pixel fragments
@@ -938,7 +978,7 @@ __device__ __forceinline__ int xslot_chunk(int slot, int chunk) {
   return chunk ^ ((slot >> 1) & 3);
 }
 
-template <int CB, int WN, int XJ, int EPI>
+template <int CB, int WN, int XJ, int EPI, bool REF = false>
 __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   using T = Mfma32;
   using S = HaloShape<CB, WN, XJ>;
@@ -1019,17 +1059,12 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
       const int dq = t2 - n * a.Do;
       const int d0 = dq * a.sd - a.pd;
       const int h0 = ho * a.sh - a.ph;
-#pragma unroll
-      for (int kd = 0; kd < 3; ++kd)
-#pragma unroll
-        for (int kh = 0; kh < 3; ++kh)
-          rmask |= (unsigned)(d0 + kd >= 0 && d0 + kd < a.D && h0 + kh >= 0 && h0 + kh < a.H)
-                   << (kd * 3 + kh);
+      rmask = row_mask<REF>(a, d0, h0);
       rbase = ((n * a.D + d0) * a.H + h0) * a.W;
     }
   }
   // Live (kd, kh) pairs of the tile: the same in every wave, no LDS needed.
-  const unsigned live = __builtin_amdgcn_readfirstlane(wave_or(lane < nseg ? rmask : 0u));
+  const unsigned live = __builtin_amdgcn_readfirstlane(wave_or(lane < nseg ? rmask : 0u)) & 511u;
 
   // Activation DMA entries of this lane: LDS unit q of a buffer holds chunk
   // xslot_chunk(q / 4, q % 4) of slot q / 4. xbase is that chunk's byte offset
@@ -1052,9 +1087,10 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     const int kk = min(k, 63);
     const unsigned m = __shfl(rmask, kk);
     const int rb = __shfl(rbase, kk);
-    const bool wok = w_in >= 0 && w_in < a.W;
+    const bool wok = REF ? (w_in >= -1 && w_in <= a.W) : (w_in >= 0 && w_in < a.W);
+    const int wc = REF ? reflect_index(w_in, a.W) : w_in;
     xmask[j] = wok ? m : 0u;
-    xbase[j] = wok ? (rb + w_in) * (a.Cin * 2) + c * 16 : 0;
+    xbase[j] = wok ? (rb + wc) * (a.Cin * 2) + c * 16 : 0;
   }
 
   // Weight DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
@@ -1136,6 +1172,8 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     unsigned wor;        // 0, or kOobOffset past the last stage
     unsigned pbit;       // bit of the (kd, kh) pair, 0 past the last stage
     int delta;           // activation byte offset of the pair and chunk
+    unsigned rbit;       // reflect padding: row flag whose rows move by radj
+    int radj;
   };
   auto stage_dma = [&](int e) -> StageDma {
     StageDma d;
@@ -1148,6 +1186,8 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     d.wor = ok ? 0u : kOobOffset;
     d.pbit = ok ? 1u << pr : 0u;
     d.delta = (kd * a.H + kh) * a.W * (a.Cin * 2) + cc * 64;
+    d.rbit = REF ? (kh == 0 ? 1u << 9 : (kh == 2 ? 1u << 10 : 0u)) : 0u;
+    d.radj = REF ? (kh == 0 ? 2 : -2) * a.W * (a.Cin * 2) : 0;
     return d;
   };
   auto issue_w_one = [&](const StageDma& d, auto b_c, auto k_c) {
@@ -1157,7 +1197,8 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   };
   auto issue_x_one = [&](const StageDma& d, auto b_c, auto j_c) {
     constexpr int j = decltype(j_c)::value;
-    const unsigned off = (xmask[j] & d.pbit) ? (unsigned)(xbase[j] + d.delta) : kOobOffset;
+    const int radj = (REF && (xmask[j] & d.rbit)) ? d.radj : 0;
+    const unsigned off = (xmask[j] & d.pbit) ? (unsigned)(xbase[j] + d.delta + radj) : kOobOffset;
     dma16(xrsrc, &xbuf(b_c)[(j * 4 + wave) * 64], off, 0u);
   };
 
@@ -1357,7 +1398,7 @@ __device__ __forceinline__ void unit_slot(int q, int& sl, int& c) {
   }
 }
 
-template <int PB, int CB, int WN, int EPI>
+template <int PB, int CB, int WN, int EPI, bool REF = false>
 __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   using T = Mfma32;
   using S = SlotShape<PB, CB, WN>;
@@ -1462,6 +1503,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     unsigned wor;        // 0, or kOobOffset past the last stage
     unsigned pbit;       // bit of the (kd, kh) pair, 0 past the last stage
     int delta;           // activation byte offset of the pair and chunk
+    unsigned rbit;       // reflect padding: row flag whose rows move by radj
+    int radj;
   };
   auto stage_dma = [&](int e) -> StageDma {
     StageDma d;
@@ -1474,6 +1517,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     d.wor = ok ? 0u : kOobOffset;
     d.pbit = ok ? 1u << pr : 0u;
     d.delta = (kd * a.H + kh) * a.W * (a.Cin * 2) + cc * 64;
+    d.rbit = REF ? (kh == 0 ? 1u << 9 : (kh == 2 ? 1u << 10 : 0u)) : 0u;
+    d.radj = REF ? (kh == 0 ? 2 : -2) * a.W * (a.Cin * 2) : 0;
     return d;
   };
   // Weight DMA instruction k of a stage (tap kw = k / WJ, piece k % WJ).
@@ -1484,7 +1529,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   };
   auto issue_x_one = [&](const StageDma& d, auto b_c, auto j_c) {
     constexpr int j = decltype(j_c)::value;
-    const unsigned off = (xmask[j] & d.pbit) ? (unsigned)(xbase[j] + d.delta) : kOobOffset;
+    const int radj = (REF && (xmask[j] & d.rbit)) ? d.radj : 0;
+    const unsigned off = (xmask[j] & d.pbit) ? (unsigned)(xbase[j] + d.delta + radj) : kOobOffset;
     dma16(xrsrc, &xbuf(b_c)[(j * 4 + wave) * 64], off, 0u);
   };
 
@@ -1521,12 +1567,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
         const int dq = t2 - n * a.Do;
         const int d0 = dq * a.sd - a.pd;
         const int h0 = ho * a.sh - a.ph;
-#pragma unroll
-        for (int kd = 0; kd < 3; ++kd)
-#pragma unroll
-          for (int kh = 0; kh < 3; ++kh)
-            rmask |= (unsigned)(d0 + kd >= 0 && d0 + kd < a.D && h0 + kh >= 0 && h0 + kh < a.H)
-                     << (kd * 3 + kh);
+        rmask = row_mask<REF>(a, d0, h0);
         rbase = ((n * a.D + d0) * a.H + h0) * a.W;
       }
     }
@@ -1549,9 +1590,11 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       const int kk = min(k, 63);
       const unsigned m = __shfl(rmask, kk);
       const int rb = __shfl(rbase, kk);
-      const bool ok = sl < S::XS && w_in >= 0 && w_in < a.W;
+      const bool ok =
+          sl < S::XS && (REF ? (w_in >= -1 && w_in <= a.W) : (w_in >= 0 && w_in < a.W));
+      const int wc = REF ? reflect_index(w_in, a.W) : w_in;
       xmask[j] = ok ? m : 0u;
-      xbase[j] = ok ? (rb + w_in) * (a.Cin * 2) + c * 16 : 0;
+      xbase[j] = ok ? (rb + wc) * (a.Cin * 2) + c * 16 : 0;
     }
     // Weight DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
     // channel order, 16-byte chunk (q % 4) XOR the row swizzle.
@@ -1742,19 +1785,19 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI>
+template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI, bool REF>
 int launch_one(const IgemmArgs& args, int grid, void* stream) {
   if constexpr (NS == -2)
-    hipLaunchKernelGGL((igemm_slot_kernel<PB, CB, WN, EPI>), dim3((unsigned)grid), dim3(256), 0,
-                       (hipStream_t)stream, args);
+    hipLaunchKernelGGL((igemm_slot_kernel<PB, CB, WN, EPI, REF>), dim3((unsigned)grid), dim3(256),
+                       0, (hipStream_t)stream, args);
   else if constexpr (NS < 0)
-    hipLaunchKernelGGL((igemm_halo_kernel<CB, WN, KB, EPI>), dim3((unsigned)grid), dim3(256), 0,
-                       (hipStream_t)stream, args);
+    hipLaunchKernelGGL((igemm_halo_kernel<CB, WN, KB, EPI, REF>), dim3((unsigned)grid), dim3(256),
+                       0, (hipStream_t)stream, args);
   else if constexpr (NS == 0)
     hipLaunchKernelGGL((igemm_tile_kernel<T, WM, WN, PB, CB, KB, EPI>), dim3((unsigned)grid),
                        dim3(64 * WM * WN), 0, (hipStream_t)stream, args);
   else
-    hipLaunchKernelGGL((igemm_kernel<T, WM, WN, PB, CB, KB, NS, EPI>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((igemm_kernel<T, WM, WN, PB, CB, KB, NS, EPI, REF>), dim3((unsigned)grid),
                        dim3(64 * WM * WN), 0, (hipStream_t)stream, args);
   return (int)hipGetLastError();
 }
@@ -1762,13 +1805,18 @@ int launch_one(const IgemmArgs& args, int grid, void* stream) {
 struct Entry {
   TileCfg cfg;
   int mode;
+  bool reflect;   // spatial reflect padding compiled in
   int (*fn)(const IgemmArgs&, int, void*);
 };
 
 #define C32(WM, WN, PB, CB, KB, NS, MODE) \
-  {{32, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE>}
+  {{32, WM, WN, PB, CB, KB, NS}, MODE, false, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, false>}
 #define C16(WM, WN, PB, CB, KB, NS, MODE) \
-  {{16, WM, WN, PB, CB, KB, NS}, MODE, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE>}
+  {{16, WM, WN, PB, CB, KB, NS}, MODE, false, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, false>}
+#define R32(WM, WN, PB, CB, KB, NS, MODE) \
+  {{32, WM, WN, PB, CB, KB, NS}, MODE, true, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, true>}
+#define R16(WM, WN, PB, CB, KB, NS, MODE) \
+  {{16, WM, WN, PB, CB, KB, NS}, MODE, true, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, true>}
 const Entry kEntries[] = {
     // ns = -2: slot kernel (stride 1 along W, Cin % 32 == 0), 512-slot tiles.
     C32(2, 2, 8, 2, 0, -2, EPI_STORE),
@@ -1807,24 +1855,51 @@ const Entry kEntries[] = {
     // Any Cout % 16 == 0.
     C16(4, 1, 4, 2, 1, 3, EPI_STORE),
     C16(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
+    // Reflect spatial padding: slot, halo and the plain kernel's channel
+    // tiles (the planner falls back to the last for anything else).
+    R32(2, 2, 8, 2, 0, -2, EPI_STORE),
+    R32(4, 1, 4, 3, 0, -2, EPI_STORE),
+    R32(2, 2, 3, 5, 0, -2, EPI_NORM),
+    R32(4, 1, 4, 4, 9, -1, EPI_STORE),
+    R32(4, 1, 4, 3, 9, -1, EPI_STORE),
+    R32(4, 1, 4, 4, 9, -1, EPI_PARTIAL),
+    R32(2, 2, 4, 4, 5, -1, EPI_PARTIAL),
+    R32(2, 2, 4, 3, 5, -1, EPI_PARTIAL),
+    R32(4, 1, 2, 4, 1, 3, EPI_STORE),
+    R32(4, 1, 2, 3, 1, 3, EPI_STORE),
+    R32(4, 1, 2, 2, 1, 3, EPI_STORE),
+    R32(4, 1, 2, 4, 1, 3, EPI_PARTIAL),
+    R32(4, 1, 1, 4, 1, 3, EPI_PARTIAL),
+    R32(4, 1, 2, 3, 1, 3, EPI_PARTIAL),
+    R32(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
+    R16(2, 2, 2, 10, 1, 3, EPI_NORM),
+    R16(4, 1, 2, 10, 1, 3, EPI_NORM),
+    R16(4, 1, 4, 2, 1, 3, EPI_STORE),
+    R16(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
 };
 #undef C32
 #undef C16
+#undef R32
+#undef R16
 
-const Entry* find_entry(const TileCfg& c, int mode) {
+const Entry* find_entry(const TileCfg& c, int mode, bool reflect) {
   for (const Entry& e : kEntries)
     if (e.cfg.r == c.r && e.cfg.wm == c.wm && e.cfg.wn == c.wn && e.cfg.pb == c.pb &&
-        e.cfg.cb == c.cb && e.cfg.kb == c.kb && e.cfg.ns == c.ns && e.mode == mode)
+        e.cfg.cb == c.cb && e.cfg.kb == c.kb && e.cfg.ns == c.ns && e.mode == mode &&
+        e.reflect == reflect)
       return &e;
   return nullptr;
 }
 
 }  // namespace
 
-bool igemm_has_config(const TileCfg& cfg, int mode) { return find_entry(cfg, mode) != nullptr; }
+bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect) {
+  return find_entry(cfg, mode, reflect) != nullptr;
+}
 
-int launch_igemm(const TileCfg& cfg, int mode, const IgemmArgs& args, int grid, void* stream) {
-  const Entry* e = find_entry(cfg, mode);
+int launch_igemm(const TileCfg& cfg, int mode, bool reflect, const IgemmArgs& args, int grid,
+                 void* stream) {
+  const Entry* e = find_entry(cfg, mode, reflect);
   if (!e) return -1;
   return e->fn(args, grid, stream);
 }

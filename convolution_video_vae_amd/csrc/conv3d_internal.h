@@ -102,9 +102,11 @@ struct GroupNormArgs {
 // the last temporal slice (kd = 2), the other slices zero.
 int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, int taps, void* stream);
 int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int a, int b, void* stream);
-// Returns -1 if no kernel is compiled for (cfg, mode).
-int launch_igemm(const TileCfg& cfg, int mode, const IgemmArgs& args, int grid, void* stream);
-bool igemm_has_config(const TileCfg& cfg, int mode);
+// Returns -1 if no kernel is compiled for (cfg, mode, reflect). reflect:
+// spatial reflect padding instead of zeros (pads of at most one).
+int launch_igemm(const TileCfg& cfg, int mode, bool reflect, const IgemmArgs& args, int grid,
+                 void* stream);
+bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect = false);
 int launch_reduce(const ReduceArgs& args, void* stream);
 int launch_queue_reset(unsigned* queue, void* stream);
 int launch_group_norm(const GroupNormArgs& args, void* stream);

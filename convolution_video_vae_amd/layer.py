@@ -44,7 +44,7 @@ class Conv3d:
                  bias: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
                  norm_silu: bool = False, residual: bool = False, residual_out: bool = False,
                  out_pad_lo=None, out_pad_hi=(0, 0, 0), history_frames: int = 0,
-                 cache_frames: int = 0):
+                 cache_frames: int = 0, pad_mode: int = 0):
         """out_pad_lo / out_pad_hi: write the output into the interior of a
         zero-bordered buffer (the history_frames planes before it are the
         caller's); cache_frames > 0: also keep the last output frames in a
@@ -54,7 +54,8 @@ class Conv3d:
         self.out_layout = layout if out_layout is None else out_layout
         self.x_shape = tuple(int(v) for v in x_shape)
         self.desc = make_desc(self.x_shape, self.cout, stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
-                              layout=layout, out_layout=self.out_layout, split_k=split_k)
+                              layout=layout, out_layout=self.out_layout, split_k=split_k,
+                              pad_mode=pad_mode)
         self.out_dhw = conv3d_output_dims(self.desc)
         n = self.x_shape[0]
         if self.out_layout == NDHWC:

@@ -100,7 +100,15 @@ typedef struct {
   int layout;      /* conv3d_layout of x */
   int out_layout;  /* conv3d_layout of y / residual / residual_out */
   int split_k;
+  int pad_mode;    /* conv3d_pad_mode of the H and W padding (time is always zero padded) */
 } conv3d_desc;
+
+/* Spatial padding: zeros, or reflection as the H3 encoder pads before each
+ * conv (FlyDSL issue, MiniMax H3 comment, the conv call site: spatial
+ * reflect pad, temporal causal zero pad): index -1 reads 1, index h reads
+ * h - 2. Reflect needs spatial pads of at most 1 (CONV3D_ERR_UNSUPPORTED
+ * above) and h, w >= 2 (CONV3D_ERR_SHAPE below). */
+typedef enum { CONV3D_PAD_ZERO = 0, CONV3D_PAD_REFLECT = 1 } conv3d_pad_mode;
 
 /* Optional fused post-operations; pass NULL to conv3d_fwd for a plain conv
  * (out = B(acc)). Pointers a flag does not use are ignored.

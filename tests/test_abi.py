@@ -33,8 +33,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_desc_struct_matches_header_layout():
-    # 6 ints, 3x3 ints, layout, out_layout, split_k = 18 ints
-    assert ctypes.sizeof(cv.conv3d_desc) == 18 * 4
+    # 6 ints, 3x3 ints, layout, out_layout, split_k, pad_mode = 19 ints
+    assert ctypes.sizeof(cv.conv3d_desc) == 19 * 4
     assert ctypes.sizeof(cv.conv3d_epilogue) == 8 + 4 * 8
 
 
@@ -299,3 +299,13 @@ def test_pack_weight_2d_rejected_calls():
     assert cv.lib().conv3d_pack_weight_2d(X, W, 0, 8, None) == 2
     assert cv.lib().conv3d_pack_weight_2d(X + 2, W, 8, 8, None) == 3
     assert cv.lib().conv3d_pack_weight_2d(X, X + 16, 8, 8, None) == 4
+
+
+def test_reflect_padding_checks():
+    d = small_desc(pad_mode=cv.PAD_REFLECT)
+    assert cv.conv3d_output_dims(d) == (3, 8, 8)
+    assert fwd(small_desc(pad_mode=2)) == 2
+    assert fwd(small_desc(pad_mode=cv.PAD_REFLECT, pad_lo=(2, 2, 1))) == 6   # spatial pad > 1
+    thin = cv.make_desc((1, 3, 1, 8, 32), 32, pad_lo=(2, 0, 1), pad_hi=(0, 0, 1), split_k=1,
+                        pad_mode=cv.PAD_REFLECT)
+    assert fwd(thin) == 2                                                    # h < 2

@@ -45,6 +45,7 @@ class Layer:
     residual: bool = False
     norm_silu: bool = False
     live_taps: int = 27         # taps that can see real pixels (T=1 causal: 9)
+    reflect: bool = False       # reflect spatial padding (the H3 encoder's own)
 
     @property
     def cin(self) -> int:
@@ -79,6 +80,9 @@ LAYERS = {
     "h3_l5_512to1024": Layer("h3_l5_512to1024", 2, (1, 5, 16, 16, 512), 1024, bias=True, **CAUSAL),
     # H3 L0: full-resolution 128->128, and its stride-(1,2,2) downsample.
     "h3_l0_128": Layer("h3_l0_128", 3, (1, 17, 256, 256, 128), 128, **CAUSAL),
+    # the same layer with H3's own spatial padding: reflect instead of zeros
+    "h3_l0_128_reflect": Layer("h3_l0_128_reflect", 3, (1, 17, 256, 256, 128), 128, reflect=True,
+                               **CAUSAL),
     "h3_l0_128_s122": Layer("h3_l0_128_s122", 3, (1, 17, 256, 256, 128), 128, stride=(1, 2, 2),
                             pad_lo=(2, 0, 0), pad_hi=(0, 1, 1)),
     # Wan encoder's pre-padded valid convs.
