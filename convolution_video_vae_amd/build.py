@@ -25,16 +25,26 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel: the implicit-GEMM file dominates)
+    and link the shared library."""
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for name in ("conv3d_kernels", "conv3d_igemm", "conv3d_norm"):
+    jobs, objs = [], []
+    for name in ("conv3d_igemm", "conv3d_kernels", "conv3d_norm"):
         obj = os.path.join(BUILD, name + ".o")
-        _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-c",
-              *DEVICE_FLAGS, "-Wall", os.path.join(CSRC, name + ".hip"), "-o", obj], verbose)
+        jobs.append([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-c",
+                     *DEVICE_FLAGS, "-Wall", os.path.join(CSRC, name + ".hip"), "-o", obj])
         objs.append(obj)
     aobj = os.path.join(BUILD, "conv3d_api.o")
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-c", "-Wall", "-Wextra",
-          os.path.join(CSRC, "conv3d_api.cpp"), "-o", aobj], verbose)
+    jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-c", "-Wall", "-Wextra",
+                 os.path.join(CSRC, "conv3d_api.cpp"), "-o", aobj])
+    procs = []
+    for cmd in jobs:
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        procs.append((cmd, subprocess.Popen(cmd)))
+    failed = [cmd for cmd, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, aobj, "-o", OUT + ".tmp"],
          verbose)
     os.replace(OUT + ".tmp", OUT)
