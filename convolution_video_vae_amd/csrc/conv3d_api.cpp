@@ -181,7 +181,8 @@ bool halo_ok(const Problem& pr, const TileCfg& c) {
          (long long)pr.n * pr.Do * pr.Ho < (1LL << 22);
 }
 
-const TileCfg kSlotStore[] = {{32, 2, 2, 8, 2, 0, -2}, {32, 4, 1, 4, 3, 0, -2}};
+const TileCfg kSlotStore[] = {{32, 2, 2, 8, 2, 0, -2}, {32, 4, 1, 4, 3, 0, -2},
+                               {32, 4, 1, 3, 5, 0, -2}};
 const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 9, -1}, {32, 4, 1, 4, 3, 9, -1}};
 const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 5, -1}, {32, 2, 2, 4, 3, 5, -1},
                                 {32, 4, 1, 4, 4, 9, -1}};
@@ -223,17 +224,22 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   // Fused-norm kernels hold the whole channel row of a pixel in one group.
   TileCfg norm_cfg = {0, 0, 0, 0, 0, 0, 0};
   if (norm) {
-    const TileCfg cands[] = {{32, 2, 2, 3, 5, 0, -2}, {16, 2, 2, 2, 10, 2, 0},
-                             {16, 2, 2, 2, 10, 1, 3}, {16, 4, 1, 2, 10, 1, 3}};
+    const TileCfg cands[] = {{32, 2, 2, 3, 5, 0, -2}, {32, 4, 1, 3, 5, 0, -2},
+                             {16, 2, 2, 2, 10, 2, 0}, {16, 2, 2, 2, 10, 1, 3},
+                             {16, 4, 1, 2, 10, 1, 3}};
     for (const TileCfg& c : cands)
       if (norm_cfg.r == 0 && c.bn() == pr.cout && halo_ok(pr, c) &&
           igemm_has_config(c, EPI_NORM, pr.reflect))
         norm_cfg = c;
   }
 
-  // Too few tiles to fill the CUs: cut K.
+  // Too few tiles to fill the CUs: cut K. (The slot kernel's tiles run so
+  // much faster than the plain kernel's split ones that a quarter of the CUs'
+  // worth of them is enough: measured on the 160-channel Wan layers, 102
+  // slot tiles take half the time of the split plan.)
   const long long store_tiles = ceil_div(pr.M, store_cfg.bm()) * ceil_div(pr.cout, store_cfg.bn());
-  const bool split = split_req > 1 || (split_req == 0 && store_tiles < kCUs / 2);
+  const long long min_tiles = store_cfg.ns == -2 ? kCUs / 4 : kCUs / 2;
+  const bool split = split_req > 1 || (split_req == 0 && store_tiles < min_tiles);
 
   // Development override of the tile (same kernels, another compiled
   // configuration): CONV3D_TILE="r,wm,wn,pb,cb,kb,ns".

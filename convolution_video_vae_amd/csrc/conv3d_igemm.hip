@@ -1822,6 +1822,8 @@ const Entry kEntries[] = {
     C32(2, 2, 8, 2, 0, -2, EPI_STORE),
     C32(4, 1, 4, 3, 0, -2, EPI_STORE),
     C32(2, 2, 3, 5, 0, -2, EPI_NORM),   // fused norm, Cout 320
+    C32(4, 1, 3, 5, 0, -2, EPI_STORE),  // 384 slots x 160 channels
+    C32(4, 1, 3, 5, 0, -2, EPI_NORM),   // fused norm, Cout 160
     // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0); kb = X DMA
     // instructions per wave and stage (the row-segment capacity).
     C32(4, 1, 4, 4, 9, -1, EPI_STORE),
@@ -1860,6 +1862,8 @@ const Entry kEntries[] = {
     R32(2, 2, 8, 2, 0, -2, EPI_STORE),
     R32(4, 1, 4, 3, 0, -2, EPI_STORE),
     R32(2, 2, 3, 5, 0, -2, EPI_NORM),
+    R32(4, 1, 3, 5, 0, -2, EPI_STORE),
+    R32(4, 1, 3, 5, 0, -2, EPI_NORM),
     R32(4, 1, 4, 4, 9, -1, EPI_STORE),
     R32(4, 1, 4, 3, 9, -1, EPI_STORE),
     R32(4, 1, 4, 4, 9, -1, EPI_PARTIAL),

@@ -43,7 +43,7 @@ def poisoned(shape):
 
 def run_gpu(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=None,
             residual=None, gamma=None, norm=False, split_k=0, want_residual_out=False,
-            layout=cv.NDHWC, out_layout=None, label=""):
+            layout=cv.NDHWC, out_layout=None, label="", reflect=False):
     """x (NDHWC or NCDHW per layout), w OIDHW: CPU tensors. Returns CPU outputs."""
     print(f"[gpu] {label} x={tuple(x.shape)} w={tuple(w.shape)} stride={stride} "
           f"pad={pad_lo}/{pad_hi} split_k={split_k} norm={norm}", flush=True)
@@ -54,7 +54,8 @@ def run_gpu(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=
     wp = torch.empty(cv.conv3d_packed_weight_bytes(cout, cin) // 2, dtype=torch.bfloat16, device="cuda")
     cv.conv3d_pack_weight(wd, wp, cout, cin)
     desc = cv.make_desc(tuple(x.shape), cout, stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
-                        layout=layout, out_layout=out_layout, split_k=split_k)
+                        layout=layout, out_layout=out_layout, split_k=split_k,
+                        pad_mode=cv.PAD_REFLECT if reflect else cv.PAD_ZERO)
     od = cv.conv3d_output_dims(desc)
     n = x.shape[0]
     yshape = (n,) + od + (cout,) if out_layout == cv.NDHWC else (n, cout) + od
@@ -75,8 +76,9 @@ def run_gpu(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=
 
 
 def run_oracle(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=None,
-               residual=None, gamma=None, norm=False, pixels=None):
-    return oracle.conv3d(bits(x), bits(w), stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
+               residual=None, gamma=None, norm=False, pixels=None, reflect=False):
+    conv = oracle.conv3d_reflect if reflect else oracle.conv3d
+    return conv(bits(x), bits(w), stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
                          bias=None if bias is None else bias.numpy(),
                          residual=None if residual is None else bits(residual),
                          gamma=None if gamma is None else bits(gamma), norm_silu=norm,
@@ -84,7 +86,8 @@ def run_oracle(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bi
 
 
 def geom(layer):
-    return dict(stride=layer.stride, pad_lo=layer.pad_lo, pad_hi=layer.pad_hi)
+    return dict(stride=layer.stride, pad_lo=layer.pad_lo, pad_hi=layer.pad_hi,
+                reflect=layer.reflect)
 
 
 # ------------------------------------------------------------------ pack / transpose
@@ -200,6 +203,8 @@ SLOT_CASES = HALO_CASES + [
     ("slot_wo8_many_rows", (1, 3, 20, 8, 64), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
     ("slot_batch3_valid96", (3, 4, 9, 37, 32), 96, (1, 1, 1), (0, 0, 0), (0, 0, 0)),
     ("slot_wo254_tile_straddles_rows", (1, 3, 5, 256, 64), 128, (1, 1, 1), (0, 1, 2), (0, 1, 0)),
+    ("slot_160_channel_tile", (1, 4, 10, 30, 32), 160, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
+    ("slot_320_two_channel_tiles", (1, 3, 8, 21, 64), 320, (1, 1, 1), (0, 0, 0), (0, 0, 0)),
 ]
 
 
@@ -280,6 +285,8 @@ SMALL = [
     ("wide_1024", "h3_l5_1024", (1, 3, 8, 8, 1024), 1024),
     ("wide_512to1024", "h3_l5_512to1024", (1, 5, 8, 8, 512), 1024),
     ("fused_160to320", "wan_fused_160to320", (1, 5, 14, 22, 160), 320),
+    ("fused_160to160", "wan_fused_160to320", (1, 5, 14, 22, 160), 160),
+    ("valid_160", "wan_valid_96", (1, 6, 20, 42, 64), 160),
 ]
 
 
@@ -384,3 +391,22 @@ def test_run_to_run_deterministic(name):
     a = run_gpu(t.x, t.w, label=name + "_a", **kw)
     b = run_gpu(t.x, t.w, label=name + "_b", **kw)
     np.testing.assert_array_equal(bits(a["y"]), bits(b["y"]))
+
+
+@pytest.mark.parametrize("kind", ["raw", "bias_residual", "norm"])
+def test_slot_160_channel_tile_random(kind):
+    """The 384-slot x 160-channel slot tile (one wave column holds the whole
+    160-channel row), without K split: raw, bias + residual, fused norm."""
+    L = workloads.LAYERS["wan_fused_160to320"]
+    t = workloads.make_tensors(L, x_shape=(1, 5, 12, 26, 160), cout=160)
+    kw = dict(bias=None if kind == "raw" else t.bias,
+              residual=None if kind == "raw" else t.residual,
+              gamma=t.gamma if kind == "norm" else None, norm=kind == "norm")
+    g = run_gpu(t.x, t.w, split_k=1, want_residual_out=kind != "raw", label="slot160_" + kind, **kw)
+    assert "pb=3 cb=5 kb=0 ns=-2 bm=384 bn=160" in g["plan"], g["plan"]
+    r = run_oracle(t.x, t.w, **kw)
+    diag = check(bits(g["y"]), r, fused=kind == "norm",
+                 gamma_bits=None if kind != "norm" else bits(t.gamma), what="slot160 " + kind)
+    assert diag["bit_identical"] > 0.99, diag
+    if kind != "raw":
+        check(bits(g["residual_out"]), dict(r, y=r["value"]), what="slot160 residual_out")
