@@ -1,5 +1,5 @@
-"""Streaming causal conv oracle: padded outputs, history planes and caches —
-TEST INFRASTRUCTURE ONLY.
+"""Streaming causal conv oracle: padded outputs, history planes, caches and
+the standalone post-operations — TEST INFRASTRUCTURE ONLY.
 
 What it computes. The cuDNN frontend page "Fused Conv3D + Bias + Residual +
 RMSNorm + SiLU" describes how a video VAE runs its causal convs on temporal
@@ -74,3 +74,51 @@ def pack_stream_input(chunk_ncthw, history=None, c_pad=16):
     padded = pad_output(xc, (2, 1, 1), (0, 1, 1), history=hc)
     cache = cache_tail(x, min(2, T + P), previous=history if P else None)
     return padded, cache
+
+
+def _b(v):
+    """B(): fp32 -> bf16 (nearest, ties to even) -> fp32."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    u = v.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _bits(v):
+    """bf16 bit patterns of fp32 values that are already bf16."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def norm_silu(raw, gamma, *, bias=None, residual=None, intermediates=False):
+    """The cuDNN page's post-operations ("Operation Contract") applied to an
+    existing bf16 tensor raw [..., C] (a raw conv output: conv = raw), as the
+    page's standalone normalization variant ("Standalone Normalization and
+    Padding Variant") does for channel counts above the fused tile:
+
+      main  = B(conv + bias)            (bias fp32 [C], optional)
+      value = B(main + residual)        (residual bf16, optional)
+      den   = max(sqrt(sum_c value^2), 1e-12)
+      y     = B(a / (1 + exp(-a))),  a = B(B(B(value / den) * sqrt(C)) * gamma)
+
+    fp32 arithmetic (IEEE, correctly rounded), the sum of squares in float64
+    rounded once to fp32, exp in float64 rounded once to fp32. Returns y bits,
+    or with intermediates a dict with y and value bits."""
+    conv = (np.asarray(raw, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    C = conv.shape[-1]
+    main = _b(conv + np.asarray(bias, dtype=np.float32)) if bias is not None else conv
+    value = main
+    if residual is not None:
+        res = (np.asarray(residual, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+        value = _b(main + res)
+    ss = np.sum(value.astype(np.float64) ** 2, axis=-1, keepdims=True)
+    den = np.maximum(np.sqrt(ss.astype(np.float32)), np.float32(1e-12))
+    g = (np.asarray(gamma, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    nrm = _b(value / den)
+    scl = _b(nrm * np.sqrt(np.float32(C)))
+    aff = _b(scl * g)
+    e = np.exp(-aff.astype(np.float64)).astype(np.float32)
+    y = _bits(_b(aff / (np.float32(1.0) + e)))
+    if not intermediates:
+        return y
+    return {"y": y, "value": _bits(value)}

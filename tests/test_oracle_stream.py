@@ -121,3 +121,38 @@ def test_cache_tail_and_history_edge_cases():
         pad_output(cur, (1, 1, 1), (0, 1, 1), history=prev)
     with pytest.raises(ValueError):
         pack_stream_input(bits(rng, (1, 12, 1, 2, 2)), c_pad=8)
+
+
+@pytest.mark.parametrize("with_bias,with_res", [(False, False), (True, False), (True, True)])
+def test_standalone_norm_silu_equals_the_fused_contract(with_bias, with_res):
+    """Post-operations on a raw conv output equal the oracle's own fused conv
+    (its C implementation of the same contract), bit for bit."""
+    from oracle.stream import norm_silu
+    rng = np.random.default_rng(26)
+    x = bits(rng, (1, 3, 4, 5, 32))
+    w = bits(rng, (64, 32, 3, 3, 3), 0.05)
+    b = (0.1 * rng.standard_normal(64)).astype(np.float32) if with_bias else None
+    res = bits(rng, (1, 3, 4, 5, 64)) if with_res else None
+    g = oracle.bf16_round(rng.uniform(0.5, 1.5, 64).astype(np.float32))
+    raw = oracle.conv3d(x, w, **CAUSAL)
+    fused = oracle.conv3d(x, w, bias=b, residual=res, gamma=g, norm_silu=True, intermediates=True,
+                          **CAUSAL)
+    got = norm_silu(raw, g, bias=b, residual=res, intermediates=True)
+    assert np.array_equal(got["y"], fused["y"])
+    assert np.array_equal(got["value"], fused["value"])
+
+
+def test_standalone_norm_silu_closed_forms():
+    """A pixel whose row is (v, 0, ..., 0): den = |v|, the first channel's
+    norm is sign(v), scaled by sqrt(C); C = 64, gamma 0.5 gives a = 4."""
+    from oracle.stream import norm_silu
+    raw = np.zeros((1, 64), np.uint16)
+    raw[0, 0] = oracle.bf16_round(np.float32([-3.0]))[0]
+    g = oracle.bf16_round(np.full(64, 0.5, np.float32))
+    y = oracle.bf16_to_f32(norm_silu(raw, g))
+    silu = lambda a: a / (1 + np.exp(-a))
+    # a = B(B(-1 * 8) * 0.5) = -4; B(silu(-4)) = B(-0.0719...) = -0.07177734375 (RNE by hand:
+    # -0.0719448 / 2^-11 = -147.34 -> -147 * 2^-11)
+    assert y[0, 0] == np.float32(-147 * 2.0 ** -11)
+    assert abs(y[0, 0] - silu(-4.0)) < 2.0 ** -11
+    assert np.all(y[0, 1:] == 0)
