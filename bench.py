@@ -157,6 +157,33 @@ def stream_cases(args, per_layer, wanted, torch, cv, workloads):
     for name, S in workloads.STREAM_LAYERS.items():
         if wanted is not None and name not in wanted:
             continue
+        if "norm" in S:
+            n, d, h, w, c = S["norm"]
+            rng = np.random.default_rng(np.random.SeedSequence([1008, 0]))
+            mk = lambda shape: torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(
+                torch.bfloat16).cuda()
+            x, res = mk((n, d, h, w, c)), mk((n, d, h, w, c))
+            prev = mk((n, S["history"], h, w, c))
+            bias = torch.from_numpy(rng.standard_normal(c, dtype=np.float32) * np.float32(0.3)).cuda()
+            gamma = torch.from_numpy(rng.uniform(0.5, 1.5, c).astype(np.float32)).to(torch.bfloat16).cuda()
+            y = torch.empty((n, d + 2, h + 2, w + 2, c), dtype=torch.bfloat16, device="cuda")
+            cache = torch.empty((n, S["cache"], h, w, c), dtype=torch.bfloat16, device="cuda")
+            rout = torch.empty_like(x)
+            epi = cv.make_epilogue(bias=bias, residual=res, gamma=gamma, residual_out=rout,
+                                   norm_silu=True)
+            op = cv.make_out_pad(S["pad_lo"], S["pad_hi"], S["history"], cache, S["cache"])
+
+            def step():
+                cv.conv3d_norm_silu(x, n, d, h, w, c, epi, op, prev, y)
+            nms, _ = time_case(step, max(5, args.steps), 3, torch)
+            moved = 2 * (3 * x.numel() + y.numel() + prev.numel() + cache.numel())
+            per_layer[name] = {
+                "us": round(nms * 1e3, 2), "gbs": round(moved / (nms * 1e-3) / 1e9, 1),
+                "pct_hbm": round(100 * moved / (nms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                "config": f"raw NDHWC {list(S['norm'])} + bias + residual -> L2 norm, SiLU; "
+                          f"written padded {list(y.shape)} with {S['history']} history frames "
+                          f"copied in, {S['cache']}-frame cache, value saved"}
+            continue
         if "video" in S:
             rng = np.random.default_rng(np.random.SeedSequence([1007, 0]))
             video = torch.from_numpy(rng.standard_normal(S["video"], dtype=np.float32)).to(

@@ -36,7 +36,7 @@ EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_d
             "conv3d_workspace_bytes", "conv3d_fwd", "conv3d_transpose", "conv3d_status_str",
             "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm",
             "conv3d_padded_workspace_bytes", "conv3d_fwd_padded", "conv3d_stream_pack_input",
-            "conv3d_pack_weight_2d")
+            "conv3d_pack_weight_2d", "conv3d_norm_silu")
 
 
 class Conv3dError(RuntimeError):
@@ -111,6 +111,8 @@ def lib():
         L.conv3d_stream_pack_input.restype = i
         L.conv3d_stream_pack_input.argtypes = [vp, ctypes.POINTER(ctypes.c_longlong * 5), i, i, i, i,
                                                i, vp, i, vp, i, vp, i, vp]
+        L.conv3d_norm_silu.restype = i
+        L.conv3d_norm_silu.argtypes = [vp, i, i, i, i, i, pe, po, vp, vp, vp]
         pg = ctypes.POINTER(conv3d_group_norm_desc)
         L.conv3d_group_norm_workspace_bytes.restype = i
         L.conv3d_group_norm_workspace_bytes.argtypes = [pg, ctypes.POINTER(sz)]
@@ -279,3 +281,10 @@ def conv3d_stream_pack_input(chunk, strides: Sequence[int], n: int, c: int, t: i
                                           _ptr(history), history_frames, _ptr(padded), c_pad,
                                           _ptr(cache), cache_frames, _stream(stream)),
            "conv3d_stream_pack_input")
+
+
+def conv3d_norm_silu(x, n: int, d: int, h: int, w: int, c: int, epi: conv3d_epilogue,
+                     out_pad: Optional[conv3d_out_pad], previous, y, stream=None) -> None:
+    _check(lib().conv3d_norm_silu(_ptr(x), n, d, h, w, c, ctypes.byref(epi),
+                                  ctypes.byref(out_pad) if out_pad else None, _ptr(previous), _ptr(y),
+                                  _stream(stream)), "conv3d_norm_silu")

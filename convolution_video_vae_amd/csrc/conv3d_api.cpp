@@ -661,6 +661,83 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   return CONV3D_OK;
 }
 
+conv3d_status conv3d_norm_silu(const void* x, int n, int d, int h, int w, int c,
+                               const conv3d_epilogue* epi, const conv3d_out_pad* op,
+                               const void* previous, void* y, void* stream) {
+  if (!x || !y || !epi) return CONV3D_ERR_NULL;
+  if (n <= 0 || d <= 0 || h <= 0 || w <= 0 || c <= 0) return CONV3D_ERR_SHAPE;
+  const unsigned f = epi->flags;
+  if (!(f & F_NORM) || (f & ~(F_BIAS | F_RESIDUAL | F_NORM | F_RESIDUAL_OUT)))
+    return CONV3D_ERR_UNSUPPORTED;
+  if (!epi->gamma || ((f & F_BIAS) && !epi->bias) || ((f & F_RESIDUAL) && !epi->residual) ||
+      ((f & F_RESIDUAL_OUT) && !epi->residual_out))
+    return CONV3D_ERR_NULL;
+  if (c % 8) return CONV3D_ERR_ALIGN;
+  if (c > 2048) return CONV3D_ERR_UNSUPPORTED;
+  const long long M = (long long)n * d * h * w;
+  const long long bytes = M * c * 2;
+  if (bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(epi->gamma) ||
+      ((f & F_RESIDUAL) && !aligned16(epi->residual)) ||
+      ((f & F_RESIDUAL_OUT) && !aligned16(epi->residual_out)) ||
+      ((f & F_BIAS) && ((uintptr_t)epi->bias & 3)))
+    return CONV3D_ERR_ALIGN;
+  // placement: the conv's padded-output rules with (Do, Ho, Wo) = (d, h, w)
+  Problem pr;
+  memset(&pr, 0, sizeof pr);
+  pr.n = n; pr.Do = d; pr.Ho = h; pr.Wo = w; pr.cout = c;
+  pr.out_layout = CONV3D_NDHWC;
+  PadPlan pp;
+  conv3d_status st = check_out_pad(op, pr, &pp);
+  if (st != CONV3D_OK) return st;
+  if (previous) {
+    if (!op || op->history_frames < 1) return CONV3D_ERR_SHAPE;
+    if (!aligned16(previous)) return CONV3D_ERR_ALIGN;
+    if (op->cache && op->cache_frames - std::min(op->cache_frames, d) > op->history_frames)
+      return CONV3D_ERR_SHAPE;   // older cache frames must come from previous
+  }
+  const long long y_bytes = pp.on ? pp.y_bytes : bytes;
+  const Range rx = range_of(x, bytes), ry = range_of(y, y_bytes);
+  const Range rr = (f & F_RESIDUAL) ? range_of(epi->residual, bytes) : Range();
+  const Range ro = (f & F_RESIDUAL_OUT) ? range_of(epi->residual_out, bytes) : Range();
+  const Range rg = range_of(epi->gamma, 2LL * c);
+  const Range rb = (f & F_BIAS) ? range_of(epi->bias, 4LL * c) : Range();
+  const Range rp = previous ? range_of(previous, (long long)n * op->history_frames * h * w * c * 2)
+                            : Range();
+  const Range rc = pp.a.cache ? range_of(pp.a.cache, (long long)n * pp.a.cache_frames * h * w * c * 2)
+                              : Range();
+  const Range outs[] = {ry, ro, rc};
+  for (const Range& o : outs)
+    for (const Range& i : {rx, rr, rg, rb, rp})
+      if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
+  if (overlaps(ry, ro) || overlaps(ry, rc) || overlaps(ro, rc)) return CONV3D_ERR_OVERLAP;
+
+  NormSiluArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = (const uint16_t*)x;
+  a.bias = (f & F_BIAS) ? epi->bias : nullptr;
+  a.residual = (f & F_RESIDUAL) ? (const uint16_t*)epi->residual : nullptr;
+  a.gamma = (const uint16_t*)epi->gamma;
+  a.residual_out = (f & F_RESIDUAL_OUT) ? (uint16_t*)epi->residual_out : nullptr;
+  a.y = (uint16_t*)y;
+  a.flags = f;
+  a.M = (int)M;
+  a.C = c;
+  a.sqrt_c = sqrtf((float)c);
+  if (pp.on) {
+    a.geo = pp.a;
+    a.geo.previous = (const uint16_t*)previous;
+  }
+  if (launch_norm_silu(a, stream)) return CONV3D_ERR_HIP;
+  if (pp.on) {
+    PlaceArgs pa = a.geo;
+    pa.y0 = nullptr;
+    pa.y = (uint16_t*)y;
+    if (launch_place(pa, stream)) return CONV3D_ERR_HIP;
+  }
+  return CONV3D_OK;
+}
+
 conv3d_status conv3d_stream_pack_input(const void* chunk, const long long strides[5], int n,
                                        int c, int t, int h, int w, const void* history,
                                        int history_frames, void* padded, int c_pad, void* cache,

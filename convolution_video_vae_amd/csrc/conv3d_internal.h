@@ -114,14 +114,36 @@ int launch_group_norm(const GroupNormArgs& args, void* stream);
 // y [N][Dy][Hy][Wy][Cout] at (pt, ph, pw); zeros elsewhere except the
 // interiors of the hist planes before pt; the last cache_k frames also into
 // cache [N][cache_frames][Ho][Wo][Cout] at its last frames (cache may be null).
+// y0 may be null (the interior is written by someone else). previous, when
+// not null, holds hist frames [N][hist][Ho][Wo][Cout] that are copied into
+// the history planes' interiors and, for the cache's older frames, into the
+// cache.
 struct PlaceArgs {
   const uint16_t* y0;
   uint16_t* y;
   uint16_t* cache;
+  const uint16_t* previous;
   int n, cout, Do, Ho, Wo, Dy, Hy, Wy, pt, ph, pw, hist;
   int cache_frames, cache_k;
 };
 int launch_place(const PlaceArgs& args, void* stream);
+
+// Standalone post-operations (bias -> residual -> L2 norm x sqrt(C) x gamma
+// -> SiLU) on an existing bf16 tensor x [M][C], written to y as geo places
+// it (geo.y0 unused; padded and cache only when geo.Dy > 0).
+struct NormSiluArgs {
+  const uint16_t* x;
+  const float* bias;
+  const uint16_t* residual;
+  const uint16_t* gamma;
+  uint16_t* residual_out;
+  uint16_t* y;
+  unsigned flags;
+  int M, C;
+  float sqrt_c;
+  PlaceArgs geo;
+};
+int launch_norm_silu(const NormSiluArgs& args, void* stream);
 // First layer of a streaming causal conv: a strided channels-first chunk and
 // up to two raw history frames -> padded NDHWC input and the raw-frame cache.
 struct StreamPackArgs {

@@ -194,33 +194,55 @@ __global__ __launch_bounds__(256) void reduce_norm_kernel(ReduceArgs a) {
 // of y: an output row is one contiguous copy plus its two border runs.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void place_kernel(PlaceArgs a) {
+  const long long rows = (long long)a.n * a.Dy * a.Hy;
+  const int V = a.cout / 8;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  if (blockIdx.x >= rows) {
+    // the cache's older frames, from previous: row (n, f, h), f < cache_frames - cache_k
+    const int old = a.cache_frames - a.cache_k;
+    const long long r = blockIdx.x - rows;
+    const int h = (int)(r % a.Ho);
+    const int f = (int)((r / a.Ho) % old);
+    const long long n = r / ((long long)a.Ho * old);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+        a.previous + ((n * a.hist + (a.hist - old) + f) * a.Ho + h) * a.Wo * a.cout);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(
+        a.cache + ((n * a.cache_frames + f) * a.Ho + h) * a.Wo * a.cout);
+    for (int i = threadIdx.x; i < a.Wo * V; i += blockDim.x) dst[i] = src[i];
+    return;
+  }
   const long long row = blockIdx.x;
   const int hh = (int)(row % a.Hy);
   const long long nt = row / a.Hy;
   const int t = (int)(nt % a.Dy);
   const long long n = nt / a.Dy;
-  const int V = a.cout / 8;
   u32x4_t* yr = reinterpret_cast<u32x4_t*>(a.y + row * a.Wy * a.cout);
-  const u32x4_t z = {0u, 0u, 0u, 0u};
   const int d = t - a.pt, h = hh - a.ph;
   const bool rowin = h >= 0 && h < a.Ho;
   if (d >= 0 && d < a.Do && rowin) {
-    const u32x4_t* src =
-        reinterpret_cast<const u32x4_t*>(a.y0 + ((n * a.Do + d) * a.Ho + h) * a.Wo * a.cout);
-    u32x4_t* cr = nullptr;
-    if (a.cache && d >= a.Do - a.cache_k)
-      cr = reinterpret_cast<u32x4_t*>(
-          a.cache + ((n * a.cache_frames + (a.cache_frames - a.Do) + d) * a.Ho + h) * a.Wo * a.cout);
-    const int inner = a.Wo * V;
-    for (int i = threadIdx.x; i < inner; i += blockDim.x) {
-      const u32x4_t v = src[i];
-      yr[a.pw * V + i] = v;
-      if (cr) cr[i] = v;
+    if (a.y0) {
+      const u32x4_t* src =
+          reinterpret_cast<const u32x4_t*>(a.y0 + ((n * a.Do + d) * a.Ho + h) * a.Wo * a.cout);
+      u32x4_t* cr = nullptr;
+      if (a.cache && d >= a.Do - a.cache_k)
+        cr = reinterpret_cast<u32x4_t*>(
+            a.cache + ((n * a.cache_frames + (a.cache_frames - a.Do) + d) * a.Ho + h) * a.Wo * a.cout);
+      const int inner = a.Wo * V;
+      for (int i = threadIdx.x; i < inner; i += blockDim.x) {
+        const u32x4_t v = src[i];
+        yr[a.pw * V + i] = v;
+        if (cr) cr[i] = v;
+      }
     }
   } else if (d < -a.hist || d >= a.Do || !rowin) {
     // a zero plane (before the history, or after the output) or a border row
     for (int i = threadIdx.x; i < a.Wy * V; i += blockDim.x) yr[i] = z;
     return;
+  } else if (a.previous) {
+    // a history row: copy the caller's previous frame into its interior
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+        a.previous + ((n * a.hist + (d + a.hist)) * a.Ho + h) * a.Wo * a.cout);
+    for (int i = threadIdx.x; i < a.Wo * V; i += blockDim.x) yr[a.pw * V + i] = src[i];
   }
   // left and right border columns of an output or history row
   const int lead = a.pw * V, tail = (a.Wy - a.pw - a.Wo) * V;
@@ -229,8 +251,95 @@ __global__ __launch_bounds__(256) void place_kernel(PlaceArgs a) {
 }
 
 int launch_place(const PlaceArgs& a, void* stream) {
-  const long long rows = (long long)a.n * a.Dy * a.Hy;
+  long long rows = (long long)a.n * a.Dy * a.Hy;
+  if (a.previous && a.cache) rows += (long long)a.n * (a.cache_frames - a.cache_k) * a.Ho;
+  if (rows == 0) return 0;
   hipLaunchKernelGGL(place_kernel, dim3((unsigned)rows), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Standalone post-operations: one wave per pixel, each lane up to 4 groups
+// of 8 channels (C <= 2048), the same arithmetic as the fused epilogue with
+// conv = x.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void norm_silu_kernel(NormSiluArgs a) {
+  constexpr int MAXG = 4;
+  const int lane = threadIdx.x & 63;
+  const int ngroups = a.C / 8;
+  const long long waves = (long long)gridDim.x * (blockDim.x / 64);
+  const PlaceArgs& g = a.geo;
+  for (long long m = (long long)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); m < a.M;
+       m += waves) {
+    float v[MAXG][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < MAXG; ++q) {
+      const int gidx = lane + 64 * q;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[q][e] = 0.f;
+      if (gidx >= ngroups) continue;
+      const int c0 = gidx * 8;
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(a.x + m * a.C + c0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[q][e] = lane_bf(xv, e);
+      if (a.flags & F_BIAS) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][e] = rbf(v[q][e] + a.bias[c0 + e]);
+      }
+      if (a.flags & F_RESIDUAL) {
+        const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.residual + m * a.C + c0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][e] = rbf(v[q][e] + lane_bf(rv, e));
+      }
+      if (a.flags & F_RESIDUAL_OUT) {
+        const u32x4_t ov = {pack2(v[q][0], v[q][1]), pack2(v[q][2], v[q][3]),
+                            pack2(v[q][4], v[q][5]), pack2(v[q][6], v[q][7])};
+        *reinterpret_cast<u32x4_t*>(a.residual_out + m * a.C + c0) = ov;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[q][e] * v[q][e];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float den = fmaxf(sqrtf(ss), 1e-12f);
+    // where the pixel goes: y (padded when geo.Dy > 0) and maybe the cache
+    long long yp = m, cp = -1;
+    if (g.Dy > 0) {
+      const int w = (int)(m % g.Wo);
+      const long long r = m / g.Wo;
+      const int h = (int)(r % g.Ho);
+      const long long nd = r / g.Ho;
+      const int d = (int)(nd % g.Do);
+      const long long n = nd / g.Do;
+      yp = ((n * g.Dy + d + g.pt) * g.Hy + h + g.ph) * g.Wy + w + g.pw;
+      if (g.cache && d >= g.Do - g.cache_k)
+        cp = ((n * g.cache_frames + (g.cache_frames - g.Do) + d) * g.Ho + h) * g.Wo + w;
+    }
+#pragma unroll
+    for (int q = 0; q < MAXG; ++q) {
+      const int gidx = lane + 64 * q;
+      if (gidx >= ngroups) continue;
+      const int c0 = gidx * 8;
+      const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.gamma + c0);
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float nrm = rbf(v[q][e] / den);
+        const float scl = rbf(nrm * a.sqrt_c);
+        const float aff = rbf(scl * lane_bf(gv, e));
+        o[e] = rbf(aff / (1.0f + expf(-aff)));
+      }
+      const u32x4_t ov = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+      *reinterpret_cast<u32x4_t*>(a.y + yp * a.C + c0) = ov;
+      if (cp >= 0) *reinterpret_cast<u32x4_t*>(g.cache + cp * a.C + c0) = ov;
+    }
+  }
+}
+
+int launch_norm_silu(const NormSiluArgs& a, void* stream) {
+  const long long blocks = std::min<long long>((a.M + 3) / 4, 8192);
+  hipLaunchKernelGGL(norm_silu_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

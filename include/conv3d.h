@@ -223,6 +223,23 @@ conv3d_status conv3d_stream_pack_input(const void* chunk, const long long stride
                                        int history_frames, void* padded, int c_pad, void* cache,
                                        int cache_frames, void* stream);
 
+/* Standalone post-operations on an existing bf16 tensor (cuDNN page,
+ * "Standalone Normalization and Padding Variant": for output channel counts
+ * above the fused tile, a raw conv is followed by this). x NDHWC
+ * [n][d][h][w][c] is taken as `conv` of the contract (see CONV3D_EPI_*):
+ *   main = B(x + bias) (CONV3D_EPI_BIAS), value = B(main + residual)
+ *   (CONV3D_EPI_RESIDUAL), y = the L2 norm x sqrt(c) x gamma -> SiLU of value
+ * (CONV3D_EPI_L2NORM_SILU must be set; gamma bf16 [c]). CONV3D_EPI_RESIDUAL_OUT
+ * writes value to residual_out, with or without a residual. y is written as
+ * out_pad places it (NULL: [n][d][h][w][c]); with previous != NULL (bf16
+ * NDHWC [n][out_pad->history_frames][h][w][c], the previous chunk's last
+ * activated frames) the history planes' interiors and the cache's older
+ * frames are copied from it. c % 8 == 0, c <= 2048; every pointer 16-byte
+ * aligned except bias (4); outputs must not overlap inputs or each other. */
+conv3d_status conv3d_norm_silu(const void* x, int n, int d, int h, int w, int c,
+                               const conv3d_epilogue* epi, const conv3d_out_pad* out_pad,
+                               const void* previous, void* y, void* stream);
+
 /* Layout change at a network boundary, bf16, exact:
  *   src_layout = CONV3D_NCDHW:  [n][c][d][h][w] -> [n][d][h][w][c]
  *   src_layout = CONV3D_NDHWC:  [n][d][h][w][c] -> [n][c][d][h][w]

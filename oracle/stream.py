@@ -103,7 +103,8 @@ def norm_silu(raw, gamma, *, bias=None, residual=None, intermediates=False):
 
     fp32 arithmetic (IEEE, correctly rounded), the sum of squares in float64
     rounded once to fp32, exp in float64 rounded once to fp32. Returns y bits,
-    or with intermediates a dict with y and value bits."""
+    or with intermediates a dict of y, conv, main, value, affine (bits) and
+    den (fp32)."""
     conv = (np.asarray(raw, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
     C = conv.shape[-1]
     main = _b(conv + np.asarray(bias, dtype=np.float32)) if bias is not None else conv
@@ -121,4 +122,5 @@ def norm_silu(raw, gamma, *, bias=None, residual=None, intermediates=False):
     y = _bits(_b(aff / (np.float32(1.0) + e)))
     if not intermediates:
         return y
-    return {"y": y, "value": _bits(value)}
+    return {"y": y, "conv": _bits(conv), "main": _bits(main), "value": _bits(value),
+            "affine": _bits(aff), "den": den[..., 0].astype(np.float32)}

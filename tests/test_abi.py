@@ -309,3 +309,29 @@ def test_reflect_padding_checks():
     thin = cv.make_desc((1, 3, 1, 8, 32), 32, pad_lo=(2, 0, 1), pad_hi=(0, 0, 1), split_k=1,
                         pad_mode=cv.PAD_REFLECT)
     assert fwd(thin) == 2                                                    # h < 2
+
+
+def norm_silu_call(epi, x=X, y=Y, op=None, prev=None, c=64, shape=(1, 3, 8, 8)):
+    n, d, h, w = shape
+    return cv.lib().conv3d_norm_silu(x, n, d, h, w, c, ctypes.byref(epi) if epi else None,
+                                     ctypes.byref(op) if op else None, prev, y, None)
+
+
+def test_norm_silu_rejected_calls():
+    ok = cv.conv3d_epilogue(cv.EPI_L2NORM_SILU, None, None, G, None)
+    assert norm_silu_call(None) == 1
+    assert norm_silu_call(ok, x=None) == 1
+    assert norm_silu_call(cv.conv3d_epilogue(cv.EPI_L2NORM_SILU, None, None, None, None)) == 1
+    assert norm_silu_call(cv.conv3d_epilogue(cv.EPI_BIAS, B, None, G, None)) == 6   # no norm flag
+    assert norm_silu_call(cv.conv3d_epilogue(cv.EPI_L2NORM_SILU | 64, None, None, G, None)) == 6
+    assert norm_silu_call(ok, c=4100) == 3                                          # c % 8
+    assert norm_silu_call(ok, c=4096) == 6                                          # c > 2048
+    assert norm_silu_call(ok, c=60) == 3
+    assert norm_silu_call(ok, y=Y + 8) == 3
+    assert norm_silu_call(ok, prev=R) == 2                                          # no history planes
+    op = cv.make_out_pad((2, 1, 1), (0, 1, 1), 1, None, 0)
+    assert norm_silu_call(ok, op=op, prev=R + 8) == 3
+    op2 = cv.make_out_pad((2, 1, 1), (0, 1, 1), 1, WS, 5)                           # cache 5 > d + 1
+    assert norm_silu_call(ok, op=op2) == 2
+    assert norm_silu_call(ok, y=X + 64) == 4                                        # y inside x
+    assert norm_silu_call(ok, op=op, prev=Y + 256) == 4                             # previous inside y

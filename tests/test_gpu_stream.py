@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import convolution_video_vae_amd as cv
 import workloads
 from convolution_video_vae_amd.layer import Conv3d, stream_pack_input
 from oracle.stream import cache_tail, pack_stream_input, pad_output
@@ -205,3 +206,83 @@ def test_streamed_chain_mechanics():
         acache = bits(cache_d)
         xcache = cache_tail(bits(x_all[:, t0:t0 + t]), min(2, t0 + t), previous=xcache)
         t0 += t
+
+
+def _norm_inputs(rng, shape, c):
+    raw = from_bits(oracle.bf16_round(rng.standard_normal(int(np.prod(shape)) * c).astype(np.float32))
+                    .reshape(shape + (c,)))
+    bias = torch.from_numpy((0.1 * rng.standard_normal(c)).astype(np.float32))
+    res = from_bits(oracle.bf16_round(rng.standard_normal(int(np.prod(shape)) * c).astype(np.float32))
+                    .reshape(shape + (c,)))
+    gamma = from_bits(oracle.bf16_round(rng.uniform(0.5, 1.5, c).astype(np.float32)))
+    return raw, bias, res, gamma
+
+
+@pytest.mark.parametrize("P", [1, 2])
+def test_standalone_norm_silu_padded_with_history(P):
+    """C640 (above the fused tile): raw conv output -> bias, residual, L2 norm,
+    SiLU, written padded, history planes and the cache's older frames copied
+    from the previous chunk's cache, residual_out saved."""
+    from oracle.stream import norm_silu
+    rng = np.random.default_rng(40 + P)
+    n, d, h, w, c = 1, 3, 6, 10, 640
+    raw, bias, res, gamma = _norm_inputs(rng, (n, d, h, w), c)
+    prev = from_bits(noise_bits(rng, (n, P, h, w, c)))
+    cf = 2
+    y = from_bits(noise_bits(rng, (n, d + 2, h + 2, w + 2, c))).cuda()
+    cache = from_bits(noise_bits(rng, (n, cf, h, w, c))).cuda()
+    rout = torch.empty((n, d, h, w, c), dtype=torch.bfloat16, device="cuda")
+    # (the epilogue holds raw addresses: keep every device tensor referenced)
+    bd, rd, gd, xd, pd = bias.cuda(), res.cuda(), gamma.cuda(), raw.cuda(), prev.cuda()
+    epi = cv.make_epilogue(bias=bd, residual=rd, gamma=gd, residual_out=rout, norm_silu=True)
+    op = cv.make_out_pad((2, 1, 1), (0, 1, 1), P, cache, cf)
+    print(f"[stream] norm_silu C{c} P={P}", flush=True)
+    cv.conv3d_norm_silu(xd, n, d, h, w, c, epi, op, pd, y)
+    torch.cuda.synchronize()
+    ref = norm_silu(bits(raw), bits(gamma), bias=bias.numpy(), residual=bits(res), intermediates=True)
+    got = bits(y)
+    check(got[:, 2:, 1:-1, 1:-1], ref, fused=True, gamma_bits=bits(gamma), what=f"norm_silu P={P}")
+    assert np.array_equal(bits(rout), ref["value"])
+    want = pad_output(np.zeros((n, d, h, w, c), np.uint16), (2, 1, 1), (0, 1, 1), history=bits(prev))
+    mask = np.ones(got.shape, bool)
+    mask[:, 2:, 1:-1, 1:-1] = False
+    assert np.array_equal(got[mask], want[mask])                     # zeros and history
+    assert np.array_equal(bits(cache), got[:, -2:, 1:-1, 1:-1])      # d >= 2: current frames
+
+
+def test_standalone_norm_silu_contiguous_and_saved_value():
+    from oracle.stream import norm_silu
+    rng = np.random.default_rng(44)
+    n, d, h, w, c = 2, 2, 5, 7, 320
+    raw, bias, _, gamma = _norm_inputs(rng, (n, d, h, w), c)
+    y = torch.empty((n, d, h, w, c), dtype=torch.bfloat16, device="cuda")
+    saved = torch.empty_like(y)
+    bd, gd, xd = bias.cuda(), gamma.cuda(), raw.cuda()
+    epi = cv.make_epilogue(bias=bd, gamma=gd, residual_out=saved, norm_silu=True)
+    cv.conv3d_norm_silu(xd, n, d, h, w, c, epi, None, None, y)
+    torch.cuda.synchronize()
+    ref = norm_silu(bits(raw), bits(gamma), bias=bias.numpy(), intermediates=True)
+    check(bits(y), ref, fused=True, gamma_bits=bits(gamma), what="norm_silu contiguous")
+    assert np.array_equal(bits(saved), ref["value"])                  # save_input: B(x + bias)
+
+
+def test_standalone_norm_silu_one_frame_cache_keeps_previous():
+    """d = 1 current frame, cache of 2: the older cache frame is the last
+    previous frame (copied by the call), the newer one the current output."""
+    from oracle.stream import norm_silu
+    rng = np.random.default_rng(45)
+    n, d, h, w, c = 1, 1, 4, 6, 640
+    raw, _, _, gamma = _norm_inputs(rng, (n, d, h, w), c)
+    prev = from_bits(noise_bits(rng, (n, 2, h, w, c)))
+    y = torch.empty((n, 3, h + 2, w + 2, c), dtype=torch.bfloat16, device="cuda")
+    cache = torch.empty((n, 2, h, w, c), dtype=torch.bfloat16, device="cuda")
+    gd, xd, pd = gamma.cuda(), raw.cuda(), prev.cuda()
+    epi = cv.make_epilogue(gamma=gd, norm_silu=True)
+    cv.conv3d_norm_silu(xd, n, d, h, w, c, epi, cv.make_out_pad((2, 1, 1), (0, 1, 1), 2, cache, 2),
+                        pd, y)
+    torch.cuda.synchronize()
+    got_cache = bits(cache)
+    assert np.array_equal(got_cache[:, 0], bits(prev)[:, 1])
+    assert np.array_equal(got_cache[:, 1], bits(y)[:, 2, 1:-1, 1:-1])
+    ref = norm_silu(bits(raw), bits(gamma), intermediates=True)
+    check(bits(y)[:, 2:, 1:-1, 1:-1], ref, fused=True, gamma_bits=bits(gamma), what="one frame")

@@ -233,4 +233,9 @@ STREAM_LAYERS = {
     # stride-2 conv)
     "wan_bias_res_pad_160to160": dict(x=(1, 7, 66, 122, 160), cout=160, pad_lo=(0, 0, 0),
                                       pad_hi=(0, 1, 1)),
+    # standalone post-operations above the fused tile (640 channels, a
+    # quarter of the 64 x 120 level): bias, residual, L2 norm, SiLU, written
+    # padded with two history frames copied in and a two-frame cache
+    "wan_norm_silu_pad_640": dict(norm=(1, 5, 16, 30, 640), pad_lo=(2, 1, 1), pad_hi=(0, 1, 1),
+                                  history=2, cache=2),
 }
