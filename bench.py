@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published 2.5 PFLOP/s)
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (published 5.0 PFLOP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 # HBM traffic of the headline layer's main kernel, from rocprofv3 --pmc
@@ -75,7 +76,8 @@ def describe(L):
             f"out {list(L.out_shape())}"
             + (", fp32 bias" if L.bias else "") + (", residual" if L.residual else "")
             + (", L2-norm*sqrt(C)*gamma+SiLU epilogue" if L.norm_silu else "")
-            + (", reflect spatial padding" if L.reflect else ""))
+            + (", reflect spatial padding" if L.reflect else "")
+            + (", e4m3fn x and w (peak 5 PFLOP/s)" if L.fp8 else ""))
 
 
 class Case:
@@ -87,6 +89,9 @@ class Case:
         t = workloads.make_tensors(L)
         self.L = L
         lay = cv.NDHWC if layout is None else layout
+        if L.fp8:   # e4m3fn operands: the same seeded tensors, cast
+            t.x = t.x.float().to(torch.float8_e4m3fn)
+            t.w = t.w.float().to(torch.float8_e4m3fn)
         x = t.x.cuda()
         if lay == cv.NCDHW:
             x = x.permute(0, 4, 1, 2, 3).contiguous()
@@ -295,11 +300,12 @@ def main():
                 c = Case(L, torch, cv, layout=lay)
                 lms, _ = time_case(c, max(5, args.steps), 3, torch)
                 lt = L.flops(live=True) / (lms * 1e-3) / 1e12
+                peak = PEAK_FP8_TFLOPS if L.fp8 else PEAK_BF16_TFLOPS
                 io = (L.m * L.cin * 0 + np.prod(L.x_shape) + L.m * L.cout
                       + 27 * L.cin * L.cout + (L.m * L.cout if L.residual else 0)) * 2
                 per_layer[vname] = {
                     "us": round(lms * 1e3, 2), "tflops": round(lt, 2),
-                    "pct_peak": round(100 * lt / PEAK_BF16_TFLOPS, 2),
+                    "pct_peak": round(100 * lt / peak, 2),
                     "algorithmic_gbs": round(io / (lms * 1e-3) / 1e9, 1),
                     "gflop": round(L.flops(live=True) / 1e9, 3), "plan": c.plan}
                 del c

@@ -23,6 +23,9 @@ NDHWC = 1
 PAD_ZERO = 0
 PAD_REFLECT = 1
 
+BF16 = 0
+FP8_E4M3 = 1
+
 EPI_BIAS = 1
 EPI_RESIDUAL = 2
 EPI_L2NORM_SILU = 4
@@ -36,7 +39,8 @@ EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_d
             "conv3d_workspace_bytes", "conv3d_fwd", "conv3d_transpose", "conv3d_status_str",
             "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm",
             "conv3d_padded_workspace_bytes", "conv3d_fwd_padded", "conv3d_stream_pack_input",
-            "conv3d_pack_weight_2d", "conv3d_norm_silu")
+            "conv3d_pack_weight_2d", "conv3d_norm_silu", "conv3d_packed_weight_bytes_fp8",
+            "conv3d_pack_weight_fp8")
 
 
 class Conv3dError(RuntimeError):
@@ -51,7 +55,7 @@ class conv3d_desc(ctypes.Structure):
                 ("stride", ctypes.c_int * 3), ("pad_lo", ctypes.c_int * 3),
                 ("pad_hi", ctypes.c_int * 3), ("layout", ctypes.c_int),
                 ("out_layout", ctypes.c_int), ("split_k", ctypes.c_int),
-                ("pad_mode", ctypes.c_int)]
+                ("pad_mode", ctypes.c_int), ("dtype", ctypes.c_int)]
 
 
 class conv3d_epilogue(ctypes.Structure):
@@ -89,6 +93,10 @@ def lib():
         L.conv3d_packed_weight_bytes.argtypes = [i, i]
         L.conv3d_pack_weight.restype = i
         L.conv3d_pack_weight.argtypes = [vp, vp, i, i, vp]
+        L.conv3d_packed_weight_bytes_fp8.restype = sz
+        L.conv3d_packed_weight_bytes_fp8.argtypes = [i, i]
+        L.conv3d_pack_weight_fp8.restype = i
+        L.conv3d_pack_weight_fp8.argtypes = [vp, vp, i, i, vp]
         L.conv3d_pack_weight_2d.restype = i
         L.conv3d_pack_weight_2d.argtypes = [vp, vp, i, i, vp]
         L.conv3d_output_dims.restype = i
@@ -148,7 +156,7 @@ def _stream(stream) -> Optional[int]:
 
 def make_desc(x_shape: Sequence[int], cout: int, *, stride=(1, 1, 1), pad_lo=(0, 0, 0),
               pad_hi=(0, 0, 0), layout=NDHWC, out_layout=None, split_k=0,
-              pad_mode=PAD_ZERO) -> conv3d_desc:
+              pad_mode=PAD_ZERO, dtype=BF16) -> conv3d_desc:
     """Descriptor from the input shape in `layout` (NDHWC or NCDHW)."""
     if layout == NDHWC:
         n, d, h, w, cin = x_shape
@@ -156,7 +164,7 @@ def make_desc(x_shape: Sequence[int], cout: int, *, stride=(1, 1, 1), pad_lo=(0,
         n, cin, d, h, w = x_shape
     return conv3d_desc(n, d, h, w, cin, cout, (ctypes.c_int * 3)(*stride),
                        (ctypes.c_int * 3)(*pad_lo), (ctypes.c_int * 3)(*pad_hi), layout,
-                       layout if out_layout is None else out_layout, split_k, pad_mode)
+                       layout if out_layout is None else out_layout, split_k, pad_mode, dtype)
 
 
 def make_epilogue(bias=None, residual=None, gamma=None, residual_out=None,
@@ -178,6 +186,15 @@ def conv3d_packed_weight_bytes(cout: int, cin: int) -> int:
 def conv3d_pack_weight(w_oidhw, w_packed, cout: int, cin: int, stream=None) -> None:
     _check(lib().conv3d_pack_weight(_ptr(w_oidhw), _ptr(w_packed), cout, cin, _stream(stream)),
            "conv3d_pack_weight")
+
+
+def conv3d_packed_weight_bytes_fp8(cout: int, cin: int) -> int:
+    return int(lib().conv3d_packed_weight_bytes_fp8(cout, cin))
+
+
+def conv3d_pack_weight_fp8(w_oidhw, w_packed, cout: int, cin: int, stream=None) -> None:
+    _check(lib().conv3d_pack_weight_fp8(_ptr(w_oidhw), _ptr(w_packed), cout, cin, _stream(stream)),
+           "conv3d_pack_weight_fp8")
 
 
 def conv3d_pack_weight_2d(w_oihw, w_packed, cout: int, cin: int, stream=None) -> None:

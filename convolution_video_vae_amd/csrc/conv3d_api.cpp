@@ -56,6 +56,7 @@ struct Problem {
   int layout, out_layout;
   unsigned flags;
   bool reflect;    // spatial reflect padding
+  bool fp8;        // e4m3 x and packed weight
 };
 
 struct Plan {
@@ -72,6 +73,14 @@ struct Plan {
   size_t off_x, off_y, off_res, off_rout, off_part, off_queue, total;
 };
 
+size_t packed_bytes(const Problem& pr) {
+  return pr.fp8 ? conv3d_packed_weight_bytes_fp8(pr.cout, pr.cin)
+                : conv3d_packed_weight_bytes(pr.cout, pr.cin);
+}
+
+// 64-byte K steps: 32 bf16 or 64 e4m3 channels.
+int k_chunks(const Problem& pr) { return pr.fp8 ? (pr.cin + 63) / 64 : (pr.cin + 31) / 32; }
+
 conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
   if (!d) return CONV3D_ERR_NULL;
   if (d->n <= 0 || d->d <= 0 || d->h <= 0 || d->w <= 0 || d->cin <= 0 || d->cout <= 0)
@@ -84,6 +93,8 @@ conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
   if (d->split_k < 0) return CONV3D_ERR_SHAPE;
   if (d->pad_mode != CONV3D_PAD_ZERO && d->pad_mode != CONV3D_PAD_REFLECT) return CONV3D_ERR_SHAPE;
   pr->reflect = d->pad_mode == CONV3D_PAD_REFLECT;
+  if (d->dtype != CONV3D_BF16 && d->dtype != CONV3D_FP8_E4M3) return CONV3D_ERR_SHAPE;
+  pr->fp8 = d->dtype == CONV3D_FP8_E4M3;
   if (pr->reflect) {
     if (d->h < 2 || d->w < 2) return CONV3D_ERR_SHAPE;
     for (int i = 1; i < 3; ++i)
@@ -98,15 +109,21 @@ conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
   pr->Wo = out_extent(d->w, d->stride[2], d->pad_lo[2], d->pad_hi[2]);
   if (pr->Do < 1 || pr->Ho < 1 || pr->Wo < 1) return CONV3D_ERR_SHAPE;
   pr->M = (long long)d->n * pr->Do * pr->Ho * pr->Wo;
-  pr->x_bytes = (long long)d->n * d->d * d->h * d->w * d->cin * 2;
+  pr->x_bytes = (long long)d->n * d->d * d->h * d->w * d->cin * (pr->fp8 ? 1 : 2);
   pr->y_bytes = pr->M * d->cout * 2;
   pr->layout = d->layout;
   pr->out_layout = d->out_layout;
   if (d->cin % 8 != 0) return CONV3D_ERR_ALIGN;
+  if (pr->fp8) {
+    if (d->cin % 16 != 0) return CONV3D_ERR_ALIGN;
+    if (d->cout % 32 != 0 || pr->reflect || d->layout != CONV3D_NDHWC ||
+        d->out_layout != CONV3D_NDHWC)
+      return CONV3D_ERR_UNSUPPORTED;
+  }
   if (d->cin > 8160) return CONV3D_ERR_UNSUPPORTED;  // K steps are encoded in 8 bits per tap
   if (d->cout % 16 != 0) return CONV3D_ERR_UNSUPPORTED;
   if (pr->x_bytes > kMaxTensorBytes || pr->y_bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
-  if ((long long)conv3d_packed_weight_bytes(d->cout, d->cin) > kMaxTensorBytes)
+  if ((long long)packed_bytes(*pr) > kMaxTensorBytes)
     return CONV3D_ERR_UNSUPPORTED;
   if (pr->M > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
   return CONV3D_OK;
@@ -190,7 +207,7 @@ const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 5, -1}, {32, 2, 2, 4, 3, 5, -1}
 template <int N>
 bool pick_halo(const Problem& pr, const TileCfg (&cands)[N], int mode, TileCfg* out) {
   for (const TileCfg& c : cands)
-    if (halo_ok(pr, c) && igemm_has_config(c, mode, pr.reflect)) {
+    if (halo_ok(pr, c) && igemm_has_config(c, mode, pr.reflect, pr.fp8)) {
       *out = c;
       return true;
     }
@@ -202,13 +219,13 @@ bool pick_halo(const Problem& pr, const TileCfg (&cands)[N], int mode, TileCfg* 
 int steps_of(const TileCfg& c, int cc) { return c.ns < 0 ? 9 * cc : 27 * cc; }
 
 void make_plan(const Problem& pr, int split_req, Plan* pl) {
-  const int cc = (pr.cin + 31) / 32;
+  const int cc = k_chunks(pr);
   const bool norm = (pr.flags & F_NORM) != 0;
   TileCfg base = channel_cfg(pr.cout);
   const long long n_tiles = ceil_div(pr.cout, base.bn());
 
   TileCfg store_cfg = store_channel_cfg(pr.cout);
-  if (!igemm_has_config(store_cfg, EPI_STORE, pr.reflect)) store_cfg = base;
+  if (!igemm_has_config(store_cfg, EPI_STORE, pr.reflect, pr.fp8)) store_cfg = base;
   if (!norm && !pick_halo(pr, kSlotStore, EPI_STORE, &store_cfg))
     pick_halo(pr, kHaloStore, EPI_STORE, &store_cfg);
   TileCfg part_cfg = base;
@@ -216,7 +233,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   if (base.r == 32 && ceil_div(pr.M, part_cfg.bm()) * n_tiles < 64) {
     TileCfg c = base;
     c.pb = 1;
-    if (igemm_has_config(c, EPI_PARTIAL, pr.reflect)) part_cfg = c;
+    if (igemm_has_config(c, EPI_PARTIAL, pr.reflect, pr.fp8)) part_cfg = c;
   }
   // (Fragment-order partials of the halo kernel have no norm reduction.)
   if (!norm) pick_halo(pr, kHaloPartial, EPI_PARTIAL, &part_cfg);
@@ -229,7 +246,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
                              {16, 4, 1, 2, 10, 1, 3}};
     for (const TileCfg& c : cands)
       if (norm_cfg.r == 0 && c.bn() == pr.cout && halo_ok(pr, c) &&
-          igemm_has_config(c, EPI_NORM, pr.reflect))
+          igemm_has_config(c, EPI_NORM, pr.reflect, pr.fp8))
         norm_cfg = c;
   }
 
@@ -248,7 +265,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     if (sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &c.r, &c.wm, &c.wn, &c.pb, &c.cb, &c.kb, &c.ns) == 7 &&
         c.bn() > 0 && pr.cout % c.bn() == 0 && halo_ok(pr, c)) {
       const int mode = split ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
-      if (igemm_has_config(c, mode, pr.reflect)) {
+      if (igemm_has_config(c, mode, pr.reflect, pr.fp8)) {
         if (mode == EPI_PARTIAL) part_cfg = c;
         else if (mode == EPI_NORM) norm_cfg = c;
         else store_cfg = c;
@@ -443,6 +460,25 @@ conv3d_status conv3d_pack_weight(const void* w_oidhw, void* w_packed, int cout, 
   return rc ? CONV3D_ERR_HIP : CONV3D_OK;
 }
 
+size_t conv3d_packed_weight_bytes_fp8(int cout, int cin) {
+  if (cout <= 0 || cin <= 0) return 0;
+  return (size_t)27 * (size_t)((cin + 63) / 64 * 64) * (size_t)cout;
+}
+
+conv3d_status conv3d_pack_weight_fp8(const void* w_oidhw, void* w_packed, int cout, int cin,
+                                     void* stream) {
+  if (!w_oidhw || !w_packed) return CONV3D_ERR_NULL;
+  if (cout <= 0 || cin <= 0) return CONV3D_ERR_SHAPE;
+  if (!aligned16(w_packed)) return CONV3D_ERR_ALIGN;
+  const long long in_bytes = 27LL * cout * cin;
+  if (overlaps(range_of(w_oidhw, in_bytes),
+               range_of(w_packed, (long long)conv3d_packed_weight_bytes_fp8(cout, cin))))
+    return CONV3D_ERR_OVERLAP;
+  return launch_pack_weight_fp8((const uint8_t*)w_oidhw, (uint8_t*)w_packed, cout, cin, stream)
+             ? CONV3D_ERR_HIP
+             : CONV3D_OK;
+}
+
 conv3d_status conv3d_pack_weight_2d(const void* w_oihw, void* w_packed, int cout, int cin,
                                     void* stream) {
   if (!w_oihw || !w_packed) return CONV3D_ERR_NULL;
@@ -551,7 +587,7 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   // each other.
   const unsigned f = pr.flags;
   const Range rx = range_of(x, pr.x_bytes);
-  const Range rw = range_of(w_packed, (long long)conv3d_packed_weight_bytes(pr.cout, pr.cin));
+  const Range rw = range_of(w_packed, (long long)packed_bytes(pr));
   const Range ry = range_of(y, pp.on ? pp.y_bytes : pr.y_bytes);
   const Range rcache = pp.a.cache ? range_of(pp.a.cache, (long long)pr.n * pp.a.cache_frames *
                                                              pr.Ho * pr.Wo * pr.cout * 2)
@@ -607,7 +643,7 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   a.Do = pr.Do; a.Ho = pr.Ho; a.Wo = pr.Wo;
   a.sd = pr.sd; a.sh = pr.sh; a.sw = pr.sw;
   a.pd = pr.pd; a.ph = pr.ph; a.pw = pr.pw;
-  a.CC = (pr.cin + 31) / 32;
+  a.CC = k_chunks(pr);
   a.M = (int)pr.M;
   a.m_tiles = pl.m_tiles; a.n_tiles = pl.n_tiles; a.splits = pl.splits;
   a.steps_per_split = pl.steps_per_split;
@@ -622,7 +658,7 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
     a.queue = (unsigned*)(ws + pl.off_queue);
     if (launch_queue_reset(a.queue, stream)) return CONV3D_ERR_HIP;
   }
-  const int rc = launch_igemm(pl.cfg, pl.mode, pr.reflect, a, (int)pl.grid, stream);
+  const int rc = launch_igemm(pl.cfg, pl.mode, pr.reflect, pr.fp8, a, (int)pl.grid, stream);
   if (rc) return rc < 0 ? CONV3D_ERR_UNSUPPORTED : CONV3D_ERR_HIP;
 
   if (pl.reduce) {

@@ -43,6 +43,10 @@ struct Mfma16 {
   static constexpr int R = 16;
   static constexpr int KS = 1;      // MFMAs per 32-channel K step
   static constexpr int NACC = 4;    // accumulator floats per lane per block
+  static constexpr int KCH = 32;    // channels per K step (64 bytes a pixel)
+  static constexpr int CCH = 8;     // channels per 16-byte chunk
+  static constexpr int ESZ = 2;     // bytes per element
+  static constexpr bool WIDE = false;  // one MFMA per chunk (not per K step)
   typedef f32x4_t acc_t;
   __device__ static int row(int lane) { return lane & 15; }
   __device__ static int grp(int lane) { return lane >> 4; }
@@ -67,6 +71,8 @@ struct Mfma32 {
   static constexpr int R = 32;
   static constexpr int KS = 2;
   static constexpr int NACC = 16;
+  static constexpr int KCH = 32, CCH = 8, ESZ = 2;
+  static constexpr bool WIDE = false;
   typedef f32x16_t acc_t;
   __device__ static int row(int lane) { return lane & 31; }
   __device__ static int grp(int lane) { return lane >> 5; }
@@ -82,6 +88,28 @@ struct Mfma32 {
     const int g = c / (16 * CB), rem = c % (16 * CB);
     cb = rem >> 4;
     r = 8 * ((rem & 15) >> 2) + 4 * g + (rem & 3);
+  }
+};
+
+// fp8 (e4m3) operands, v_mfma_f32_32x32x64_f8f6f4: a K step is 64 channels
+// (64 bytes of a pixel, the same four 16-byte chunks as a bf16 step); lane l
+// supplies row/col (l & 31) and the 32 bytes of chunks 2*(l >> 5) and
+// 2*(l >> 5) + 1 of both operands, so the hardware's assignment of those
+// bytes to K only has to agree between A and B, which it does. One MFMA per K
+// step; D as for Mfma32.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+struct Mfma32F8 : Mfma32 {
+  static constexpr int KCH = 64, CCH = 16, ESZ = 1;
+  static constexpr bool WIDE = true;
+  __device__ static int chunk(int lane, int h) { return 2 * (lane >> 5) + h; }
+  __device__ static acc_t mma2(const u32x4_t& a0, const u32x4_t& a1, const u32x4_t& b0,
+                               const u32x4_t& b1, acc_t c) {
+    const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                       (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8_t b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                       (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    // formats 0/0: e4m3 x e4m3; zero scale operands select the unscaled form
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
 };
 
@@ -116,7 +144,7 @@ __device__ __forceinline__ TileCoord tile_coord(const IgemmArgs& a, int BM, int 
 // 27-bit mask of the taps that fall inside the input. With reflect padding
 // every spatial tap reads real input and bits 27-30 flag the pixels whose
 // first row / last row / first column / last column tap is reflected.
-template <int PB, int R, bool REF = false>
+template <int PB, int R, bool REF = false, int ESZ = 2>
 __device__ __forceinline__ unsigned pixel_geometry(const IgemmArgs& a, int m_first,
                                                    long long (&base)[PB], unsigned (&tapmask)[PB]) {
   unsigned live = 0;
@@ -149,7 +177,7 @@ __device__ __forceinline__ unsigned pixel_geometry(const IgemmArgs& a, int m_fir
         tm |= ((unsigned)(h0 < 0) << 27) | ((unsigned)(h0 + 2 >= a.H) << 28) |
               ((unsigned)(w0 < 0) << 29) | ((unsigned)(w0 + 2 >= a.W) << 30);
       tapmask[p] = tm;
-      base[p] = ((((long long)n * a.D + d0) * a.H + h0) * a.W + w0) * (a.Cin * 2);
+      base[p] = ((((long long)n * a.D + d0) * a.H + h0) * a.W + w0) * (a.Cin * ESZ);
     }
     live |= tapmask[p];
   }
@@ -244,18 +272,18 @@ __device__ __forceinline__ void gather_x(const IgemmArgs& a, __amdgpu_buffer_rsr
   const int t = valid ? e >> 8 : 0, cc = valid ? e & 255 : 0;
   const int kd = t / 9, kh = (t / 3) % 3, kw = t % 3;
   const long long delta =
-      (((long long)kd * a.H + kh) * a.W + kw) * (long long)(a.Cin * 2) + cc * 64;
+      (((long long)kd * a.H + kh) * a.W + kw) * (long long)(a.Cin * T::ESZ) + cc * 64;
 #pragma unroll
   for (int h = 0; h < T::KS; ++h) {
     const int ch = T::chunk(lane, h);
-    const unsigned chan_ok = (unsigned)(valid && cc * 32 + ch * 8 < a.Cin);
+    const unsigned chan_ok = (unsigned)(valid && cc * T::KCH + ch * T::CCH < a.Cin);
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
       const unsigned ok = chan_ok & (tapmask[p] >> t);
       long long adj = 0;
       if (REF) {  // reflected taps: two rows / columns back inside
         const unsigned f = tapmask[p];
-        const int rowb = a.W * a.Cin * 2, colb = a.Cin * 2;
+        const int rowb = a.W * a.Cin * T::ESZ, colb = a.Cin * T::ESZ;
         if (kh == 0 && ((f >> 27) & 1u)) adj += 2 * rowb;
         if (kh == 2 && ((f >> 28) & 1u)) adj -= 2 * rowb;
         if (kw == 0 && ((f >> 29) & 1u)) adj += 2 * colb;
@@ -450,7 +478,7 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
 
   long long base[PB];
   unsigned tapmask[PB];
-  unsigned live = wave_or(pixel_geometry<PB, R, REF>(a, m_first, base, tapmask));
+  unsigned live = wave_or(pixel_geometry<PB, R, REF, T::ESZ>(a, m_first, base, tapmask));
   // Taps no pixel of the tile can see are skipped by the whole work-group.
   if (tid == 0) live_sh = 0;
   __syncthreads();
@@ -596,16 +624,27 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_kernel(IgemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     gather(ev[NS - 1], xr[sx]);
     load_w(ev[NS], wst[slot]);
+    if constexpr (T::WIDE) {
 #pragma unroll
-    for (int k = 0; k < KB; ++k)
-#pragma unroll
-      for (int h = 0; h < KS; ++h)
+      for (int k = 0; k < KB; ++k)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int p = 0; p < PB; ++p)
-            acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wfr[f0][k][cb][h]),
-                                __builtin_bit_cast(bf16x8_t, xr[slot][k][p][h]), acc[cb][p]);
+            acc[cb][p] = T::mma2(wfr[f0][k][cb][0], wfr[f0][k][cb][1], xr[slot][k][p][0],
+                                 xr[slot][k][p][1], acc[cb][p]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+#pragma unroll
+        for (int h = 0; h < KS; ++h)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int p = 0; p < PB; ++p)
+              acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wfr[f0][k][cb][h]),
+                                  __builtin_bit_cast(bf16x8_t, xr[slot][k][p][h]), acc[cb][p]);
+    }
     // Step i+2's slices into their stage, last read before the previous
     // barrier.
     store_w(s2, wst[s2]);
@@ -1806,17 +1845,20 @@ struct Entry {
   TileCfg cfg;
   int mode;
   bool reflect;   // spatial reflect padding compiled in
+  bool fp8;       // e4m3 operands
   int (*fn)(const IgemmArgs&, int, void*);
 };
 
 #define C32(WM, WN, PB, CB, KB, NS, MODE) \
-  {{32, WM, WN, PB, CB, KB, NS}, MODE, false, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, false>}
+  {{32, WM, WN, PB, CB, KB, NS}, MODE, false, false, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, false>}
 #define C16(WM, WN, PB, CB, KB, NS, MODE) \
-  {{16, WM, WN, PB, CB, KB, NS}, MODE, false, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, false>}
+  {{16, WM, WN, PB, CB, KB, NS}, MODE, false, false, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, false>}
 #define R32(WM, WN, PB, CB, KB, NS, MODE) \
-  {{32, WM, WN, PB, CB, KB, NS}, MODE, true, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, true>}
+  {{32, WM, WN, PB, CB, KB, NS}, MODE, true, false, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, true>}
 #define R16(WM, WN, PB, CB, KB, NS, MODE) \
-  {{16, WM, WN, PB, CB, KB, NS}, MODE, true, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, true>}
+  {{16, WM, WN, PB, CB, KB, NS}, MODE, true, false, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, true>}
+#define F32(WM, WN, PB, CB, KB, NS, MODE) \
+  {{32, WM, WN, PB, CB, KB, NS}, MODE, false, true, &launch_one<Mfma32F8, WM, WN, PB, CB, KB, NS, MODE, false>}
 const Entry kEntries[] = {
     // ns = -2: slot kernel (stride 1 along W, Cin % 32 == 0), 512-slot tiles.
     C32(2, 2, 8, 2, 0, -2, EPI_STORE),
@@ -1880,30 +1922,39 @@ const Entry kEntries[] = {
     R16(4, 1, 2, 10, 1, 3, EPI_NORM),
     R16(4, 1, 4, 2, 1, 3, EPI_STORE),
     R16(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
+    // e4m3 operands: the plain kernel's 32-row channel tiles.
+    F32(4, 1, 2, 4, 1, 3, EPI_STORE),
+    F32(4, 1, 2, 3, 1, 3, EPI_STORE),
+    F32(4, 1, 2, 2, 1, 3, EPI_STORE),
+    F32(4, 1, 2, 4, 1, 3, EPI_PARTIAL),
+    F32(4, 1, 1, 4, 1, 3, EPI_PARTIAL),
+    F32(4, 1, 2, 3, 1, 3, EPI_PARTIAL),
+    F32(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
 };
 #undef C32
 #undef C16
 #undef R32
 #undef R16
+#undef F32
 
-const Entry* find_entry(const TileCfg& c, int mode, bool reflect) {
+const Entry* find_entry(const TileCfg& c, int mode, bool reflect, bool fp8) {
   for (const Entry& e : kEntries)
     if (e.cfg.r == c.r && e.cfg.wm == c.wm && e.cfg.wn == c.wn && e.cfg.pb == c.pb &&
         e.cfg.cb == c.cb && e.cfg.kb == c.kb && e.cfg.ns == c.ns && e.mode == mode &&
-        e.reflect == reflect)
+        e.reflect == reflect && e.fp8 == fp8)
       return &e;
   return nullptr;
 }
 
 }  // namespace
 
-bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect) {
-  return find_entry(cfg, mode, reflect) != nullptr;
+bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect, bool fp8) {
+  return find_entry(cfg, mode, reflect, fp8) != nullptr;
 }
 
-int launch_igemm(const TileCfg& cfg, int mode, bool reflect, const IgemmArgs& args, int grid,
-                 void* stream) {
-  const Entry* e = find_entry(cfg, mode, reflect);
+int launch_igemm(const TileCfg& cfg, int mode, bool reflect, bool fp8, const IgemmArgs& args,
+                 int grid, void* stream) {
+  const Entry* e = find_entry(cfg, mode, reflect, fp8);
   if (!e) return -1;
   return e->fn(args, grid, stream);
 }

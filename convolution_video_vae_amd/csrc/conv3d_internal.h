@@ -101,12 +101,15 @@ struct GroupNormArgs {
 // taps = 27: an OIDHW weight; taps = 9: a [cout][cin][3][3] weight placed in
 // the last temporal slice (kd = 2), the other slices zero.
 int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, int taps, void* stream);
+// e4m3 OIDHW [cout][cin][27] bytes -> [27][ceil(cin / 64)][cout][64] bytes, zero beyond cin.
+int launch_pack_weight_fp8(const uint8_t* w, uint8_t* wp, int cout, int cin, void* stream);
 int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int a, int b, void* stream);
 // Returns -1 if no kernel is compiled for (cfg, mode, reflect). reflect:
 // spatial reflect padding instead of zeros (pads of at most one).
-int launch_igemm(const TileCfg& cfg, int mode, bool reflect, const IgemmArgs& args, int grid,
-                 void* stream);
-bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect = false);
+// fp8: e4m3 activations and packed weight (bf16 otherwise).
+int launch_igemm(const TileCfg& cfg, int mode, bool reflect, bool fp8, const IgemmArgs& args,
+                 int grid, void* stream);
+bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect = false, bool fp8 = false);
 int launch_reduce(const ReduceArgs& args, void* stream);
 int launch_queue_reset(unsigned* queue, void* stream);
 int launch_group_norm(const GroupNormArgs& args, void* stream);

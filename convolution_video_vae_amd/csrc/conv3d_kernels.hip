@@ -435,6 +435,44 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
   }
 }
 
+// e4m3 weights: [cout][cin][27] bytes -> [27][cc_n][cout][64] bytes, zero
+// beyond cin. One thread per 16-byte output chunk (16 channels).
+__global__ __launch_bounds__(256) void pack_weight_fp8_kernel(const uint8_t* __restrict__ w,
+                                                              uint8_t* __restrict__ wp, int cout,
+                                                              int cin, int cc_n) {
+  const long long total = 27LL * cc_n * cout * 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int q = (int)(i & 3);
+    long long r = i >> 2;
+    const int co = (int)(r % cout); r /= cout;
+    const int cc = (int)(r % cc_n);
+    const int t = (int)(r / cc_n);
+    u32x4_t out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      unsigned v4 = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int ci = cc * 64 + q * 16 + 4 * k + b;
+        const unsigned v = (ci < cin) ? w[((long long)co * cin + ci) * 27 + t] : 0u;
+        v4 |= v << (8 * b);
+      }
+      out[k] = v4;
+    }
+    reinterpret_cast<u32x4_t*>(wp)[i] = out;
+  }
+}
+
+int launch_pack_weight_fp8(const uint8_t* w, uint8_t* wp, int cout, int cin, void* stream) {
+  const int cc_n = (cin + 63) / 64;
+  const long long total = 27LL * cc_n * cout * 4;
+  const long long blocks = std::min<long long>((total + 255) / 256, 65535);
+  hipLaunchKernelGGL(pack_weight_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, w, wp, cout, cin, cc_n);
+  return (int)hipGetLastError();
+}
+
 // --------------------------------------------------------------------------
 // Batched 2D transpose [n][A][B] -> [n][B][A] of 16-bit elements, through a
 // 64x64 LDS tile. Reads run along B and writes along A, both coalesced.

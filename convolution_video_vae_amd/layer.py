@@ -13,7 +13,8 @@ import torch
 
 from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_fwd_padded, conv3d_group_norm,
                conv3d_group_norm_workspace_bytes, conv3d_output_dims, conv3d_pack_weight,
-               conv3d_pack_weight_2d, conv3d_packed_weight_bytes, conv3d_padded_workspace_bytes,
+               conv3d_pack_weight_2d, conv3d_pack_weight_fp8, conv3d_packed_weight_bytes,
+               conv3d_packed_weight_bytes_fp8, conv3d_padded_workspace_bytes,
                conv3d_stream_pack_input, conv3d_workspace_bytes, make_desc, make_epilogue,
                make_group_norm_desc, make_out_pad)
 
@@ -21,7 +22,15 @@ from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_fwd_padded, conv3d_group_norm,
 def pack_weight(w_oidhw: torch.Tensor, stream=None) -> torch.Tensor:
     """OIDHW bf16 [Cout][Cin][3][3][3] on the GPU -> packed weight buffer.
     A 4-D [Cout][Cin][3][3] weight is packed as the last temporal slice of a
-    3x3x3 weight (for 2D and 1x3x3 layers run on single frames)."""
+    3x3x3 weight (for 2D and 1x3x3 layers run on single frames); an
+    float8_e4m3fn 5-D weight is packed for the fp8 conv."""
+    if w_oidhw.dtype == torch.float8_e4m3fn and w_oidhw.is_cuda and w_oidhw.dim() == 5:
+        cout, cin = w_oidhw.shape[:2]
+        w = w_oidhw.contiguous()
+        out = torch.empty(conv3d_packed_weight_bytes_fp8(cout, cin), dtype=torch.uint8,
+                          device=w.device)
+        conv3d_pack_weight_fp8(w, out, cout, cin, stream)
+        return out
     if w_oidhw.dtype != torch.bfloat16 or not w_oidhw.is_cuda or w_oidhw.dim() not in (4, 5):
         raise ValueError("weight must be a 4-D or 5-D bf16 CUDA tensor")
     cout, cin = w_oidhw.shape[:2]
@@ -53,9 +62,11 @@ class Conv3d:
         self.layout = layout
         self.out_layout = layout if out_layout is None else out_layout
         self.x_shape = tuple(int(v) for v in x_shape)
+        self.fp8 = weight.dtype == torch.float8_e4m3fn
+        self.in_dtype = torch.float8_e4m3fn if self.fp8 else torch.bfloat16
         self.desc = make_desc(self.x_shape, self.cout, stride=stride, pad_lo=pad_lo, pad_hi=pad_hi,
                               layout=layout, out_layout=self.out_layout, split_k=split_k,
-                              pad_mode=pad_mode)
+                              pad_mode=pad_mode, dtype=1 if self.fp8 else 0)
         self.out_dhw = conv3d_output_dims(self.desc)
         n = self.x_shape[0]
         if self.out_layout == NDHWC:
@@ -100,8 +111,8 @@ class Conv3d:
     def __call__(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
                  y: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
                  stream=None, cache: Optional[torch.Tensor] = None) -> torch.Tensor:
-        if tuple(x.shape) != self.x_shape or x.dtype != torch.bfloat16 or not x.is_contiguous():
-            raise ValueError(f"x must be a contiguous bf16 tensor of shape {self.x_shape}")
+        if tuple(x.shape) != self.x_shape or x.dtype != self.in_dtype or not x.is_contiguous():
+            raise ValueError(f"x must be a contiguous {self.in_dtype} tensor of shape {self.x_shape}")
         if self.has_residual != (residual is not None):
             raise ValueError("residual presence differs from construction")
         if self.has_residual_out != (residual_out is not None):

@@ -101,7 +101,16 @@ typedef struct {
   int out_layout;  /* conv3d_layout of y / residual / residual_out */
   int split_k;
   int pad_mode;    /* conv3d_pad_mode of the H and W padding (time is always zero padded) */
+  int dtype;       /* conv3d_dtype of x and the packed weight (y, residual stay bf16) */
 } conv3d_desc;
+
+/* Operand type. FP8_E4M3 (Qwen PR: the FP8 suite of the implicit-GEMM conv,
+ * e4m3fn activations and weights, fp32 bias, bf16 output): x holds e4m3fn
+ * bytes, the weight is packed by conv3d_pack_weight_fp8, products and sums
+ * are fp32 as for bf16 and the epilogue is unchanged. Requires cin % 16 == 0
+ * (CONV3D_ERR_ALIGN), cout % 32 == 0, NDHWC, zero padding
+ * (CONV3D_ERR_UNSUPPORTED). */
+typedef enum { CONV3D_BF16 = 0, CONV3D_FP8_E4M3 = 1 } conv3d_dtype;
 
 /* Spatial padding: zeros, or reflection as the H3 encoder pads before each
  * conv (FlyDSL issue, MiniMax H3 comment, the conv call site: spatial
@@ -136,6 +145,16 @@ size_t conv3d_packed_weight_bytes(int cout, int cin);
  * one contiguous [cout][32] block. w_oidhw and w_packed must not overlap. */
 conv3d_status conv3d_pack_weight(const void* w_oidhw, void* w_packed, int cout, int cin,
                                  void* stream);
+
+/* Bytes of the packed e4m3 weight for (cout, cin). */
+size_t conv3d_packed_weight_bytes_fp8(int cout, int cin);
+
+/* Pack an e4m3fn OIDHW weight [cout][cin][3][3][3] (1 byte each):
+ *   packed[t][c / 64][co][c % 64],  t = kd*9 + kh*3 + kw,  c < roundup(cin, 64)
+ * with the channels c >= cin zero (one 64-channel K step of a tap is one
+ * contiguous [cout][64] block). w and w_packed must not overlap. */
+conv3d_status conv3d_pack_weight_fp8(const void* w_oidhw, void* w_packed, int cout, int cin,
+                                     void* stream);
 
 /* Pack a 2D weight [cout][cin][3][3] (bf16) as the last temporal slice
  * (kd = 2) of a 3x3x3 weight whose other slices are zero; same packed layout

@@ -107,3 +107,33 @@ def check_group_norm(y_bits, ref, *, what=""):
         raise AssertionError(f"{what}: {int(bad.sum())} of {r.size} outside the rule; "
                              f"first {detail}; diag {diag}")
     return diag
+
+
+def check_fp8(y_bits, ref, sum_abs, *, what=""):
+    """e4m3 operands: the raw rule plus an accumulation term. The gfx950 fp8
+    MFMA (32x32x64) does not sum its 64 products exactly: measured on N(0,1)
+    operands its error stays below 2^-18.9 of the sum of the products'
+    magnitudes (it behaves like aligning a group to its largest product and
+    keeping about 20 bits), while bf16 products are summed exactly. So
+
+      |y - r| <= 2 ulp(max(|r|, |conv|, 2^-8 RMS(r))) + 2^-16 * sum_k |x_k w_k|
+
+    (8x the largest measured ratio); sum_abs is that sum per output."""
+    y = b2f(y_bits).astype(np.float64)
+    r = b2f(ref["y"]).astype(np.float64)
+    assert y.shape == r.shape, (y.shape, r.shape)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    conv = np.abs(b2f(ref["conv"]).astype(np.float64))
+    scale = np.maximum.reduce([np.abs(r), conv, np.full_like(r, 2.0 ** -8 * rms)])
+    allowed = 2.0 * ulp_bf16(scale) + 2.0 ** -16 * np.asarray(sum_abs, dtype=np.float64)
+    err = np.abs(y - r)
+    diag = {"n": int(r.size), "bit_identical": float(np.mean(y_bits == ref["y"])),
+            "max_err_over_sum_abs": float(np.max(err / np.maximum(sum_abs, 1e-30)))}
+    bad = err > allowed
+    if np.any(bad):
+        idx = np.argwhere(bad)[:5]
+        detail = [(tuple(int(v) for v in i), float(y[tuple(i)]), float(r[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {r.size} outside the rule; "
+                             f"first {detail}; diag {diag}")
+    return diag

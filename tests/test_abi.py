@@ -33,8 +33,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_desc_struct_matches_header_layout():
-    # 6 ints, 3x3 ints, layout, out_layout, split_k, pad_mode = 19 ints
-    assert ctypes.sizeof(cv.conv3d_desc) == 19 * 4
+    # 6 ints, 3x3 ints, layout, out_layout, split_k, pad_mode, dtype = 20 ints
+    assert ctypes.sizeof(cv.conv3d_desc) == 20 * 4
     assert ctypes.sizeof(cv.conv3d_epilogue) == 8 + 4 * 8
 
 
@@ -335,3 +335,21 @@ def test_norm_silu_rejected_calls():
     assert norm_silu_call(ok, op=op2) == 2
     assert norm_silu_call(ok, y=X + 64) == 4                                        # y inside x
     assert norm_silu_call(ok, op=op, prev=Y + 256) == 4                             # previous inside y
+
+
+def test_fp8_checks():
+    assert cv.conv3d_packed_weight_bytes_fp8(128, 128) == 27 * 128 * 128
+    assert cv.conv3d_packed_weight_bytes_fp8(64, 40) == 27 * 64 * 64        # cin padded to 64
+    f8 = dict(dtype=cv.FP8_E4M3)
+    assert fwd(small_desc(dtype=2)) == 2
+    assert fwd(cv.make_desc((1, 3, 8, 8, 24), 32, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=1,
+                            **f8)) == 3                                    # cin % 16
+    assert fwd(small_desc(**f8, pad_mode=cv.PAD_REFLECT)) == 6
+    d = small_desc(**f8)
+    d.layout = cv.NCDHW
+    assert fwd(d) == 6
+    assert fwd(cv.make_desc((1, 3, 8, 8, 32), 48, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=1,
+                            **f8)) == 6                                    # cout % 32
+    assert cv.lib().conv3d_pack_weight_fp8(None, W, 8, 8, None) == 1
+    assert cv.lib().conv3d_pack_weight_fp8(X, W + 8, 8, 8, None) == 3
+    assert cv.lib().conv3d_pack_weight_fp8(X, X + 16, 8, 8, None) == 4

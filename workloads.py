@@ -46,6 +46,7 @@ class Layer:
     norm_silu: bool = False
     live_taps: int = 27         # taps that can see real pixels (T=1 causal: 9)
     reflect: bool = False       # reflect spatial padding (the H3 encoder's own)
+    fp8: bool = False           # e4m3fn activations and weights (bf16 output)
 
     @property
     def cin(self) -> int:
@@ -83,6 +84,8 @@ LAYERS = {
     # the same layer with H3's own spatial padding: reflect instead of zeros
     "h3_l0_128_reflect": Layer("h3_l0_128_reflect", 3, (1, 17, 256, 256, 128), 128, reflect=True,
                                **CAUSAL),
+    # the same layer with e4m3fn operands (the FP8 variant of the conv)
+    "h3_l0_128_fp8": Layer("h3_l0_128_fp8", 3, (1, 17, 256, 256, 128), 128, fp8=True, **CAUSAL),
     "h3_l0_128_s122": Layer("h3_l0_128_s122", 3, (1, 17, 256, 256, 128), 128, stride=(1, 2, 2),
                             pad_lo=(2, 0, 0), pad_hi=(0, 1, 1)),
     # Wan encoder's pre-padded valid convs.
