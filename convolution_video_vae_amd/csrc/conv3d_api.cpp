@@ -177,7 +177,7 @@ TileCfg store_channel_cfg(int cout) {
 int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1; }
 
 // Slot kernel {32, WM, WN, PB, CB, 0, -2}: stride 1 along W and whole
-// 32-channel chunks. Output row r owns Wo + 2 slots and a tile is bm() of
+// K-step chunks (32 bf16 or 64 e4m3 channels). Output row r owns Wo + 2 slots and a tile is bm() of
 // them; the bm() slots staged per stage must span at most 64 output rows
 // (one lane each), and slot indices are split with a float-reciprocal
 // division, exact below 2^22.
@@ -185,7 +185,7 @@ long long slot_rows(const Problem& pr) { return (long long)pr.n * pr.Do * pr.Ho;
 
 bool slot_ok(const Problem& pr, const TileCfg& c) {
   const long long wp = pr.Wo + 2;
-  return pr.sw == 1 && pr.cin % 32 == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
+  return pr.sw == 1 && pr.cin % (pr.fp8 ? 64 : 32) == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
          (c.bm() + 1) / wp + 2 <= 64 && slot_rows(pr) * wp + c.bm() + 2048 < (1LL << 22);
 }
 

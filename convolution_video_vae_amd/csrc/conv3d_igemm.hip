@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "conv3d_device.h"
 #include "conv3d_internal.h"
 
@@ -1390,7 +1392,30 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 // barrier frees the buffer, also two stages ahead. LDS fragment reads run
 // one to two sub-steps ahead of their MFMAs, every load and DMA spread
 // between single MFMAs.
+//
+// e4m3 operands (F8): a stage is a 64-channel chunk, which is 64 bytes of a
+// pixel as a bf16 stage's 32 channels are, so staging, LDS layout and
+// fragment addresses are the bf16 ones. One v_mfma_f32_32x32x64_f8f6f4 per
+// (tap, channel block, pixel block) takes the whole chunk: lane group g
+// supplies the bytes of chunks g and g + 2 (the bf16 K halves' fragments) of
+// both operands, so three sub-steps (s = kw) of CB*PB MFMAs, each as long as
+// two bf16 ones. Memory operations of sub-step s of stage i:
+//   s0: weight reads for taps 1 and 2, pixel fragments PB and PB+1 (the last
+//       reads of stage i's buffers), the activation DMA of stage i+2;
+//   s1: barrier (stage i+1 landed, stage i's buffers free), then stage
+//       i+1's tap-0 weights and fragments 0 and 1 (fragment 1 once the MFMAs
+//       reading its register have issued), half the weight DMA of stage i+2;
+//   s2: stage i+1's fragments 2 .. PB-1, fragment f after the MFMAs of pixel
+//       block f-2 (its register's last reader), the rest of the weight DMA.
 // ----------------------------------------------------------------------------
+// MFMA slot before which read o of e4m3 sub-step s goes out: evenly spread,
+// but no earlier than the last MFMA reading the register it overwrites.
+constexpr int f8_read_slot(int s, int o, int nrd, int nm, int cb) {
+  const int g = o * nm / nrd;
+  const int lo = s == 1 ? (o >= 2 * cb + 2 ? cb : 0) : (s == 2 ? (o / 2 + 1) * cb : 0);
+  return g > lo ? g : lo;
+}
+
 template <int PB, int CB, int WN>
 struct SlotShape {
   static constexpr int R = 32;
@@ -1437,9 +1462,10 @@ __device__ __forceinline__ void unit_slot(int q, int& sl, int& c) {
   }
 }
 
-template <int PB, int CB, int WN, int EPI, bool REF = false>
+template <int PB, int CB, int WN, int EPI, bool REF = false, bool F8 = false>
 __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   using T = Mfma32;
+  constexpr int ESZ = F8 ? 1 : 2;       // bytes per activation element
   using S = SlotShape<PB, CB, WN>;
   constexpr int R = S::R, WM = S::WM, NACC = T::NACC, RUN = NACC * CB;
   constexpr int XU = S::XU, XJ = S::XJ, NF = S::NF, WU = S::WU, WJ = S::WJ, WUP = S::WUP;
@@ -1450,6 +1476,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
   static_assert(EPI != EPI_NORM || WM * WN * PB * R * 4 <= 2048, "norm exchange area");
   static_assert(NW + XJ + EPI_VM <= 63, "vmcnt range");
+  static_assert(!(F8 && REF), "e4m3 operands take zero padding only");
 
   __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
   __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
@@ -1555,9 +1582,9 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       d.wsoff[kw] = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
     d.wor = ok ? 0u : kOobOffset;
     d.pbit = ok ? 1u << pr : 0u;
-    d.delta = (kd * a.H + kh) * a.W * (a.Cin * 2) + cc * 64;
+    d.delta = (kd * a.H + kh) * a.W * (a.Cin * ESZ) + cc * 64;
     d.rbit = REF ? (kh == 0 ? 1u << 9 : (kh == 2 ? 1u << 10 : 0u)) : 0u;
-    d.radj = REF ? (kh == 0 ? 2 : -2) * a.W * (a.Cin * 2) : 0;
+    d.radj = REF ? (kh == 0 ? 2 : -2) * a.W * (a.Cin * ESZ) : 0;
     return d;
   };
   // Weight DMA instruction k of a stage (tap kw = k / WJ, piece k % WJ).
@@ -1633,7 +1660,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
           sl < S::XS && (REF ? (w_in >= -1 && w_in <= a.W) : (w_in >= 0 && w_in < a.W));
       const int wc = REF ? reflect_index(w_in, a.W) : w_in;
       xmask[j] = ok ? m : 0u;
-      xbase[j] = ok ? (rb + wc) * (a.Cin * 2) + c * 16 : 0;
+      xbase[j] = ok ? (rb + wc) * (a.Cin * ESZ) + c * 16 : 0;
     }
     // Weight DMA entries: LDS unit q of a tap holds row q / 4 of the permuted
     // channel order, 16-byte chunk (q % 4) XOR the row swizzle.
@@ -1688,8 +1715,9 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   };
 
   // Pixel fragments by K half; weight fragments in a ring of three sub-steps
-  // (sub-step t uses ring slot t % 3).
-  u32x4_t xf[2][NF], wf[3][CB];
+  // (sub-step t uses ring slot t % 3), for e4m3 both halves of each tap
+  // (tap kw, half h in slot 2*kw + h).
+  u32x4_t xf[2][NF], wf[F8 ? 6 : 3][CB];
   auto read_x = [&](auto b_c, int h, int f) {
     const char* xb = reinterpret_cast<const char*>(xbuf(b_c));
     xf[h][f] = *reinterpret_cast<const u32x4_t*>(xb + (h ? (ax[f] ^ 32) : ax[f]));
@@ -1697,6 +1725,10 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   auto read_w = [&](auto b_c, int t, int cb) {
     const char* wb = reinterpret_cast<const char*>(wbuf(b_c));
     wf[t % 3][cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][t / 3] + (t % 3) * WTAP);
+  };
+  auto read_w8 = [&](auto b_c, int kw, int h, int cb) {
+    const char* wb = reinterpret_cast<const char*>(wbuf(b_c));
+    wf[2 * kw + h][cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][h] + kw * WTAP);
   };
 
   // Main loop of one tile. Memory operations of sub-step u of a stage, in
@@ -1711,52 +1743,103 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     constexpr int XB = I % 3, WB = I % 2;
     if (e0 == kEnd) return false;
     const StageDma d2 = stage_dma(e2);
-    static_for<6>([&](auto u_c) {
-      constexpr int u = decltype(u_c)::value;
-      constexpr int h = u / 3, kw = u % 3;
-      constexpr int NURG = (u < 2) ? 1 : (u >= 4 ? (u - 3) * PB / 2 - (u - 4) * PB / 2 : 0);
-      constexpr int URG0 = (u == 0) ? PB : (u == 1 ? PB + 1 : (u >= 4 ? (u - 4) * PB / 2 : 0));
-      constexpr int H1LO = (u < 3) ? u * PB / 3 : (u == 3 ? PB : 0);
-      constexpr int H1HI = (u < 3) ? (u + 1) * PB / 3 : (u == 3 ? PB + 2 : 0);
-      constexpr int DXLO = (u < 4) ? u * XJ / 4 : 0, DXHI = (u < 4) ? (u + 1) * XJ / 4 : 0;
-      constexpr int DWLO = (u >= 4) ? (u - 4) * NW / 2 : 0, DWHI = (u >= 4) ? (u - 3) * NW / 2 : 0;
-      constexpr int NOPS = NURG + CB + (H1HI - H1LO) + (DXHI - DXLO) + (DWHI - DWLO);
-      constexpr int NM = CB * PB;
-      if constexpr (u == 4) {
-        // Stage i+1 has landed everywhere (only stage i+2's activations may
-        // be in flight) and no wave reads stage i's buffers any more.
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      static_for<NM>([&](auto g_c) {
-        constexpr int g = decltype(g_c)::value;
-        static_for<NOPS>([&](auto o_c) {
-          constexpr int o = decltype(o_c)::value;
-          if constexpr (o * NM / NOPS == g) {
-            if constexpr (o < NURG) {
-              if constexpr (u < 2) read_x(SlotC<XB>{}, 0, URG0 + o);
-              else read_x(SlotC<(I + 1) % 3>{}, 0, URG0 + o);
-            } else if constexpr (o < NURG + CB) {
-              constexpr int cb = o - NURG;
-              if constexpr (u < 4) read_w(SlotC<WB>{}, u + 2, cb);
-              else read_w(SlotC<(I + 1) % 2>{}, u - 4, cb);
-            } else if constexpr (o < NURG + CB + (H1HI - H1LO)) {
-              read_x(SlotC<XB>{}, 1, H1LO + (o - NURG - CB));
-            } else if constexpr (o < NURG + CB + (H1HI - H1LO) + (DXHI - DXLO)) {
-              issue_x_one(d2, SlotC<(I + 2) % 3>{}, SlotC<DXLO + (o - NURG - CB - (H1HI - H1LO))>{});
-            } else {
-              issue_w_one(d2, SlotC<WB>{},
-                          SlotC<DWLO + (o - NURG - CB - (H1HI - H1LO) - (DXHI - DXLO))>{});
+    if constexpr (F8) {
+      static_for<3>([&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        constexpr int NM = CB * PB;
+        constexpr int NRD = s == 0 ? 4 * CB + 4 : (s == 1 ? 2 * CB + 4 : 2 * (PB - 2));
+        constexpr int DW0 = s == 2 ? NW / 2 : 0;
+        constexpr int ND = s == 0 ? XJ : (s == 1 ? NW / 2 : NW - NW / 2);
+        if constexpr (s == 1) {
+          // Stage i+1 has landed everywhere (only stage i+2's activations may
+          // be in flight) and no wave reads stage i's buffers any more.
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        static_for<NM>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          static_for<NRD>([&](auto o_c) {
+            constexpr int o = decltype(o_c)::value;
+            if constexpr (f8_read_slot(s, o, NRD, NM, CB) == g) {
+              if constexpr (s == 0) {
+                if constexpr (o < 2 * CB)
+                  read_w8(SlotC<WB>{}, 1, o / CB, o % CB);
+                else if constexpr (o < 2 * CB + 4)
+                  read_x(SlotC<XB>{}, (o - 2 * CB) % 2, PB + (o - 2 * CB) / 2);
+                else
+                  read_w8(SlotC<WB>{}, 2, (o - 2 * CB - 4) / CB, (o - 2 * CB - 4) % CB);
+              } else if constexpr (s == 1) {
+                if constexpr (o < 2 * CB)
+                  read_w8(SlotC<(I + 1) % 2>{}, 0, o / CB, o % CB);
+                else
+                  read_x(SlotC<(I + 1) % 3>{}, (o - 2 * CB) % 2, (o - 2 * CB) / 2);
+              } else {
+                read_x(SlotC<(I + 1) % 3>{}, o % 2, 2 + o / 2);
+              }
             }
-          }
+          });
+          static_for<ND>([&](auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+            if constexpr (k * NM / ND == g) {
+              if constexpr (s == 0) issue_x_one(d2, SlotC<(I + 2) % 3>{}, SlotC<k>{});
+              else issue_w_one(d2, SlotC<WB>{}, SlotC<DW0 + k>{});
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int cb = g % CB, p = g / CB;
+          acc[cb][p] = Mfma32F8::mma2(wf[2 * s][cb], wf[2 * s + 1][cb], xf[0][p + s],
+                                      xf[1][p + s], acc[cb][p]);
+          __builtin_amdgcn_sched_barrier(0);
         });
-        __builtin_amdgcn_sched_barrier(0);
-        constexpr int cb = g % CB, p = g / CB;
-        acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wf[u % 3][cb]),
-                            __builtin_bit_cast(bf16x8_t, xf[h][p + kw]), acc[cb][p]);
-        __builtin_amdgcn_sched_barrier(0);
       });
-    });
+    } else {
+      static_for<6>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr int h = u / 3, kw = u % 3;
+        constexpr int NURG = (u < 2) ? 1 : (u >= 4 ? (u - 3) * PB / 2 - (u - 4) * PB / 2 : 0);
+        constexpr int URG0 = (u == 0) ? PB : (u == 1 ? PB + 1 : (u >= 4 ? (u - 4) * PB / 2 : 0));
+        constexpr int H1LO = (u < 3) ? u * PB / 3 : (u == 3 ? PB : 0);
+        constexpr int H1HI = (u < 3) ? (u + 1) * PB / 3 : (u == 3 ? PB + 2 : 0);
+        constexpr int DXLO = (u < 4) ? u * XJ / 4 : 0, DXHI = (u < 4) ? (u + 1) * XJ / 4 : 0;
+        constexpr int DWLO = (u >= 4) ? (u - 4) * NW / 2 : 0, DWHI = (u >= 4) ? (u - 3) * NW / 2 : 0;
+        constexpr int NOPS = NURG + CB + (H1HI - H1LO) + (DXHI - DXLO) + (DWHI - DWLO);
+        constexpr int NM = CB * PB;
+        if constexpr (u == 4) {
+          // Stage i+1 has landed everywhere (only stage i+2's activations may
+          // be in flight) and no wave reads stage i's buffers any more.
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        static_for<NM>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          static_for<NOPS>([&](auto o_c) {
+            constexpr int o = decltype(o_c)::value;
+            if constexpr (o * NM / NOPS == g) {
+              if constexpr (o < NURG) {
+                if constexpr (u < 2) read_x(SlotC<XB>{}, 0, URG0 + o);
+                else read_x(SlotC<(I + 1) % 3>{}, 0, URG0 + o);
+              } else if constexpr (o < NURG + CB) {
+                constexpr int cb = o - NURG;
+                if constexpr (u < 4) read_w(SlotC<WB>{}, u + 2, cb);
+                else read_w(SlotC<(I + 1) % 2>{}, u - 4, cb);
+              } else if constexpr (o < NURG + CB + (H1HI - H1LO)) {
+                read_x(SlotC<XB>{}, 1, H1LO + (o - NURG - CB));
+              } else if constexpr (o < NURG + CB + (H1HI - H1LO) + (DXHI - DXLO)) {
+                issue_x_one(d2, SlotC<(I + 2) % 3>{}, SlotC<DXLO + (o - NURG - CB - (H1HI - H1LO))>{});
+              } else {
+                issue_w_one(d2, SlotC<WB>{},
+                            SlotC<DWLO + (o - NURG - CB - (H1HI - H1LO) - (DXHI - DXLO))>{});
+              }
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int cb = g % CB, p = g / CB;
+          acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wf[u % 3][cb]),
+                              __builtin_bit_cast(bf16x8_t, xf[h][p + kw]), acc[cb][p]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    }
     e0 = e1;
     e1 = e2;
     e2 = next_stage(e2);
@@ -1793,12 +1876,25 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW + XJ + EPI_VM) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW + XJ) : "memory");
+    if constexpr (F8) {
 #pragma unroll
-    for (int f = 0; f < PB; ++f) read_x(SlotC<0>{}, 0, f);
+      for (int f = 0; f < PB; ++f) {
+        read_x(SlotC<0>{}, 0, f);
+        read_x(SlotC<0>{}, 1, f);
+      }
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      read_w(SlotC<0>{}, 0, cb);
-      read_w(SlotC<0>{}, 1, cb);
+      for (int cb = 0; cb < CB; ++cb) {
+        read_w8(SlotC<0>{}, 0, 0, cb);
+        read_w8(SlotC<0>{}, 0, 1, cb);
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < PB; ++f) read_x(SlotC<0>{}, 0, f);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        read_w(SlotC<0>{}, 0, cb);
+        read_w(SlotC<0>{}, 1, cb);
+      }
     }
     for (;;) {
       if (!iteration(SlotC<0>{})) break;
@@ -1827,7 +1923,8 @@ namespace {
 template <class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI, bool REF>
 int launch_one(const IgemmArgs& args, int grid, void* stream) {
   if constexpr (NS == -2)
-    hipLaunchKernelGGL((igemm_slot_kernel<PB, CB, WN, EPI, REF>), dim3((unsigned)grid), dim3(256),
+    hipLaunchKernelGGL((igemm_slot_kernel<PB, CB, WN, EPI, REF, std::is_same<T, Mfma32F8>::value>),
+                       dim3((unsigned)grid), dim3(256),
                        0, (hipStream_t)stream, args);
   else if constexpr (NS < 0)
     hipLaunchKernelGGL((igemm_halo_kernel<CB, WN, KB, EPI, REF>), dim3((unsigned)grid), dim3(256),
@@ -1922,7 +2019,9 @@ const Entry kEntries[] = {
     R16(4, 1, 2, 10, 1, 3, EPI_NORM),
     R16(4, 1, 4, 2, 1, 3, EPI_STORE),
     R16(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
-    // e4m3 operands: the plain kernel's 32-row channel tiles.
+    // e4m3 operands: the slot kernel (Cin % 64 == 0) and the plain kernel's
+    // 32-row channel tiles.
+    F32(2, 2, 8, 2, 0, -2, EPI_STORE),
     F32(4, 1, 2, 4, 1, 3, EPI_STORE),
     F32(4, 1, 2, 3, 1, 3, EPI_STORE),
     F32(4, 1, 2, 2, 1, 3, EPI_STORE),

@@ -1,6 +1,7 @@
 """GPU parity of the e4m3fn (fp8) conv: activations and weights in e4m3fn,
 fp32 accumulation, bf16 output (Qwen PR, "Test plan": the FP8 suite). Small
-e4m3 values keep every sum exact, so those cases are bit-exact against the
+e4m3 values keep every sum exact, so those cases, across the slot kernel
+(whole 64-channel chunks) and the plain kernel, are bit-exact against the
 oracle on the decoded operands; random operands use the raw parity rule plus
 the fp8 MFMA's accumulation term (tests/parity.py, check_fp8); and
 the pages' own criterion (mean relative error of the fp8 conv against the
@@ -34,17 +35,23 @@ def bits(t):
 
 
 CASES = [
-    # label, x shape, cout, stride, pad_lo, pad_hi, split_k
-    ("causal_128", (1, 4, 10, 22, 128), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1), 1),
-    ("valid_96_cin_48", (1, 5, 9, 13, 48), 96, (1, 1, 1), (0, 0, 0), (0, 0, 0), 1),
-    ("stride122_64", (1, 3, 12, 15, 64), 64, (1, 2, 2), (2, 0, 0), (0, 1, 1), 1),
-    ("split_k_512", (1, 3, 6, 6, 512), 512, (1, 1, 1), (2, 1, 1), (0, 1, 1), 0),
-    ("cin_16", (2, 3, 7, 9, 16), 32, (1, 1, 1), (2, 1, 1), (0, 1, 1), 1),
+    # label, x shape, cout, stride, pad_lo, pad_hi, split_k, expected kernel (plan substring)
+    ("slot_causal_128", (1, 4, 10, 22, 128), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1), 1, "ns=-2"),
+    ("slot_cin_192_rows_straddle", (1, 3, 9, 37, 192), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1), 1,
+     "ns=-2"),
+    ("slot_cin_64_cout_256_batch_2", (2, 3, 7, 30, 64), 256, (1, 1, 1), (2, 1, 1), (0, 1, 1), 1,
+     "ns=-2"),
+    ("slot_valid_wide_rows", (1, 4, 5, 150, 64), 128, (1, 1, 1), (0, 0, 0), (0, 0, 0), 1, "ns=-2"),
+    ("valid_96_cin_48", (1, 5, 9, 13, 48), 96, (1, 1, 1), (0, 0, 0), (0, 0, 0), 1, "ns=3"),
+    ("stride122_64", (1, 3, 12, 15, 64), 64, (1, 2, 2), (2, 0, 0), (0, 1, 1), 1, "ns=3"),
+    ("split_k_512", (1, 3, 6, 6, 512), 512, (1, 1, 1), (2, 1, 1), (0, 1, 1), 0, "mode=partial"),
+    ("cin_16", (2, 3, 7, 9, 16), 32, (1, 1, 1), (2, 1, 1), (0, 1, 1), 1, ""),
+    ("cin_96_not_slot", (1, 3, 8, 20, 96), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1), 1, "ns=3"),
 ]
 
 
-@pytest.mark.parametrize("label,xs,cout,st,lo,hi,sk", CASES, ids=[c[0] for c in CASES])
-def test_fp8_small_values_bit_exact(label, xs, cout, st, lo, hi, sk):
+@pytest.mark.parametrize("label,xs,cout,st,lo,hi,sk,kern", CASES, ids=[c[0] for c in CASES])
+def test_fp8_small_values_bit_exact(label, xs, cout, st, lo, hi, sk, kern):
     rng = np.random.default_rng(71)
     xc = rng.choice(SMALL_CODES, size=xs)
     wc = rng.choice(SMALL_CODES, size=(cout, xs[4], 3, 3, 3))
@@ -52,6 +59,7 @@ def test_fp8_small_values_bit_exact(label, xs, cout, st, lo, hi, sk):
     conv = Conv3d(f8(wc).cuda(), xs, stride=st, pad_lo=lo, pad_hi=hi, split_k=sk, bias=b)
     plan = cv.conv3d_plan_describe(conv.desc, cv.make_epilogue(bias=conv.bias))
     print(f"[fp8] {label} x={xs} cout={cout} plan: {plan}", flush=True)
+    assert kern in plan
     y = conv(f8(xc).cuda())
     torch.cuda.synchronize()
     ref = conv3d_fp8(xc, wc, stride=st, pad_lo=lo, pad_hi=hi, bias=b.numpy())
@@ -73,6 +81,28 @@ def test_fp8_random_operands_against_oracle():
     mag = conv3d_fp8(xc & 0x7F, wc & 0x7F, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), intermediates=True)
     diag = check_fp8(bits(y), ref, mag["acc"], what="fp8 random")
     print(f"[fp8] random: {diag}", flush=True)
+    assert diag["bit_identical"] > 0.98, diag
+
+
+def test_fp8_slot_kernel_random_operands_against_oracle():
+    """The slot kernel's MFMAs take a whole 64-channel chunk each; random
+    operands over several tiles, two chunks and a row that straddles tiles."""
+    rng = np.random.default_rng(75)
+    xs, cout = (1, 4, 11, 45, 128), 128
+    x = torch.from_numpy(rng.standard_normal(xs).astype(np.float32)).to(torch.float8_e4m3fn)
+    w = torch.from_numpy(rng.standard_normal((cout, 128, 3, 3, 3)).astype(np.float32) * 0.5).to(
+        torch.float8_e4m3fn)
+    conv = Conv3d(w.cuda(), xs, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=1)
+    plan = cv.conv3d_plan_describe(conv.desc, cv.make_epilogue())
+    print(f"[fp8] slot random plan: {plan}", flush=True)
+    assert "ns=-2" in plan
+    y = conv(x.cuda())
+    torch.cuda.synchronize()
+    xc, wc = codes_of(x), codes_of(w)
+    ref = conv3d_fp8(xc, wc, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), intermediates=True)
+    mag = conv3d_fp8(xc & 0x7F, wc & 0x7F, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), intermediates=True)
+    diag = check_fp8(bits(y), ref, mag["acc"], what="fp8 slot random")
+    print(f"[fp8] slot random: {diag}", flush=True)
     assert diag["bit_identical"] > 0.98, diag
 
 
@@ -106,6 +136,9 @@ def test_fp8_full_size_h3_l0_sampled():
     x8 = t.x.float().to(torch.float8_e4m3fn)
     w8 = t.w.float().to(torch.float8_e4m3fn)
     conv = Conv3d(w8.cuda(), L.x_shape, pad_lo=L.pad_lo, pad_hi=L.pad_hi)
+    plan = cv.conv3d_plan_describe(conv.desc, cv.make_epilogue())
+    print(f"[fp8] h3 l0 plan: {plan}", flush=True)
+    assert "ns=-2" in plan
     y = conv(x8.cuda())
     torch.cuda.synchronize()
     D, H, W = L.out_dhw()
