@@ -66,6 +66,24 @@ def test_fp8_small_values_bit_exact(label, xs, cout, st, lo, hi, sk, kern):
     assert np.array_equal(bits(y), ref)
 
 
+def test_fp8_slot_kernel_persistent_bit_exact():
+    """290 slot tiles on 256 persistent work-groups (a second tile for some,
+    its first stages fetched during the last two of the first); small values,
+    so exact."""
+    rng = np.random.default_rng(76)
+    xs, cout = (1, 9, 128, 126, 128), 128
+    xc = rng.choice(SMALL_CODES, size=xs)
+    wc = rng.choice(SMALL_CODES, size=(cout, xs[4], 3, 3, 3))
+    conv = Conv3d(f8(wc).cuda(), xs, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))
+    plan = cv.conv3d_plan_describe(conv.desc, cv.make_epilogue())
+    print(f"[fp8] persistent plan: {plan}", flush=True)
+    assert "ns=-2" in plan and "persistent=1" in plan
+    y = conv(f8(xc).cuda())
+    torch.cuda.synchronize()
+    ref = conv3d_fp8(xc, wc, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))
+    assert np.array_equal(bits(y), ref)
+
+
 def test_fp8_random_operands_against_oracle():
     rng = np.random.default_rng(72)
     xs, cout = (1, 5, 12, 20, 96), 96

@@ -220,6 +220,28 @@ def test_slot_kernel_integer_bit_exact(case, with_bias):
     np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
 
 
+PERSIST_CASES = [
+    # label, x shape, cout: 290 slot tiles on 256 persistent work-groups, so
+    # some work-groups take a second tile from their queue. With Cin = 128
+    # every tile's stage count (live (kd, kh) pairs x 4 chunks) is a multiple
+    # of six and the next tile's set-up and first two stages go out during
+    # the current tile's last two; with Cin = 160 (5 chunks) only tiles with
+    # six live pairs have such a count, the rest start the plain way.
+    ("slot_persistent_cin128", (1, 9, 128, 126, 128), 128),
+    ("slot_persistent_cin160_mixed", (1, 9, 128, 126, 160), 128),
+]
+
+
+@pytest.mark.parametrize("case", PERSIST_CASES, ids=[c[0] for c in PERSIST_CASES])
+def test_slot_kernel_persistent_integer_bit_exact(case):
+    label, xs, cout = case
+    x, w, b = workloads.integer_tensors(xs, cout, seed=len(label) + 13, bias=True)
+    g = run_gpu(x, w, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), bias=b, split_k=0, label=label)
+    assert "ns=-2" in g["plan"] and "persistent=1" in g["plan"], g["plan"]
+    r = run_oracle(x, w, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), bias=b)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
+
+
 HALO_SPLIT_CASES = [
     # label, x shape, cout, stride, pad_lo, pad_hi: K-split halo kernel (fp32
     # partials summed in fixed order by the reduce kernel).
