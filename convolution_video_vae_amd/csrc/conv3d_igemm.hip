@@ -1408,6 +1408,66 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 //   s2: stage i+1's fragments 2 .. PB-1, fragment f after the MFMAs of pixel
 //       block f-2 (its register's last reader), the rest of the weight DMA.
 // ----------------------------------------------------------------------------
+// Store of a 512-slot x 128-channel slot tile through LDS. The plain store's
+// instructions each write 16-byte pieces of 32 pixels PB slots apart, which
+// the store path absorbs about three times more slowly than whole lines. Here
+// the tile goes out in PB/2 rounds: every lane writes the bf16 values of its
+// pixel blocks 2*rho and 2*rho+1 into a [slot][128 channels] block of an idle
+// activation buffer (16-byte unit u of row r at u ^ ((r >> 1) & 15), so
+// consecutive lanes hit distinct banks); after a barrier the 256 threads read
+// the block in row order and store it, 16 threads to a pixel's 256 bytes, so
+// one instruction writes two pairs of adjacent pixels. Each wave issues
+// PB * 4 stores, as the plain store does (dropped slots get out-of-range
+// offsets), which the caller's wait counts rely on. Barriers wait for LDS
+// operations only; the stores stay in flight.
+template <int PB>
+__device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t (&acc)[2][PB],
+                                             u32x4_t* sbuf, int m0, int m_end, int WP,
+                                             float inv_wp, int co0, int wave_m, int wave_n,
+                                             int lrow, int lgrp) {
+  constexpr int RBU = 16;                 // 16-byte units per slot row
+  constexpr int UNITS = 32 * 2 * 2 * RBU; // per round: 64 lane rows x 2 pixel blocks
+  static_assert(PB % 2 == 0 && UNITS % 256 == 0, "rounds of two pixel blocks");
+  const __amdgpu_buffer_rsrc_t yr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
+                                        0x00020000);
+  const int tid = threadIdx.x;
+  static_for<PB / 2>([&](auto rc) {
+    constexpr int rho = decltype(rc)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = (wave_m * 32 + lrow) * 2 + j;
+      const int sw = (r >> 1) & 15;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x4_t ov;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 8 * k + 2 * q;   // lane channel 0 .. 31: acc[c / 16][p][c % 16]
+          ov[q] = pack2(acc[c / 16][2 * rho + j][c % 16], acc[(c + 1) / 16][2 * rho + j][(c + 1) % 16]);
+        }
+        sbuf[r * RBU + ((wave_n * 8 + lgrp * 4 + k) ^ sw)] = ov;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < UNITS / 256; ++i) {
+      const int q = i * 256 + tid;
+      const int r = q >> 4, pos = q & 15;
+      const u32x4_t v = sbuf[r * RBU + (pos ^ ((r >> 1) & 15))];
+      const int s = m0 + (r >> 1) * PB + 2 * rho + (r & 1);
+      const int row = small_div(s, WP, inv_wp);
+      const int col = s - row * WP;
+      const unsigned off = (s < m_end && col < a.Wo)
+                               ? (unsigned)((row * a.Wo + col) * a.Cout + co0 + pos * 8) * 2u
+                               : kOobOffset;
+      __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)off, 0, 0);
+    }
+    // every wave has read this round's block before the next one overwrites it
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  });
+}
+
 // MFMA slot before which read o of e4m3 sub-step s goes out: evenly spread,
 // but no earlier than the last MFMA reading the register it overwrites.
 constexpr int f8_read_slot(int s, int o, int nrd, int nm, int cb) {
@@ -1477,6 +1537,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   static_assert(EPI != EPI_NORM || WM * WN * PB * R * 4 <= 2048, "norm exchange area");
   static_assert(NW + XJ + EPI_VM <= 63, "vmcnt range");
   static_assert(!(F8 && REF), "e4m3 operands take zero padding only");
+  static_assert(!(PB == 8 && CB == 2 && WN == 2) || XU >= 2048, "staged store block");
 
   __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
   __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
@@ -1707,11 +1768,18 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       }
     }
     const int cbase = pt.co0 + wave_n * R * CB + elgrp * RUN;
-    if (EPI == EPI_STORE && a.flags == 0)
-      store_plain<T, PB, CB>(a, acc, mp, cbase);
-    else
+    if (EPI == EPI_STORE && a.flags == 0) {
+      // 512 x 128 tiles store through the activation buffer the next tile
+      // first fills in its main loop (its set-up has filled the other two).
+      if constexpr (PB == 8 && CB == 2 && WN == 2)
+        store_staged<PB>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m, wave_n,
+                         elrow, elgrp);
+      else
+        store_plain<T, PB, CB>(a, acc, mp, cbase);
+    } else {
       epilogue<T, WM, WN, PB, CB, EPI>(a, acc, mp, cbase, pt.split, wave_m, wave_n, elrow, elgrp,
                                        red);
+    }
   };
 
   // Pixel fragments by K half; weight fragments in a ring of three sub-steps

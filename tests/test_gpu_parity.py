@@ -232,10 +232,13 @@ PERSIST_CASES = [
 ]
 
 
+@pytest.mark.parametrize("with_bias", [False, True], ids=["plain_store", "bias_epilogue"])
 @pytest.mark.parametrize("case", PERSIST_CASES, ids=[c[0] for c in PERSIST_CASES])
-def test_slot_kernel_persistent_integer_bit_exact(case):
+def test_slot_kernel_persistent_integer_bit_exact(case, with_bias):
+    """(Without an epilogue the 512 x 128 tiles store through LDS in rounds.)"""
     label, xs, cout = case
     x, w, b = workloads.integer_tensors(xs, cout, seed=len(label) + 13, bias=True)
+    b = b if with_bias else None
     g = run_gpu(x, w, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), bias=b, split_k=0, label=label)
     assert "ns=-2" in g["plan"] and "persistent=1" in g["plan"], g["plan"]
     r = run_oracle(x, w, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), bias=b)
