@@ -265,7 +265,8 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     if (sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &c.r, &c.wm, &c.wn, &c.pb, &c.cb, &c.kb, &c.ns) == 7 &&
         c.bn() > 0 && pr.cout % c.bn() == 0 && halo_ok(pr, c)) {
       const int mode = split ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
-      if (igemm_has_config(c, mode, pr.reflect, pr.fp8)) {
+      // (A fused-norm tile must hold the whole channel row of a pixel.)
+      if (igemm_has_config(c, mode, pr.reflect, pr.fp8) && (mode != EPI_NORM || c.bn() == pr.cout)) {
         if (mode == EPI_PARTIAL) part_cfg = c;
         else if (mode == EPI_NORM) norm_cfg = c;
         else store_cfg = c;

@@ -353,3 +353,20 @@ def test_fp8_checks():
     assert cv.lib().conv3d_pack_weight_fp8(None, W, 8, 8, None) == 1
     assert cv.lib().conv3d_pack_weight_fp8(X, W + 8, 8, 8, None) == 3
     assert cv.lib().conv3d_pack_weight_fp8(X, X + 16, 8, 8, None) == 4
+
+
+def test_tile_override_keeps_fused_norm_rows_whole(monkeypatch):
+    """The development tile override (CONV3D_TILE) may only pick a fused-norm
+    tile that holds the whole channel row; a 160-channel tile for the
+    320-channel fused layer is ignored. Plan queries launch nothing."""
+    L = workloads.LAYERS["wan_fused_160to320"]
+    d = cv.make_desc(L.x_shape, L.cout, pad_lo=L.pad_lo, pad_hi=L.pad_hi)
+    import torch
+    g = torch.ones(L.cout, dtype=torch.bfloat16)
+    epi = cv.make_epilogue(gamma=g, norm_silu=True)
+    base = cv.conv3d_plan_describe(d, epi)
+    assert "mode=norm" in base and "bn=320" in base
+    monkeypatch.setenv("CONV3D_TILE", "32,4,1,3,5,0,-2")
+    assert cv.conv3d_plan_describe(d, epi) == base
+    monkeypatch.setenv("CONV3D_TILE", "32,2,2,3,5,0,-2")
+    assert "bn=320" in cv.conv3d_plan_describe(d, epi)
