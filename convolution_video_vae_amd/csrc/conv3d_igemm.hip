@@ -1377,11 +1377,13 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 // own. The two unused slots of a row cost 2 / (Wo + 2) of the MFMA work.
 //
 // LDS layout of an activation buffer, PB = 2^SH: staged slot s (64 bytes,
-// four 16-byte chunks) sits at position s ^ ((s >> SH) & 1), its chunks
-// XORed with (s >> (SH + 1)) & 3. A fragment read's lanes step PB slots; any
-// eight consecutive lanes then hit eight distinct 16-byte bank groups of a
-// 128-byte window. The permutation stays inside aligned groups of 16 slots,
-// the span of one DMA instruction.
+// four 16-byte chunks) sits at position s ^ m, m = bit SH of s | bit SH + 3 of
+// s << 1, its chunks XORed with (s >> (SH + 1)) & 3. A fragment read's lanes
+// step PB slots, so lane-row bits 0, 3 pick m and bits 1-2 the chunk XOR: any
+// 8 consecutive lanes hit 8 distinct 16-byte bank groups of a 128-byte window
+// and any 16 consecutive lanes 16 distinct groups of a 256-byte window (one
+// ds_read_b128 cycle serves 16 lanes). The permutation stays inside aligned
+// groups of 16 slots, the span of one DMA instruction.
 //
 // Each wave computes R*PB slots x R*CB channels with v_mfma_f32_32x32x16_bf16.
 // Operands reach LDS by buffer-to-LDS DMA (a padding pixel is an
@@ -1506,7 +1508,8 @@ __device__ __forceinline__ int slot_unit(int s, int c) {
     return (s << 2) | (c ^ ((s / 6) & 3));
   } else {
     constexpr int SH = PB == 4 ? 2 : 3;
-    return ((s ^ ((s >> SH) & 1)) << 2) | (c ^ ((s >> (SH + 1)) & 3));
+    const int m = ((s >> SH) & 1) | (((s >> (SH + 3)) & 1) << 1);
+    return ((s ^ m) << 2) | (c ^ ((s >> (SH + 1)) & 3));
   }
 }
 template <int PB>
@@ -1517,7 +1520,8 @@ __device__ __forceinline__ void unit_slot(int q, int& sl, int& c) {
     c = (q & 3) ^ ((sl / 6) & 3);
   } else {
     constexpr int SH = PB == 4 ? 2 : 3;
-    sl = sp ^ ((sp >> SH) & 1);
+    // m depends on slot bits SH and SH + 3 only, which the XOR leaves alone
+    sl = sp ^ (((sp >> SH) & 1) | (((sp >> (SH + 3)) & 1) << 1));
     c = (q & 3) ^ ((sl >> (SH + 1)) & 3);
   }
 }
