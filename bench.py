@@ -256,8 +256,8 @@ def stream_cases(args, per_layer, wanted, torch, cv, workloads):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this "
-              "build (the kernel is measured at one GPU's real shape)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the kernel "
+              "is measured at one GPU's share of the work, at its real shape)", file=sys.stderr)
         sys.exit(2)
     import torch
     import convolution_video_vae_amd as cv

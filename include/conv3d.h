@@ -54,7 +54,7 @@ typedef enum {
   CONV3D_ERR_ALIGN = 3,       /* pointer not 16-byte aligned, or Cin % 8 != 0 */
   CONV3D_ERR_OVERLAP = 4,     /* an output overlaps an input or another output */
   CONV3D_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
-  CONV3D_ERR_UNSUPPORTED = 6, /* a case this build does not implement (no fallback) */
+  CONV3D_ERR_UNSUPPORTED = 6, /* a case the library does not implement (no fallback) */
   CONV3D_ERR_HIP = 7          /* the HIP runtime refused a launch */
 } conv3d_status;
 
