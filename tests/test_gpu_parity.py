@@ -205,6 +205,9 @@ SLOT_CASES = HALO_CASES + [
     ("slot_wo254_tile_straddles_rows", (1, 3, 5, 256, 64), 128, (1, 1, 1), (0, 1, 2), (0, 1, 0)),
     ("slot_160_channel_tile", (1, 4, 10, 30, 32), 160, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
     ("slot_320_two_channel_tiles", (1, 3, 8, 21, 64), 320, (1, 1, 1), (0, 0, 0), (0, 0, 0)),
+    # 512 x 128 tiles store through LDS in pairs of adjacent slots; with Wo + 2
+    # odd, pairs straddle output rows
+    ("slot_staged_store_odd_rows", (1, 3, 7, 37, 64), 128, (1, 1, 1), (2, 1, 1), (0, 1, 1)),
 ]
 
 
