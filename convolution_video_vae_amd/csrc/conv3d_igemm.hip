@@ -1470,6 +1470,61 @@ __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t 
   });
 }
 
+// The same for tiles whose waves each hold all BN = 32*CB channels of 32*PB
+// consecutive slots (one wave across the channels, CB <= 4): round rho is
+// wave rho's block, written by that wave alone as rows of 16 units (CB*4 of
+// them used; unit u of row r at u ^ ((r / PB) & 15), so 16 consecutive lanes
+// hit distinct banks) and stored by all 256 threads in row order, i.e.
+// 32*PB consecutive slots of whole pixels. Each wave issues PB * CB * 2
+// stores, as the plain store does.
+template <int PB, int CB>
+__device__ __forceinline__ void store_staged_rows(const IgemmArgs& a, const f32x16_t (&acc)[CB][PB],
+                                                  u32x4_t* sbuf, int m0, int m_end, int WP,
+                                                  float inv_wp, int co0, int wave, int lrow,
+                                                  int lgrp) {
+  constexpr int ROWS = 32 * PB, USED = CB * 4;   // 16-byte units used per row
+  constexpr int UNITS = ROWS * USED;
+  static_assert(USED <= 16 && UNITS % 256 == 0, "rows of at most 16 units");
+  const __amdgpu_buffer_rsrc_t yr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
+                                        0x00020000);
+  const int tid = threadIdx.x;
+  static_for<4>([&](auto rc) {
+    constexpr int rho = decltype(rc)::value;
+    if (wave == rho) {
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        const int r = lrow * PB + p;
+#pragma unroll
+        for (int k = 0; k < 2 * CB; ++k) {
+          u32x4_t ov;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = 8 * k + 2 * q;   // lane channel 0 .. 16*CB-1: acc[c / 16][p][c % 16]
+            ov[q] = pack2(acc[c / 16][p][c % 16], acc[(c + 1) / 16][p][(c + 1) % 16]);
+          }
+          sbuf[r * 16 + ((lgrp * 2 * CB + k) ^ (lrow & 15))] = ov;
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < UNITS / 256; ++i) {
+      const int q = i * 256 + tid;
+      const int r = q / USED, pos = q - r * USED;
+      const u32x4_t v = sbuf[r * 16 + (pos ^ ((r / PB) & 15))];
+      const int s = m0 + rho * ROWS + r;
+      const int row = small_div(s, WP, inv_wp);
+      const int col = s - row * WP;
+      const unsigned off = (s < m_end && col < a.Wo)
+                               ? (unsigned)((row * a.Wo + col) * a.Cout + co0 + pos * 8) * 2u
+                               : kOobOffset;
+      __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)off, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  });
+}
+
 // MFMA slot before which read o of e4m3 sub-step s goes out: evenly spread,
 // but no earlier than the last MFMA reading the register it overwrites.
 constexpr int f8_read_slot(int s, int o, int nrd, int nm, int cb) {
@@ -1542,6 +1597,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   static_assert(NW + XJ + EPI_VM <= 63, "vmcnt range");
   static_assert(!(F8 && REF), "e4m3 operands take zero padding only");
   static_assert(!(PB == 8 && CB == 2 && WN == 2) || XU >= 2048, "staged store block");
+  static_assert(!(PB == 4 && CB <= 4 && WN == 1) || XU >= 32 * PB * 16, "staged store rows");
+  static_assert(!(PB == 4 && CB <= 4 && WN == 1) || EPI_VM == PB * CB * 2, "store count");
 
   __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
   __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
@@ -1778,6 +1835,9 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       if constexpr (PB == 8 && CB == 2 && WN == 2)
         store_staged<PB>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m, wave_n,
                          elrow, elgrp);
+      else if constexpr (PB == 4 && CB <= 4 && WN == 1)
+        store_staged_rows<PB, CB>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m,
+                                  elrow, elgrp);
       else
         store_plain<T, PB, CB>(a, acc, mp, cbase);
     } else {
