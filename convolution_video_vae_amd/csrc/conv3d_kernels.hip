@@ -500,6 +500,52 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
   }
 }
 
+// The same with 8-byte accesses, for A % 4 == 0 and B % 4 == 0 (every
+// 4-element vector of a 64-aligned tile is then wholly inside or outside the
+// array, and 8-byte aligned). Each thread loads four 4-element runs along B
+// into the tile (rows padded to 68 elements, 8-byte aligned), then reads pairs
+// of adjacent output rows as 32-bit words to assemble two 4-element runs along
+// A at a time: a wave instruction moves 512 bytes instead of 128.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose4_kernel(const uint16_t* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, int A, int B,
+                                                         int tiles_a, int tiles_b) {
+  constexpr int RW = 68;   // tile row stride in elements
+  __shared__ __align__(16) uint16_t tile[64 * RW];
+  const int tb = blockIdx.x % tiles_b;
+  const int ta = (blockIdx.x / tiles_b) % tiles_a;
+  const long long n = blockIdx.x / ((long long)tiles_b * tiles_a);
+  const int a0 = ta * 64, b0 = tb * 64;
+  const uint16_t* s = src + n * (long long)A * B;
+  uint16_t* d = dst + n * (long long)A * B;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int v = k * 256 + t;
+    const int a = v >> 4, b4 = v & 15;
+    if (a0 + a < A && b0 + b4 * 4 < B)
+      *reinterpret_cast<uint2*>(&tile[a * RW + b4 * 4]) =
+          *reinterpret_cast<const uint2*>(s + (long long)(a0 + a) * B + b0 + b4 * 4);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = k * 256 + t;
+    const int a4 = q & 15, b2 = q >> 4;   // output rows 2*b2, 2*b2 + 1; A elements a4*4 .. +4
+    unsigned w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = *reinterpret_cast<const unsigned*>(&tile[(a4 * 4 + i) * RW + 2 * b2]);
+    const uint2 lo = {(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
+    const uint2 hi = {(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+    const int bi = b0 + 2 * b2, ai = a0 + a4 * 4;
+    if (ai < A) {
+      if (bi < B) *reinterpret_cast<uint2*>(d + (long long)bi * A + ai) = lo;
+      if (bi + 1 < B) *reinterpret_cast<uint2*>(d + (long long)(bi + 1) * A + ai) = hi;
+    }
+  }
+}
+
 // --------------------------------------------------------------------------
 // Zeroes the persistent tile queues before a launch (a kernel rather than a
 // memset so the sequence can be captured in a graph).
@@ -524,8 +570,12 @@ int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, int t
 int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int A, int B, void* stream) {
   const int ta = (A + 63) / 64, tb = (B + 63) / 64;
   const long long blocks = (long long)n * ta * tb;
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                     src, dst, A, B, ta, tb);
+  if (A % 4 == 0 && B % 4 == 0)
+    hipLaunchKernelGGL(transpose4_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, src, dst, A, B, ta, tb);
+  else
+    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, src, dst, A, B, ta, tb);
   return (int)hipGetLastError();
 }
 
