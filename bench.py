@@ -114,6 +114,7 @@ class Case:
 
 
 def time_case(case, steps, warmup, torch):
+    """Mean ms per call over `steps` back-to-back calls between two events."""
     for _ in range(warmup):
         case()
     torch.cuda.synchronize()
@@ -127,6 +128,96 @@ def time_case(case, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(stop) / steps, wall
+
+
+SCRUB_BYTES = 512 << 20     # twice the 256 MB memory-side cache
+
+
+class Scrubber:
+    """Writes 512 MB between timed calls, so the L2s and the memory-side
+    cache hold none of the layer's operands when a cold call starts."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.k = 0
+
+    def __call__(self):
+        self.k += 1
+        self.buf.fill_(float(self.k))
+
+
+def time_each(case, n, torch, scrub=None):
+    """Median ms of n calls, each between its own pair of events; with a
+    scrubber, 512 MB are written (outside the events) before every call."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        if scrub is not None:
+            scrub()
+        a.record()
+        case()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def time_layer(case, steps, warmup, torch, scrub):
+    """Back-to-back mean (the stepped figure), warm per-call median and cold
+    per-call median, all in ms."""
+    mean, wall = time_case(case, steps, warmup, torch)
+    warm = time_each(case, max(50, steps), torch)
+    cold = time_each(case, 20, torch, scrub)
+    return mean, warm, cold, wall
+
+
+def host_enqueue_us(torch, cv, workloads, n=200):
+    """Host time per conv3d_fwd call (µs): through the Conv3d layer wrapper
+    (Python argument checks and marshalling included), and as a bare ctypes
+    call of the C entry point with prepared arguments. Measured on the tiny
+    causal layer, whose kernels finish faster than they are enqueued, so the
+    launch queue never blocks the host."""
+    import ctypes
+    from convolution_video_vae_amd.layer import Conv3d
+    L = workloads.LAYERS["tiny_causal_64"]
+    t = workloads.make_tensors(L)
+    conv = Conv3d(t.w.cuda(), L.x_shape, stride=L.stride, pad_lo=L.pad_lo, pad_hi=L.pad_hi,
+                  bias=t.bias)
+    x = t.x.cuda()
+    y = conv.new_output()
+    for _ in range(20):
+        conv(x, y=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        conv(x, y=y)
+    layer_us = (time.perf_counter() - t0) / n * 1e6
+    torch.cuda.synchronize()
+    lib = cv.lib()
+    epi = cv.make_epilogue(bias=conv.bias)
+    args = (ctypes.byref(conv.desc), x.data_ptr(), conv.w_packed.data_ptr(), ctypes.byref(epi),
+            y.data_ptr(), conv.workspace.data_ptr(), conv.workspace_bytes,
+            torch.cuda.current_stream().cuda_stream)
+    fn = lib.conv3d_fwd
+    t0 = time.perf_counter()
+    for _ in range(n):
+        rc = fn(*args)
+    c_us = (time.perf_counter() - t0) / n * 1e6
+    torch.cuda.synchronize()
+    assert rc == 0
+    return {"layer_call_us": round(layer_us, 2), "c_call_us": round(c_us, 2), "calls": n,
+            "layer": L.name, "plan": cv.conv3d_plan_describe(conv.desc, epi)}
+
+
+def host_cpu():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(L, seconds):
@@ -149,7 +240,7 @@ def cpu_baseline(L, seconds):
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(done * per_pixel / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count(),
             "sample": f"{done} output pixels (all {L.cout} channels each) of {L.name} "
                       f"({L.m} in the layer), in random contiguous runs of {chunk}, "
                       f"{dt:.1f} s wall"}
@@ -284,10 +375,14 @@ def main():
     flops = head.flops(live=True)
     tflops = flops / (ms * 1e-3) / 1e12
     assert torch.isfinite(case.y.float()).all().item()
-    del case
+    head_scrub = Scrubber(torch)
+    head_warm = time_each(case, max(20, args.steps), torch)
+    head_cold = time_each(case, 10, torch, head_scrub)
+    del case, head_scrub
     torch.cuda.empty_cache()
 
     per_layer = {}
+    scrub = Scrubber(torch)
     if not args.no_layers:
         wanted = None if args.layers is None else set(args.layers.split(","))
         for name, L in workloads.LAYERS.items():
@@ -298,7 +393,7 @@ def main():
                 variants.append((name + "_ncdhw", cv.NCDHW))
             for vname, lay in variants:
                 c = Case(L, torch, cv, layout=lay)
-                lms, _ = time_case(c, max(5, args.steps), 3, torch)
+                lms, warm, cold, _ = time_layer(c, max(5, args.steps), 3, torch, scrub)
                 lt = L.flops(live=True) / (lms * 1e-3) / 1e12
                 peak = PEAK_FP8_TFLOPS if L.fp8 else PEAK_BF16_TFLOPS
                 io = (L.m * L.cin * 0 + np.prod(L.x_shape) + L.m * L.cout
@@ -306,7 +401,10 @@ def main():
                 per_layer[vname] = {
                     "us": round(lms * 1e3, 2), "tflops": round(lt, 2),
                     "pct_peak": round(100 * lt / peak, 2),
+                    "us_warm_median": round(warm * 1e3, 2), "us_cold": round(cold * 1e3, 2),
+                    "pct_peak_cold": round(100 * L.flops(live=True) / (cold * 1e-3) / 1e12 / peak, 2),
                     "algorithmic_gbs": round(io / (lms * 1e-3) / 1e9, 1),
+                    "algorithmic_gbs_cold": round(io / (cold * 1e-3) / 1e9, 1),
                     "gflop": round(L.flops(live=True) / 1e9, 3), "plan": c.plan}
                 del c
                 torch.cuda.empty_cache()
@@ -316,10 +414,26 @@ def main():
         src = torch.zeros((n, c, d, h, w), dtype=torch.bfloat16, device="cuda")
         dst = torch.empty((n, d, h, w, c), dtype=torch.bfloat16, device="cuda")
         tcase = lambda: cv.conv3d_transpose(src, cv.NCDHW, dst, n, c, d, h, w)
-        tms, _ = time_case(tcase, max(5, args.steps), 3, torch)
+        tms, twarm, tcold, _ = time_layer(tcase, max(5, args.steps), 3, torch, scrub)
+        moved = 2 * src.numel() * 2
         per_layer["transpose_ncdhw_to_ndhwc_" + L.name] = {
-            "us": round(tms * 1e3, 2), "gbs": round(2 * src.numel() * 2 / (tms * 1e-3) / 1e9, 1),
-            "pct_hbm": round(100 * 2 * src.numel() * 2 / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+            "us": round(tms * 1e3, 2), "gbs": round(moved / (tms * 1e-3) / 1e9, 1),
+            "pct_hbm": round(100 * moved / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+            "us_warm_median": round(twarm * 1e3, 2), "us_cold": round(tcold * 1e3, 2),
+            "gbs_cold": round(moved / (tcold * 1e-3) / 1e9, 1)}
+        # and back: the conv's NDHWC output to NCDHW at the network's edge
+        n2, d2, h2, w2, c2 = L.out_shape()
+        src2 = torch.zeros((n2, d2, h2, w2, c2), dtype=torch.bfloat16, device="cuda")
+        dst2 = torch.empty((n2, c2, d2, h2, w2), dtype=torch.bfloat16, device="cuda")
+        tcase2 = lambda: cv.conv3d_transpose(src2, cv.NDHWC, dst2, n2, c2, d2, h2, w2)
+        tms, twarm, tcold, _ = time_layer(tcase2, max(5, args.steps), 3, torch, scrub)
+        moved = 2 * src2.numel() * 2
+        per_layer["transpose_ndhwc_to_ncdhw_" + L.name] = {
+            "us": round(tms * 1e3, 2), "gbs": round(moved / (tms * 1e-3) / 1e9, 1),
+            "pct_hbm": round(100 * moved / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+            "us_warm_median": round(twarm * 1e3, 2), "us_cold": round(tcold * 1e3, 2),
+            "gbs_cold": round(moved / (tcold * 1e-3) / 1e9, 1)}
+        del src2, dst2
         del src, dst
         # channels-last GroupNorm (+ SiLU) between the convs
         from convolution_video_vae_amd.layer import GroupNorm
@@ -331,11 +445,13 @@ def main():
             y = torch.empty_like(x)
             gn = GroupNorm(N.x_shape, N.groups, gamma.cuda(), beta.cuda(), eps=N.eps,
                            silu=N.silu, t_isolated=N.t_isolated)
-            gms, _ = time_case(lambda: gn(x, y=y), max(5, args.steps), 3, torch)
+            gms, gwarm, gcold, _ = time_layer(lambda: gn(x, y=y), max(5, args.steps), 3, torch,
+                                              scrub)
             assert torch.isfinite(y.float()).all().item()
             per_layer[name] = {
                 "us": round(gms * 1e3, 2), "algorithmic_gbs": round(N.bytes / (gms * 1e-3) / 1e9, 1),
                 "pct_hbm": round(100 * N.bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                "us_warm_median": round(gwarm * 1e3, 2), "us_cold": round(gcold * 1e3, 2),
                 "algorithmic_mb": round(N.bytes / 1e6, 1),
                 "config": f"x NDHWC {list(N.x_shape)} bf16, {N.groups} groups, "
                           f"{'per-frame' if N.t_isolated else 'per-sample'} statistics"
@@ -361,6 +477,9 @@ def main():
             and TRAFFIC.get("workload") == head.name:
         traffic = TRAFFIC["bytes"]
 
+    enqueue = host_enqueue_us(torch, cv, workloads)
+    torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head, args.cpu_seconds)
@@ -381,6 +500,13 @@ def main():
         "config": {"workload": describe(head), "gflop_per_step": round(flops / 1e9, 2),
                    "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
                    "parallelism": "single GPU"},
+        "headline_timing": {
+            "ms_back_to_back_mean": round(ms, 4),
+            "ms_warm_median": round(head_warm, 4),
+            "ms_cold_median": round(head_cold, 4),
+            "tflops_cold": round(flops / (head_cold * 1e-3) / 1e12, 2),
+            "cold": "512 MB written between calls, each call between its own events"},
+        "host_enqueue": enqueue,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_hash": kernel_hash(),

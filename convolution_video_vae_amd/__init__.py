@@ -174,7 +174,54 @@ def make_epilogue(bias=None, residual=None, gamma=None, residual_out=None,
     flags |= EPI_RESIDUAL if residual is not None else 0
     flags |= EPI_L2NORM_SILU if norm_silu else 0
     flags |= EPI_RESIDUAL_OUT if residual_out is not None else 0
-    return conv3d_epilogue(flags, _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(residual_out))
+    e = conv3d_epilogue(flags, _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(residual_out))
+    # the tensors themselves, so the calls can check their sizes and types
+    e.tensors = dict(bias=bias, residual=residual, gamma=gamma, residual_out=residual_out)
+    return e
+
+
+_DTYPE_NAMES = {"bf16": "bfloat16", "fp32": "float32"}
+
+
+def _check_buffer(t, nbytes: int, what: str, dtype: Optional[str] = None) -> None:
+    """A tensor handed to the library as a buffer must be a contiguous GPU
+    tensor holding at least nbytes (of the stated dtype); the library sizes
+    every access from the descriptor, so a short buffer would be overrun.
+    Raw integer addresses are the caller's responsibility and pass as is."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and str(t.dtype) != "torch." + _DTYPE_NAMES[dtype]:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes, the call needs {nbytes}")
+
+
+def _check_conv_buffers(desc: conv3d_desc, x, w_packed, epi: Optional[conv3d_epilogue], y,
+                        y_bytes: Optional[int] = None) -> None:
+    esz = 1 if desc.dtype == FP8_E4M3 else 2
+    od = conv3d_output_dims(desc)
+    out_bytes = desc.n * od[0] * od[1] * od[2] * desc.cout * 2
+    _check_buffer(x, desc.n * desc.d * desc.h * desc.w * desc.cin * esz, "x")
+    pw = (conv3d_packed_weight_bytes_fp8 if esz == 1 else conv3d_packed_weight_bytes)(
+        desc.cout, desc.cin)
+    _check_buffer(w_packed, pw, "w_packed")
+    _check_buffer(y, out_bytes if y_bytes is None else y_bytes, "y", "bf16")
+    if epi is not None:
+        t = getattr(epi, "tensors", {})
+        _check_buffer(t.get("bias"), 4 * desc.cout, "bias", "fp32")
+        _check_buffer(t.get("gamma"), 2 * desc.cout, "gamma", "bf16")
+        _check_buffer(t.get("residual"), out_bytes, "residual", "bf16")
+        _check_buffer(t.get("residual_out"), out_bytes, "residual_out", "bf16")
+
+
+def _check_workspace(workspace, workspace_bytes: int) -> None:
+    if workspace is not None and not isinstance(workspace, int):
+        _check_buffer(workspace, workspace_bytes, "workspace")
 
 
 # --------------------------------------------------------------------------- C entry points
@@ -219,6 +266,8 @@ def conv3d_fwd(desc: conv3d_desc, x, w_packed, epi: Optional[conv3d_epilogue], y
                workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     if workspace is not None and not workspace_bytes and not isinstance(workspace, int):
         workspace_bytes = workspace.numel() * workspace.element_size()
+    _check_conv_buffers(desc, x, w_packed, epi, y)
+    _check_workspace(workspace, workspace_bytes)
     _check(lib().conv3d_fwd(ctypes.byref(desc), _ptr(x), _ptr(w_packed),
                             ctypes.byref(epi) if epi else None, _ptr(y), _ptr(workspace),
                             workspace_bytes, _stream(stream)), "conv3d_fwd")
@@ -264,8 +313,10 @@ def conv3d_group_norm(desc: conv3d_group_norm_desc, x, gamma, beta, y, workspace
 def make_out_pad(pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), history_frames: int = 0, cache=None,
                  cache_frames: int = 0) -> conv3d_out_pad:
     """Padded-output placement for conv3d_fwd_padded."""
-    return conv3d_out_pad((ctypes.c_int * 3)(*pad_lo), (ctypes.c_int * 3)(*pad_hi),
-                          history_frames, cache_frames, _ptr(cache))
+    op = conv3d_out_pad((ctypes.c_int * 3)(*pad_lo), (ctypes.c_int * 3)(*pad_hi),
+                        history_frames, cache_frames, _ptr(cache))
+    op.cache_tensor = cache
+    return op
 
 
 def conv3d_padded_workspace_bytes(desc: conv3d_desc, epi: Optional[conv3d_epilogue],
@@ -283,6 +334,18 @@ def conv3d_fwd_padded(desc: conv3d_desc, x, w_packed, epi: Optional[conv3d_epilo
                       workspace_bytes: int = 0, stream=None) -> None:
     if workspace is not None and not workspace_bytes and not isinstance(workspace, int):
         workspace_bytes = workspace.numel() * workspace.element_size()
+    y_bytes = None
+    if out_pad is not None:
+        od = conv3d_output_dims(desc)
+        y_bytes = desc.n * desc.cout * 2
+        for i in range(3):
+            y_bytes *= od[i] + out_pad.pad_lo[i] + out_pad.pad_hi[i]
+        cache = getattr(out_pad, "cache_tensor", None)
+        if out_pad.cache:
+            _check_buffer(cache, desc.n * out_pad.cache_frames * od[1] * od[2] * desc.cout * 2,
+                          "cache", "bf16")
+    _check_conv_buffers(desc, x, w_packed, epi, y, y_bytes)
+    _check_workspace(workspace, workspace_bytes)
     _check(lib().conv3d_fwd_padded(ctypes.byref(desc), _ptr(x), _ptr(w_packed),
                                    ctypes.byref(epi) if epi else None,
                                    ctypes.byref(out_pad) if out_pad else None, _ptr(y),

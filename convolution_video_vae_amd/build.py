@@ -16,6 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+IGEMM_PARTS = 8
 
 
 def _run(cmd, verbose):
@@ -29,10 +30,15 @@ def build(verbose: bool = False) -> str:
     and link the shared library."""
     os.makedirs(BUILD, exist_ok=True)
     jobs, objs = [], []
-    for name in ("conv3d_igemm", "conv3d_kernels", "conv3d_norm"):
-        obj = os.path.join(BUILD, name + ".o")
+    # The implicit-GEMM configurations compile as IGEMM_PARTS units of one
+    # source (each instantiates every IGEMM_PARTS-th configuration).
+    units = [("conv3d_igemm", [f"-DCONV3D_PART={k}", f"-DCONV3D_NPARTS={IGEMM_PARTS}"],
+              f"conv3d_igemm_{k}") for k in range(IGEMM_PARTS)]
+    units += [("conv3d_kernels", [], "conv3d_kernels"), ("conv3d_norm", [], "conv3d_norm")]
+    for name, defs, oname in units:
+        obj = os.path.join(BUILD, oname + ".o")
         jobs.append([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-c",
-                     *DEVICE_FLAGS, "-Wall", os.path.join(CSRC, name + ".hip"), "-o", obj])
+                     *DEVICE_FLAGS, *defs, "-Wall", os.path.join(CSRC, name + ".hip"), "-o", obj])
         objs.append(obj)
     aobj = os.path.join(BUILD, "conv3d_api.o")
     jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-c", "-Wall", "-Wextra",

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "../../include/conv3d.h"
 #include "conv3d_internal.h"
@@ -42,8 +43,22 @@ bool overlaps(const Range& a, const Range& b) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int out_extent(int in, int s, int lo, int hi) {
-  const int span = in + lo + hi - 3;
-  return span < 0 ? 0 : span / s + 1;
+  const long long span = (long long)in + lo + hi - 3;
+  if (span < 0) return 0;
+  const long long o = span / s + 1;
+  return o > 0x7fffffffLL ? 0x7fffffff : (int)o;
+}
+
+// Product of non-negative sizes, saturating at 2^62 (every size check
+// rejects far smaller values), so no size computation overflows.
+constexpr long long kSat = 1LL << 62;
+long long prod(std::initializer_list<long long> v) {
+  long long r = 1;
+  for (long long a : v) {
+    if (a <= 0) return a < 0 ? kSat : 0;
+    r = (r > kSat / a) ? kSat : r * a;
+  }
+  return r;
 }
 
 // Everything derived from a descriptor.
@@ -108,9 +123,9 @@ conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
   pr->Ho = out_extent(d->h, d->stride[1], d->pad_lo[1], d->pad_hi[1]);
   pr->Wo = out_extent(d->w, d->stride[2], d->pad_lo[2], d->pad_hi[2]);
   if (pr->Do < 1 || pr->Ho < 1 || pr->Wo < 1) return CONV3D_ERR_SHAPE;
-  pr->M = (long long)d->n * pr->Do * pr->Ho * pr->Wo;
-  pr->x_bytes = (long long)d->n * d->d * d->h * d->w * d->cin * (pr->fp8 ? 1 : 2);
-  pr->y_bytes = pr->M * d->cout * 2;
+  pr->M = prod({d->n, pr->Do, pr->Ho, pr->Wo});
+  pr->x_bytes = prod({d->n, d->d, d->h, d->w, d->cin, pr->fp8 ? 1 : 2});
+  pr->y_bytes = prod({pr->M, d->cout, 2});
   pr->layout = d->layout;
   pr->out_layout = d->out_layout;
   if (d->cin % 8 != 0) return CONV3D_ERR_ALIGN;
@@ -181,7 +196,7 @@ int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1
 // them; the bm() slots staged per stage must span at most 64 output rows
 // (one lane each), and slot indices are split with a float-reciprocal
 // division, exact below 2^22.
-long long slot_rows(const Problem& pr) { return (long long)pr.n * pr.Do * pr.Ho; }
+long long slot_rows(const Problem& pr) { return prod({pr.n, pr.Do, pr.Ho}); }
 
 bool slot_ok(const Problem& pr, const TileCfg& c) {
   const long long wp = pr.Wo + 2;
@@ -195,7 +210,7 @@ bool halo_ok(const Problem& pr, const TileCfg& c) {
   // (Output rows are split with a float-reciprocal division, exact below 2^22.)
   return pr.sw == 1 && pr.cin % 32 == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
          ceil_div(c.bm() - 1, pr.Wo) + 1 <= halo_maxseg(c) &&
-         (long long)pr.n * pr.Do * pr.Ho < (1LL << 22);
+         prod({pr.n, pr.Do, pr.Ho}) < (1LL << 22);
 }
 
 const TileCfg kSlotStore[] = {{32, 2, 2, 8, 2, 0, -2}, {32, 4, 1, 4, 3, 0, -2},
@@ -265,8 +280,10 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     if (sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &c.r, &c.wm, &c.wn, &c.pb, &c.cb, &c.kb, &c.ns) == 7 &&
         c.bn() > 0 && pr.cout % c.bn() == 0 && halo_ok(pr, c)) {
       const int mode = split ? EPI_PARTIAL : (norm ? EPI_NORM : EPI_STORE);
-      // (A fused-norm tile must hold the whole channel row of a pixel.)
-      if (igemm_has_config(c, mode, pr.reflect, pr.fp8) && (mode != EPI_NORM || c.bn() == pr.cout)) {
+      // (A fused-norm tile must hold the whole channel row of a pixel, and the
+      // fragment-order partials of the halo kernel have no norm reduction.)
+      if (igemm_has_config(c, mode, pr.reflect, pr.fp8) && (mode != EPI_NORM || c.bn() == pr.cout) &&
+          !(mode == EPI_PARTIAL && norm && c.ns == -1)) {
         if (mode == EPI_PARTIAL) part_cfg = c;
         else if (mode == EPI_NORM) norm_cfg = c;
         else store_cfg = c;
@@ -369,8 +386,8 @@ conv3d_status check_out_pad(const conv3d_out_pad* op, const Problem& pr, PadPlan
   a.cache = (uint16_t*)op->cache;
   a.cache_frames = op->cache ? op->cache_frames : 0;
   a.cache_k = op->cache ? std::min(op->cache_frames, pr.Do) : 0;
-  pp->y_bytes = (long long)pr.n * a.Dy * a.Hy * a.Wy * pr.cout * 2;
-  if (pp->y_bytes > kMaxTensorBytes || (long long)pr.n * a.Dy * a.Hy > 0x7fffffffLL)
+  pp->y_bytes = prod({pr.n, a.Dy, a.Hy, a.Wy, pr.cout, 2});
+  if (pp->y_bytes > kMaxTensorBytes || prod({pr.n, a.Dy, a.Hy}) > 0x7fffffffLL)
     return CONV3D_ERR_UNSUPPORTED;
   pp->on = true;
   return CONV3D_OK;
@@ -394,9 +411,9 @@ conv3d_status plan_group_norm(const conv3d_group_norm_desc* d, GnPlan* pl) {
   if (d->c % d->groups) return CONV3D_ERR_SHAPE;
   if (d->c % 8) return CONV3D_ERR_ALIGN;
   if (d->c > 2048 || d->groups > 256) return CONV3D_ERR_UNSUPPORTED;
-  const long long units = d->t_isolated ? (long long)d->n * d->d : d->n;
-  const long long P = (d->t_isolated ? 1LL : (long long)d->d) * d->h * d->w;
-  const long long bytes = units * P * d->c * 2;
+  const long long units = d->t_isolated ? prod({d->n, d->d}) : d->n;
+  const long long P = prod({d->t_isolated ? 1LL : (long long)d->d, d->h, d->w});
+  const long long bytes = prod({units, P, d->c, 2});
   if (bytes > (1LL << 40) || units > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
   GroupNormArgs& a = pl->a;
   a = GroupNormArgs{};
@@ -590,8 +607,7 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   const Range rx = range_of(x, pr.x_bytes);
   const Range rw = range_of(w_packed, (long long)packed_bytes(pr));
   const Range ry = range_of(y, pp.on ? pp.y_bytes : pr.y_bytes);
-  const Range rcache = pp.a.cache ? range_of(pp.a.cache, (long long)pr.n * pp.a.cache_frames *
-                                                             pr.Ho * pr.Wo * pr.cout * 2)
+  const Range rcache = pp.a.cache ? range_of(pp.a.cache, prod({pr.n, pp.a.cache_frames, pr.Ho, pr.Wo, pr.cout, 2}))
                                   : Range();
   const Range rb = (f & F_BIAS) ? range_of(epi->bias, 4LL * pr.cout) : Range();
   const Range rr = (f & F_RESIDUAL) ? range_of(epi->residual, pr.y_bytes) : Range();
@@ -711,8 +727,8 @@ conv3d_status conv3d_norm_silu(const void* x, int n, int d, int h, int w, int c,
     return CONV3D_ERR_NULL;
   if (c % 8) return CONV3D_ERR_ALIGN;
   if (c > 2048) return CONV3D_ERR_UNSUPPORTED;
-  const long long M = (long long)n * d * h * w;
-  const long long bytes = M * c * 2;
+  const long long M = prod({n, d, h, w});
+  const long long bytes = prod({M, c, 2});
   if (bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(y) || !aligned16(epi->gamma) ||
       ((f & F_RESIDUAL) && !aligned16(epi->residual)) ||
@@ -739,9 +755,9 @@ conv3d_status conv3d_norm_silu(const void* x, int n, int d, int h, int w, int c,
   const Range ro = (f & F_RESIDUAL_OUT) ? range_of(epi->residual_out, bytes) : Range();
   const Range rg = range_of(epi->gamma, 2LL * c);
   const Range rb = (f & F_BIAS) ? range_of(epi->bias, 4LL * c) : Range();
-  const Range rp = previous ? range_of(previous, (long long)n * op->history_frames * h * w * c * 2)
+  const Range rp = previous ? range_of(previous, prod({n, op->history_frames, h, w, c, 2}))
                             : Range();
-  const Range rc = pp.a.cache ? range_of(pp.a.cache, (long long)n * pp.a.cache_frames * h * w * c * 2)
+  const Range rc = pp.a.cache ? range_of(pp.a.cache, prod({n, pp.a.cache_frames, h, w, c, 2}))
                               : Range();
   const Range outs[] = {ry, ro, rc};
   for (const Range& o : outs)
@@ -790,15 +806,15 @@ conv3d_status conv3d_stream_pack_input(const void* chunk, const long long stride
   if (!aligned16(padded) || ((uintptr_t)chunk & 1) || ((uintptr_t)history & 1) ||
       ((uintptr_t)cache & 1))
     return CONV3D_ERR_ALIGN;
-  const long long padded_bytes = (long long)n * (t + 2) * (h + 2) * (w + 2) * c_pad * 2;
+  const long long padded_bytes = prod({n, t + 2LL, h + 2LL, w + 2LL, c_pad, 2});
   if (padded_bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
   const long long dims[5] = {n, c, t, h, w};
   long long last = 0;
   for (int i = 0; i < 5; ++i) last += (dims[i] - 1) * strides[i];
   const Range rchunk = range_of(chunk, (last + 1) * 2);
-  const Range rhist = range_of(history, (long long)n * history_frames * h * w * c * 2);
+  const Range rhist = range_of(history, prod({n, history_frames, h, w, c, 2}));
   const Range rpad = range_of(padded, padded_bytes);
-  const Range rcache = cache ? range_of(cache, (long long)n * cache_frames * h * w * c * 2) : Range();
+  const Range rcache = cache ? range_of(cache, prod({n, cache_frames, h, w, c, 2})) : Range();
   for (const Range& o : {rpad, rcache})
     for (const Range& i : {rchunk, rhist})
       if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
@@ -861,8 +877,8 @@ conv3d_status conv3d_transpose(const void* src, int src_layout, void* dst, int n
   if (n <= 0 || c <= 0 || d <= 0 || h <= 0 || w <= 0) return CONV3D_ERR_SHAPE;
   if (src_layout != CONV3D_NCDHW && src_layout != CONV3D_NDHWC) return CONV3D_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(dst)) return CONV3D_ERR_ALIGN;
-  const long long s = (long long)d * h * w;
-  const long long bytes = (long long)n * c * s * 2;
+  const long long s = prod({d, h, w});
+  const long long bytes = prod({n, c, s, 2});
   if (s > 0x7fffffffLL || bytes > (1LL << 40)) return CONV3D_ERR_UNSUPPORTED;
   if (overlaps(range_of(src, bytes), range_of(dst, bytes))) return CONV3D_ERR_OVERLAP;
   const int rc = (src_layout == CONV3D_NCDHW)

@@ -2070,24 +2070,46 @@ int launch_one(const IgemmArgs& args, int grid, void* stream) {
   return (int)hipGetLastError();
 }
 
+// The configurations are compiled in CONV3D_NPARTS translation units (the
+// same source built with CONV3D_PART = 0 .. CONV3D_NPARTS - 1, so the build
+// runs in parallel): every unit holds the whole table, and entry i's kernel
+// is instantiated only in unit i % CONV3D_NPARTS. Unit 0 dispatches.
+#ifndef CONV3D_PART
+#define CONV3D_PART 0
+#endif
+#ifndef CONV3D_NPARTS
+#define CONV3D_NPARTS 1
+#endif
+static_assert(CONV3D_NPARTS >= 1 && CONV3D_NPARTS <= 8 && CONV3D_PART < CONV3D_NPARTS,
+              "between one and eight parts");
+
+using LaunchFn = int (*)(const IgemmArgs&, int, void*);
+
+template <int IDX, class T, int WM, int WN, int PB, int CB, int KB, int NS, int EPI, bool REF>
+constexpr LaunchFn pick() {
+  if constexpr (IDX % CONV3D_NPARTS == CONV3D_PART)
+    return &launch_one<T, WM, WN, PB, CB, KB, NS, EPI, REF>;
+  else
+    return nullptr;
+}
+
 struct Entry {
   TileCfg cfg;
   int mode;
   bool reflect;   // spatial reflect padding compiled in
   bool fp8;       // e4m3 operands
-  int (*fn)(const IgemmArgs&, int, void*);
+  LaunchFn fn;    // null outside this entry's translation unit
 };
 
-#define C32(WM, WN, PB, CB, KB, NS, MODE) \
-  {{32, WM, WN, PB, CB, KB, NS}, MODE, false, false, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, false>}
-#define C16(WM, WN, PB, CB, KB, NS, MODE) \
-  {{16, WM, WN, PB, CB, KB, NS}, MODE, false, false, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, false>}
-#define R32(WM, WN, PB, CB, KB, NS, MODE) \
-  {{32, WM, WN, PB, CB, KB, NS}, MODE, true, false, &launch_one<Mfma32, WM, WN, PB, CB, KB, NS, MODE, true>}
-#define R16(WM, WN, PB, CB, KB, NS, MODE) \
-  {{16, WM, WN, PB, CB, KB, NS}, MODE, true, false, &launch_one<Mfma16, WM, WN, PB, CB, KB, NS, MODE, true>}
-#define F32(WM, WN, PB, CB, KB, NS, MODE) \
-  {{32, WM, WN, PB, CB, KB, NS}, MODE, false, true, &launch_one<Mfma32F8, WM, WN, PB, CB, KB, NS, MODE, false>}
+constexpr int kCounterBase = __COUNTER__;
+#define ENTRY(T, R, REFL, F8, WM, WN, PB, CB, KB, NS, MODE)                 \
+  {{R, WM, WN, PB, CB, KB, NS}, MODE, REFL, F8,                              \
+   pick<__COUNTER__ - kCounterBase - 1, T, WM, WN, PB, CB, KB, NS, MODE, REFL>()}
+#define C32(...) ENTRY(Mfma32, 32, false, false, __VA_ARGS__)
+#define C16(...) ENTRY(Mfma16, 16, false, false, __VA_ARGS__)
+#define R32(...) ENTRY(Mfma32, 32, true, false, __VA_ARGS__)
+#define R16(...) ENTRY(Mfma16, 16, true, false, __VA_ARGS__)
+#define F32(...) ENTRY(Mfma32F8, 32, false, true, __VA_ARGS__)
 const Entry kEntries[] = {
     // ns = -2: slot kernel (stride 1 along W, Cin % 32 == 0), 512-slot tiles.
     C32(2, 2, 8, 2, 0, -2, EPI_STORE),
@@ -2167,27 +2189,87 @@ const Entry kEntries[] = {
 #undef R32
 #undef R16
 #undef F32
+#undef ENTRY
 
-const Entry* find_entry(const TileCfg& c, int mode, bool reflect, bool fp8) {
-  for (const Entry& e : kEntries)
+constexpr int kNumEntries = (int)(sizeof kEntries / sizeof kEntries[0]);
+
+int find_entry(const TileCfg& c, int mode, bool reflect, bool fp8) {
+  for (int i = 0; i < kNumEntries; ++i) {
+    const Entry& e = kEntries[i];
     if (e.cfg.r == c.r && e.cfg.wm == c.wm && e.cfg.wn == c.wn && e.cfg.pb == c.pb &&
         e.cfg.cb == c.cb && e.cfg.kb == c.kb && e.cfg.ns == c.ns && e.mode == mode &&
         e.reflect == reflect && e.fp8 == fp8)
-      return &e;
-  return nullptr;
+      return i;
+  }
+  return -1;
 }
 
 }  // namespace
 
+#define PART_FN_(P) igemm_launch_part_##P
+#define PART_FN(P) PART_FN_(P)
+// Launch of entry idx, which must belong to this translation unit.
+int PART_FN(CONV3D_PART)(int idx, const IgemmArgs& args, int grid, void* stream) {
+  return kEntries[idx].fn(args, grid, stream);
+}
+
+#if CONV3D_PART == 0
+#if CONV3D_NPARTS > 1
+int igemm_launch_part_1(int, const IgemmArgs&, int, void*);
+#endif
+#if CONV3D_NPARTS > 2
+int igemm_launch_part_2(int, const IgemmArgs&, int, void*);
+#endif
+#if CONV3D_NPARTS > 3
+int igemm_launch_part_3(int, const IgemmArgs&, int, void*);
+#endif
+#if CONV3D_NPARTS > 4
+int igemm_launch_part_4(int, const IgemmArgs&, int, void*);
+#endif
+#if CONV3D_NPARTS > 5
+int igemm_launch_part_5(int, const IgemmArgs&, int, void*);
+#endif
+#if CONV3D_NPARTS > 6
+int igemm_launch_part_6(int, const IgemmArgs&, int, void*);
+#endif
+#if CONV3D_NPARTS > 7
+int igemm_launch_part_7(int, const IgemmArgs&, int, void*);
+#endif
+
 bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect, bool fp8) {
-  return find_entry(cfg, mode, reflect, fp8) != nullptr;
+  return find_entry(cfg, mode, reflect, fp8) >= 0;
 }
 
 int launch_igemm(const TileCfg& cfg, int mode, bool reflect, bool fp8, const IgemmArgs& args,
                  int grid, void* stream) {
-  const Entry* e = find_entry(cfg, mode, reflect, fp8);
-  if (!e) return -1;
-  return e->fn(args, grid, stream);
+  const int i = find_entry(cfg, mode, reflect, fp8);
+  if (i < 0) return -1;
+  static int (*const parts[CONV3D_NPARTS])(int, const IgemmArgs&, int, void*) = {
+      igemm_launch_part_0,
+#if CONV3D_NPARTS > 1
+      igemm_launch_part_1,
+#endif
+#if CONV3D_NPARTS > 2
+      igemm_launch_part_2,
+#endif
+#if CONV3D_NPARTS > 3
+      igemm_launch_part_3,
+#endif
+#if CONV3D_NPARTS > 4
+      igemm_launch_part_4,
+#endif
+#if CONV3D_NPARTS > 5
+      igemm_launch_part_5,
+#endif
+#if CONV3D_NPARTS > 6
+      igemm_launch_part_6,
+#endif
+#if CONV3D_NPARTS > 7
+      igemm_launch_part_7,
+#endif
+  };
+  return parts[i % CONV3D_NPARTS](i, args, grid, stream);
 }
+#endif  // CONV3D_PART == 0
 
 }  // namespace conv3d

@@ -19,6 +19,19 @@ from . import (NCDHW, NDHWC, conv3d_fwd, conv3d_fwd_padded, conv3d_group_norm,
                make_group_norm_desc, make_out_pad)
 
 
+def _expect(t: Optional[torch.Tensor], shape, what: str) -> None:
+    """An output or operand tensor of the layer: bf16, contiguous, on a GPU,
+    of exactly the layer's shape (the library sizes every access from the
+    layer's descriptor)."""
+    if t is None:
+        return
+    if (tuple(t.shape) != tuple(shape) or t.dtype != torch.bfloat16 or not t.is_contiguous()
+            or not t.is_cuda):
+        raise ValueError(f"{what} must be a contiguous bf16 GPU tensor of shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)} {t.dtype} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
 def pack_weight(w_oidhw: torch.Tensor, stream=None) -> torch.Tensor:
     """OIDHW bf16 [Cout][Cin][3][3][3] on the GPU -> packed weight buffer.
     A 4-D [Cout][Cin][3][3] weight is packed as the last temporal slice of a
@@ -111,12 +124,22 @@ class Conv3d:
     def __call__(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
                  y: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
                  stream=None, cache: Optional[torch.Tensor] = None) -> torch.Tensor:
-        if tuple(x.shape) != self.x_shape or x.dtype != self.in_dtype or not x.is_contiguous():
-            raise ValueError(f"x must be a contiguous {self.in_dtype} tensor of shape {self.x_shape}")
+        if (tuple(x.shape) != self.x_shape or x.dtype != self.in_dtype or not x.is_contiguous()
+                or not x.is_cuda):
+            raise ValueError(f"x must be a contiguous {self.in_dtype} GPU tensor of shape "
+                             f"{self.x_shape}")
         if self.has_residual != (residual is not None):
             raise ValueError("residual presence differs from construction")
         if self.has_residual_out != (residual_out is not None):
             raise ValueError("residual_out presence differs from construction")
+        n = self.x_shape[0]
+        plain = ((n,) + self.out_dhw + (self.cout,) if self.out_layout == NDHWC
+                 else (n, self.cout) + self.out_dhw)
+        _expect(residual, plain, "residual")
+        _expect(residual_out, plain, "residual_out")
+        _expect(y, self.out_shape, "y")
+        if self.padded:
+            _expect(cache, self.cache_shape, "cache")
         if y is None:
             y = self.new_output()
         epi = make_epilogue(bias=self.bias, residual=residual, gamma=self.gamma,

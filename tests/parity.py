@@ -34,13 +34,22 @@ def ulp_bf16(s: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(s)) - 7)
 
 
-def check(y_bits, ref, *, fused=False, gamma_bits=None, cout=None, what=""):
-    """Assert the rule; return diagnostics. ref: oracle dict (intermediates=True)."""
+def rms_of(bits) -> float:
+    """Root mean square of a bf16 tensor given as bit patterns."""
+    r = b2f(bits).astype(np.float64)
+    return float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+
+
+def check(y_bits, ref, *, fused=False, gamma_bits=None, cout=None, what="", rms=None):
+    """Assert the rule; return diagnostics. ref: oracle dict (intermediates=True).
+    rms: the RMS of the whole reference output when y / ref are one chunk of
+    it (the floor is a property of the layer, not of the chunk)."""
     y = b2f(y_bits).astype(np.float64)
     r = b2f(ref["y"]).astype(np.float64)
     assert y.shape == r.shape, (y.shape, r.shape)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
-    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    if rms is None:
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     floor = 2.0 ** -8 * rms
     conv = np.abs(b2f(ref["conv"]).astype(np.float64))
     if fused:
@@ -74,7 +83,7 @@ def check(y_bits, ref, *, fused=False, gamma_bits=None, cout=None, what=""):
     return diag
 
 
-def check_group_norm(y_bits, ref, *, what=""):
+def check_group_norm(y_bits, ref, *, what="", rms=None):
     """GroupNorm (+ SiLU) rule. The GPU forms the affine as an fp32 fma on
     fp32 statistics (mean and 1/sqrt(var + eps) from fp32 per-thread sums
     combined in fp64), the oracle in fp64; either side's value can land on
@@ -91,7 +100,8 @@ def check_group_norm(y_bits, ref, *, what=""):
     a = b2f(ref["a"]).astype(np.float64)
     assert y.shape == r.shape, (y.shape, r.shape)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
-    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    if rms is None:
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     scale = np.maximum.reduce([np.abs(r), np.abs(a), np.full_like(r, 2.0 ** -8 * rms)])
     err = np.abs(y - r)
     allowed = 2.0 * ulp_bf16(scale)
@@ -109,7 +119,7 @@ def check_group_norm(y_bits, ref, *, what=""):
     return diag
 
 
-def check_fp8(y_bits, ref, sum_abs, *, what=""):
+def check_fp8(y_bits, ref, sum_abs, *, what="", rms=None):
     """e4m3 operands: the raw rule plus an accumulation term. The gfx950 fp8
     MFMA (32x32x64) does not sum its 64 products exactly: measured on N(0,1)
     operands its error stays below 2^-18.9 of the sum of the products'
@@ -123,7 +133,8 @@ def check_fp8(y_bits, ref, sum_abs, *, what=""):
     r = b2f(ref["y"]).astype(np.float64)
     assert y.shape == r.shape, (y.shape, r.shape)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
-    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    if rms is None:
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     conv = np.abs(b2f(ref["conv"]).astype(np.float64))
     scale = np.maximum.reduce([np.abs(r), conv, np.full_like(r, 2.0 ** -8 * rms)])
     allowed = 2.0 * ulp_bf16(scale) + 2.0 ** -16 * np.asarray(sum_abs, dtype=np.float64)
@@ -136,4 +147,47 @@ def check_fp8(y_bits, ref, sum_abs, *, what=""):
         detail = [(tuple(int(v) for v in i), float(y[tuple(i)]), float(r[tuple(i)])) for i in idx]
         raise AssertionError(f"{what}: {int(bad.sum())} of {r.size} outside the rule; "
                              f"first {detail}; diag {diag}")
+    return diag
+
+
+# ------------------------------------------------------------ whole layers
+
+RULE_KEYS = ("y", "conv", "main", "value", "affine", "den")
+
+
+def oracle_every_pixel(run, M: int, chunk: int, what: str = ""):
+    """The oracle over all M output pixels, chunk pixels per call: run(pixels)
+    returns the oracle's dict for those pixels; the pieces the parity rules
+    read are concatenated ([M, C] bit patterns, den [M])."""
+    parts = {k: [] for k in RULE_KEYS}
+    for p0 in range(0, M, chunk):
+        ref = run(np.arange(p0, min(M, p0 + chunk)))
+        for k in RULE_KEYS:
+            if k in ref:
+                parts[k].append(ref[k])
+        if what and (p0 // chunk) % 8 == 0:
+            print(f"  oracle {what}: {min(M, p0 + chunk)} of {M} pixels", flush=True)
+    return {k: np.concatenate(v) for k, v in parts.items() if v}
+
+
+def check_every_element(y_bits, ref, *, chunk: int, what: str = "", **kw):
+    """The rule of check() on every element of [M, C] outputs, in chunks of
+    pixels with the whole layer's RMS floor; returns merged diagnostics."""
+    M = ref["y"].shape[0]
+    rms = rms_of(ref["y"])
+    n = 0
+    same = 0.0
+    diag = {"max_ulp_rule": 0.0, "max_ulp_at_r": 0.0}
+    signed = 0.0
+    for p0 in range(0, M, chunk):
+        sl = slice(p0, min(M, p0 + chunk))
+        part = {k: v[sl] for k, v in ref.items()}
+        d = check(y_bits[sl], part, what=f"{what} pixels {sl.start}..{sl.stop - 1}", rms=rms,
+                  **kw)
+        n += d["n"]
+        same += d["bit_identical"] * d["n"]
+        signed += d["mean_signed_ulp"] * d["n"]
+        diag["max_ulp_rule"] = max(diag["max_ulp_rule"], d["max_ulp_rule"])
+        diag["max_ulp_at_r"] = max(diag["max_ulp_at_r"], d["max_ulp_at_r"])
+    diag.update(n=n, bit_identical=same / max(n, 1), mean_signed_ulp=signed / max(n, 1))
     return diag

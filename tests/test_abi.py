@@ -370,3 +370,21 @@ def test_tile_override_keeps_fused_norm_rows_whole(monkeypatch):
     assert cv.conv3d_plan_describe(d, epi) == base
     monkeypatch.setenv("CONV3D_TILE", "32,2,2,3,5,0,-2")
     assert "bn=320" in cv.conv3d_plan_describe(d, epi)
+
+
+def test_tile_override_never_gives_a_norm_layer_halo_partials(monkeypatch):
+    """A split fused-norm layer reduces [S][M][Cout] partials with the norm
+    epilogue; the halo kernel's fragment-order partials have a reduction
+    without it, so the override may not select a halo tile there."""
+    d = cv.make_desc((1, 5, 16, 16, 128), 256, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=4)
+    import torch
+    g = torch.ones(256, dtype=torch.bfloat16)
+    epi = cv.make_epilogue(gamma=g, norm_silu=True)
+    base = cv.conv3d_plan_describe(d, epi)
+    assert "mode=partial" in base and "ns=-1" not in base
+    for tile in ("32,2,2,4,4,5,-1", "32,4,1,4,4,9,-1"):
+        monkeypatch.setenv("CONV3D_TILE", tile)
+        assert cv.conv3d_plan_describe(d, epi) == base
+    # the same tiles are taken for a split layer without the norm
+    monkeypatch.setenv("CONV3D_TILE", "32,2,2,4,4,5,-1")
+    assert "ns=-1" in cv.conv3d_plan_describe(d, None)

@@ -6,8 +6,8 @@ bits. Cases span the kernel's thread mappings (8 to 2048 channels, 1 to 64
 channels per group, a group inside one 16-byte vector or across several),
 many chunks with a ragged last one, one-pixel frames, statistics per frame
 and per clip, in-place calls, a mean far above the spread, constant frames
-and the full-size H3 L0 activation (checked on sampled frames, which the
-per-frame statistics make exact to check one by one).
+and the full-size H3 L0 activation (every frame, which the per-frame
+statistics make exact to check one by one).
 """
 import numpy as np
 import pytest
@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads
 from convolution_video_vae_amd.layer import GroupNorm
-from parity import check_group_norm
+from parity import check_group_norm, rms_of
 
 pytestmark = pytest.mark.gpu
 
@@ -109,16 +109,20 @@ def test_constant_frame_gives_silu_of_beta_exactly():
     assert np.max(step) <= 1 and np.array_equal(np.sign(b2f_(y[:, 1])), np.sign(b2f_(r["y"][:, 1])))
 
 
-def test_full_size_h3_l0_sampled_frames():
+def test_full_size_h3_l0_every_frame():
     """The bench workload (x [1, 17, 256, 256, 128], 32 groups, per-frame
-    statistics, SiLU) in the launch configuration the bench times; frames
-    are independent, so the oracle checks frames 0, 8 and 16 one by one."""
+    statistics, SiLU) in the launch configuration the bench times, against
+    the oracle on every element: frames are independent, so the oracle runs
+    frame by frame, and the floor uses the whole tensor's RMS."""
     L = BASE
     x, gamma, beta = workloads.norm_tensors(L)
     y = run(x, gamma, beta, L.groups, eps=L.eps, silu=L.silu, t_isolated=L.t_isolated)
-    for d in (0, 8, 16):
-        xf = x[:, d:d + 1]
-        r = ref(xf, gamma, beta, L.groups, eps=L.eps, silu=L.silu)
-        diag = check_group_norm(y[:, d:d + 1], r, what=f"frame {d}")
+    refs = []
+    for d in range(L.x_shape[1]):
+        r = ref(x[:, d:d + 1], gamma, beta, L.groups, eps=L.eps, silu=L.silu)
+        refs.append({"y": r["y"], "a": r["a"]})
+    rms = rms_of(np.concatenate([r["y"].ravel() for r in refs]))
+    for d, r in enumerate(refs):
+        diag = check_group_norm(y[:, d:d + 1], r, what=f"frame {d}", rms=rms)
         print(f"[gn] frame {d}: {diag}", flush=True)
         assert diag["bit_identical"] > 0.99, diag

@@ -2,10 +2,9 @@
 
 Integer-valued data, impulses, packing and transposes must match bit for bit;
 random data must satisfy the ulp rule in tests/parity.py. Small cases span
-several tiles and a ragged tail and are compared element by element; the
-full-size layers are compared on sampled output pixels (all channels of each)
-in the launch configuration the benchmark times, and every output element is
-checked to have been written (outputs are pre-filled with NaN).
+several tiles and a ragged tail; the full-size layers run in the launch
+configuration the benchmark times. Every case is compared on every output
+element, and outputs are pre-filled with NaN so an unwritten element fails.
 """
 import numpy as np
 import pytest
@@ -14,7 +13,8 @@ import torch
 import convolution_video_vae_amd as cv
 import oracle
 import workloads
-from parity import b2f, check
+from guard import Guarded
+from parity import b2f, check, check_every_element, oracle_every_pixel
 
 pytestmark = pytest.mark.gpu
 
@@ -59,18 +59,23 @@ def run_gpu(x, w, *, stride=(1, 1, 1), pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), bias=
     od = cv.conv3d_output_dims(desc)
     n = x.shape[0]
     yshape = (n,) + od + (cout,) if out_layout == cv.NDHWC else (n, cout) + od
-    y = poisoned(yshape)
+    yg = Guarded(yshape)
+    y = yg.t
     bd = bias.cuda() if bias is not None else None
     rd = residual.cuda().contiguous() if residual is not None else None
     gd = gamma.cuda() if gamma is not None else None
-    ro = poisoned(yshape) if want_residual_out else None
+    rog = Guarded(yshape) if want_residual_out else None
+    ro = rog.t if rog is not None else None
     epi = cv.make_epilogue(bias=bd, residual=rd, gamma=gd, residual_out=ro, norm_silu=norm)
     ws_bytes = cv.conv3d_workspace_bytes(desc, epi)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    cv.conv3d_fwd(desc, xd, wp, epi if epi.flags else None, y, ws, ws_bytes)
+    wsg = Guarded((max(ws_bytes, 16),), dtype=torch.uint8, fill=0)
+    cv.conv3d_fwd(desc, xd, wp, epi if epi.flags else None, y, wsg.t, ws_bytes)
     torch.cuda.synchronize()
+    yg.assert_intact(label + " y")
+    wsg.assert_intact(label + " workspace")
     out = {"y": y.cpu(), "plan": cv.conv3d_plan_describe(desc, epi if epi.flags else None)}
     if ro is not None:
+        rog.assert_intact(label + " residual_out")
         out["residual_out"] = ro.cpu()
     return out
 
@@ -362,38 +367,39 @@ def test_bias_residual_without_norm():
 
 # ------------------------------------------------------------------ full-size layers
 
-def sample_pixels(layer, count, seed):
-    M = layer.m
-    rng = np.random.default_rng(seed)
-    n, d, h, w = (layer.x_shape[0],) + layer.out_dhw()
-    edges = []
-    for dq in sorted({0, min(1, d - 1), d - 1}):
-        for hq in sorted({0, h - 1}):
-            for wq in sorted({0, min(1, w - 1), w - 1}):
-                edges.append((dq * h + hq) * w + wq)
-    pix = np.concatenate([np.arange(min(64, M)), np.arange(max(0, M - 64), M), np.array(edges),
-                          rng.integers(0, M, size=count)])
-    return np.unique(pix)
-
-
 FULL = [n for n, L in workloads.LAYERS.items() if not L.fp8]   # fp8: tests/test_gpu_fp8.py
 
 
+def oracle_chunk(layer):
+    """Output pixels per oracle call: about 50 GFLOP of direct convolution."""
+    per_pixel = 2.0 * layer.cout * layer.cin * layer.live_taps
+    return int(max(1024, min(layer.m, 5e10 // per_pixel)))
+
+
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_layer_sampled(name):
+def test_full_size_layer_every_element(name):
+    """The layer at its full size, in the launch configuration the benchmark
+    times, against the oracle on every output element (and, for the fused
+    layer, every element of the saved residual sum)."""
     L = workloads.LAYERS[name]
     t = workloads.make_tensors(L)
     kw = dict(bias=t.bias, residual=t.residual, gamma=t.gamma, norm=L.norm_silu, **geom(L))
     g = run_gpu(t.x, t.w, want_residual_out=L.residual, label=name, **kw)
-    y = bits(g["y"])
+    y = bits(g["y"]).reshape(-1, L.cout)
     assert not np.any(y == NAN_BF16), "unwritten output elements"
-    count = 96 if L.cin >= 512 else 1500
-    pix = sample_pixels(L, count, seed=L.family)
-    r = run_oracle(t.x, t.w, pixels=pix, **kw)
-    diag = check(y.reshape(-1, L.cout)[pix], r, fused=L.norm_silu,
-                 gamma_bits=None if t.gamma is None else bits(t.gamma), what=name)
-    print(name, g["plan"], diag)
+    chunk = oracle_chunk(L)
+    ref = oracle_every_pixel(lambda pix: run_oracle(t.x, t.w, pixels=pix, **kw), L.m, chunk,
+                             what=name)
+    diag = check_every_element(y, ref, chunk=chunk, fused=L.norm_silu,
+                               gamma_bits=None if t.gamma is None else bits(t.gamma), what=name)
+    print(name, g["plan"], diag, flush=True)
     assert diag["bit_identical"] > 0.97
+    if L.residual:
+        ro = bits(g["residual_out"]).reshape(-1, L.cout)
+        assert not np.any(ro == NAN_BF16), "unwritten residual_out elements"
+        dv = check_every_element(ro, dict(ref, y=ref["value"]), chunk=chunk,
+                                 what=name + " residual_out")
+        print(name, "residual_out", dv, flush=True)
 
 
 def test_fused_layer_ncdhw_boundary_variants_are_bit_identical():
@@ -442,3 +448,52 @@ def test_slot_160_channel_tile_random(kind):
     assert diag["bit_identical"] > 0.99, diag
     if kind != "raw":
         check(bits(g["residual_out"]), dict(r, y=r["value"]), what="slot160 residual_out")
+
+
+# ------------------------------------------------------------------ contract edge cases
+
+def _closed_forms():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "epilogue_closed_forms.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("route", ["fused_slot", "split_reduce"])
+@pytest.mark.parametrize("case", _closed_forms(), ids=lambda c: c["name"])
+def test_contract_closed_forms_on_the_gpu(case, route):
+    """The hand-worked rows of the contract (cuDNN page, "Operation
+    Contract"; tests/golden) through the HIP epilogues: a zero weight makes
+    the conv exactly 0, so bias, residual and gamma fix every value. Both the
+    single-pass fused kernel (the whole 320-channel row in one work-group)
+    and the split-K route (fp32 partials, then the reducing norm epilogue)
+    must give the golden numbers bit for bit, and the saved residual sum."""
+    C = 320
+    rng = np.random.default_rng(23)
+    x = torch.from_numpy(rng.standard_normal((1, 3, 6, 9, 32)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.zeros((C, 32, 3, 3, 3), dtype=torch.bfloat16)
+    bias = torch.full((C,), case["bias"], dtype=torch.float32)
+    if "bias_channel0" in case:
+        bias[0] = case["bias_channel0"]
+    gamma = torch.full((C,), case["gamma"], dtype=torch.float32)
+    if "gamma_channel0" in case:
+        gamma[0] = case["gamma_channel0"]
+    gamma = gamma.to(torch.bfloat16)
+    out_shape = (1, 1, 4, 7, C)
+    residual = None
+    if case["residual"] is not None:
+        residual = torch.full(out_shape, case["residual"], dtype=torch.bfloat16)
+    g = run_gpu(x, w, bias=bias, residual=residual, gamma=gamma, norm=True,
+                split_k=1 if route == "fused_slot" else 3, want_residual_out=residual is not None,
+                label=f"golden_{case['name']}_{route}")
+    want_plan = "mode=norm" if route == "fused_slot" else "mode=partial"
+    assert want_plan in g["plan"], g["plan"]
+    y = b2f(bits(g["y"])).reshape(-1, C)
+    np.testing.assert_array_equal(y[:, 0], np.float32(case["out_channel0"]))
+    np.testing.assert_array_equal(y[:, 1:], np.float32(case["out"]))
+    r = run_oracle(x, w, bias=bias, residual=residual, gamma=gamma, norm=True)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"])
+    if residual is not None:
+        v = b2f(bits(g["residual_out"])).reshape(-1, C)
+        np.testing.assert_array_equal(v[:, 1:], np.float32(case["value"]))
+        np.testing.assert_array_equal(bits(g["residual_out"]), r["value"])

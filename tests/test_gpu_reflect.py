@@ -14,7 +14,7 @@ import oracle
 import workloads
 import convolution_video_vae_amd as cv
 from convolution_video_vae_amd.layer import Conv3d
-from parity import check
+from parity import check, check_every_element, oracle_every_pixel
 
 pytestmark = pytest.mark.gpu
 
@@ -78,23 +78,22 @@ def test_reflect_fused_norm_random():
     check(bits(y), ref, fused=True, gamma_bits=bits(t.gamma), what="reflect fused")
 
 
-def test_reflect_h3_l0_sampled():
+def test_reflect_h3_l0_every_element():
     """H3 L0 at full size with its own padding (reflect spatial, causal time)
-    in the launch configuration the benchmark times; the oracle on sampled
-    output pixels, among them every border case (rows and columns 0, 1, 254,
-    255, the first frames)."""
-    L = workloads.LAYERS["h3_l0_128"]
+    in the launch configuration the benchmark times, against the oracle on
+    every output element (the reflected border rows and columns included)."""
+    L = workloads.LAYERS["h3_l0_128_reflect"]
     t = workloads.make_tensors(L)
     conv = Conv3d(t.w.cuda(), L.x_shape, pad_lo=L.pad_lo, pad_hi=L.pad_hi, pad_mode=R)
     y = conv(t.x.cuda())
     torch.cuda.synchronize()
-    D, H, W = L.out_dhw()
-    rng = np.random.default_rng(14)
-    pts = [(d, h, w) for d in (0, 1, 16) for h in (0, 1, 254, 255) for w in (0, 1, 254, 255)]
-    pts += [tuple(int(v) for v in rng.integers(0, (D, H, W))) for _ in range(64)]
-    pix = np.array([(d * H + h) * W + w for d, h, w in pts])
+    got = bits(y).reshape(-1, L.cout)
     xr = oracle.reflect_pad_hw(bits(t.x), (1, 1), (1, 1))
-    ref = oracle.conv3d(xr, bits(t.w), pad_lo=(2, 0, 0), pad_hi=(0, 0, 0), pixels=pix,
-                        intermediates=True)
-    got = bits(y).reshape(-1, L.cout)[pix]
-    check(got, ref, what="h3 l0 reflect sampled")
+    wb = bits(t.w)
+    chunk = 1 << 16
+    ref = oracle_every_pixel(
+        lambda pix: oracle.conv3d(xr, wb, pad_lo=(2, 0, 0), pad_hi=(0, 0, 0), pixels=pix,
+                                  intermediates=True), L.m, chunk, what="h3 l0 reflect")
+    diag = check_every_element(got, ref, chunk=chunk, what="h3 l0 reflect")
+    print("[reflect] h3 l0 every element:", diag, flush=True)
+    assert diag["bit_identical"] > 0.97

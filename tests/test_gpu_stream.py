@@ -15,6 +15,7 @@ import convolution_video_vae_amd as cv
 import workloads
 from convolution_video_vae_amd.layer import Conv3d, stream_pack_input
 from oracle.stream import cache_tail, pack_stream_input, pad_output
+from guard import Guarded
 from parity import check
 
 pytestmark = pytest.mark.gpu
@@ -54,10 +55,13 @@ def test_padded_output_integer_exact(name, xs, cout, P, cf):
     hist = noise_bits(rng, (1, P, Ho, Wo, cout))
     y0[:, 2 - P:2, 1:1 + Ho, 1:1 + Wo] = hist
     c0 = noise_bits(rng, conv.cache_shape)
-    y = from_bits(y0).cuda()
-    cache = from_bits(c0).cuda()
+    yg = Guarded(y0.shape, fill=y0)
+    cg = Guarded(c0.shape, fill=c0)
+    y, cache = yg.t, cg.t
     conv(x.cuda(), y=y, cache=cache)
     torch.cuda.synchronize()
+    yg.assert_intact(name + " padded y")
+    cg.assert_intact(name + " cache")
     ref = oracle.conv3d(bits(x), bits(w), bias=b.numpy())
     want = pad_output(ref, (2, 1, 1), (0, 1, 1), history=hist if P else None)
     assert np.array_equal(bits(y), want)
