@@ -10,6 +10,8 @@ can have been made at:
 
   ulp(s) = 2^(floor(log2 s) - 7)                       (bf16: 8 significant bits)
   raw:    |y - r| <= 2 ulp(max(|r|, |conv|, 2^-8 RMS(r)))
+          (the saved residual sum value = B(B(conv + bias) + residual) is
+          measured at max(|r|, |conv|, |main|, 2^-8 RMS(r)))
   fused:  |y - r| <= 4 ulp(max(|r|, |affine|, k*max(|conv|,|main|,|value|), 2^-8 RMS(r)))
           with k = sqrt(C) |gamma_c| / den, which carries a pre-norm error to
           the output's scale.
@@ -40,10 +42,16 @@ def rms_of(bits) -> float:
     return float(np.sqrt(np.mean(r * r))) if r.size else 0.0
 
 
-def check(y_bits, ref, *, fused=False, gamma_bits=None, cout=None, what="", rms=None):
+def check(y_bits, ref, *, fused=False, gamma_bits=None, cout=None, what="", rms=None,
+          through=("conv",)):
     """Assert the rule; return diagnostics. ref: oracle dict (intermediates=True).
     rms: the RMS of the whole reference output when y / ref are one chunk of
-    it (the floor is a property of the layer, not of the chunk)."""
+    it (the floor is a property of the layer, not of the chunk).
+    through: the oracle intermediates the raw result was rounded through;
+    the error is measured in ulps of the largest of them. A raw conv output
+    passes through `conv` alone; the saved residual sum `value` =
+    B(main + residual) with main = B(conv + bias) passes through conv and
+    main, so one ulp of a correct conv can move it by one ulp of main."""
     y = b2f(y_bits).astype(np.float64)
     r = b2f(ref["y"]).astype(np.float64)
     assert y.shape == r.shape, (y.shape, r.shape)
@@ -62,18 +70,21 @@ def check(y_bits, ref, *, fused=False, gamma_bits=None, cout=None, what="", rms=
                                    k * pre, np.full_like(r, floor)])
         nulp = 4.0
     else:
-        scale = np.maximum.reduce([np.abs(r), conv, np.full_like(r, floor)])
+        terms = [np.abs(r), np.full_like(r, floor)]
+        terms += [np.abs(b2f(ref[k]).astype(np.float64)) for k in through]
+        scale = np.maximum.reduce(terms)
         nulp = 2.0
     err = np.abs(y - r)
     allowed = nulp * ulp_bf16(scale)
     bad = err > allowed
-    at_r = err / ulp_bf16(np.abs(r))
+    # diagnostics in ulps of |r| (floored, so exact zeros do not divide by ~0)
+    at = ulp_bf16(np.maximum(np.abs(r), floor))
     diag = {
         "n": int(r.size),
         "bit_identical": float(np.mean(y_bits == ref["y"])) if r.size else 1.0,
         "max_ulp_rule": float(np.max(err / ulp_bf16(scale))) if r.size else 0.0,
-        "max_ulp_at_r": float(np.max(at_r)) if r.size else 0.0,
-        "mean_signed_ulp": float(np.mean((y - r) / ulp_bf16(np.abs(r)))) if r.size else 0.0,
+        "max_ulp_at_r": float(np.max(err / at)) if r.size else 0.0,
+        "mean_signed_ulp": float(np.mean((y - r) / at)) if r.size else 0.0,
     }
     if np.any(bad):
         idx = np.argwhere(bad)[:5]

@@ -25,12 +25,15 @@ def bits(t):
 
 
 CASES = [
-    # name, x shape, cout, pad_lo, pad_hi, epilogue, plan substrings
-    ("persistent_slot", (1, 9, 128, 126, 128), 128, (2, 1, 1), (0, 1, 1), "none",
+    # name, x shape, cout, pad_lo, pad_hi, epilogue, split_k, plan substrings
+    ("persistent_slot", (1, 9, 128, 126, 128), 128, (2, 1, 1), (0, 1, 1), "none", 0,
      ("ns=-2", "persistent=1")),
-    ("split_k_halo", (1, 5, 16, 16, 512), 1024, (2, 1, 1), (0, 1, 1), "bias",
+    ("split_k_halo", (1, 5, 16, 16, 512), 1024, (2, 1, 1), (0, 1, 1), "bias", 0,
      ("ns=-1", "mode=partial")),
-    ("fused_norm", (1, 5, 14, 22, 160), 320, (0, 0, 0), (0, 0, 0), "norm", ("mode=norm",)),
+    ("fused_norm_slot", (1, 5, 14, 22, 160), 320, (0, 0, 0), (0, 0, 0), "norm", 1,
+     ("mode=norm", "ns=-2")),
+    ("fused_norm_split_reduce", (1, 5, 14, 22, 160), 320, (0, 0, 0), (0, 0, 0), "norm", 0,
+     ("mode=partial", "reduce=1")),
 ]
 
 
@@ -42,14 +45,15 @@ def _device():
     yield
 
 
-@pytest.mark.parametrize("name,xs,cout,lo,hi,epi,plan_has", CASES, ids=[c[0] for c in CASES])
-def test_graph_replay_is_bit_identical(name, xs, cout, lo, hi, epi, plan_has):
+@pytest.mark.parametrize("name,xs,cout,lo,hi,epi,split_k,plan_has", CASES,
+                         ids=[c[0] for c in CASES])
+def test_graph_replay_is_bit_identical(name, xs, cout, lo, hi, epi, split_k, plan_has):
     print(f"[graph] {name} x={xs} cout={cout} epilogue={epi}", flush=True)
     L = workloads.Layer(name, 5, xs, cout, pad_lo=lo, pad_hi=hi, bias=epi != "none",
                         residual=epi == "norm", norm_silu=epi == "norm")
     t = workloads.make_tensors(L)
     conv = Conv3d(t.w.cuda(), xs, pad_lo=lo, pad_hi=hi, bias=t.bias, gamma=t.gamma,
-                  norm_silu=L.norm_silu, residual=L.residual)
+                  norm_silu=L.norm_silu, residual=L.residual, split_k=split_k)
     probe = cv.make_epilogue(bias=conv.bias, gamma=conv.gamma, norm_silu=conv.norm_silu)
     probe.flags |= cv.EPI_RESIDUAL if L.residual else 0
     plan = cv.conv3d_plan_describe(conv.desc, probe if probe.flags else None)

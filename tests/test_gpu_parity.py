@@ -339,7 +339,8 @@ def test_random_small_against_oracle(case):
                  gamma_bits=None if t.gamma is None else bits(t.gamma), what=name)
     print(name, g["plan"], diag)
     if L.residual:
-        check(bits(g["residual_out"]), dict(r, y=r["value"]), what=name + " residual_out")
+        check(bits(g["residual_out"]), dict(r, y=r["value"]), what=name + " residual_out",
+              through=("conv", "main"))
 
 
 def test_fused_reduce_path_matches_fused_kernel():
@@ -361,7 +362,7 @@ def test_bias_residual_without_norm():
     t = workloads.make_tensors(L, x_shape=(1, 4, 9, 13, 160))
     g = run_gpu(t.x, t.w, bias=t.bias, residual=t.residual, want_residual_out=True, label="bias_res")
     r = run_oracle(t.x, t.w, bias=t.bias, residual=t.residual)
-    check(bits(g["y"]), r, what="bias+residual")
+    check(bits(g["y"]), r, what="bias+residual", through=("conv", "main"))
     np.testing.assert_array_equal(bits(g["residual_out"]), bits(g["y"]))
 
 
@@ -398,7 +399,7 @@ def test_full_size_layer_every_element(name):
         ro = bits(g["residual_out"]).reshape(-1, L.cout)
         assert not np.any(ro == NAN_BF16), "unwritten residual_out elements"
         dv = check_every_element(ro, dict(ref, y=ref["value"]), chunk=chunk,
-                                 what=name + " residual_out")
+                                 what=name + " residual_out", through=("conv", "main"))
         print(name, "residual_out", dv, flush=True)
 
 
@@ -447,7 +448,8 @@ def test_slot_160_channel_tile_random(kind):
                  gamma_bits=None if kind != "norm" else bits(t.gamma), what="slot160 " + kind)
     assert diag["bit_identical"] > 0.99, diag
     if kind != "raw":
-        check(bits(g["residual_out"]), dict(r, y=r["value"]), what="slot160 residual_out")
+        check(bits(g["residual_out"]), dict(r, y=r["value"]), what="slot160 residual_out",
+              through=("conv", "main"))
 
 
 # ------------------------------------------------------------------ contract edge cases
