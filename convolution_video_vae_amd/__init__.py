@@ -40,7 +40,7 @@ EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_d
             "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm",
             "conv3d_padded_workspace_bytes", "conv3d_fwd_padded", "conv3d_stream_pack_input",
             "conv3d_pack_weight_2d", "conv3d_norm_silu", "conv3d_packed_weight_bytes_fp8",
-            "conv3d_pack_weight_fp8")
+            "conv3d_pack_weight_fp8", "conv3d_fwd_noalloc")
 
 
 class Conv3dError(RuntimeError):
@@ -105,6 +105,8 @@ def lib():
         L.conv3d_workspace_bytes.argtypes = [pd, pe, ctypes.POINTER(sz)]
         L.conv3d_fwd.restype = i
         L.conv3d_fwd.argtypes = [pd, vp, vp, pe, vp, vp, sz, vp]
+        L.conv3d_fwd_noalloc.restype = i
+        L.conv3d_fwd_noalloc.argtypes = [pd, vp, vp, pe, vp, vp]
         L.conv3d_transpose.restype = i
         L.conv3d_transpose.argtypes = [vp, i, vp, i, i, i, i, i, vp]
         L.conv3d_status_str.restype = ctypes.c_char_p
@@ -271,6 +273,16 @@ def conv3d_fwd(desc: conv3d_desc, x, w_packed, epi: Optional[conv3d_epilogue], y
     _check(lib().conv3d_fwd(ctypes.byref(desc), _ptr(x), _ptr(w_packed),
                             ctypes.byref(epi) if epi else None, _ptr(y), _ptr(workspace),
                             workspace_bytes, _stream(stream)), "conv3d_fwd")
+
+
+def conv3d_fwd_noalloc(desc: conv3d_desc, x, w_packed, epi: Optional[conv3d_epilogue], y,
+                       stream=None) -> None:
+    """conv3d_fwd without a workspace: the library's fixed per-device
+    scratch serves instead (calls on one GPU must not overlap in time)."""
+    _check_conv_buffers(desc, x, w_packed, epi, y)
+    _check(lib().conv3d_fwd_noalloc(ctypes.byref(desc), _ptr(x), _ptr(w_packed),
+                                    ctypes.byref(epi) if epi else None, _ptr(y),
+                                    _stream(stream)), "conv3d_fwd_noalloc")
 
 
 def conv3d_transpose(src, src_layout: int, dst, n: int, c: int, d: int, h: int, w: int,

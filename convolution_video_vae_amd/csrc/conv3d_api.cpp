@@ -577,6 +577,18 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
   return conv3d_fwd_padded(desc, x, w_packed, epi, nullptr, y, workspace, workspace_bytes, stream);
 }
 
+conv3d_status conv3d_fwd_noalloc(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                 const conv3d_epilogue* epi, void* y, void* stream) {
+  size_t need = 0;
+  const conv3d_status st = conv3d_workspace_bytes(desc, epi, &need);
+  if (st != CONV3D_OK) return st;
+  if (!x || !w_packed || !y) return CONV3D_ERR_NULL;
+  if (need > kScratchBytes) return CONV3D_ERR_WORKSPACE;   // beyond the fixed scratch
+  void* ws = nullptr;
+  if (need > 0 && scratch_address(&ws) != 0) return CONV3D_ERR_HIP;
+  return conv3d_fwd(desc, x, w_packed, epi, y, ws, need > 0 ? kScratchBytes : 0, stream);
+}
+
 conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const void* w_packed,
                                 const conv3d_epilogue* epi, const conv3d_out_pad* op, void* y,
                                 void* workspace, size_t workspace_bytes, void* stream) {

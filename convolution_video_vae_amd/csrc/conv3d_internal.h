@@ -111,6 +111,13 @@ int launch_igemm(const TileCfg& cfg, int mode, bool reflect, bool fp8, const Ige
                  int grid, void* stream);
 bool igemm_has_config(const TileCfg& cfg, int mode, bool reflect = false, bool fp8 = false);
 int launch_reduce(const ReduceArgs& args, void* stream);
+// Scratch memory of conv3d_fwd_noalloc: a file-scope device array of
+// kScratchBytes (conv3d_kernels.hip) that every GPU the library runs on
+// holds until the process ends. scratch_address stores the current
+// device's address of it in *ptr (looked up once per device with
+// hipGetSymbolAddress) and returns 0, or a nonzero HIP error code.
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+int scratch_address(void** ptr);
 int launch_queue_reset(unsigned* queue, void* stream);
 int launch_group_norm(const GroupNormArgs& args, void* stream);
 // Padded outputs: the unpadded output y0 [N][Do][Ho][Wo][Cout] placed into

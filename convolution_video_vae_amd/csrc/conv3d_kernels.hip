@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "conv3d_device.h"
 #include "conv3d_internal.h"
@@ -577,6 +578,33 @@ int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int A, int B, vo
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        (hipStream_t)stream, src, dst, A, B, ta, tb);
   return (int)hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Scratch of the entry point that allocates nothing. In host code `scratch`
+// names a host-side stand-in, not device memory: only the address
+// hipGetSymbolAddress returns for the current device may reach a kernel.
+// --------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int launch_queue_reset(unsigned* queue, void* stream) {

@@ -201,6 +201,25 @@ conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_p
  * With cache != NULL, the last min(cache_frames, Do) output frames of each
  * sample are also written to the last frames of cache, NDHWC
  * [n][cache_frames][Ho][Wo][cout]; older cache frames are the caller's. */
+/* conv3d_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, semantics, kernels and results as conv3d_fwd, but no workspace
+ * argument: the split-K partials, the tile queues and the NDHWC staging of
+ * NCDHW operands live in a fixed device array of 96 MiB that the library
+ * holds on every GPU it runs on until the process ends (looked up once per
+ * device on the first call there, with that device current). Nothing is
+ * allocated by the call.
+ * Calls whose plan needs more than 96 MiB (conv3d_workspace_bytes) return
+ * CONV3D_ERR_WORKSPACE before anything is enqueued. All calls on one GPU
+ * share that GPU's array: calls that may overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller;
+ * calls on one stream are ordered and safe. Every value a call reads from
+ * the array is written earlier in the same call (the tile queues are
+ * cleared by a kernel, not by a memset). Other errors as conv3d_fwd;
+ * CONV3D_ERR_HIP if the array's address cannot be obtained. */
+conv3d_status conv3d_fwd_noalloc(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                 const conv3d_epilogue* epi, void* y, void* stream);
+
 typedef struct {
   int pad_lo[3];       /* >= 0: time, h, w */
   int pad_hi[3];       /* >= 0 */

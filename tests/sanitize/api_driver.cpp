@@ -195,6 +195,21 @@ int main() {
     EXPECT(conv3d::g_launches, n0);
   }
 
+  // The entry point without a workspace: the fixed scratch serves.
+  {
+    conv3d_desc d = make(1, 5, 16, 16, 1024, 1024, 2, 1, 1, 0, 1, 1);
+    const int n0 = conv3d::g_launches;
+    EXPECT(conv3d_fwd_noalloc(&d, buf(1), buf(2), nullptr, buf(3), nullptr), CONV3D_OK);
+    if (conv3d::g_launches == n0) ++g_fail;
+    conv3d_desc big = make(1, 17, 256, 256, 128, 128, 2, 1, 1, 0, 1, 1);
+    big.layout = CONV3D_NCDHW;   // a 285 MB staging copy: more than the scratch
+    const int n1 = conv3d::g_launches;
+    EXPECT(conv3d_fwd_noalloc(&big, buf(1), buf(2), nullptr, buf(3), nullptr),
+           CONV3D_ERR_WORKSPACE);
+    EXPECT(conv3d_fwd_noalloc(&d, nullptr, buf(2), nullptr, buf(3), nullptr), CONV3D_ERR_NULL);
+    EXPECT(conv3d::g_launches, n1);
+  }
+
   // The other entry points.
   EXPECT(conv3d_pack_weight(buf(1), buf(2), 128, 128, nullptr), CONV3D_OK);
   EXPECT(conv3d_pack_weight(buf(1), buf(1), 128, 128, nullptr), CONV3D_ERR_OVERLAP);

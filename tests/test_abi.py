@@ -388,3 +388,23 @@ def test_tile_override_never_gives_a_norm_layer_halo_partials(monkeypatch):
     # the same tiles are taken for a split layer without the norm
     monkeypatch.setenv("CONV3D_TILE", "32,2,2,4,4,5,-1")
     assert "ns=-1" in cv.conv3d_plan_describe(d, None)
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """conv3d_fwd_noalloc checks the descriptor, the pointers and the plan's
+    scratch need on the host first: a plan above the fixed 96 MiB (here the
+    headline layer given NCDHW, whose 285 MB staging copy would not fit)
+    is refused with CONV3D_ERR_WORKSPACE and nothing is enqueued."""
+    lib = cv.lib()
+    L = workloads.LAYERS["h3_l0_128"]
+    n, d, h, w, c = L.x_shape
+    big = cv.make_desc((n, c, d, h, w), L.cout, pad_lo=L.pad_lo, pad_hi=L.pad_hi, layout=cv.NCDHW)
+    assert cv.conv3d_workspace_bytes(big) > 96 << 20
+    X = 1 << 32
+    assert lib.conv3d_fwd_noalloc(ctypes.byref(big), X, X + (1 << 31), None, X + (1 << 33),
+                                  None) == 5
+    small = cv.make_desc(L.x_shape, L.cout, pad_lo=L.pad_lo, pad_hi=L.pad_hi)
+    assert lib.conv3d_fwd_noalloc(ctypes.byref(small), None, X, None, X + (1 << 33), None) == 1
+    bad = cv.make_desc((1, 1, 4, 4, 64), 64)          # empty valid output
+    assert lib.conv3d_fwd_noalloc(ctypes.byref(bad), X, X, None, X, None) == 2
+    assert lib.conv3d_fwd_noalloc(None, X, X, None, X, None) == 1
