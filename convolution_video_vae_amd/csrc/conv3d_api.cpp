@@ -76,6 +76,11 @@ struct Problem {
 
 struct Plan {
   TileCfg cfg;
+  // live-balanced K split of halo-kernel partials (IgemmArgs::vsplit)
+  bool vsplit = false;
+  int per_n = 0;
+  uint16_t split_base[kMaxVTiles + 1] = {};
+  uint16_t wg[kMaxVWG] = {};
   int mode;        // EPI_STORE / EPI_NORM / EPI_PARTIAL
   int splits;      // >1 or reduce needed -> partial + reduce
   bool reduce;     // a reduce kernel finishes the epilogue
@@ -229,6 +234,75 @@ bool pick_halo(const Problem& pr, const TileCfg (&cands)[N], int mode, TileCfg* 
   return false;
 }
 
+// Live K steps of halo-kernel pixel tile t (BM output pixels from t * BM):
+// the (kd, kh) pairs for which some output row of the tile reads real input
+// (the kernel's per-row masks, ORed over the tile's rows), times the
+// 32-channel chunks.
+int tile_live_steps(const Problem& pr, int BM, int t, int cc) {
+  const long long m0 = (long long)t * BM, m1 = std::min<long long>(m0 + BM, pr.M) - 1;
+  unsigned mask = 0;
+  for (long long r = m0 / pr.Wo; r <= m1 / pr.Wo && mask != 511u; ++r) {
+    const long long t2 = r / pr.Ho;
+    const int ho = (int)(r - t2 * pr.Ho);
+    const int dq = (int)(t2 % pr.Do);
+    const int d0 = dq * pr.sd - pr.pd, h0 = ho * pr.sh - pr.ph;
+    for (int kd = 0; kd < 3; ++kd)
+      for (int kh = 0; kh < 3; ++kh) {
+        const bool dv = d0 + kd >= 0 && d0 + kd < pr.d;
+        const bool hv = pr.reflect || (h0 + kh >= 0 && h0 + kh < pr.h);
+        if (dv && hv) mask |= 1u << (kd * 3 + kh);
+      }
+  }
+  return __builtin_popcount(mask) * cc;
+}
+
+// Live-balanced K split of a halo-kernel partial plan: every pixel tile is
+// cut into slices of at most q live K steps, q the smallest quota (of at
+// least 4) whose slices fit one round of work-groups (kCUs over all channel
+// tiles). Tiles
+// that see fewer taps (a causal layer's first frames) get fewer slices, so
+// all work-groups carry about the same live work. Launch order is slice-
+// major (slice s of every tile, then s + 1), which keeps the same slice of
+// tiles with the same live taps, i.e. the same weight rows, next to each
+// other (they land on one XCD's L2). Returns false when the plan does not
+// fit the tables.
+bool plan_vsplit(const Problem& pr, int cc, Plan* pl) {
+  const int T = pl->m_tiles, NT = pl->n_tiles;
+  if (T > kMaxVTiles || NT <= 0) return false;
+  const int cap = std::min(kCUs / NT, kMaxVWG);
+  if (cap < T) return false;
+  int L[kMaxVTiles];
+  long long total = 0;
+  for (int t = 0; t < T; ++t) {
+    L[t] = tile_live_steps(pr, pl->cfg.bm(), t, cc);
+    total += L[t];
+  }
+  // (at least 4 live steps per slice, as the uniform split keeps)
+  int q = (int)std::max(4LL, ceil_div(total, cap));
+  for (;; ++q) {
+    long long n = 0;
+    for (int t = 0; t < T; ++t) n += std::max(1LL, ceil_div(L[t], q));
+    if (n <= cap) break;
+  }
+  int S[kMaxVTiles], smax = 0;
+  pl->split_base[0] = 0;
+  for (int t = 0; t < T; ++t) {
+    S[t] = (int)std::max(1LL, ceil_div(L[t], q));
+    if (S[t] > 255) return false;
+    smax = std::max(smax, S[t]);
+    pl->split_base[t + 1] = (uint16_t)(pl->split_base[t] + S[t]);
+  }
+  int i = 0;
+  for (int sl = 0; sl < smax; ++sl)
+    for (int t = 0; t < T; ++t)
+      if (sl < S[t]) pl->wg[i++] = (uint16_t)((t << 8) | sl);
+  pl->per_n = i;
+  pl->vsplit = true;
+  pl->splits = smax;
+  pl->grid = (long long)i * NT;
+  return true;
+}
+
 // K steps a kernel walks: 27 taps x 32-channel chunks, or for the halo
 // kernel 9 (kd, kh) pairs x 32-channel chunks.
 int steps_of(const TileCfg& c, int cc) { return c.ns < 0 ? 9 * cc : 27 * cc; }
@@ -324,6 +398,11 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
                                  : (int)ceil_div(pr.M, pl->cfg.bm());
   pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());
   pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;
+  // An automatic split of halo-kernel partials follows the live work.
+  pl->vsplit = false;
+  if (split && split_req == 0 && pl->mode == EPI_PARTIAL && pl->cfg.ns == -1 &&
+      !getenv("CONV3D_UNIFORM_SPLIT"))
+    plan_vsplit(pr, cc, pl);
   // Halo kernel with more tiles than CUs: persistent work-groups.
   pl->persistent = pl->cfg.ns < 0 && pl->grid > kCUs && !getenv("CONV3D_NO_PERSIST");
   if (pl->persistent) pl->grid = kCUs;
@@ -339,11 +418,14 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
     if (pr.flags & F_RESIDUAL_OUT) { pl->off_rout = off; off = align256(off + pr.y_bytes); }
   }
   if (pl->reduce) {
-    // Halo-kernel partials are whole tiles in fragment order.
-    const size_t rows = pl->cfg.ns == -1 ? (size_t)pl->m_tiles * pl->cfg.bm() : (size_t)pr.M;
-    const size_t cols = pl->cfg.ns == -1 ? (size_t)pl->n_tiles * pl->cfg.bn() : (size_t)pr.cout;
+    // Halo-kernel partials are whole tiles in fragment order, one per
+    // work-group.
     pl->off_part = off;
-    off = align256(off + (size_t)pl->splits * rows * cols * 4);
+    if (pl->cfg.ns == -1) {
+      off = align256(off + (size_t)pl->grid * pl->cfg.bm() * pl->cfg.bn() * 4);
+    } else {
+      off = align256(off + (size_t)pl->splits * (size_t)pr.M * (size_t)pr.cout * 4);
+    }
   }
   if (pl->persistent) {
     pl->off_queue = off;
@@ -563,10 +645,10 @@ conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogu
     static const char* names[] = {"store", "norm", "partial"};
     snprintf(buf, len,
              "igemm mfma=%d wm=%d wn=%d pb=%d cb=%d kb=%d ns=%d bm=%d bn=%d mode=%s splits=%d "
-             "steps=%d grid=%lld persistent=%d reduce=%d workspace=%zu",
+             "steps=%d grid=%lld persistent=%d reduce=%d workspace=%zu%s",
              pl.cfg.r, pl.cfg.wm, pl.cfg.wn, pl.cfg.pb, pl.cfg.cb, pl.cfg.kb, pl.cfg.ns, pl.cfg.bm(),
              pl.cfg.bn(), names[pl.mode], pl.splits, pl.steps, pl.grid, (int)pl.persistent,
-             (int)pl.reduce, pl.total);
+             (int)pl.reduce, pl.total, pl.vsplit ? " split=live" : "");
   }
   return CONV3D_OK;
 }
@@ -682,6 +764,12 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   a.inv_ho = 1.0f / (float)pr.Ho;
   a.inv_do = 1.0f / (float)pr.Do;
   a.inv_wp = 1.0f / (float)(pr.Wo + 2);
+  if (pl.vsplit) {
+    a.vsplit = 1;
+    a.per_n = pl.per_n;
+    memcpy(a.split_base, pl.split_base, sizeof a.split_base);
+    memcpy(a.wg, pl.wg, sizeof a.wg);
+  }
   if (pl.grid > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
   if (pl.persistent) {
     a.queue = (unsigned*)(ws + pl.off_queue);
@@ -709,6 +797,9 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
     r.wm = pl.cfg.wm;
     r.pb = pl.cfg.pb;
     r.cb = pl.cfg.cb;
+    r.vsplit = pl.vsplit ? 1 : 0;
+    r.per_n = pl.per_n;
+    memcpy(r.split_base, pl.split_base, sizeof r.split_base);
     if (launch_reduce(r, stream)) return CONV3D_ERR_HIP;
   }
   if (pp.on) {

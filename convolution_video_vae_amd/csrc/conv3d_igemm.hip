@@ -127,19 +127,47 @@ __device__ __forceinline__ int lds_idx(int row, int chunk) {
 // sharing input rows or a weight slice meet in the same L2.
 struct TileCoord {
   int m0, co0, split;
-  int m_end;  // slot kernel: end of the tile's slot range
+  int m_end;   // slot kernel: end of the tile's slot range
+  int nsplit;  // K slices of this tile
+  int slot;    // halo-kernel partials: the work-group's partial tile
 };
-__device__ __forceinline__ TileCoord tile_coord(const IgemmArgs& a, int BM, int BN) {
-  int bid = blockIdx.x;
+__device__ __forceinline__ int xcd_run(int bid) {
   const int G8 = gridDim.x & ~7;
-  if (bid < G8) bid = (bid & 7) * (G8 >> 3) + (bid >> 3);
+  return bid < G8 ? (bid & 7) * (G8 >> 3) + (bid >> 3) : bid;
+}
+__device__ __forceinline__ TileCoord tile_coord(const IgemmArgs& a, int BM, int BN) {
+  const int bid = xcd_run(blockIdx.x);
   const int m_tile = bid % a.m_tiles;
   const int rest = bid / a.m_tiles;
   TileCoord t;
   t.m0 = m_tile * BM;
   t.co0 = (rest % a.n_tiles) * BN;
   t.split = rest / a.n_tiles;
+  t.nsplit = a.splits;
+  t.slot = (t.split * a.m_tiles + m_tile) * a.n_tiles + rest % a.n_tiles;
   return t;
+}
+// The same for a live-balanced split (a.vsplit): the launch-order table
+// gives the pixel tile and slice of each work-group of a channel tile.
+__device__ __forceinline__ TileCoord tile_coord_live(const IgemmArgs& a, int BM, int BN) {
+  const int bid = xcd_run(blockIdx.x);
+  const int nt = bid / a.per_n, i = bid - nt * a.per_n;
+  const int e = a.wg[i];
+  const int mt = e >> 8;
+  TileCoord t;
+  t.m0 = mt * BM;
+  t.co0 = nt * BN;
+  t.split = e & 255;
+  t.nsplit = a.split_base[mt + 1] - a.split_base[mt];
+  t.slot = nt * a.per_n + a.split_base[mt] + t.split;
+  return t;
+}
+// Nominal K step (pair * CC + chunk) of the j-th live step, j < popc(live) * CC.
+__device__ __forceinline__ int live_step(unsigned live, int j, int CC) {
+  const int k = j / CC;
+  unsigned m = live;
+  for (int i = 0; i < k; ++i) m &= m - 1;
+  return __builtin_ctz(m) * CC + (j - k * CC);
 }
 
 // Per-lane geometry of PB pixel blocks: byte offset of tap (0,0,0) and a
@@ -710,7 +738,7 @@ template <int PB, int CB>
 __device__ __forceinline__ void store_partial_frag(const IgemmArgs& a, f32x16_t (&acc)[CB][PB],
                                                    const TileCoord& tc, int BM, int BN, int wave,
                                                    int lane) {
-  const long long tile = ((long long)tc.split * a.m_tiles + tc.m0 / BM) * a.n_tiles + tc.co0 / BN;
+  const long long tile = tc.slot;
   f32x4_t* base = reinterpret_cast<f32x4_t*>(a.partial) + (tile * 4 + wave) * (PB * CB * 4 * 64) + lane;
 #pragma unroll
   for (int p = 0; p < PB; ++p)
@@ -1075,6 +1103,10 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     const int rest = tile_lin / a.m_tiles;
     tc.co0 = (rest % a.n_tiles) * S::BN;
     tc.split = rest / a.n_tiles;
+    tc.nsplit = a.splits;
+    tc.slot = (tc.split * a.m_tiles + tile_lin % a.m_tiles) * a.n_tiles + rest % a.n_tiles;
+  } else if (a.vsplit) {
+    tc = tile_coord_live(a, S::BM, S::BN);
   } else {
     tc = tile_coord(a, S::BM, S::BN);
   }
@@ -1167,9 +1199,20 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   const __amdgpu_buffer_rsrc_t xrsrc = x_rsrc(a);
   const __amdgpu_buffer_rsrc_t wrsrc = w_rsrc(a);
 
-  // Stages e = (pair << 8) | cc over the live (kd, kh) pairs.
-  const int s_begin = tc.split * a.steps_per_split;
-  const int s_end = min(s_begin + a.steps_per_split, 9 * a.CC);
+  // Stages e = (pair << 8) | cc over the live (kd, kh) pairs. A uniform
+  // split takes a fixed range of nominal steps; a live-balanced one the
+  // tile's live steps [split * q, split * q + q), q = ceil(live / nsplit).
+  int s_begin, s_end;
+  if (a.vsplit) {
+    const int L = __builtin_popcount(live) * a.CC;
+    const int q = (L + tc.nsplit - 1) / tc.nsplit;
+    const int j0 = min(tc.split * q, L), j1 = min(j0 + q, L);
+    s_begin = j0 < L ? live_step(live, j0, a.CC) : 9 * a.CC;
+    s_end = j1 < L ? live_step(live, j1, a.CC) : 9 * a.CC;
+  } else {
+    s_begin = tc.split * a.steps_per_split;
+    s_end = min(s_begin + a.steps_per_split, 9 * a.CC);
+  }
   auto valid_stage = [&](int pr, int cc) -> int {
     return (pr < 9 && pr * a.CC + cc < s_end) ? ((pr << 8) | cc) : kEnd;
   };

@@ -18,6 +18,11 @@ enum EpiMode : int {
 // Epilogue flag bits (same values as the public CONV3D_EPI_* flags).
 enum : unsigned { F_BIAS = 1u, F_RESIDUAL = 2u, F_NORM = 4u, F_RESIDUAL_OUT = 8u };
 
+// Live-balanced K split of the halo kernel: at most kMaxVTiles pixel tiles
+// and kMaxVWG work-groups per channel tile.
+constexpr int kMaxVTiles = 64;
+constexpr int kMaxVWG = 256;
+
 // Everything one implicit-GEMM launch needs; passed by value as the kernel
 // argument. All tensors NDHWC.
 struct IgemmArgs {
@@ -44,6 +49,16 @@ struct IgemmArgs {
   // fp32 reciprocals of Ho, Do and Wo + 2 (row splits with one correction
   // step each way; uniform, so they stay in scalar registers).
   float inv_ho, inv_do, inv_wp;
+  // Live-balanced K split (halo kernel partials, vsplit != 0): pixel tile t
+  // is cut into split_base[t + 1] - split_base[t] slices of about equal
+  // live work (taps that read real input), so tiles of a causal layer's
+  // first frames, which see fewer taps, get fewer slices. Each channel tile
+  // has per_n work-groups; work-group i of a channel tile (in launch order)
+  // computes slice wg[i] & 255 of pixel tile wg[i] >> 8, and writes its
+  // partials to slot split_base[t] + slice of the channel tile's per_n.
+  int vsplit, per_n;
+  uint16_t split_base[kMaxVTiles + 1];
+  uint16_t wg[kMaxVWG];
 };
 
 // Persistent tile queues: one counter per XCD, kQueueStride words apart;
@@ -65,6 +80,10 @@ struct ReduceArgs {
   // Fragment-order partials of the halo kernel (frag != 0): tile grid and
   // shape (4 waves as wm x 4/wm, each pb x cb blocks of 32 x 32).
   int frag, m_tiles, n_tiles, wm, pb, cb;
+  // Live-balanced split (as IgemmArgs): pixel tile t's slices are slots
+  // split_base[t] .. split_base[t + 1] - 1 of each channel tile's per_n.
+  int vsplit, per_n;
+  uint16_t split_base[kMaxVTiles + 1];
 };
 
 // A main-kernel configuration: MFMA block size R (16: v_mfma_f32_16x16x32_bf16,

@@ -82,12 +82,45 @@ __global__ __launch_bounds__(256) void reduce_frag_kernel(ReduceArgs a) {
     const long long m = (long long)mt * BM + (w % WM) * PB * 32 + p * 32 + (L & 31);
     if (m >= a.M) continue;
     const int c0 = nt * BN + (w / WM) * 32 * CB + (L >> 5) * 16 * CB + 16 * cb + 8 * qq;
+    // Partial tiles of this output tile, summed in slice order s = 0, 1, ...:
+    // slot (s * m_tiles + mt) * n_tiles + nt of a uniform split, or slot
+    // nt * per_n + split_base[mt] + s of a live-balanced one.
+    const long long blk_in = blk - tile * (4LL * PB * CB);
+    const long long bps = 4LL * PB * CB;
+    long long slot0, sstep;
+    int count;
+    if (a.vsplit) {
+      slot0 = (long long)nt * a.per_n + a.split_base[mt];
+      sstep = 1;
+      count = a.split_base[mt + 1] - a.split_base[mt];
+    } else {
+      slot0 = (long long)mt * a.n_tiles + nt;
+      sstep = (long long)a.m_tiles * a.n_tiles;
+      count = a.splits;
+    }
+    const f32x4_t* src0 = part + ((slot0 * bps + blk_in) * 4 + 2 * qq) * 64 + L;
+    const long long step = sstep * bps * 4 * 64;   // f32x4 elements between slices
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const f32x4_t* src = part + ((s * blocks_per_split + blk) * 4 + 2 * qq) * 64 + L;
-      const f32x4_t lo = src[0], hi = src[64];
+    int s = 0;
+    for (; s + 4 <= count; s += 4) {   // four slices' loads in flight, then the adds in order
+      f32x4_t lo[4], hi[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lo[u] = src0[(s + u) * step];
+        hi[u] = src0[(s + u) * step + 64];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] += lo[u][e];
+          v[4 + e] += hi[u][e];
+        }
+    }
+    for (; s < count; ++s) {
+      const f32x4_t lo = src0[s * step], hi = src0[s * step + 64];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[e] += lo[e];

@@ -84,7 +84,15 @@ def test_workspace_and_plans():
     plan = cv.conv3d_plan_describe(d)
     splits = int(re.search(r"splits=(\d+)", plan).group(1))
     assert splits > 1
-    assert cv.conv3d_workspace_bytes(d) >= splits * wide.m * wide.cout * 4
+    # one fp32 partial tile per work-group (the halo kernel's fragment order)
+    grid, bm, bn = (int(re.search(k + r"=(\d+)", plan).group(1)) for k in ("grid", "bm", "bn"))
+    assert grid <= 256 and bm * bn * grid >= wide.m * wide.cout
+    assert cv.conv3d_workspace_bytes(d) >= grid * bm * bn * 4
+    # the automatic split follows the live taps; an explicit one is uniform
+    assert "split=live" in plan
+    d.split_k = 4
+    assert "split=live" not in cv.conv3d_plan_describe(d)
+    assert cv.conv3d_workspace_bytes(d) >= 4 * wide.m * wide.cout * 4
     d.split_k = 1
     assert cv.conv3d_workspace_bytes(d) == 0
     # NCDHW in and out need NDHWC staging copies

@@ -145,6 +145,10 @@ INT_CASES = [
     ("cin40_cout48", (1, 3, 7, 9, 40), 48, (1, 1, 1), (2, 1, 1), (0, 1, 1), True),
     ("s222", (1, 9, 12, 12, 64), 64, (2, 2, 2), (2, 1, 1), (0, 1, 1), False),
     ("wide512", (1, 3, 6, 6, 512), 1024, (1, 1, 1), (2, 1, 1), (0, 1, 1), True),
+    # one 256-pixel tile per frame: the automatic split gives the first two
+    # frames' tiles (3 and 6 live (kd, kh) pairs) fewer slices than the rest
+    ("wide_live_split", (1, 5, 16, 16, 256), 512, (1, 1, 1), (2, 1, 1), (0, 1, 1), True),
+    ("live_split_ragged", (2, 4, 7, 13, 96), 192, (1, 1, 1), (2, 1, 1), (0, 1, 1), True),
 ]
 
 
