@@ -772,6 +772,11 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   }
   if (pl.grid > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
   if (pl.persistent) {
+    const long long T = (long long)pl.m_tiles * pl.n_tiles * pl.splits;
+    a.queue_tail = tail_tiles((int)T);
+    // (development override of the shared tail's size, for A/B timing)
+    if (const char* env = getenv("CONV3D_QUEUE_TAIL"))
+      a.queue_tail = std::max(0, std::min((int)T, atoi(env)));
     a.queue = (unsigned*)(ws + pl.off_queue);
     if (launch_queue_reset(a.queue, stream)) return CONV3D_ERR_HIP;
   }

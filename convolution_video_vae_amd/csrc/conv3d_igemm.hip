@@ -162,6 +162,21 @@ __device__ __forceinline__ TileCoord tile_coord_live(const IgemmArgs& a, int BM,
   t.slot = nt * a.per_n + a.split_base[mt] + t.split;
   return t;
 }
+// Next tile of a persistent work-group (called by one thread): hand-out
+// position i comes from this XCD's queue (XCD x owns chunks x, x + 8, ... of
+// kQueueChunk positions) until that reaches the shared tail of the last
+// `tail` positions, which every XCD then draws from in turn. Tiles
+// go out in reverse order (position i is tile T - 1 - i), longest first for
+// a causal layer. Returns -1 when every tile is taken.
+__device__ __forceinline__ int queue_take(unsigned* q, int T, int tail) {
+  const int split = T - tail;
+  const int x = blockIdx.x & 7;
+  const int j = (int)atomicAdd(q + x * kQueueStride, 1u);
+  int i = ((j / kQueueChunk) * 8 + x) * kQueueChunk + j % kQueueChunk;
+  if (i >= split) i = split + (int)atomicAdd(q + 8 * kQueueStride, 1u);
+  return i < T ? T - 1 - i : -1;
+}
+
 // Nominal K step (pair * CC + chunk) of the j-th live step, j < popc(live) * CC.
 __device__ __forceinline__ int live_step(unsigned live, int j, int CC) {
   const int k = j / CC;
@@ -1079,12 +1094,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   __shared__ int tile_sh;
   const int T_all = a.m_tiles * a.n_tiles * a.splits;
   auto fetch_tile = [&]() -> int {
-    if (tid == 0) {
-      const int x = blockIdx.x & 7;
-      const int j = (int)atomicAdd(a.queue + x * kQueueStride, 1u);
-      const int i = ((j / kQueueChunk) * 8 + x) * kQueueChunk + j % kQueueChunk;
-      tile_sh = i < T_all ? T_all - 1 - i : -1;
-    }
+    if (tid == 0) tile_sh = queue_take(a.queue, T_all, a.queue_tail);
     __syncthreads();
     return tile_sh;
   };
@@ -1661,12 +1671,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   // of the next tile is taken when a tile starts, so its latency is hidden.
   __shared__ int tile_sh;
   const int T_all = a.m_tiles * a.n_tiles * a.splits;
-  auto take_ticket = [&]() -> unsigned { return atomicAdd(a.queue + (blockIdx.x & 7) * kQueueStride, 1u); };
-  auto ticket_tile = [&](unsigned t) -> int {
-    const int x = blockIdx.x & 7, j = (int)t;
-    const int i = ((j / kQueueChunk) * 8 + x) * kQueueChunk + j % kQueueChunk;
-    return i < T_all ? T_all - 1 - i : -1;
-  };
+  auto take_ticket = [&]() -> int { return queue_take(a.queue, T_all, a.queue_tail); };
+  auto ticket_tile = [&](int t) -> int { return t; };
   const int rows_total = a.N * a.Do * a.Ho;
   const int WP = a.Wo + 2;
   const float inv_wp = a.inv_wp, inv_ho = a.inv_ho, inv_do = a.inv_do;
@@ -2032,7 +2038,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   TileCoord prev;
   bool have_prev = false;
   for (;;) {
-    unsigned next_ticket = 0;
+    int next_ticket = -1;
     if (cur >= 0) {
       if (a.queue && tid == 0) next_ticket = take_ticket();
       start_tile(cur);

@@ -46,6 +46,7 @@ struct IgemmArgs {
   unsigned x_bytes;         // size of x, for the buffer range check
   float sqrt_c;             // sqrtf((float)Cout)
   unsigned* queue;          // persistent tile queues (kQueueBytes, zeroed), or null
+  int queue_tail;           // tiles of the shared tail queue (tail_tiles of the tile count)
   // fp32 reciprocals of Ho, Do and Wo + 2 (row splits with one correction
   // step each way; uniform, so they stay in scalar registers).
   float inv_ho, inv_do, inv_wp;
@@ -62,10 +63,14 @@ struct IgemmArgs {
 };
 
 // Persistent tile queues: one counter per XCD, kQueueStride words apart;
-// XCD x takes chunks of kQueueChunk consecutive tiles.
+// XCD x takes chunks of kQueueChunk consecutive tiles. The last tiles of
+// the hand-out order (queue_tail, normally tail_tiles(T) of T) form a ninth, shared queue that
+// the work-groups of every XCD draw from once their own share is done, so
+// XCDs that run ahead take more of the tail.
 constexpr int kQueueStride = 64;
 constexpr int kQueueChunk = 8;
-constexpr size_t kQueueBytes = 8 * kQueueStride * 4;
+constexpr size_t kQueueBytes = 9 * kQueueStride * 4;
+constexpr int tail_tiles(int T) { return T / 4 < 512 ? T / 4 : 512; }
 
 struct ReduceArgs {
   const float* partial;     // [splits][M][Cout]
