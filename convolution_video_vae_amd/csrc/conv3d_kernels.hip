@@ -580,6 +580,61 @@ __global__ __launch_bounds__(256) void transpose4_kernel(const uint16_t* __restr
   }
 }
 
+// The same with 16-byte accesses and no LDS, for A % 8 == 0: each thread
+// moves one 8 x 8 block of elements, eight 16-byte loads along B (two
+// 8-byte loads per row when B % 8 == 4), a register transpose (one byte
+// permute per output word) and eight 16-byte stores along A. A wave covers 8 x 8 blocks with the B block fastest across lanes,
+// so every load and every store instruction moves eight whole 128-byte lines
+// (8 rows x 8 lanes x 16 bytes). Blocks that reach past B, and every block
+// when B % 4 != 0, move element by element.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose8_kernel(const uint16_t* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, int batch,
+                                                         int A, int B, int groups_a, int groups_b) {
+  const int lane = threadIdx.x & 63;
+  const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long per_n = (long long)groups_a * groups_b;
+  const long long n = wave / per_n;
+  if (n >= batch) return;   // the last work-group's spare waves
+  const int rest = (int)(wave - n * per_n);
+  const int ga = rest / groups_b, gb = rest - ga * groups_b;
+  const int a0 = (ga * 8 + (lane >> 3)) * 8;     // this thread's block: rows a0 .. a0 + 7
+  const int b0 = (gb * 8 + (lane & 7)) * 8;      // columns b0 .. b0 + 7
+  if (a0 >= A || b0 >= B) return;
+  const uint16_t* s = src + n * (long long)A * B;
+  uint16_t* d = dst + n * (long long)A * B;
+  if (b0 + 8 <= B && (B & 3) == 0) {
+    uint4 in[8];
+    if ((B & 7) == 0) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        in[r] = *reinterpret_cast<const uint4*>(s + (long long)(a0 + r) * B + b0);
+    } else {   // rows 8-byte aligned only: two 8-byte loads per row
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(s + (long long)(a0 + r) * B + b0);
+        const uint2 hi = *reinterpret_cast<const uint2*>(s + (long long)(a0 + r) * B + b0 + 4);
+        in[r] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+    const unsigned* w = reinterpret_cast<const unsigned*>(in);   // w[r * 4 + k]: halves 2k, 2k+1
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // output row b0 + c: element r is input row r's half c
+      const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      uint4 o;
+      o.x = __builtin_amdgcn_perm(w[1 * 4 + c / 2], w[0 * 4 + c / 2], sel);
+      o.y = __builtin_amdgcn_perm(w[3 * 4 + c / 2], w[2 * 4 + c / 2], sel);
+      o.z = __builtin_amdgcn_perm(w[5 * 4 + c / 2], w[4 * 4 + c / 2], sel);
+      o.w = __builtin_amdgcn_perm(w[7 * 4 + c / 2], w[6 * 4 + c / 2], sel);
+      *reinterpret_cast<uint4*>(d + (long long)(b0 + c) * A + a0) = o;
+    }
+  } else {
+    for (int c = 0; c < 8 && b0 + c < B; ++c)
+      for (int r = 0; r < 8; ++r) d[(long long)(b0 + c) * A + a0 + r] = s[(long long)(a0 + r) * B + b0 + c];
+  }
+}
+
 // --------------------------------------------------------------------------
 // Zeroes the persistent tile queues before a launch (a kernel rather than a
 // memset so the sequence can be captured in a graph).
@@ -602,6 +657,13 @@ int launch_pack_weight(const uint16_t* w, uint16_t* wp, int cout, int cin, int t
 }
 
 int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int A, int B, void* stream) {
+  if (A % 8 == 0) {   // 16-byte path; ragged B handled inside
+    const int ga = (A / 8 + 7) / 8, gb = ((B + 7) / 8 + 7) / 8;
+    const long long waves = (long long)n * ga * gb;
+    hipLaunchKernelGGL(transpose8_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       (hipStream_t)stream, src, dst, n, A, B, ga, gb);
+    return (int)hipGetLastError();
+  }
   const int ta = (A + 63) / 64, tb = (B + 63) / 64;
   const long long blocks = (long long)n * ta * tb;
   if (A % 4 == 0 && B % 4 == 0)

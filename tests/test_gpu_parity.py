@@ -114,12 +114,16 @@ def test_pack_weight_matches_documented_layout(cout, cin):
     np.testing.assert_array_equal(got, want.ravel())
 
 
-# (Extents that are multiples of 4 take the 8-byte-vector kernel: 160 x 56364,
-# 320 x 38400, and the ragged 12 x 60 and 68 x 180 tiles; the others the
+# (A leading extent that is a multiple of 8 takes the 16-byte register-
+# transpose kernel: 16-byte loads when the other extent is a multiple of 8
+# (320 x 38400, 40 x 64), 8-byte loads for 4 mod 8 (160 x 56364, 16 x 252
+# with a ragged last block), element by element otherwise (24 x 105,
+# 72 x 234, 8 x 1). Other extents that are multiples of 4 take the
+# 8-byte LDS-tile kernel (56364 x 160, 12 x 60, 68 x 180), the rest the
 # 2-byte one.)
 @pytest.mark.parametrize("shape", [(2, 24, 3, 5, 7), (1, 160, 7, 66, 122), (1, 320, 5, 64, 120),
                                    (3, 8, 1, 1, 1), (1, 72, 2, 9, 13), (2, 12, 3, 4, 5),
-                                   (1, 68, 3, 5, 12)])
+                                   (1, 68, 3, 5, 12), (2, 40, 2, 4, 8), (1, 16, 3, 7, 12)])
 def test_transpose_round_trip_is_exact(shape):
     n, c, d, h, w = shape
     rng = np.random.default_rng(sum(shape))
