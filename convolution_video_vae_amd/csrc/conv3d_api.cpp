@@ -87,6 +87,10 @@ struct Plan {
   int steps;       // 27 * CC
   int steps_per_split;
   int m_tiles, n_tiles;
+  // slot kernels: frames tiled one by one, tiles of the same rows of
+  // consecutive frames next to each other (IgemmArgs::frames)
+  bool frame_order = false;
+  int frame_slots = 0, frame_tiles = 0, head = 0;
   long long grid;
   // workspace carve (bytes, 256-aligned offsets)
   bool persistent; // one work-group per CU taking tiles from queues
@@ -209,9 +213,34 @@ bool slot_ok(const Problem& pr, const TileCfg& c) {
          (c.bm() + 1) / wp + 2 <= 64 && slot_rows(pr) * wp + c.bm() + 2048 < (1LL << 22);
 }
 
+// Stride 2 along W on the pixel-pair view (slot kernel, ns = -3): the input
+// [n][d][h][w][cin] read as [n][d][h][w / 2][2 * cin], a stride-1 conv with
+// two taps along W (tap kw' of the pair view, chunk half e: the layer's tap
+// 2 * kw' + e). It needs no leading W padding (output column wo then reads
+// pairs wo and wo + 1), an even W and whole 32-channel chunks per pixel, so
+// that each chunk of a pair lies in one of its two pixels.
+Problem pair_view(const Problem& pr) {
+  Problem v = pr;
+  v.w = pr.w / 2;
+  v.cin = 2 * pr.cin;
+  v.sw = 1;
+  v.pw = 0;
+  return v;
+}
+
+bool pair_ok(const Problem& pr, const TileCfg& c) {
+  if (pr.sw != 2 || pr.pw != 0 || pr.w % 2 != 0 || pr.cin % 32 != 0 || pr.reflect || pr.fp8)
+    return false;
+  const Problem v = pair_view(pr);
+  const long long wp = v.Wo + 1;
+  return c.bn() > 0 && v.cout % c.bn() == 0 && (c.bm() + 1) / wp + 2 <= 64 &&
+         slot_rows(v) * wp + c.bm() + 2048 < (1LL << 22);
+}
+
 bool halo_ok(const Problem& pr, const TileCfg& c) {
   if (c.ns >= 0) return true;
   if (c.ns == -2) return slot_ok(pr, c);
+  if (c.ns == -3) return pair_ok(pr, c);
   // (Output rows are split with a float-reciprocal division, exact below 2^22.)
   return pr.sw == 1 && pr.cin % 32 == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
          ceil_div(c.bm() - 1, pr.Wo) + 1 <= halo_maxseg(c) &&
@@ -221,6 +250,7 @@ bool halo_ok(const Problem& pr, const TileCfg& c) {
 const TileCfg kSlotStore[] = {{32, 2, 2, 8, 2, 0, -2}, {32, 4, 1, 4, 3, 0, -2},
                                {32, 4, 1, 3, 5, 0, -2}};
 const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 9, -1}, {32, 4, 1, 4, 3, 9, -1}};
+const TileCfg kPairStore[] = {{32, 2, 2, 8, 2, 0, -3}};
 const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 5, -1}, {32, 2, 2, 4, 3, 5, -1},
                                 {32, 4, 1, 4, 4, 9, -1}};
 
@@ -305,7 +335,9 @@ bool plan_vsplit(const Problem& pr, int cc, Plan* pl) {
 
 // K steps a kernel walks: 27 taps x 32-channel chunks, or for the halo
 // kernel 9 (kd, kh) pairs x 32-channel chunks.
-int steps_of(const TileCfg& c, int cc) { return c.ns < 0 ? 9 * cc : 27 * cc; }
+int steps_of(const TileCfg& c, int cc) {
+  return c.ns == -3 ? 9 * 2 * cc : (c.ns < 0 ? 9 * cc : 27 * cc);   // pair view: 2 * cc chunks
+}
 
 void make_plan(const Problem& pr, int split_req, Plan* pl) {
   const int cc = k_chunks(pr);
@@ -315,7 +347,8 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
 
   TileCfg store_cfg = store_channel_cfg(pr.cout);
   if (!igemm_has_config(store_cfg, EPI_STORE, pr.reflect, pr.fp8)) store_cfg = base;
-  if (!norm && !pick_halo(pr, kSlotStore, EPI_STORE, &store_cfg))
+  if (!norm && !pick_halo(pr, kPairStore, EPI_STORE, &store_cfg) &&
+      !pick_halo(pr, kSlotStore, EPI_STORE, &store_cfg))
     pick_halo(pr, kHaloStore, EPI_STORE, &store_cfg);
   TileCfg part_cfg = base;
   part_cfg.pb = 2;
@@ -344,7 +377,7 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   // worth of them is enough: measured on the 160-channel Wan layers, 102
   // slot tiles take half the time of the split plan.)
   const long long store_tiles = ceil_div(pr.M, store_cfg.bm()) * ceil_div(pr.cout, store_cfg.bn());
-  const long long min_tiles = store_cfg.ns == -2 ? kCUs / 4 : kCUs / 2;
+  const long long min_tiles = store_cfg.ns <= -2 ? kCUs / 4 : kCUs / 2;
   const bool split = split_req > 1 || (split_req == 0 && store_tiles < min_tiles);
 
   // Development override of the tile (same kernels, another compiled
@@ -394,8 +427,26 @@ void make_plan(const Problem& pr, int split_req, Plan* pl) {
   pl->steps_per_split = (pl->steps + splits - 1) / splits;
   pl->splits = (pl->steps + pl->steps_per_split - 1) / pl->steps_per_split;
   // (Slot kernel tiles compute bm() slots and store bm() - 2.)
-  pl->m_tiles = pl->cfg.ns == -2 ? (int)ceil_div(slot_rows(pr) * (pr.Wo + 2), pl->cfg.bm() - 2)
-                                 : (int)ceil_div(pr.M, pl->cfg.bm());
+  pl->m_tiles = pl->cfg.ns == -2   ? (int)ceil_div(slot_rows(pr) * (pr.Wo + 2), pl->cfg.bm() - 2)
+                : pl->cfg.ns == -3 ? (int)ceil_div(slot_rows(pr) * (pr.Wo + 1), pl->cfg.bm() - 1)
+                                   : (int)ceil_div(pr.M, pl->cfg.bm());
+  // Frame order for the slot kernels (one K slice per tile): the L2 of an
+  // XCD then serves the input frames that the tiles of consecutive output
+  // frames share.
+  pl->frame_order = false;
+  if (pl->cfg.ns <= -2 && pl->steps_per_split == pl->steps) {
+    const char* env = getenv("CONV3D_FRAME_ORDER");
+    pl->frame_order = env ? atoi(env) != 0 : pl->cfg.ns == -3;
+  }
+  if (pl->frame_order) {
+    const int ts = pl->cfg.bm() - (pl->cfg.ns == -3 ? 1 : 2);
+    pl->frame_slots = pr.Ho * (pr.Wo + (pl->cfg.ns == -3 ? 1 : 2));
+    pl->frame_tiles = (int)ceil_div(pl->frame_slots, ts);
+    pl->m_tiles = (int)(prod({pr.n, pr.Do}) * pl->frame_tiles);
+    // Leading frames whose kd = 0 tap lies before the input: handed out last
+    // (the queues take tiles from the end), they shorten the final round.
+    pl->head = std::min(pr.Do, (int)ceil_div(pr.pd, pr.sd));
+  }
   pl->n_tiles = (int)ceil_div(pr.cout, pl->cfg.bn());
   pl->grid = (long long)pl->m_tiles * pl->n_tiles * pl->splits;
   // An automatic split of halo-kernel partials follows the live work.
@@ -645,10 +696,12 @@ conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogu
     static const char* names[] = {"store", "norm", "partial"};
     snprintf(buf, len,
              "igemm mfma=%d wm=%d wn=%d pb=%d cb=%d kb=%d ns=%d bm=%d bn=%d mode=%s splits=%d "
-             "steps=%d grid=%lld persistent=%d reduce=%d workspace=%zu%s",
+             "steps=%d m_tiles=%d n_tiles=%d grid=%lld persistent=%d reduce=%d workspace=%zu%s%s",
              pl.cfg.r, pl.cfg.wm, pl.cfg.wn, pl.cfg.pb, pl.cfg.cb, pl.cfg.kb, pl.cfg.ns, pl.cfg.bm(),
-             pl.cfg.bn(), names[pl.mode], pl.splits, pl.steps, pl.grid, (int)pl.persistent,
-             (int)pl.reduce, pl.total, pl.vsplit ? " split=live" : "");
+             pl.cfg.bn(), names[pl.mode], pl.splits, pl.steps, pl.m_tiles, pl.n_tiles, pl.grid,
+             (int)pl.persistent,
+             (int)pl.reduce, pl.total, pl.vsplit ? " split=live" : "",
+             pl.frame_order ? " order=frame" : "");
   }
   return CONV3D_OK;
 }
@@ -764,6 +817,18 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   a.inv_ho = 1.0f / (float)pr.Ho;
   a.inv_do = 1.0f / (float)pr.Do;
   a.inv_wp = 1.0f / (float)(pr.Wo + 2);
+  if (pl.cfg.ns == -3) {   // the pixel-pair view (stride 2 along W)
+    const Problem v = pair_view(pr);
+    a.W = v.w; a.Cin = v.cin; a.sw = v.sw; a.pw = v.pw;
+    a.CC = 2 * k_chunks(pr);
+    a.inv_wp = 1.0f / (float)(pr.Wo + 1);
+  }
+  if (pl.frame_order) {
+    a.frames = pr.n * pr.Do;
+    a.frame_slots = pl.frame_slots;
+    a.frame_tiles = pl.frame_tiles;
+    a.head = pl.head;
+  }
   if (pl.vsplit) {
     a.vsplit = 1;
     a.per_n = pl.per_n;

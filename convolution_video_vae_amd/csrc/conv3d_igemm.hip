@@ -1586,21 +1586,21 @@ constexpr int f8_read_slot(int s, int o, int nrd, int nm, int cb) {
   return g > lo ? g : lo;
 }
 
-template <int PB, int CB, int WN>
+template <int PB, int CB, int WN, int KW = 3>
 struct SlotShape {
   static constexpr int R = 32;
   static constexpr int WM = 4 / WN;
   static constexpr int BM = R * PB * WM;            // slots computed per tile
-  static constexpr int TS = BM - 2;                 // slots stored per tile (tile stride)
+  static constexpr int TS = BM - (KW - 1);          // slots stored per tile (tile stride)
   static constexpr int BN = R * CB * WN;            // output channels per tile
   static constexpr int XS = BM;                     // slots staged per stage
   static constexpr int XJ = (XS * 4 + 255) / 256;   // activation DMA instructions per wave
   static constexpr int XU = XJ * 256;               // 16-byte units per activation buffer
-  static constexpr int NF = PB + 2;                 // pixel fragments per K half
+  static constexpr int NF = PB + KW - 1;            // pixel fragments per K half
   static constexpr int WU = BN * 4;                 // weight units per tap
   static constexpr int WJ = (WU / 64 + 3) / 4;      // weight DMA instructions per wave per tap
   static constexpr int WUP = WJ * 256;
-  static constexpr int NW = 3 * WJ;                 // weight DMA instructions per wave per stage
+  static constexpr int NW = KW * WJ;                // weight DMA instructions per wave per stage
   static_assert(PB == 3 || PB == 4 || PB == 8, "slot swizzle");
   static_assert(WN == 1 || WN == 2 || WN == 4, "4 waves");
   static_assert(XU % 64 == 0, "the slot permutation works on 16-slot groups");
@@ -1634,14 +1634,18 @@ __device__ __forceinline__ void unit_slot(int q, int& sl, int& c) {
   }
 }
 
-template <int PB, int CB, int WN, int EPI, bool REF = false, bool F8 = false>
+template <int PB, int CB, int WN, int EPI, bool REF = false, bool F8 = false, int KW = 3>
 __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   using T = Mfma32;
   constexpr int ESZ = F8 ? 1 : 2;       // bytes per activation element
-  using S = SlotShape<PB, CB, WN>;
+  using S = SlotShape<PB, CB, WN, KW>;
+  static_assert(KW == 3 || (KW == 2 && !F8 && !REF), "two-tap pairs: bf16, zero padding");
   constexpr int R = S::R, WM = S::WM, NACC = T::NACC, RUN = NACC * CB;
   constexpr int XU = S::XU, XJ = S::XJ, NF = S::NF, WU = S::WU, WJ = S::WJ, WUP = S::WUP;
   constexpr int NW = S::NW;
+  // Weight DMA instructions of a tile's second stage (two-tap pairs: an
+  // odd-pixel chunk, whose pair tap 1 is not loaded).
+  constexpr int NW1 = KW == 2 ? WJ : NW;
   constexpr int WTAP = WUP * 16;        // bytes
   constexpr int EPI_VM = PB * RUN / 8;  // stores of the plain epilogue per wave
   typedef typename T::acc_t acc_t;
@@ -1654,7 +1658,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   static_assert(!(PB == 4 && CB <= 4 && WN == 1) || EPI_VM == PB * CB * 2, "store count");
 
   __shared__ u32x4_t xbuf0[XU], xbuf1[XU], xbuf2[XU];
-  __shared__ u32x4_t wbuf0[3 * WUP], wbuf1[3 * WUP];
+  __shared__ u32x4_t wbuf0[KW * WUP], wbuf1[KW * WUP];
   // Fused norm: per-pixel sums of squares of the WN waves sharing a pixel.
   __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
 
@@ -1674,7 +1678,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   auto take_ticket = [&]() -> int { return queue_take(a.queue, T_all, a.queue_tail); };
   auto ticket_tile = [&](int t) -> int { return t; };
   const int rows_total = a.N * a.Do * a.Ho;
-  const int WP = a.Wo + 2;
+  const int WP = a.Wo + KW - 1;
   const float inv_wp = a.inv_wp, inv_ho = a.inv_ho, inv_do = a.inv_do;
 
   // Fragment addresses (bytes within a buffer): pixel fragment f of K half 0
@@ -1691,11 +1695,16 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     for (int h = 0; h < 2; ++h) aw[cb][h] = lds_idx((wave_n * CB + cb) * R + lrow, 2 * h + lgrp) * 16;
 
   const __amdgpu_buffer_rsrc_t xrsrc = x_rsrc(a);
-  const __amdgpu_buffer_rsrc_t wrsrc = w_rsrc(a);
+  // (two-tap pairs: a.CC counts the chunks of a pixel pair, twice the layer's)
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      KW == 2 ? __builtin_amdgcn_make_buffer_rsrc((void*)a.wp, (short)0,
+                                                  (int)(27u * (a.CC >> 1) * a.Cout * 64u), 0x00020000)
+              : w_rsrc(a);
 
   // State of the current tile.
   TileCoord tc;
   unsigned live = 0;
+  int krot = 0;   // kd of the first stage (frame order)
   int xbase[XJ];
   unsigned xmask[XJ];
   unsigned woff[WJ];
@@ -1736,7 +1745,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     return b == 0 ? wbuf0 : wbuf1;
   };
   struct StageDma {
-    unsigned wsoff[3];   // weight byte offset of each kw tap
+    unsigned wsoff[KW];  // weight byte offset of each kw tap
+    unsigned wtap[KW];   // 0, or kOobOffset for a tap without weights (two-tap pairs)
     unsigned wor;        // 0, or kOobOffset past the last stage
     unsigned pbit;       // bit of the (kd, kh) pair, 0 past the last stage
     int delta;           // activation byte offset of the pair and chunk
@@ -1746,14 +1756,35 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   auto stage_dma = [&](int e) -> StageDma {
     StageDma d;
     const bool ok = e != kEnd;
-    const int pr = ok ? e >> 8 : 0, cc = ok ? e & 255 : 0;
-    const int kd = pr / 3, kh = pr - kd * 3;
+    const int q = ok ? e >> 8 : 0, cc = ok ? e & 255 : 0;
+    const int kq = q / 3, kh = q - kq * 3;
+    const int kd = kq + krot >= 3 ? kq + krot - 3 : kq + krot;
+    const int pr = kd * 3 + kh;
+    if constexpr (KW == 2) {
+      // Two-tap pairs: the input is viewed as pixel pairs of 2 * Cin channels
+      // (chunks [0, CC / 2) the even pixel, the rest the odd one). Stage cc
+      // takes chunk cc / 2 of pixel cc % 2, so even and odd pixels alternate.
+      // Pair tap kw' of a chunk of pixel e is the layer's tap 2 * kw' + e;
+      // tap 3 does not exist and reads zeros.
+      const int cco = a.CC >> 1;
+      const int odd = cc & 1, k = cc >> 1;
 #pragma unroll
-    for (int kw = 0; kw < 3; ++kw)
-      d.wsoff[kw] = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
+      for (int kp = 0; kp < 2; ++kp) {
+        const int kw = 2 * kp + odd;
+        d.wsoff[kp] = (unsigned)(((kd * 9 + kh * 3 + min(kw, 2)) * cco + k) * a.Cout) * 64u;
+        d.wtap[kp] = kw > 2 ? kOobOffset : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) {
+        d.wsoff[kw] = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
+        d.wtap[kw] = 0u;
+      }
+    }
     d.wor = ok ? 0u : kOobOffset;
     d.pbit = ok ? 1u << pr : 0u;
-    d.delta = (kd * a.H + kh) * a.W * (a.Cin * ESZ) + cc * 64;
+    d.delta = (kd * a.H + kh) * a.W * (a.Cin * ESZ) +
+              (KW == 2 ? (cc & 1) * (a.CC >> 1) + (cc >> 1) : cc) * 64;
     d.rbit = REF ? (kh == 0 ? 1u << 9 : (kh == 2 ? 1u << 10 : 0u)) : 0u;
     d.radj = REF ? (kh == 0 ? 2 : -2) * a.W * (a.Cin * ESZ) : 0;
     return d;
@@ -1762,7 +1793,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   auto issue_w_one = [&](const StageDma& d, auto b_c, auto k_c) {
     constexpr int k = decltype(k_c)::value;
     constexpr int kw = k / WJ, j = k % WJ;
-    dma16(wrsrc, &wbuf(b_c)[kw * WUP + (j * 4 + wave) * 64], woff[j] | d.wor, d.wsoff[kw]);
+    dma16(wrsrc, &wbuf(b_c)[kw * WUP + (j * 4 + wave) * 64], woff[j] | d.wor | d.wtap[kw],
+          d.wsoff[kw]);
   };
   auto issue_x_one = [&](const StageDma& d, auto b_c, auto j_c) {
     constexpr int j = decltype(j_c)::value;
@@ -1784,8 +1816,37 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     } else {
       tc = tile_coord(a, S::BM, S::BN);
     }
-    tc.m0 = (tc.m0 / S::BM) * S::TS;
-    tc.m_end = min(tc.m0 + S::TS, rows_total * WP);
+    // Pixel tile mt: the mt-th run of TS slots, or (frame order) a run of
+    // one frame, consecutive tiles taking the same rows of consecutive frames
+    // (IgemmArgs::frames), and the tile walks its kd taps
+    // starting from the input frame that is a multiple of 3: the tiles of
+    // three consecutive frames then read each shared input frame at about
+    // the same time.
+    {
+      const int mt = tc.m0 / S::BM;
+      krot = 0;
+      if (a.frames) {
+        const int HT = a.N * a.head * a.frame_tiles;
+        int f, b;
+        if (mt < HT) {
+          const int hf = mt / a.frame_tiles;
+          b = mt - hf * a.frame_tiles;
+          f = (hf / a.head) * a.Do + hf % a.head;
+        } else {
+          const int rest = a.Do - a.head, r = mt - HT;
+          const int fr = r % (a.N * rest);
+          b = r / (a.N * rest);
+          f = (fr / rest) * a.Do + a.head + fr % rest;
+        }
+        tc.m0 = f * a.frame_slots + b * S::TS;
+        tc.m_end = min(tc.m0 + S::TS, (f + 1) * a.frame_slots);
+        const int d_in = (f % a.Do) * a.sd - a.pd;   // input frame of kd = 0
+        krot = ((-d_in) % 3 + 3) % 3;
+      } else {
+        tc.m0 = mt * S::TS;
+        tc.m_end = min(tc.m0 + S::TS, rows_total * WP);
+      }
+    }
     const int s0 = tc.m0;  // first slot of the tile
     const int row0 = small_div(s0, WP, inv_wp);
     const int s_last = tc.m_end - 1;
@@ -1810,6 +1871,9 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     }
     // (kd, kh) pairs live for some row with an output in the tile.
     live = wave_or9(lane < nrows ? rmask : 0u);
+    // Stage order: (kd, kh) pairs by (kd - krot) mod 3, then kh; bit q of
+    // live becomes the q-th pair of that order.
+    live = ((live >> (3 * krot)) | (live << (9 - 3 * krot))) & 0x1FFu;
 
     // Activation DMA entries: LDS unit q of a buffer holds chunk c of staged
     // slot sl (inverse of slot_unit). xbase is that chunk's byte offset in x
@@ -1851,7 +1915,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     const StageDma d0 = stage_dma(e0), d1 = stage_dma(e1);
     static_for<NW>([&](auto k) { issue_w_one(d0, SlotC<0>{}, k); });
     static_for<XJ>([&](auto j) { issue_x_one(d0, SlotC<0>{}, j); });
-    static_for<NW>([&](auto k) { issue_w_one(d1, SlotC<1>{}, k); });
+    static_for<NW1>([&](auto k) { issue_w_one(d1, SlotC<1>{}, k); });
     static_for<XJ>([&](auto j) { issue_x_one(d1, SlotC<1>{}, j); });
   };
 
@@ -1898,7 +1962,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   // Pixel fragments by K half; weight fragments in a ring of three sub-steps
   // (sub-step t uses ring slot t % 3), for e4m3 both halves of each tap
   // (tap kw, half h in slot 2*kw + h).
-  u32x4_t xf[2][NF], wf[F8 ? 6 : 3][CB];
+  u32x4_t xf[2][NF], wf[F8 ? 6 : (KW == 2 ? 4 : 3)][CB];
   auto read_x = [&](auto b_c, int h, int f) {
     const char* xb = reinterpret_cast<const char*>(xbuf(b_c));
     xf[h][f] = *reinterpret_cast<const u32x4_t*>(xb + (h ? (ax[f] ^ 32) : ax[f]));
@@ -1906,6 +1970,11 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   auto read_w = [&](auto b_c, int t, int cb) {
     const char* wb = reinterpret_cast<const char*>(wbuf(b_c));
     wf[t % 3][cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][t / 3] + (t % 3) * WTAP);
+  };
+  // Two-tap pairs: sub-step t is K half t / 2 of tap t % 2, ring slot t.
+  auto read_w2 = [&](auto b_c, int t, int cb) {
+    const char* wb = reinterpret_cast<const char*>(wbuf(b_c));
+    wf[t][cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][t >> 1] + (t & 1) * WTAP);
   };
   auto read_w8 = [&](auto b_c, int kw, int h, int cb) {
     const char* wb = reinterpret_cast<const char*>(wbuf(b_c));
@@ -1924,7 +1993,115 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     constexpr int XB = I % 3, WB = I % 2;
     if (e0 == kEnd) return false;
     const StageDma d2 = stage_dma(e2);
-    if constexpr (F8) {
+    if constexpr (KW == 2) {
+      // Two-tap pairs: four sub-steps u (K half u / 2, tap u % 2), each CB*PB
+      // MFMAs; tap kw of pixel block p reads fragment p + kw. Memory
+      // operations of stage i, spread between single MFMAs:
+      //   u0: fragment PB of half 0 (needed in u1), the weights of u2, the
+      //       first half of the half-1 fragments, half of the activation DMA
+      //       of stage i+2;
+      //   u1: the weights of u3, the other half-1 fragments, the rest of the
+      //       activation DMA;
+      //   barrier (stage i+1 landed, stage i's buffers free), then
+      //   u2: stage i+1's half-0 fragments [0, PB/2) and u0 weights, half the
+      //       weight DMA of stage i+2 (into stage i's weight buffer);
+      //   u3: stage i+1's half-0 fragments [PB/2, PB) and u1 weights, the
+      //       rest of the weight DMA.
+      // Each register a read overwrites was last read by an MFMA of an
+      // earlier sub-step. Chunks of the odd pixel have no tap 3, so their
+      // stages (every other one: the chunk order alternates pixels) skip
+      // pair tap 1 (below).
+      if constexpr (I % 2 == 0) static_for<4>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr int h = u >> 1, kw = u & 1;
+        constexpr int NM = CB * PB;
+        constexpr int H1 = (NF + 1) / 2;
+        constexpr int NX = u == 0 ? 1 + (H1) : (u == 1 ? NF - H1 : (u == 2 ? PB / 2 : PB - PB / 2));
+        constexpr int ND = u < 2 ? (u == 0 ? XJ / 2 : XJ - XJ / 2) : (u == 2 ? NW / 2 : NW - NW / 2);
+        constexpr int NOPS = NX + CB + ND;
+        if constexpr (u == 2) {
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        static_for<NM>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          static_for<NOPS>([&](auto o_c) {
+            constexpr int o = decltype(o_c)::value;
+            if constexpr (o * NM / NOPS == g) {
+              if constexpr (o < NX) {
+                if constexpr (u == 0) {
+                  if constexpr (o == 0) read_x(SlotC<XB>{}, 0, PB);
+                  else read_x(SlotC<XB>{}, 1, o - 1);
+                } else if constexpr (u == 1) {
+                  read_x(SlotC<XB>{}, 1, H1 + o);
+                } else if constexpr (u == 2) {
+                  read_x(SlotC<(I + 1) % 3>{}, 0, o);
+                } else {
+                  read_x(SlotC<(I + 1) % 3>{}, 0, PB / 2 + o);
+                }
+              } else if constexpr (o < NX + CB) {
+                constexpr int cb = o - NX;
+                if constexpr (u < 2) read_w2(SlotC<WB>{}, u + 2, cb);
+                else read_w2(SlotC<(I + 1) % 2>{}, u - 2, cb);
+              } else {
+                constexpr int k = o - NX - CB;
+                if constexpr (u == 0) issue_x_one(d2, SlotC<(I + 2) % 3>{}, SlotC<k>{});
+                else if constexpr (u == 1) issue_x_one(d2, SlotC<(I + 2) % 3>{}, SlotC<XJ / 2 + k>{});
+                else if constexpr (u == 2) issue_w_one(d2, SlotC<WB>{}, SlotC<k>{});
+                else issue_w_one(d2, SlotC<WB>{}, SlotC<NW / 2 + k>{});
+              }
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int cb = g % CB, p = g / CB;
+          acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wf[u][cb]),
+                              __builtin_bit_cast(bf16x8_t, xf[h][p + kw]), acc[cb][p]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+      else static_for<2>([&](auto v_c) {
+        // Odd-pixel chunk (odd stages: a tile's stages start at chunk 0 of a
+        // (kd, kh) pair, and each pair has an even number of them): pair
+        // tap 0 (the layer's tap 1) alone, one sub-step per K half:
+        //   v0: the half-1 fragments [0, PB) and tap-0 half-1 weights, all of
+        //       the activation DMA of stage i+2;
+        //   barrier, then
+        //   v1: stage i+1's half-0 fragments [0, PB) and half-0 weights of
+        //       both taps, the weight DMA of stage i+2 (pair tap 0 only).
+        // (On entry, as for the four-sub-step form, half 0's fragments and
+        // weights are in xf[0] and wf[0].)
+        constexpr int v = decltype(v_c)::value;
+        constexpr int NM = CB * PB;
+        constexpr int NOPS = v == 0 ? PB + CB + XJ : PB + 2 * CB + WJ;
+        if constexpr (v == 1) {
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        static_for<NM>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          static_for<NOPS>([&](auto o_c) {
+            constexpr int o = decltype(o_c)::value;
+            if constexpr (o * NM / NOPS == g) {
+              if constexpr (v == 0) {
+                if constexpr (o < PB) read_x(SlotC<XB>{}, 1, o);
+                else if constexpr (o < PB + CB) read_w2(SlotC<WB>{}, 2, o - PB);
+                else issue_x_one(d2, SlotC<(I + 2) % 3>{}, SlotC<o - PB - CB>{});
+              } else {
+                if constexpr (o < PB) read_x(SlotC<(I + 1) % 3>{}, 0, o);
+                else if constexpr (o < PB + 2 * CB)
+                  read_w2(SlotC<(I + 1) % 2>{}, (o - PB) / CB, (o - PB) % CB);
+                else issue_w_one(d2, SlotC<WB>{}, SlotC<o - PB - 2 * CB>{});
+              }
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int cb = g % CB, p = g / CB;
+          acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wf[2 * v][cb]),
+                              __builtin_bit_cast(bf16x8_t, xf[v][p]), acc[cb][p]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    } else if constexpr (F8) {
       static_for<3>([&](auto s_c) {
         constexpr int s = decltype(s_c)::value;
         constexpr int NM = CB * PB;
@@ -2054,9 +2231,9 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     // Stage 0 of this tile has landed everywhere; the previous tile's plain
     // stores (issued after this tile's DMA) may still be in flight.
     if (have_prev && EPI == EPI_STORE && a.flags == 0)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW + XJ + EPI_VM) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW1 + XJ + EPI_VM) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW + XJ) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW1 + XJ) : "memory");
     if constexpr (F8) {
 #pragma unroll
       for (int f = 0; f < PB; ++f) {
@@ -2107,6 +2284,9 @@ int launch_one(const IgemmArgs& args, int grid, void* stream) {
     hipLaunchKernelGGL((igemm_slot_kernel<PB, CB, WN, EPI, REF, std::is_same<T, Mfma32F8>::value>),
                        dim3((unsigned)grid), dim3(256),
                        0, (hipStream_t)stream, args);
+  else if constexpr (NS == -3)   // two-tap pairs: stride 2 along W on the pair view
+    hipLaunchKernelGGL((igemm_slot_kernel<PB, CB, WN, EPI, false, false, 2>), dim3((unsigned)grid),
+                       dim3(256), 0, (hipStream_t)stream, args);
   else if constexpr (NS < 0)
     hipLaunchKernelGGL((igemm_halo_kernel<CB, WN, KB, EPI, REF>), dim3((unsigned)grid), dim3(256),
                        0, (hipStream_t)stream, args);
@@ -2166,6 +2346,10 @@ const Entry kEntries[] = {
     C32(2, 2, 3, 5, 0, -2, EPI_NORM),   // fused norm, Cout 320
     C32(4, 1, 3, 5, 0, -2, EPI_STORE),  // 384 slots x 160 channels
     C32(4, 1, 3, 5, 0, -2, EPI_NORM),   // fused norm, Cout 160
+    // ns = -3: slot kernel on the pixel-pair view (stride 2 along W, two taps).
+    C32(2, 2, 8, 2, 0, -3, EPI_STORE),
+    C32(4, 1, 3, 4, 0, -3, EPI_STORE),
+    C32(4, 1, 4, 4, 0, -3, EPI_STORE),
     // ns = -1: halo kernel (stride 1 along W, Cin % 32 == 0); kb = X DMA
     // instructions per wave and stage (the row-segment capacity).
     C32(4, 1, 4, 4, 9, -1, EPI_STORE),

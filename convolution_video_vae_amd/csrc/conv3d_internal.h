@@ -60,6 +60,14 @@ struct IgemmArgs {
   int vsplit, per_n;
   uint16_t split_base[kMaxVTiles + 1];
   uint16_t wg[kMaxVWG];
+  // Slot kernels, frame order (frames != 0): the N * Do output frames of
+  // frame_slots = Ho * (slots per row) slots each are tiled separately into
+  // frame_tiles runs. Pixel tiles [0, N * head * frame_tiles) are the first
+  // `head` frames of each sample (frames with taps before the input's
+  // start, which cost less), frame by frame; the rest are the other frames
+  // with run index major and frame minor, so consecutive tiles are the same
+  // rows of consecutive frames.
+  int frames, frame_slots, frame_tiles, head;
 };
 
 // Persistent tile queues: one counter per XCD, kQueueStride words apart;

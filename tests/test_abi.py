@@ -95,6 +95,19 @@ def test_workspace_and_plans():
     assert cv.conv3d_workspace_bytes(d) >= 4 * wide.m * wide.cout * 4
     d.split_k = 1
     assert cv.conv3d_workspace_bytes(d) == 0
+    # stride 2 along W, no leading W pad, even W: the pixel-pair view of the
+    # slot kernel (Wo + 1 slots per output row, 511 stored per tile), each
+    # frame's 128 x 129 slots tiled on their own
+    s2 = workloads.LAYERS["h3_l0_128_s122"]
+    d = cv.make_desc(s2.x_shape, s2.cout, stride=s2.stride, pad_lo=s2.pad_lo, pad_hi=s2.pad_hi)
+    plan = cv.conv3d_plan_describe(d)
+    assert "ns=-3" in plan and "persistent=1" in plan and "splits=1" in plan, plan
+    assert "order=frame" in plan and f"m_tiles={17 * -(-128 * 129 // 511)}" in plan, plan
+    assert cv.conv3d_workspace_bytes(d) <= 4096
+    # odd W or a leading W pad: not a whole number of pairs per row
+    for shape, lo in (((1, 17, 256, 255, 128), (2, 0, 0)), ((1, 17, 256, 256, 128), (2, 0, 1))):
+        d = cv.make_desc(shape, 128, stride=(1, 2, 2), pad_lo=lo, pad_hi=(0, 1, 1))
+        assert "ns=-3" not in cv.conv3d_plan_describe(d)
     # NCDHW in and out need NDHWC staging copies
     d = cv.make_desc((1, 160, 7, 66, 122), 320, layout=cv.NCDHW)
     assert cv.conv3d_workspace_bytes(d) >= 1 * 160 * 7 * 66 * 122 * 2 + 5 * 64 * 120 * 320 * 2

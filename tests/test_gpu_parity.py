@@ -240,6 +240,48 @@ def test_slot_kernel_integer_bit_exact(case, with_bias):
     np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
 
 
+PAIR_CASES = [
+    # label, x shape, cout, stride, pad_lo, pad_hi: stride 2 along W with no
+    # leading W pad, even W and Cin % 32 == 0 -> the slot kernel on the
+    # pixel-pair view (two taps along W, Wo + 1 slots per output row).
+    ("pair_s122", (1, 4, 17, 24, 128), 128, (1, 2, 2), (2, 0, 0), (0, 1, 1)),
+    ("pair_cin32_wo15", (1, 3, 9, 30, 32), 128, (1, 2, 2), (2, 0, 0), (0, 1, 1)),
+    # no trailing pad: the last input column is read by no output
+    ("pair_batch2_no_hi_pad", (2, 3, 10, 40, 64), 128, (1, 2, 2), (2, 0, 0), (0, 0, 0)),
+    # a trailing pad of 3: the last output column sees only padding
+    ("pair_hi_pad3_two_channel_tiles", (1, 3, 8, 20, 64), 256, (1, 2, 2), (0, 0, 0), (0, 2, 3)),
+    ("pair_stride222", (1, 9, 12, 16, 64), 128, (2, 2, 2), (2, 1, 0), (0, 1, 1)),
+    ("pair_wo8_many_rows", (1, 3, 30, 16, 32), 128, (1, 2, 2), (2, 1, 0), (0, 1, 1)),
+    ("pair_wo256_tiles_straddle_rows", (1, 3, 5, 512, 64), 128, (1, 2, 2), (2, 0, 0), (0, 1, 1)),
+    ("pair_cin96_t1", (1, 1, 21, 66, 96), 128, (1, 2, 2), (2, 0, 0), (0, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("with_bias", [False, True], ids=["plain_store", "bias_epilogue"])
+@pytest.mark.parametrize("case", PAIR_CASES, ids=[c[0] for c in PAIR_CASES])
+def test_pair_view_integer_bit_exact(case, with_bias):
+    label, xs, cout, st, lo, hi = case
+    x, w, b = workloads.integer_tensors(xs, cout, seed=len(label) + 17, bias=True)
+    b = b if with_bias else None
+    g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b, split_k=1, label=label)
+    assert "ns=-3" in g["plan"], g["plan"]
+    r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi, bias=b)
+    np.testing.assert_array_equal(bits(g["y"]), r["y"], err_msg=g["plan"])
+
+
+@pytest.mark.parametrize("case", PAIR_CASES[:3], ids=[c[0] for c in PAIR_CASES[:3]])
+def test_pair_view_random_against_oracle(case):
+    label, xs, cout, st, lo, hi = case
+    rng = np.random.default_rng(len(label) + 5)
+    x = torch.from_numpy(rng.standard_normal(xs).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((cout, xs[-1], 3, 3, 3)) / np.sqrt(27 * xs[-1]))
+                         .astype(np.float32)).to(torch.bfloat16)
+    g = run_gpu(x, w, stride=st, pad_lo=lo, pad_hi=hi, split_k=1, label=label + "_random")
+    assert "ns=-3" in g["plan"], g["plan"]
+    r = run_oracle(x, w, stride=st, pad_lo=lo, pad_hi=hi)
+    check(bits(g["y"]), r, what=label)
+
+
 PERSIST_CASES = [
     # label, x shape, cout: 290 slot tiles on 256 persistent work-groups, so
     # some work-groups take a second tile from their queue. With Cin = 128
