@@ -48,12 +48,23 @@ def _device():
 @pytest.mark.parametrize("name,xs,cout,lo,hi,epi,split_k,plan_has", CASES,
                          ids=[c[0] for c in CASES])
 def test_graph_replay_is_bit_identical(name, xs, cout, lo, hi, epi, split_k, plan_has):
-    print(f"[graph] {name} x={xs} cout={cout} epilogue={epi}", flush=True)
-    L = workloads.Layer(name, 5, xs, cout, pad_lo=lo, pad_hi=hi, bias=epi != "none",
-                        residual=epi == "norm", norm_silu=epi == "norm")
+    _check_graph(name, xs, cout, lo, hi, epi, split_k, plan_has)
+
+
+def test_graph_replay_pair_view_frame_order():
+    """Stride 2 along W: the persistent pixel-pair plan in frame order (297
+    tiles on 256 work-groups, tile-queue reset captured with it)."""
+    _check_graph("pair_view_persistent", (1, 9, 256, 256, 128), 128, (2, 0, 0), (0, 1, 1),
+                 "none", 0, ("ns=-3", "persistent=1", "order=frame"), stride=(1, 2, 2))
+
+
+def _check_graph(name, xs, cout, lo, hi, epi, split_k, plan_has, stride=(1, 1, 1)):
+    print(f"[graph] {name} x={xs} cout={cout} stride={stride} epilogue={epi}", flush=True)
+    L = workloads.Layer(name, 5, xs, cout, stride=stride, pad_lo=lo, pad_hi=hi,
+                        bias=epi != "none", residual=epi == "norm", norm_silu=epi == "norm")
     t = workloads.make_tensors(L)
-    conv = Conv3d(t.w.cuda(), xs, pad_lo=lo, pad_hi=hi, bias=t.bias, gamma=t.gamma,
-                  norm_silu=L.norm_silu, residual=L.residual, split_k=split_k)
+    conv = Conv3d(t.w.cuda(), xs, stride=stride, pad_lo=lo, pad_hi=hi, bias=t.bias,
+                  gamma=t.gamma, norm_silu=L.norm_silu, residual=L.residual, split_k=split_k)
     probe = cv.make_epilogue(bias=conv.bias, gamma=conv.gamma, norm_silu=conv.norm_silu)
     probe.flags |= cv.EPI_RESIDUAL if L.residual else 0
     plan = cv.conv3d_plan_describe(conv.desc, probe if probe.flags else None)
