@@ -26,4 +26,32 @@ __device__ __forceinline__ float lane_bf(const u32x4_t& v, int e) {
   return bf2f((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
 }
 
+// The fused post-operations after the row norm, for one value v of a pixel
+// whose channel row has norm den = max(sqrt(sum v^2), 1e-12), passed as
+// rden = 1 / den (correctly rounded, once per pixel):
+//   nrm = B(v / den), scl = B(nrm * sqrt(C)), aff = B(scl * gamma),
+//   out = B(aff / (1 + e^-aff)).
+// v / den is formed as v * rden (within 1.5 fp32 ulps of the quotient). e^x
+// is 2^(x log2 e) with the product split into a rounded part t and its
+// remainder r (from an fma and the low half of log2 e), so the hardware
+// exp2 of t times 1 + r ln 2 keeps the result within about 2 ulps for any
+// |x| of a normalised row; the quotient is aff times the hardware
+// reciprocal. Each stays a few fp32 ulps from the exact value, far below the
+// bf16 rounding that follows, and the three kernels that finish the contract
+// share this code, so they agree bit for bit.
+__device__ __forceinline__ float norm_silu_value(float v, float rden, float sqrt_c, float g) {
+  const float nrm = rbf(v * rden);
+  const float scl = rbf(nrm * sqrt_c);
+  const float aff = rbf(scl * g);
+  constexpr float kLog2eHi = 1.44269502162933349609375f;   // fp32 nearest log2(e)
+  constexpr float kLog2eLo = 1.925963033500011e-08f;       // log2(e) - kLog2eHi
+  constexpr float kLn2 = 0.693147182464599609375f;
+  const float x = -aff;
+  const float t = x * kLog2eHi;
+  const float r = __builtin_fmaf(x, kLog2eLo, __builtin_fmaf(x, kLog2eHi, -t));
+  const float e2 = __builtin_amdgcn_exp2f(t);
+  const float ex = __builtin_fmaf(e2, r * kLn2, e2);
+  return rbf(aff * __builtin_amdgcn_rcpf(1.0f + ex));
+}
+
 }  // namespace conv3d

@@ -414,23 +414,31 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
     return;
   }
   // EPI_NORM. value is bf16 by construction, so it is kept packed two per
-  // register while the row's sum of squares is formed.
+  // register while the row's sum of squares is formed. Channel groups are the
+  // outer loop, so a group's bias and gamma are loaded once for all of the
+  // lane's pixel blocks.
   unsigned vpk[PB][RUN / 2];
   float ss[PB];
 #pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    const int m = mp[p];
-    const bool ok = m >= 0;
-    const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
-    float t = 0.f;
+  for (int p = 0; p < PB; ++p) ss[p] = 0.f;
 #pragma unroll
-    for (int c8 = 0; c8 < RUN; c8 += 8) {
+  for (int c8 = 0; c8 < RUN; c8 += 8) {
+    float b[8];
+    if (a.flags & F_BIAS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = a.bias[cbase + c8 + e];
+    }
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const int m = mp[p];
+      const bool ok = m >= 0;
+      const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = rbf(acc[(c8 + e) / NACC][p][(c8 + e) % NACC]);
       if (a.flags & F_BIAS) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + a.bias[cbase + c8 + e]);
+        for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + b[e]);
       }
       if ((a.flags & F_RESIDUAL) && ok) {
         const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.residual + off + c8);
@@ -442,8 +450,12 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
 #pragma unroll
       for (int q = 0; q < 4; ++q) vpk[p][c8 / 2 + q] = ov[q];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t += v[e] * v[e];
+      for (int e = 0; e < 8; ++e) ss[p] += v[e] * v[e];
     }
+  }
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    float t = ss[p];
 #pragma unroll
     for (int o = R; o < 64; o <<= 1) t += __shfl_xor(t, o);  // lanes of the same pixel
     ss[p] = t;
@@ -461,26 +473,22 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
       ss[p] = t;
     }
   }
+  float rden[PB];
 #pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    const int m = mp[p];
-    if (m < 0) continue;
-    const float den = fmaxf(sqrtf(ss[p]), 1e-12f);
-    const long long off = (long long)m * a.Cout + cbase;
+  for (int p = 0; p < PB; ++p) rden[p] = 1.0f / fmaxf(sqrtf(ss[p]), 1e-12f);
 #pragma unroll
-    for (int c8 = 0; c8 < RUN; c8 += 8) {
-      const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.gamma + cbase + c8);
+  for (int c8 = 0; c8 < RUN; c8 += 8) {
+    const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.gamma + cbase + c8);
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const int m = mp[p];
+      if (m < 0) continue;
       const u32x4_t vv = {vpk[p][c8 / 2], vpk[p][c8 / 2 + 1], vpk[p][c8 / 2 + 2], vpk[p][c8 / 2 + 3]};
       float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float nrm = rbf(lane_bf(vv, e) / den);
-        const float scl = rbf(nrm * a.sqrt_c);
-        const float aff = rbf(scl * lane_bf(gv, e));
-        o[e] = rbf(aff / (1.0f + expf(-aff)));
-      }
+      for (int e = 0; e < 8; ++e) o[e] = norm_silu_value(lane_bf(vv, e), rden[p], a.sqrt_c, lane_bf(gv, e));
       const u32x4_t ov = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
-      *reinterpret_cast<u32x4_t*>(a.y + off + c8) = ov;
+      *reinterpret_cast<u32x4_t*>(a.y + (long long)m * a.Cout + cbase + c8) = ov;
     }
   }
 }

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void reduce_norm_kernel(ReduceArgs a) {
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-    const float den = fmaxf(sqrtf(ss), 1e-12f);
+    const float rden = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll
     for (int q = 0; q < MAXG; ++q) {
       const int gidx = lane + 64 * q;
@@ -207,12 +207,8 @@ __global__ __launch_bounds__(256) void reduce_norm_kernel(ReduceArgs a) {
       u32x4_t ov;
       float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float nrm = rbf(v[q][e] / den);
-        const float scl = rbf(nrm * a.sqrt_c);
-        const float aff = rbf(scl * bf2f(a.gamma[c0 + e]));
-        o[e] = rbf(aff / (1.0f + expf(-aff)));
-      }
+      for (int e = 0; e < 8; ++e)
+        o[e] = norm_silu_value(v[q][e], rden, a.sqrt_c, bf2f(a.gamma[c0 + e]));
 #pragma unroll
       for (int k = 0; k < 4; ++k) ov[k] = (unsigned)f2bf(o[2 * k]) | ((unsigned)f2bf(o[2 * k + 1]) << 16);
       *reinterpret_cast<u32x4_t*>(a.y + m * a.Cout + c0) = ov;
@@ -336,7 +332,7 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(NormSiluArgs a) {
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-    const float den = fmaxf(sqrtf(ss), 1e-12f);
+    const float rden = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
     // where the pixel goes: y (padded when geo.Dy > 0) and maybe the cache
     long long yp = m, cp = -1;
     if (g.Dy > 0) {
@@ -358,12 +354,7 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(NormSiluArgs a) {
       const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.gamma + c0);
       float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float nrm = rbf(v[q][e] / den);
-        const float scl = rbf(nrm * a.sqrt_c);
-        const float aff = rbf(scl * lane_bf(gv, e));
-        o[e] = rbf(aff / (1.0f + expf(-aff)));
-      }
+      for (int e = 0; e < 8; ++e) o[e] = norm_silu_value(v[q][e], rden, a.sqrt_c, lane_bf(gv, e));
       const u32x4_t ov = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
       *reinterpret_cast<u32x4_t*>(a.y + yp * a.C + c0) = ov;
       if (cp >= 0) *reinterpret_cast<u32x4_t*>(g.cache + cp * a.C + c0) = ov;
