@@ -413,32 +413,24 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
     }
     return;
   }
-  // EPI_NORM. value is bf16 by construction, so it is kept packed two per
-  // register while the row's sum of squares is formed. Channel groups are the
-  // outer loop, so a group's bias and gamma are loaded once for all of the
-  // lane's pixel blocks.
-  unsigned vpk[PB][RUN / 2];
-  float ss[PB];
+  // EPI_NORM, one pixel block at a time: the block's values (bf16 by
+  // construction, kept packed two per register) and its row sum of squares,
+  // the sum over the WN waves sharing the pixel, then the post-operations.
 #pragma unroll
-  for (int p = 0; p < PB; ++p) ss[p] = 0.f;
+  for (int p = 0; p < PB; ++p) {
+    const int m = mp[p];
+    const bool ok = m >= 0;
+    const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
+    unsigned vpk[RUN / 2];
+    float t = 0.f;
 #pragma unroll
-  for (int c8 = 0; c8 < RUN; c8 += 8) {
-    float b[8];
-    if (a.flags & F_BIAS) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = a.bias[cbase + c8 + e];
-    }
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int m = mp[p];
-      const bool ok = m >= 0;
-      const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
+    for (int c8 = 0; c8 < RUN; c8 += 8) {
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = rbf(acc[(c8 + e) / NACC][p][(c8 + e) % NACC]);
       if (a.flags & F_BIAS) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + b[e]);
+        for (int e = 0; e < 8; ++e) v[e] = rbf(v[e] + a.bias[cbase + c8 + e]);
       }
       if ((a.flags & F_RESIDUAL) && ok) {
         const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(a.residual + off + c8);
@@ -448,47 +440,28 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
       const u32x4_t ov = {pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
       if ((a.flags & F_RESIDUAL_OUT) && ok) *reinterpret_cast<u32x4_t*>(a.residual_out + off + c8) = ov;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vpk[p][c8 / 2 + q] = ov[q];
+      for (int q = 0; q < 4; ++q) vpk[c8 / 2 + q] = ov[q];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss[p] += v[e] * v[e];
+      for (int e = 0; e < 8; ++e) t += v[e] * v[e];
     }
-  }
-#pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    float t = ss[p];
 #pragma unroll
     for (int o = R; o < 64; o <<= 1) t += __shfl_xor(t, o);  // lanes of the same pixel
-    ss[p] = t;
-  }
-  if (WN > 1) {  // ... and the WN waves
-    if (lgrp == 0) {
-#pragma unroll
-      for (int p = 0; p < PB; ++p) red[((wave_n * WM + wave_m) * PB + p) * R + lrow] = ss[p];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      float t = 0.f;
+    if (WN > 1) {  // ... and the WN waves (a slot per pixel block: no reuse)
+      if (lgrp == 0) red[((wave_n * WM + wave_m) * PB + p) * R + lrow] = t;
+      __syncthreads();
+      t = 0.f;
       for (int wn = 0; wn < WN; ++wn) t += red[((wn * WM + wave_m) * PB + p) * R + lrow];
-      ss[p] = t;
     }
-  }
-  float rden[PB];
+    const float rden = 1.0f / fmaxf(sqrtf(t), 1e-12f);
 #pragma unroll
-  for (int p = 0; p < PB; ++p) rden[p] = 1.0f / fmaxf(sqrtf(ss[p]), 1e-12f);
-#pragma unroll
-  for (int c8 = 0; c8 < RUN; c8 += 8) {
-    const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.gamma + cbase + c8);
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int m = mp[p];
-      if (m < 0) continue;
-      const u32x4_t vv = {vpk[p][c8 / 2], vpk[p][c8 / 2 + 1], vpk[p][c8 / 2 + 2], vpk[p][c8 / 2 + 3]};
+    for (int c8 = 0; c8 < RUN; c8 += 8) {
+      const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(a.gamma + cbase + c8);
+      const u32x4_t vv = {vpk[c8 / 2], vpk[c8 / 2 + 1], vpk[c8 / 2 + 2], vpk[c8 / 2 + 3]};
       float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = norm_silu_value(lane_bf(vv, e), rden[p], a.sqrt_c, lane_bf(gv, e));
+      for (int e = 0; e < 8; ++e) o[e] = norm_silu_value(lane_bf(vv, e), rden, a.sqrt_c, lane_bf(gv, e));
       const u32x4_t ov = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
-      *reinterpret_cast<u32x4_t*>(a.y + (long long)m * a.Cout + cbase + c8) = ov;
+      if (ok) *reinterpret_cast<u32x4_t*>(a.y + off + c8) = ov;
     }
   }
 }
