@@ -72,6 +72,10 @@ struct Problem {
   unsigned flags;
   bool reflect;    // spatial reflect padding
   bool fp8;        // e4m3 x and packed weight
+  // Samples per pass: a call whose tensors exceed the 32-bit buffer range
+  // runs as passes over nb consecutive samples each (N is the outermost
+  // dimension of every tensor involved); nb == n for one pass.
+  int nb;
 };
 
 struct Plan {
@@ -146,10 +150,17 @@ conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
   }
   if (d->cin > 8160) return CONV3D_ERR_UNSUPPORTED;  // K steps are encoded in 8 bits per tap
   if (d->cout % 16 != 0) return CONV3D_ERR_UNSUPPORTED;
-  if (pr->x_bytes > kMaxTensorBytes || pr->y_bytes > kMaxTensorBytes) return CONV3D_ERR_UNSUPPORTED;
+  // One sample's tensors must fit the 32-bit buffer range; larger batches
+  // run in passes of nb samples.
+  const long long xs = prod({d->d, d->h, d->w, d->cin, pr->fp8 ? 1 : 2});
+  const long long ms = prod({pr->Do, pr->Ho, pr->Wo});
+  const long long ys = prod({ms, d->cout, 2});
+  if (xs > kMaxTensorBytes || ys > kMaxTensorBytes || ms > 0x7fffffffLL)
+    return CONV3D_ERR_UNSUPPORTED;
   if ((long long)packed_bytes(*pr) > kMaxTensorBytes)
     return CONV3D_ERR_UNSUPPORTED;
-  if (pr->M > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
+  pr->nb = (int)std::min<long long>(
+      {(long long)d->n, kMaxTensorBytes / xs, kMaxTensorBytes / ys, 0x7fffffffLL / ms});
   return CONV3D_OK;
 }
 
@@ -204,13 +215,16 @@ int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1
 // K-step chunks (32 bf16 or 64 e4m3 channels). Output row r owns Wo + 2 slots and a tile is bm() of
 // them; the bm() slots staged per stage must span at most 64 output rows
 // (one lane each), and slot indices are split with a float-reciprocal
-// division, exact below 2^22.
+// division, exact below 2^24: the index converts to fp32 exactly, and for a
+// divisor of at least 2 the product with the rounded reciprocal is within
+// one of the quotient, which the kernel's correction steps absorb (a divisor
+// of 1 is exact).
 long long slot_rows(const Problem& pr) { return prod({pr.n, pr.Do, pr.Ho}); }
 
 bool slot_ok(const Problem& pr, const TileCfg& c) {
   const long long wp = pr.Wo + 2;
   return pr.sw == 1 && pr.cin % (pr.fp8 ? 64 : 32) == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
-         (c.bm() + 1) / wp + 2 <= 64 && slot_rows(pr) * wp + c.bm() + 2048 < (1LL << 22);
+         (c.bm() + 1) / wp + 2 <= 64 && slot_rows(pr) * wp + c.bm() + 2048 < (1LL << 24);
 }
 
 // Stride 2 along W on the pixel-pair view (slot kernel, ns = -3): the input
@@ -234,7 +248,7 @@ bool pair_ok(const Problem& pr, const TileCfg& c) {
   const Problem v = pair_view(pr);
   const long long wp = v.Wo + 1;
   return c.bn() > 0 && v.cout % c.bn() == 0 && (c.bm() + 1) / wp + 2 <= 64 &&
-         slot_rows(v) * wp + c.bm() + 2048 < (1LL << 22);
+         slot_rows(v) * wp + c.bm() + 2048 < (1LL << 24);
 }
 
 bool halo_ok(const Problem& pr, const TileCfg& c) {
@@ -526,6 +540,21 @@ conv3d_status check_out_pad(const conv3d_out_pad* op, const Problem& pr, PadPlan
   return CONV3D_OK;
 }
 
+// Samples per pass for a call with output placement op (padded y, cache):
+// pr.nb, lowered so that one pass's padded output stays in range too.
+int batch_chunk(const Problem& pr, const conv3d_out_pad* op) {
+  long long nb = pr.nb;
+  if (op) {
+    const long long dy = (long long)pr.Do + op->pad_lo[0] + op->pad_hi[0];
+    const long long hy = (long long)pr.Ho + op->pad_lo[1] + op->pad_hi[1];
+    const long long wy = (long long)pr.Wo + op->pad_lo[2] + op->pad_hi[2];
+    const long long per = prod({dy, hy, wy, pr.cout, 2});
+    if (per > 0) nb = std::min(nb, std::max(1LL, kMaxTensorBytes / per));
+    if (dy * hy > 0) nb = std::min(nb, std::max(1LL, 0x7fffffffLL / (dy * hy)));
+  }
+  return (int)std::max(1LL, nb);
+}
+
 // GroupNorm planning: units, chunking and the workspace carve.
 struct GnPlan {
   GroupNormArgs a;
@@ -655,40 +684,50 @@ conv3d_status conv3d_output_dims(const conv3d_desc* desc, int out_dhw[3]) {
 
 conv3d_status conv3d_workspace_bytes(const conv3d_desc* desc, const conv3d_epilogue* epi,
                                      size_t* bytes) {
-  if (!bytes) return CONV3D_ERR_NULL;
-  Problem pr;
-  conv3d_status st = check_desc(desc, &pr);
-  if (st != CONV3D_OK) return st;
-  Problem pe = pr;
-  pe.flags = epi ? epi->flags : 0u;
-  Plan pl;
-  make_plan(pe, desc->split_k, &pl);
-  *bytes = pl.total;
-  return CONV3D_OK;
+  return conv3d_padded_workspace_bytes(desc, epi, nullptr, bytes);
 }
 
 conv3d_status conv3d_padded_workspace_bytes(const conv3d_desc* desc, const conv3d_epilogue* epi,
                                             const conv3d_out_pad* out_pad, size_t* bytes) {
   if (!bytes) return CONV3D_ERR_NULL;
-  Problem pr;
-  conv3d_status st = check_desc(desc, &pr);
+  Problem full;
+  conv3d_status st = check_desc(desc, &full);
   if (st != CONV3D_OK) return st;
-  PadPlan pp;
-  st = check_out_pad(out_pad, pr, &pp);
-  if (st != CONV3D_OK) return st;
-  Problem pe = pr;
-  pe.flags = epi ? epi->flags : 0u;
-  Plan pl;
-  make_plan(pe, desc->split_k, &pl);
-  *bytes = pp.on ? pl.total + align256(pr.y_bytes) : pl.total;
+  // The passes reuse one workspace: the largest of a full pass and the last,
+  // shorter one (whose plan may differ).
+  const int nb = batch_chunk(full, out_pad);
+  const int sizes[2] = {std::min(nb, full.n), full.n % nb};
+  size_t need = 0;
+  for (int n : sizes) {
+    if (n <= 0) continue;
+    conv3d_desc ds = *desc;
+    ds.n = n;
+    Problem pr;
+    st = check_desc(&ds, &pr);
+    if (st != CONV3D_OK) return st;
+    PadPlan pp;
+    st = check_out_pad(out_pad, pr, &pp);
+    if (st != CONV3D_OK) return st;
+    pr.flags = epi ? epi->flags : 0u;
+    Plan pl;
+    make_plan(pr, desc->split_k, &pl);
+    need = std::max(need, pp.on ? pl.total + align256(pr.y_bytes) : pl.total);
+  }
+  *bytes = need;
   return CONV3D_OK;
 }
 
 conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogue* epi,
                                    char* buf, size_t len) {
-  Problem pr;
-  conv3d_status st = check_desc(desc, &pr);
+  Problem full;
+  conv3d_status st = check_desc(desc, &full);
   if (st != CONV3D_OK) return st;
+  conv3d_desc ds = *desc;   // (the plan of a full pass when the batch runs in passes)
+  ds.n = full.nb;
+  Problem pr;
+  st = check_desc(&ds, &pr);
+  if (st != CONV3D_OK) return st;
+  const int passes = (full.n + full.nb - 1) / full.nb;
   pr.flags = epi ? epi->flags : 0u;
   Plan pl;
   make_plan(pr, desc->split_k, &pl);
@@ -702,6 +741,11 @@ conv3d_status conv3d_plan_describe(const conv3d_desc* desc, const conv3d_epilogu
              (int)pl.persistent,
              (int)pl.reduce, pl.total, pl.vsplit ? " split=live" : "",
              pl.frame_order ? " order=frame" : "");
+    if (passes > 1) {
+      const size_t used = strlen(buf);
+      if (used + 1 < len)
+        snprintf(buf + used, len - used, " passes=%d samples_per_pass=%d", passes, full.nb);
+    }
   }
   return CONV3D_OK;
 }
@@ -724,12 +768,14 @@ conv3d_status conv3d_fwd_noalloc(const conv3d_desc* desc, const void* x, const v
   return conv3d_fwd(desc, x, w_packed, epi, y, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
-conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const void* w_packed,
-                                const conv3d_epilogue* epi, const conv3d_out_pad* op, void* y,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// One pass: every tensor within the 32-bit buffer range (nb == n).
+static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                     const conv3d_epilogue* epi, const conv3d_out_pad* op, void* y,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   Problem pr;
   conv3d_status st = check_desc(desc, &pr);
   if (st != CONV3D_OK) return st;
+  if (pr.nb < pr.n || batch_chunk(pr, op) < pr.n) return CONV3D_ERR_UNSUPPORTED;
   if (!x || !w_packed || !y) return CONV3D_ERR_NULL;
   st = check_epi(epi, &pr);
   if (st != CONV3D_OK) return st;
@@ -883,6 +929,79 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
     if (launch_transpose(yout, (uint16_t*)y, pr.n, So, pr.cout, stream)) return CONV3D_ERR_HIP;
     if (rout && launch_transpose(rout, (uint16_t*)epi->residual_out, pr.n, So, pr.cout, stream))
       return CONV3D_ERR_HIP;
+  }
+  return CONV3D_OK;
+}
+
+conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                const conv3d_epilogue* epi, const conv3d_out_pad* op, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  Problem pr;
+  conv3d_status st = check_desc(desc, &pr);
+  if (st != CONV3D_OK) return st;
+  const int nb = batch_chunk(pr, op);
+  if (nb >= pr.n)
+    return fwd_padded_pass(desc, x, w_packed, epi, op, y, workspace, workspace_bytes, stream);
+
+  // A batch beyond the 32-bit buffer range: passes over nb consecutive
+  // samples, in order on the stream, reusing the workspace. Each pass checks
+  // its own slices; the whole tensors are checked for overlap here.
+  if (!x || !w_packed || !y) return CONV3D_ERR_NULL;
+  st = check_epi(epi, &pr);
+  if (st != CONV3D_OK) return st;
+  const unsigned f = pr.flags;
+  const long long xs = prod({pr.d, pr.h, pr.w, pr.cin, pr.fp8 ? 1 : 2});
+  const long long rs = prod({pr.Do, pr.Ho, pr.Wo, pr.cout, 2});
+  long long ys = rs, cs = 0;
+  if (op) {
+    PadPlan pp;
+    conv3d_desc d1 = *desc;
+    d1.n = 1;
+    Problem p1;
+    st = check_desc(&d1, &p1);
+    if (st != CONV3D_OK) return st;
+    st = check_out_pad(op, p1, &pp);
+    if (st != CONV3D_OK) return st;
+    if (pp.on) ys = pp.y_bytes;
+    if (op->cache) cs = prod({op->cache_frames, pr.Ho, pr.Wo, pr.cout, 2});
+  }
+  size_t ws_need = 0;
+  st = conv3d_padded_workspace_bytes(desc, epi, op, &ws_need);
+  if (st != CONV3D_OK) return st;
+  const Range rx = range_of(x, prod({pr.n, xs}));
+  const Range rw = range_of(w_packed, (long long)packed_bytes(pr));
+  const Range ry = range_of(y, prod({pr.n, ys}));
+  const Range rcache = (op && op->cache) ? range_of(op->cache, prod({pr.n, cs})) : Range();
+  const Range rb = (f & F_BIAS) ? range_of(epi->bias, 4LL * pr.cout) : Range();
+  const Range rr = (f & F_RESIDUAL) ? range_of(epi->residual, prod({pr.n, rs})) : Range();
+  const Range rg = (f & F_NORM) ? range_of(epi->gamma, 2LL * pr.cout) : Range();
+  const Range ro = (f & F_RESIDUAL_OUT) ? range_of(epi->residual_out, prod({pr.n, rs})) : Range();
+  const Range rs_ = range_of(workspace, (long long)ws_need);
+  const Range outs[] = {ry, ro, rs_, rcache};
+  const Range ins[] = {rx, rw, rb, rr, rg};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return CONV3D_ERR_OVERLAP;
+  for (int b0 = 0; b0 < pr.n; b0 += nb) {
+    conv3d_desc ds = *desc;
+    ds.n = std::min(nb, pr.n - b0);
+    conv3d_epilogue es;
+    if (epi) {
+      es = *epi;
+      if (f & F_RESIDUAL) es.residual = (const char*)epi->residual + b0 * rs;
+      if (f & F_RESIDUAL_OUT) es.residual_out = (char*)epi->residual_out + b0 * rs;
+    }
+    conv3d_out_pad os;
+    if (op) {
+      os = *op;
+      if (op->cache) os.cache = (char*)op->cache + b0 * cs;
+    }
+    st = fwd_padded_pass(&ds, (const char*)x + b0 * xs, w_packed, epi ? &es : nullptr,
+                         op ? &os : nullptr, (char*)y + b0 * ys, workspace, workspace_bytes, stream);
+    if (st != CONV3D_OK) return st;
   }
   return CONV3D_OK;
 }

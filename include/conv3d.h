@@ -181,7 +181,12 @@ conv3d_status conv3d_workspace_bytes(const conv3d_desc* desc, const conv3d_epilo
  *   y          bf16, output shape in out_layout
  *   workspace  device scratch of at least conv3d_workspace_bytes() bytes
  * y must not overlap x, w_packed, the workspace, residual or residual_out.
- * Channel requirements: cin % 8 == 0, cout % 16 == 0. */
+ * Channel requirements: cin % 8 == 0, cout % 16 == 0.
+ * Size: one sample's input, output and (padded) output must each stay below
+ * 2 GiB (CONV3D_ERR_UNSUPPORTED otherwise). A batch whose tensors exceed it
+ * runs as passes over as many consecutive samples as fit, in order on the
+ * stream, reusing the workspace (whose size conv3d_workspace_bytes already
+ * covers); conv3d_plan_describe reports the passes. */
 conv3d_status conv3d_fwd(const conv3d_desc* desc, const void* x, const void* w_packed,
                          const conv3d_epilogue* epi, void* y, void* workspace,
                          size_t workspace_bytes, void* stream);

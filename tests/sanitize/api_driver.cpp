@@ -176,8 +176,9 @@ int main() {
            CONV3D_ERR_OVERLAP);
     EXPECT(conv3d_fwd(&d, buf(1), buf(2), nullptr, buf(3), (char*)buf(3) + 256, 1 << 30, nullptr),
            CONV3D_ERR_OVERLAP);
-    conv3d_desc big = make(64, 17, 256, 256, 128, 128, 2, 1, 1, 0, 1, 1);   // x above 2 GiB
-    EXPECT(conv3d_fwd(&big, buf(1), buf(2), nullptr, buf(3), buf(4), 1 << 30, nullptr),
+    // one sample above it is refused
+    conv3d_desc one_big = make(1, 35, 512, 512, 128, 128, 2, 1, 1, 0, 1, 1);
+    EXPECT(conv3d_fwd(&one_big, buf(1), buf(2), nullptr, buf(3), buf(4), 1 << 30, nullptr),
            CONV3D_ERR_UNSUPPORTED);
     conv3d_desc huge = make(0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7ffffff8,
                             0x7ffffff0, 2, 1, 1, 0, 1, 1);   // sizes that overflow 64 bits
@@ -193,6 +194,33 @@ int main() {
     EXPECT(conv3d_fwd(&d, buf(1), buf(2), &e, buf(3), buf(4), 1 << 30, nullptr),
            CONV3D_ERR_UNSUPPORTED);
     EXPECT(conv3d::g_launches, n0);
+  }
+
+  // A batch above the 32-bit buffer range runs in passes of 7 samples, each
+  // pass launching its own kernels; the whole tensors are checked first.
+  {
+    conv3d_desc big = make(16, 17, 256, 256, 128, 128, 2, 1, 1, 0, 1, 1);
+    const int n0 = conv3d::g_launches;
+    EXPECT(conv3d_fwd(&big, buf(1), buf(2), nullptr, buf(3), buf(4), 1 << 30, nullptr),
+           CONV3D_OK);
+    EXPECT(conv3d::g_launches - n0, 6);   // 3 passes x (queue reset + conv)
+    char pd[512];
+    EXPECT(conv3d_plan_describe(&big, nullptr, pd, sizeof pd), CONV3D_OK);
+    EXPECT(strstr(pd, " passes=3 samples_per_pass=7") != nullptr, 1);
+    conv3d_epilogue eb;
+    memset(&eb, 0, sizeof eb);
+    eb.flags = CONV3D_EPI_BIAS | CONV3D_EPI_RESIDUAL | CONV3D_EPI_RESIDUAL_OUT;
+    eb.bias = (const float*)buf(5);
+    eb.residual = buf(6);
+    eb.residual_out = buf(7);
+    EXPECT(conv3d_fwd(&big, buf(1), buf(2), &eb, buf(3), buf(4), 1 << 30, nullptr), CONV3D_OK);
+    // residual_out 2 GiB into y: it misses the first pass's slice of y but
+    // not y, so the call is refused before any pass launches
+    const int n1 = conv3d::g_launches;
+    eb.residual_out = (char*)buf(3) + (2LL << 30);
+    EXPECT(conv3d_fwd(&big, buf(1), buf(2), &eb, buf(3), buf(4), 1 << 30, nullptr),
+           CONV3D_ERR_OVERLAP);
+    EXPECT(conv3d::g_launches, n1);
   }
 
   // The entry point without a workspace: the fixed scratch serves.

@@ -108,6 +108,14 @@ def test_workspace_and_plans():
     for shape, lo in (((1, 17, 256, 255, 128), (2, 0, 0)), ((1, 17, 256, 256, 128), (2, 0, 1))):
         d = cv.make_desc(shape, 128, stride=(1, 2, 2), pad_lo=lo, pad_hi=(0, 1, 1))
         assert "ns=-3" not in cv.conv3d_plan_describe(d)
+    # a batch above the 32-bit buffer range runs in passes of as many samples
+    # as fit (7 of H3 L0's 285 MB), each still on the slot kernel
+    d = cv.make_desc((16,) + big.x_shape[1:], big.cout, pad_lo=big.pad_lo, pad_hi=big.pad_hi)
+    plan = cv.conv3d_plan_describe(d)
+    assert "passes=3 samples_per_pass=7" in plan and "ns=-2" in plan, plan
+    # the fused layer's 24.6 MB outputs: passes of 87 samples, NCDHW included
+    d = cv.make_desc((120, 160, 7, 66, 122), 320, layout=cv.NCDHW)
+    assert "passes=2 samples_per_pass=87" in cv.conv3d_plan_describe(d)
     # NCDHW in and out need NDHWC staging copies
     d = cv.make_desc((1, 160, 7, 66, 122), 320, layout=cv.NCDHW)
     assert cv.conv3d_workspace_bytes(d) >= 1 * 160 * 7 * 66 * 122 * 2 + 5 * 64 * 120 * 320 * 2
