@@ -555,6 +555,14 @@ int batch_chunk(const Problem& pr, const conv3d_out_pad* op) {
   return (int)std::max(1LL, nb);
 }
 
+// The slot kernels write a padded output in place (IgemmArgs::ypad) when
+// they finish the epilogue themselves; otherwise the output is staged in the
+// workspace and placed by a second pass.
+bool direct_pad(const Problem& pr, const Plan& pl, const PadPlan& pp) {
+  return pp.on && pl.cfg.ns <= -2 && !pl.reduce && pr.M < (1LL << 24) &&
+         pr.out_layout == CONV3D_NDHWC && !getenv("CONV3D_STAGED_PAD");
+}
+
 // GroupNorm planning: units, chunking and the workspace carve.
 struct GnPlan {
   GroupNormArgs a;
@@ -711,7 +719,8 @@ conv3d_status conv3d_padded_workspace_bytes(const conv3d_desc* desc, const conv3
     pr.flags = epi ? epi->flags : 0u;
     Plan pl;
     make_plan(pr, desc->split_k, &pl);
-    need = std::max(need, pp.on ? pl.total + align256(pr.y_bytes) : pl.total);
+    const bool staged = pp.on && !direct_pad(pr, pl, pp);
+    need = std::max(need, staged ? pl.total + align256(pr.y_bytes) : pl.total);
   }
   *bytes = need;
   return CONV3D_OK;
@@ -787,8 +796,9 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
   if (st != CONV3D_OK) return st;
   Plan pl;
   make_plan(pr, desc->split_k, &pl);
+  const bool direct = direct_pad(pr, pl, pp);
   const size_t off_stage = pl.total;                     // staged unpadded output
-  const size_t ws_total = pp.on ? off_stage + align256(pr.y_bytes) : pl.total;
+  const size_t ws_total = pp.on && !direct ? off_stage + align256(pr.y_bytes) : pl.total;
   if (ws_total > 0) {
     if (!workspace || workspace_bytes < ws_total) return CONV3D_ERR_WORKSPACE;
     if (!aligned16(workspace)) return CONV3D_ERR_ALIGN;
@@ -818,7 +828,7 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
 
   char* ws = (char*)workspace;
   const uint16_t* xin = (const uint16_t*)x;
-  uint16_t* yout = pp.on ? (uint16_t*)(ws + off_stage) : (uint16_t*)y;
+  uint16_t* yout = pp.on && !direct ? (uint16_t*)(ws + off_stage) : (uint16_t*)y;
   const uint16_t* res = (f & F_RESIDUAL) ? (const uint16_t*)epi->residual : nullptr;
   uint16_t* rout = (f & F_RESIDUAL_OUT) ? (uint16_t*)epi->residual_out : nullptr;
   const int S = pr.d * pr.h * pr.w;
@@ -863,6 +873,12 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
   a.inv_ho = 1.0f / (float)pr.Ho;
   a.inv_do = 1.0f / (float)pr.Do;
   a.inv_wp = 1.0f / (float)(pr.Wo + 2);
+  a.inv_wo = 1.0f / (float)pr.Wo;
+  if (direct) {   // the padded output written in place
+    a.ypad = 1;
+    a.yDy = pp.a.Dy; a.yHy = pp.a.Hy; a.yWy = pp.a.Wy;
+    a.ypt = pp.a.pt; a.yph = pp.a.ph; a.ypw = pp.a.pw;
+  }
   if (pl.cfg.ns == -3) {   // the pixel-pair view (stride 2 along W)
     const Problem v = pair_view(pr);
     a.W = v.w; a.Cin = v.cin; a.sw = v.sw; a.pw = v.pw;
@@ -918,9 +934,9 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
     memcpy(r.split_base, pl.split_base, sizeof r.split_base);
     if (launch_reduce(r, stream)) return CONV3D_ERR_HIP;
   }
-  if (pp.on) {
+  if (pp.on) {   // borders, history planes and cache (and the interior when staged)
     PlaceArgs pa = pp.a;
-    pa.y0 = yout;
+    pa.y0 = direct ? nullptr : yout;
     pa.y = (uint16_t*)y;
     if (launch_place(pa, stream)) return CONV3D_ERR_HIP;
   }

@@ -238,6 +238,22 @@ __device__ __forceinline__ int small_div(int n, int d, float inv_d) {
   return q;
 }
 
+// Index in y of output pixel m: m itself, or (a.ypad) its place in the
+// padded output (pixel indices below 2^24, so the float splits are exact).
+__device__ __forceinline__ int y_pixel(const IgemmArgs& a, int m) {
+  if (!a.ypad) return m;
+  const int r = small_div(m, a.Wo, a.inv_wo);
+  const int t = small_div(r, a.Ho, a.inv_ho);
+  const int n = small_div(t, a.Do, a.inv_do);
+  return ((n * a.yDy + (t - n * a.Do) + a.ypt) * a.yHy + (r - t * a.Ho) + a.yph) * a.yWy +
+         (m - r * a.Wo) + a.ypw;
+}
+// Elements of y: M x Cout, or the padded output's.
+__device__ __forceinline__ unsigned y_elems(const IgemmArgs& a) {
+  return a.ypad ? (unsigned)a.N * (unsigned)(a.yDy * a.yHy * a.yWy) * (unsigned)a.Cout
+                : (unsigned)a.M * (unsigned)a.Cout;
+}
+
 // Reflect padding (the H3 encoder's spatial pad): index -1 reads 1 and index
 // n reads n - 2 (pads of at most one, extents of at least two).
 __device__ __forceinline__ int reflect_index(int i, int n) {
@@ -392,6 +408,7 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
       const int m = mp[p];
       if (m < 0 || cbase >= a.Cout) continue;
       const long long off = (long long)m * a.Cout + cbase;
+      const long long yoff = (long long)y_pixel(a, m) * a.Cout + cbase;
 #pragma unroll
       for (int c8 = 0; c8 < RUN; c8 += 8) {
         float v[8];
@@ -408,7 +425,7 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
         }
         const u32x4_t ov = {pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
         if (a.flags & F_RESIDUAL_OUT) *reinterpret_cast<u32x4_t*>(a.residual_out + off + c8) = ov;
-        *reinterpret_cast<u32x4_t*>(a.y + off + c8) = ov;
+        *reinterpret_cast<u32x4_t*>(a.y + yoff + c8) = ov;
       }
     }
     return;
@@ -421,6 +438,7 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
     const int m = mp[p];
     const bool ok = m >= 0;
     const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
+    const long long yoff = (long long)y_pixel(a, ok ? m : 0) * a.Cout + cbase;
     unsigned vpk[RUN / 2];
     float t = 0.f;
 #pragma unroll
@@ -461,7 +479,7 @@ __device__ __forceinline__ void epilogue(const IgemmArgs& a, typename T::acc_t (
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = norm_silu_value(lane_bf(vv, e), rden, a.sqrt_c, lane_bf(gv, e));
       const u32x4_t ov = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
-      if (ok) *reinterpret_cast<u32x4_t*>(a.y + off + c8) = ov;
+      if (ok) *reinterpret_cast<u32x4_t*>(a.y + yoff + c8) = ov;
     }
   }
 }
@@ -706,12 +724,11 @@ __device__ __forceinline__ void store_plain(const IgemmArgs& a, typename T::acc_
                                             const int (&mp)[PB], int cbase) {
   constexpr int NACC = T::NACC, RUN = NACC * CB;
   const __amdgpu_buffer_rsrc_t yr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
-                                        0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)(y_elems(a) * 2u), 0x00020000);
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
     const int m = mp[p];
-    const unsigned off = (m >= 0) ? (unsigned)(m * a.Cout + cbase) * 2u : kOobOffset;
+    const unsigned off = (m >= 0) ? (unsigned)(y_pixel(a, m) * a.Cout + cbase) * 2u : kOobOffset;
 #pragma unroll
     for (int c8 = 0; c8 < RUN; c8 += 8) {
       u32x4_t ov;
@@ -1923,7 +1940,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       }
     }
     const int cbase = pt.co0 + wave_n * R * CB + elgrp * RUN;
-    if (EPI == EPI_STORE && a.flags == 0) {
+    if (EPI == EPI_STORE && a.flags == 0 && !a.ypad) {
       // 512 x 128 tiles store through the activation buffer the next tile
       // first fills in its main loop (its set-up has filled the other two).
       if constexpr (PB == 8 && CB == 2 && WN == 2)

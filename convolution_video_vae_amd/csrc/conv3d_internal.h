@@ -60,6 +60,11 @@ struct IgemmArgs {
   int vsplit, per_n;
   uint16_t split_base[kMaxVTiles + 1];
   uint16_t wg[kMaxVWG];
+  // Padded output (ypad != 0; slot kernels without a reduce): y is
+  // [N][yDy][yHy][yWy][Cout] and output pixel (n, d, h, w) is stored at
+  // (n, d + ypt, h + yph, w + ypw); residual and residual_out stay unpadded.
+  int ypad, yDy, yHy, yWy, ypt, yph, ypw;
+  float inv_wo;             // fp32 reciprocal of Wo (the padded pixel split)
   // Slot kernels, frame order (frames != 0): the N * Do output frames of
   // frame_slots = Ho * (slots per row) slots each are tiled separately into
   // frame_tiles runs. Pixel tiles [0, N * head * frame_tiles) are the first
@@ -156,7 +161,9 @@ int launch_group_norm(const GroupNormArgs& args, void* stream);
 // y [N][Dy][Hy][Wy][Cout] at (pt, ph, pw); zeros elsewhere except the
 // interiors of the hist planes before pt; the last cache_k frames also into
 // cache [N][cache_frames][Ho][Wo][Cout] at its last frames (cache may be null).
-// y0 may be null (the interior is written by someone else). previous, when
+// y0 may be null: the interior is then already in y (written in place by
+// the conv or the standalone norm) and the cache's current frames are copied
+// from there. previous, when
 // not null, holds hist frames [N][hist][Ho][Wo][Cout] that are copied into
 // the history planes' interiors and, for the cache's older frames, into the
 // cache.

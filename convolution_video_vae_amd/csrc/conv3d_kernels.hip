@@ -250,17 +250,20 @@ __global__ __launch_bounds__(256) void place_kernel(PlaceArgs a) {
   const int d = t - a.pt, h = hh - a.ph;
   const bool rowin = h >= 0 && h < a.Ho;
   if (d >= 0 && d < a.Do && rowin) {
-    if (a.y0) {
+    // The interior: copied from y0, or (y0 null) already written in place by
+    // the conv, which the cache then copies from.
+    u32x4_t* cr = nullptr;
+    if (a.cache && d >= a.Do - a.cache_k)
+      cr = reinterpret_cast<u32x4_t*>(
+          a.cache + ((n * a.cache_frames + (a.cache_frames - a.Do) + d) * a.Ho + h) * a.Wo * a.cout);
+    if (a.y0 || cr) {
       const u32x4_t* src =
-          reinterpret_cast<const u32x4_t*>(a.y0 + ((n * a.Do + d) * a.Ho + h) * a.Wo * a.cout);
-      u32x4_t* cr = nullptr;
-      if (a.cache && d >= a.Do - a.cache_k)
-        cr = reinterpret_cast<u32x4_t*>(
-            a.cache + ((n * a.cache_frames + (a.cache_frames - a.Do) + d) * a.Ho + h) * a.Wo * a.cout);
+          a.y0 ? reinterpret_cast<const u32x4_t*>(a.y0 + ((n * a.Do + d) * a.Ho + h) * a.Wo * a.cout)
+               : yr + a.pw * V;
       const int inner = a.Wo * V;
       for (int i = threadIdx.x; i < inner; i += blockDim.x) {
         const u32x4_t v = src[i];
-        yr[a.pw * V + i] = v;
+        if (a.y0) yr[a.pw * V + i] = v;
         if (cr) cr[i] = v;
       }
     }
