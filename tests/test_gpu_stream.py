@@ -34,25 +34,44 @@ def noise_bits(rng, shape):
     return (rng.integers(0, 0x7f00, size=shape) | (rng.integers(0, 2, size=shape) << 15)).astype(np.uint16)
 
 
+VALID = ((1, 1, 1), (0, 0, 0), (0, 0, 0))
+CAUSAL = ((1, 1, 1), (2, 1, 1), (0, 1, 1))
+
 PAD_CASES = [
-    # name, x shape, cout, history frames, cache frames
-    ("slot_path_128", (1, 5, 10, 20, 32), 128, 1, 2),
-    ("generic_path_160", (1, 4, 6, 9, 64), 160, 2, 2),
-    ("split_k_512", (1, 3, 5, 5, 512), 512, 0, 1),
-    ("one_output_frame", (1, 3, 7, 11, 32), 64, 2, 2),
+    # name, x shape, cout, history frames, cache frames, (stride, pad_lo, pad_hi),
+    # split_k, plan
+    ("slot_path_128", (1, 5, 10, 20, 32), 128, 1, 2, VALID, 0, None),
+    ("generic_path_160", (1, 4, 6, 9, 64), 160, 2, 2, VALID, 0, None),
+    ("split_k_512", (1, 3, 5, 5, 512), 512, 0, 1, VALID, 0, None),
+    ("one_output_frame", (1, 3, 7, 11, 32), 64, 2, 2, VALID, 0, None),
+    # slot kernels write the padded output in place (the placement pass then
+    # writes only the border, history and cache)
+    ("in_place_slot_512x128", (1, 5, 10, 40, 32), 128, 2, 2, CAUSAL, 1, "ns=-2"),
+    ("in_place_slot_512x128_nobias", (1, 5, 10, 40, 32), 128, 0, 1, CAUSAL, 1, "ns=-2"),
+    ("in_place_slot_384x160_batch2", (2, 4, 9, 21, 64), 160, 1, 2, CAUSAL, 1, "ns=-2"),
+    ("in_place_pair_view", (1, 4, 10, 24, 64), 128, 2, 2, ((1, 2, 2), (2, 0, 0), (0, 1, 1)), 1,
+     "ns=-3"),
 ]
 
 
-@pytest.mark.parametrize("name,xs,cout,P,cf", PAD_CASES, ids=[c[0] for c in PAD_CASES])
-def test_padded_output_integer_exact(name, xs, cout, P, cf):
+@pytest.mark.parametrize("name,xs,cout,P,cf,geo,split_k,plan_has", PAD_CASES,
+                         ids=[c[0] for c in PAD_CASES])
+def test_padded_output_integer_exact(name, xs, cout, P, cf, geo, split_k, plan_has):
     print(f"[stream] padded {name} x={xs} cout={cout} P={P} cache={cf}", flush=True)
     rng = np.random.default_rng(31)
     x, w, b = workloads.integer_tensors(xs, cout, seed=5, bias=True)
-    conv = Conv3d(w.cuda(), xs, bias=b, out_pad_lo=(2, 1, 1), out_pad_hi=(0, 1, 1),
-                  history_frames=P, cache_frames=cf)
+    if name.endswith("_nobias"):   # the plain store path of the kernel
+        b = None
+    stride, lo, hi = geo
+    conv = Conv3d(w.cuda(), xs, stride=stride, pad_lo=lo, pad_hi=hi, split_k=split_k, bias=b,
+                  out_pad_lo=(2, 1, 1), out_pad_hi=(0, 1, 1), history_frames=P, cache_frames=cf)
+    if plan_has:
+        e = cv.make_epilogue(bias=conv.bias)
+        plan = cv.conv3d_plan_describe(conv.desc, e if e.flags else None)
+        assert plan_has in plan and "reduce=0" in plan, plan
     Do, Ho, Wo = conv.out_dhw
     y0 = noise_bits(rng, conv.out_shape)
-    hist = noise_bits(rng, (1, P, Ho, Wo, cout))
+    hist = noise_bits(rng, (xs[0], P, Ho, Wo, cout))
     y0[:, 2 - P:2, 1:1 + Ho, 1:1 + Wo] = hist
     c0 = noise_bits(rng, conv.cache_shape)
     yg = Guarded(y0.shape, fill=y0)
@@ -62,7 +81,8 @@ def test_padded_output_integer_exact(name, xs, cout, P, cf):
     torch.cuda.synchronize()
     yg.assert_intact(name + " padded y")
     cg.assert_intact(name + " cache")
-    ref = oracle.conv3d(bits(x), bits(w), bias=b.numpy())
+    ref = oracle.conv3d(bits(x), bits(w), bias=None if b is None else b.numpy(), stride=stride,
+                        pad_lo=lo, pad_hi=hi)
     want = pad_output(ref, (2, 1, 1), (0, 1, 1), history=hist if P else None)
     assert np.array_equal(bits(y), want)
     k = min(cf, Do)
