@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # writes a known number of bytes (the --calibrate-copy pass). Valid only for
 # the kernel source it was taken on: reported as null once the source hash
 # differs.
-TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "a97f20cf8378c62c",
-           "bytes": 1624551104}   # 1332.0 MB fetched (FETCH_SIZE x 2.000) + 292.6 MB written
+TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "999665d8f32f477b",
+           "bytes": 1603808960}   # 1313.8 MB fetched (FETCH_SIZE x 2.000) + 290.0 MB written
 KERNEL_SOURCES = ("convolution_video_vae_amd/csrc/conv3d_igemm.hip",
                   "convolution_video_vae_amd/csrc/conv3d_device.h")
 
