@@ -1018,18 +1018,20 @@ __global__ __launch_bounds__(64 * WM * WN) void igemm_tile_kernel(IgemmArgs a) {
 // output pixels cover, that segment's input pixels plus the two-pixel halo
 // once, and the kw taps read it at slot offsets 0, 1, 2: a third of the
 // activation traffic of staging every tap separately. A slot is one pixel's
-// 64 bytes; its four 16-byte chunks are XOR-swizzled by (slot / 2) % 4, which
-// puts any eight consecutive slots of one chunk in eight distinct 16-byte
-// bank groups.
+// 64 bytes; its four 16-byte chunks are XOR-swizzled by (slot / 4) % 4, which
+// puts any sixteen consecutive slots of one chunk in the sixteen 16-byte bank
+// groups of a 256-byte window (one ds_read_b128 cycle serves 16 lanes; a
+// fragment read's lanes take consecutive slots, two skipped at a row break).
 //
 // Both operands reach LDS by buffer-to-LDS DMA (no staging registers); a
 // padding tap is an out-of-range lane, which writes zeros. Each wave computes
 // 128 pixels x 32*CB channels with v_mfma_f32_32x32x16_bf16 (16 accumulator
 // blocks for CB = 4). Three activation buffers and two weight buffers: while
-// stage i is computed, the weights of stage i+1 and the activations of stage
-// i+2 are fetched, a few DMA instructions between each group of MFMAs so the
-// address unit is never handed a burst. One barrier per stage, before the
-// last sub-step, whose MFMAs then cover the first fragment reads of stage i+1.
+// stage i is computed, the weights of stage i+1 (half of them from the last
+// sub-step of stage i-1 on) and the activations of stage i+2 are fetched.
+// Every DMA instruction and fragment read goes out on its own between single
+// MFMAs. One barrier per stage, before the last sub-step, whose MFMAs then
+// cover the first fragment reads of stage i+1.
 // ----------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
@@ -1057,7 +1059,7 @@ struct HaloShape {
 };
 
 __device__ __forceinline__ int xslot_chunk(int slot, int chunk) {
-  return chunk ^ ((slot >> 1) & 3);
+  return chunk ^ ((slot >> 2) & 3);
 }
 
 template <int CB, int WN, int XJ, int EPI, bool REF = false>
@@ -1303,26 +1305,16 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
       for (int e = 0; e < NACC; ++e) acc[cb][p][e] = 0.f;
 
   u32x4_t xf[2][PB], wf[2][CB];
-  // Fragments of sub-step u (tap kw = u / 2, K half h = u % 2).
-  auto read_frags = [&](auto xb_c, auto wb_c, int u, u32x4_t (&x)[PB], u32x4_t (&w)[CB]) {
+  // Fragments of sub-step u (tap kw = u / 2, K half h = u % 2) into register
+  // set u % 2: pixel block p, channel block cb.
+  auto read_x = [&](auto xb_c, int u, int p) {
     const char* xb = reinterpret_cast<const char*>(xbuf(xb_c));
-    const char* wb = reinterpret_cast<const char*>(wbuf(wb_c));
-    const int kw = u >> 1, h = u & 1;
-#pragma unroll
-    for (int p = 0; p < PB; ++p)
-      x[p] = *reinterpret_cast<const u32x4_t*>(xb + (h ? (ax[p][kw] ^ 32) : ax[p][kw]));
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      w[cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][h] + kw * WTAP);
+    const int kw = u >> 1;
+    xf[u & 1][p] = *reinterpret_cast<const u32x4_t*>(xb + ((u & 1) ? (ax[p][kw] ^ 32) : ax[p][kw]));
   };
-  // MFMAs of channel blocks [cb0, cb1).
-  auto mfmas = [&](const u32x4_t (&x)[PB], const u32x4_t (&w)[CB], int cb0, int cb1) {
-#pragma unroll
-    for (int cb = cb0; cb < cb1; ++cb)
-#pragma unroll
-      for (int p = 0; p < PB; ++p)
-        acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, w[cb]), __builtin_bit_cast(bf16x8_t, x[p]),
-                            acc[cb][p]);
+  auto read_w = [&](auto wb_c, int u, int cb) {
+    const char* wb = reinterpret_cast<const char*>(wbuf(wb_c));
+    wf[u & 1][cb] = *reinterpret_cast<const u32x4_t*>(wb + aw[cb][u & 1] + (u >> 1) * WTAP);
   };
 
   int e0 = first_stage();
@@ -1335,48 +1327,74 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     static_for<XJ>([&](auto j) { issue_x_one(d1, SlotC<1>{}, j); });
   }
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(XJ) : "memory");
-  read_frags(SlotC<0>{}, SlotC<0>{}, 0, xf[0], wf[0]);
+  static_for<PB>([&](auto p) { read_x(SlotC<0>{}, 0, decltype(p)::value); });
+  static_for<CB>([&](auto cb) { read_w(SlotC<0>{}, 0, decltype(cb)::value); });
 
-  // Stage i (activation buffer i % 3, weight buffer i % 2) fetches the
-  // weights of stage i+1 and the activations of stage i+2 during sub-steps
-  // 0-4, DMA instruction k after MFMA group k * NG / ND of those sub-steps.
-  constexpr int GPS = CB;                 // MFMA groups (one channel block) per sub-step
-  constexpr int NG = 5 * GPS, ND = NW + XJ;
-  static_assert(ND <= NG * 4, "DMA must fit in sub-steps 0-4");
+  // Stage i (activation buffer i % 3, weight buffer i % 2): six sub-steps u
+  // of CB * PB MFMAs (channel block cb = g / PB, pixel block p = g % PB). With
+  // one wave per SIMD a wave issues one instruction per four cycles, so the
+  // memory operations go out one or two between single MFMAs rather than in
+  // bunches the matrix core would wait behind. Each sub-step first issues its
+  // share of the DMA, then the next sub-step's fragments (pixel blocks, then
+  // the weights, in the order its MFMAs use them; during sub-step 4 within
+  // its first three quarters, so they have landed by the barrier):
+  //   - sub-steps 0-4: weight DMA instructions [NW5, NW) of stage i+1, then
+  //     the activations of stage i+2;
+  //   - barrier between sub-steps 4 and 5: stage i+1 has landed everywhere
+  //     (only stage i+2's activations, the last XJ DMA instructions, may be
+  //     in flight), and no wave reads stage i's buffers any more;
+  //   - sub-step 5: weight DMA instructions [0, NW5) of stage i+2 into stage
+  //     i's weight buffer, which the barrier has just freed, and stage i+1's
+  //     first fragments.
+    constexpr int NM = CB * PB, NR = PB + CB, NW5 = NW / 2, ND = NW - NW5 + XJ;
+  StageDma dnext = stage_dma(e1);
+  static_for<NW5>([&](auto k) { issue_w_one(dnext, SlotC<1>{}, k); });
   auto iteration = [&](auto i_c) -> bool {
     constexpr int I = decltype(i_c)::value;
     constexpr int XB = I % 3, WB = I % 2;
     if (e0 == kEnd) return false;
-    const StageDma dw = stage_dma(e1), dx = stage_dma(e2);
-    static_for<5>([&](auto u_c) {
+    // (The weight DMA of stage i+1 reuses the descriptor computed for its
+    // activations one stage earlier.)
+    const StageDma dw = dnext, dx = stage_dma(e2);
+    static_for<6>([&](auto u_c) {
       constexpr int u = decltype(u_c)::value;
-      read_frags(SlotC<XB>{}, SlotC<WB>{}, u + 1, xf[(u + 1) & 1], wf[(u + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<GPS>([&](auto cb_c) {
-        constexpr int cb = decltype(cb_c)::value;
-        constexpr int g = u * GPS + cb;
-        mfmas(xf[u & 1], wf[u & 1], cb, cb + 1);
+      constexpr int D0 = u < 5 ? u * ND / 5 : 0, D1 = u < 5 ? (u + 1) * ND / 5 : NW5;
+      constexpr int NOPS = D1 - D0 + NR;
+      constexpr int SPAN = u == 4 ? NM * 3 / 4 : NM;
+      if constexpr (u == 5) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
         __builtin_amdgcn_sched_barrier(0);
-        static_for<ND>([&](auto d_c) {
-          constexpr int d = decltype(d_c)::value;
-          if constexpr (d * NG / ND == g) {
-            if constexpr (d < NW) issue_w_one(dw, SlotC<(I + 1) % 2>{}, SlotC<d>{});
-            else issue_x_one(dx, SlotC<(I + 2) % 3>{}, SlotC<d - NW>{});
+      }
+      static_for<NM>([&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
+        static_for<NOPS>([&](auto o_c) {
+          constexpr int o = decltype(o_c)::value;
+          if constexpr (o * SPAN / NOPS == g) {
+            if constexpr (o < D1 - D0) {
+              constexpr int d = D0 + o;
+              if constexpr (u == 5) issue_w_one(dx, SlotC<WB>{}, SlotC<d>{});
+              else if constexpr (d < NW - NW5) issue_w_one(dw, SlotC<(I + 1) % 2>{}, SlotC<NW5 + d>{});
+              else issue_x_one(dx, SlotC<(I + 2) % 3>{}, SlotC<d - (NW - NW5)>{});
+            } else {
+              constexpr int r = o - (D1 - D0), un = (u + 1) % 6;
+              if constexpr (u < 5) {
+                if constexpr (r < PB) read_x(SlotC<XB>{}, un, r);
+                else read_w(SlotC<WB>{}, un, r - PB);
+              } else {
+                if constexpr (r < PB) read_x(SlotC<(I + 1) % 3>{}, un, r);
+                else read_w(SlotC<(I + 1) % 2>{}, un, r - PB);
+              }
+            }
           }
         });
         __builtin_amdgcn_sched_barrier(0);
+        constexpr int cb = g / PB, p = g % PB;
+        acc[cb][p] = T::mma(__builtin_bit_cast(bf16x8_t, wf[u & 1][cb]),
+                            __builtin_bit_cast(bf16x8_t, xf[u & 1][p]), acc[cb][p]);
+        __builtin_amdgcn_sched_barrier(0);
       });
     });
-    // Stage i+1 has landed everywhere (only stage i+2's activations may be
-    // in flight) and no wave reads stage i's buffers any more.
-    // (The XJ activation instructions of stage i+2 are always the last ones
-    // issued; past the end they load zeros into an idle buffer.)
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(XJ) : "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(SlotC<(I + 1) % 3>{}, SlotC<(I + 1) % 2>{}, 0, xf[0], wf[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(xf[1], wf[1], 0, CB);
-    __builtin_amdgcn_sched_barrier(0);
+    dnext = dx;
     e0 = e1;
     e1 = e2;
     e2 = next_stage(e2);
