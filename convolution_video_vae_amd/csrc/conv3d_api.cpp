@@ -218,13 +218,16 @@ int halo_maxseg(const TileCfg& c) { return (c.kb * 256 / 4 - c.bm() - 2) / 2 + 1
 // division, exact below 2^24: the index converts to fp32 exactly, and for a
 // divisor of at least 2 the product with the rounded reciprocal is within
 // one of the quotient, which the kernel's correction steps absorb (a divisor
-// of 1 is exact).
+// of 1 is exact). A tile's stages (9 (kd, kh) pairs x chunks) must fit the
+// kernel's per-tile stage table (kSlotMaxStages: Cin up to 448 bf16 or 896
+// e4m3 channels, 224 on the pixel-pair view).
 long long slot_rows(const Problem& pr) { return prod({pr.n, pr.Do, pr.Ho}); }
 
 bool slot_ok(const Problem& pr, const TileCfg& c) {
   const long long wp = pr.Wo + 2;
   return pr.sw == 1 && pr.cin % (pr.fp8 ? 64 : 32) == 0 && c.bn() > 0 && pr.cout % c.bn() == 0 &&
-         (c.bm() + 1) / wp + 2 <= 64 && slot_rows(pr) * wp + c.bm() + 2048 < (1LL << 24);
+         (c.bm() + 1) / wp + 2 <= 64 && slot_rows(pr) * wp + c.bm() + 2048 < (1LL << 24) &&
+         9 * k_chunks(pr) <= kSlotMaxStages;
 }
 
 // Stride 2 along W on the pixel-pair view (slot kernel, ns = -3): the input
@@ -248,7 +251,7 @@ bool pair_ok(const Problem& pr, const TileCfg& c) {
   const Problem v = pair_view(pr);
   const long long wp = v.Wo + 1;
   return c.bn() > 0 && v.cout % c.bn() == 0 && (c.bm() + 1) / wp + 2 <= 64 &&
-         slot_rows(v) * wp + c.bm() + 2048 < (1LL << 24);
+         slot_rows(v) * wp + c.bm() + 2048 < (1LL << 24) && 9 * k_chunks(v) <= kSlotMaxStages;
 }
 
 bool halo_ok(const Problem& pr, const TileCfg& c) {

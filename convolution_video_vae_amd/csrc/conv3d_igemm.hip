@@ -1346,16 +1346,18 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
   //   - sub-step 5: weight DMA instructions [0, NW5) of stage i+2 into stage
   //     i's weight buffer, which the barrier has just freed, and stage i+1's
   //     first fragments.
-    constexpr int NM = CB * PB, NR = PB + CB, NW5 = NW / 2, ND = NW - NW5 + XJ;
+  constexpr int NM = CB * PB, NR = PB + CB, NW5 = NW / 2, ND = NW - NW5 + XJ;
   StageDma dnext = stage_dma(e1);
+  StageDma dcar = stage_dma(e2);   // descriptor of stage e2
+  const unsigned cstep = (unsigned)a.Cout * 64u;   // weight bytes per chunk
   static_for<NW5>([&](auto k) { issue_w_one(dnext, SlotC<1>{}, k); });
   auto iteration = [&](auto i_c) -> bool {
     constexpr int I = decltype(i_c)::value;
     constexpr int XB = I % 3, WB = I % 2;
     if (e0 == kEnd) return false;
-    // (The weight DMA of stage i+1 reuses the descriptor computed for its
+    // (The weight DMA of stage i+1 reuses the descriptor formed for its
     // activations one stage earlier.)
-    const StageDma dw = dnext, dx = stage_dma(e2);
+    const StageDma dw = dnext, dx = dcar;
     static_for<6>([&](auto u_c) {
       constexpr int u = decltype(u_c)::value;
       constexpr int D0 = u < 5 ? u * ND / 5 : 0, D1 = u < 5 ? (u + 1) * ND / 5 : NW5;
@@ -1397,7 +1399,19 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     dnext = dx;
     e0 = e1;
     e1 = e2;
-    e2 = next_stage(e2);
+    // The next stage and its descriptor: the next chunk of the same (kd, kh)
+    // pair moves both offsets by one chunk (the common case, a few scalar
+    // adds); a new pair forms them afresh.
+    const int cc2 = (e2 & 255) + 1;
+    if (e2 != kEnd && cc2 < a.CC && (e2 >> 8) * a.CC + cc2 < s_end) {
+      ++e2;
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw) dcar.wsoff[kw] += cstep;
+      dcar.delta += 64;
+    } else {
+      e2 = next_stage(e2);
+      dcar = stage_dma(e2);
+    }
     return true;
   };
   for (;;) {
@@ -1677,6 +1691,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   __shared__ u32x4_t wbuf0[KW * WUP], wbuf1[KW * WUP];
   // Fused norm: per-pixel sums of squares of the WN waves sharing a pixel.
   __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
+  // Stage table of the current tile (see start_tile).
+  __shared__ u32x4_t stab[kSlotMaxStages];
 
   const int tid = threadIdx.x;
   const int lane0 = tid & 63;
@@ -1725,32 +1741,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   unsigned xmask[XJ];
   unsigned woff[WJ];
   int s_begin = 0, s_end = 0;
-  int e0 = kEnd, e1 = kEnd, e2 = kEnd;
-
-  // Stages e = (pair << 8) | cc over the live (kd, kh) pairs.
-  auto valid_stage = [&](int pr, int cc) -> int {
-    return (pr < 9 && pr * a.CC + cc < s_end) ? ((pr << 8) | cc) : kEnd;
-  };
-  auto next_stage = [&](int e) -> int {
-    if (e == kEnd) return kEnd;
-    int pr = e >> 8, cc = (e & 255) + 1;
-    if (cc == a.CC) {
-      cc = 0;
-      const unsigned rest = live & (~0u << (pr + 1));
-      pr = rest ? __builtin_ctz(rest) : 9;
-    }
-    return valid_stage(pr, cc);
-  };
-  auto first_stage = [&]() -> int {
-    if (s_begin >= s_end) return kEnd;
-    int pr = s_begin / a.CC, cc = s_begin % a.CC;
-    if (!((live >> pr) & 1u)) {
-      const unsigned rest = live & (~0u << pr);
-      pr = rest ? __builtin_ctz(rest) : 9;
-      cc = 0;
-    }
-    return valid_stage(pr, cc);
-  };
+  int si = 0, nst = 0;   // index of the current stage in the tile, stages of the tile
 
   auto xbuf = [&](auto b_c) -> u32x4_t* {
     constexpr int b = decltype(b_c)::value;
@@ -1769,41 +1760,72 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     unsigned rbit;       // reflect padding: row flag whose rows move by radj
     int radj;
   };
-  auto stage_dma = [&](int e) -> StageDma {
-    StageDma d;
-    const bool ok = e != kEnd;
-    const int q = ok ? e >> 8 : 0, cc = ok ? e & 255 : 0;
-    const int kq = q / 3, kh = q - kq * 3;
+  // Stage j of a tile is the j-th live (pair, chunk) step of [s_begin,
+  // s_end): pairs in stage order q (bit q of live), then chunks cc. Its
+  // table entry (formed per lane at tile set-up): the weight byte offset of
+  // (pair) tap 0; the activation byte offset; the pair's bit in the
+  // original (kd, kh) order (bits 0-8), the reflect row flags (bits 9-10)
+  // and, for two-tap pairs, the odd-pixel flag (bit 11); the reflect row
+  // adjustment. Two-tap pairs: the input is viewed as pixel pairs of
+  // 2 * Cin channels (chunks [0, CC / 2) the even pixel, the rest the odd
+  // one); stage cc takes chunk cc / 2 of pixel cc % 2, so even and odd
+  // pixels alternate. Pair tap kw' of a chunk of pixel e is the layer's tap
+  // 2 * kw' + e; tap 3 does not exist and reads zeros.
+  auto stage_entry = [&](int q, int cc) -> u32x4_t {
+    const int kq = (q >= 3) + (q >= 6), kh = q - kq * 3;
     const int kd = kq + krot >= 3 ? kq + krot - 3 : kq + krot;
     const int pr = kd * 3 + kh;
+    unsigned w0, odd = 0;
+    int ch;
     if constexpr (KW == 2) {
-      // Two-tap pairs: the input is viewed as pixel pairs of 2 * Cin channels
-      // (chunks [0, CC / 2) the even pixel, the rest the odd one). Stage cc
-      // takes chunk cc / 2 of pixel cc % 2, so even and odd pixels alternate.
-      // Pair tap kw' of a chunk of pixel e is the layer's tap 2 * kw' + e;
-      // tap 3 does not exist and reads zeros.
-      const int cco = a.CC >> 1;
-      const int odd = cc & 1, k = cc >> 1;
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        const int kw = 2 * kp + odd;
-        d.wsoff[kp] = (unsigned)(((kd * 9 + kh * 3 + min(kw, 2)) * cco + k) * a.Cout) * 64u;
-        d.wtap[kp] = kw > 2 ? kOobOffset : 0u;
-      }
+      const int cco = a.CC >> 1, k = cc >> 1;
+      odd = (unsigned)(cc & 1);
+      w0 = (unsigned)(((pr * 3 + (int)odd) * cco + k) * a.Cout) * 64u;
+      ch = (int)odd * cco + k;
+    } else {
+      w0 = (unsigned)((pr * 3 * a.CC + cc) * a.Cout) * 64u;
+      ch = cc;
+    }
+    u32x4_t e;
+    e[0] = w0;
+    e[1] = (unsigned)((kd * a.H + kh) * a.W * (a.Cin * ESZ) + ch * 64);
+    e[2] = (1u << pr) | (REF ? (kh == 0 ? 1u << 9 : (kh == 2 ? 1u << 10 : 0u)) : 0u) | (odd << 11);
+    e[3] = REF ? (unsigned)((kh == 0 ? 2 : -2) * a.W * (a.Cin * ESZ)) : 0u;
+    return e;
+  };
+  // The DMA descriptor of a (uniform) table entry; past the tile's last
+  // stage (ok false) every load is out of range.
+  const unsigned kws = (unsigned)((KW == 2 ? (a.CC >> 1) : a.CC) * a.Cout) * 64u;  // bytes per tap
+  auto stage_decode = [&](unsigned w0, unsigned w1, unsigned w2, unsigned w3, bool ok) -> StageDma {
+    StageDma d;
+    if constexpr (KW == 2) {
+      const unsigned odd = (w2 >> 11) & 1u;
+      d.wsoff[0] = ok ? w0 : 0u;
+      d.wsoff[1] = ok ? w0 + (2u - odd) * kws : 0u;
+      d.wtap[0] = 0u;
+      d.wtap[1] = odd ? kOobOffset : 0u;
     } else {
 #pragma unroll
       for (int kw = 0; kw < KW; ++kw) {
-        d.wsoff[kw] = (unsigned)(((kd * 9 + kh * 3 + kw) * a.CC + cc) * a.Cout) * 64u;
+        d.wsoff[kw] = ok ? w0 + (unsigned)kw * kws : 0u;
         d.wtap[kw] = 0u;
       }
     }
     d.wor = ok ? 0u : kOobOffset;
-    d.pbit = ok ? 1u << pr : 0u;
-    d.delta = (kd * a.H + kh) * a.W * (a.Cin * ESZ) +
-              (KW == 2 ? (cc & 1) * (a.CC >> 1) + (cc >> 1) : cc) * 64;
-    d.rbit = REF ? (kh == 0 ? 1u << 9 : (kh == 2 ? 1u << 10 : 0u)) : 0u;
-    d.radj = REF ? (kh == 0 ? 2 : -2) * a.W * (a.Cin * ESZ) : 0;
+    d.pbit = ok ? (w2 & 511u) : 0u;
+    d.delta = ok ? (int)w1 : 0;
+    d.rbit = REF ? (w2 & (3u << 9)) : 0u;
+    d.radj = REF ? (int)w3 : 0;
     return d;
+  };
+  // Table entry of stage si + 2 (uniform; decoded into scalar registers
+  // where a stage starts).
+  u32x4_t tnext;
+  auto decode_uniform = [&](const u32x4_t& t, bool ok) -> StageDma {
+    return stage_decode((unsigned)__builtin_amdgcn_readfirstlane((int)t[0]),
+                        (unsigned)__builtin_amdgcn_readfirstlane((int)t[1]),
+                        (unsigned)__builtin_amdgcn_readfirstlane((int)t[2]),
+                        (unsigned)__builtin_amdgcn_readfirstlane((int)t[3]), ok);
   };
   // Weight DMA instruction k of a stage (tap kw = k / WJ, piece k % WJ).
   auto issue_w_one = [&](const StageDma& d, auto b_c, auto k_c) {
@@ -1925,10 +1947,43 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     }
     s_begin = tc.split * a.steps_per_split;
     s_end = min(s_begin + a.steps_per_split, 9 * a.CC);
-    e0 = first_stage();
-    e1 = next_stage(e0);
-    e2 = next_stage(e1);
-    const StageDma d0 = stage_dma(e0), d1 = stage_dma(e1);
+    // Stage table: a scalar walk over the live pairs hands out the steps;
+    // lanes j = lane and 64 + lane of every wave form entries j and j + 64,
+    // wave 0 stores them (read from the first barrier of the tile's main
+    // loop on), and stages 0-2 come straight from lanes 0-2.
+    // (Entries 64 and up only when the K range holds more than 64 steps.)
+    const bool two = s_end - s_begin > 64;
+    int sq[2] = {0, 0}, scc[2] = {0, 0};
+    nst = 0;
+    for (int q = 0; q < 9; ++q) {
+      const int lo = max(s_begin, q * a.CC), hi = min(s_end, (q + 1) * a.CC);
+      if (!((live >> q) & 1u) || lo >= hi) continue;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int j = p * 64 + lane - nst;
+        if ((p == 0 || two) && j >= 0 && j < hi - lo) {
+          sq[p] = q;
+          scc[p] = lo - q * a.CC + j;
+        }
+      }
+      nst += hi - lo;
+    }
+    si = 0;
+    u32x4_t ent[2];
+    ent[0] = stage_entry(sq[0], scc[0]);
+    if (wave == 0 && lane < nst) stab[lane] = ent[0];
+    if (two) {
+      ent[1] = stage_entry(sq[1], scc[1]);
+      if (wave == 0 && 64 + lane < nst) stab[64 + lane] = ent[1];
+    }
+    auto lane_entry = [&](int L) -> u32x4_t {
+      u32x4_t t;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t[c] = (unsigned)__builtin_amdgcn_readlane((int)ent[0][c], L);
+      return t;
+    };
+    const StageDma d0 = decode_uniform(lane_entry(0), 0 < nst), d1 = decode_uniform(lane_entry(1), 1 < nst);
+    tnext = lane_entry(2);
     static_for<NW>([&](auto k) { issue_w_one(d0, SlotC<0>{}, k); });
     static_for<XJ>([&](auto j) { issue_x_one(d0, SlotC<0>{}, j); });
     static_for<NW1>([&](auto k) { issue_w_one(d1, SlotC<1>{}, k); });
@@ -2007,8 +2062,9 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   auto iteration = [&](auto i_c) -> bool {
     constexpr int I = decltype(i_c)::value;
     constexpr int XB = I % 3, WB = I % 2;
-    if (e0 == kEnd) return false;
-    const StageDma d2 = stage_dma(e2);
+    if (si >= nst) return false;
+    const StageDma d2 = decode_uniform(tnext, si + 2 < nst);
+    tnext = stab[min(si + 3, kSlotMaxStages - 1)];   // (for the next stage)
     if constexpr (KW == 2) {
       // Two-tap pairs: four sub-steps u (K half u / 2, tap u % 2), each CB*PB
       // MFMAs; tap kw of pixel block p reads fragment p + kw. Memory
@@ -2214,9 +2270,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
         });
       });
     }
-    e0 = e1;
-    e1 = e2;
-    e2 = next_stage(e2);
+    ++si;
     return true;
   };
 
@@ -2246,10 +2300,11 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
         for (int e = 0; e < NACC; ++e) acc[cb][p][e] = 0.f;
     // Stage 0 of this tile has landed everywhere; the previous tile's plain
     // stores (issued after this tile's DMA) may still be in flight.
+    // (The barrier also publishes wave 0's stage table.)
     if (have_prev && EPI == EPI_STORE && a.flags == 0)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW1 + XJ + EPI_VM) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW1 + XJ + EPI_VM) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NW1 + XJ) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW1 + XJ) : "memory");
     if constexpr (F8) {
 #pragma unroll
       for (int f = 0; f < PB; ++f) {

@@ -22,6 +22,9 @@ enum : unsigned { F_BIAS = 1u, F_RESIDUAL = 2u, F_NORM = 4u, F_RESIDUAL_OUT = 8u
 // and kMaxVWG work-groups per channel tile.
 constexpr int kMaxVTiles = 64;
 constexpr int kMaxVWG = 256;
+// Stages (live (kd, kh) pair x chunk steps) of one slot-kernel tile: its
+// per-tile stage table holds at most this many.
+constexpr int kSlotMaxStages = 128;
 
 // Everything one implicit-GEMM launch needs; passed by value as the kernel
 // argument. All tensors NDHWC.
