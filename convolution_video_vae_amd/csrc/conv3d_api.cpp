@@ -897,8 +897,21 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
   if (pl.vsplit) {
     a.vsplit = 1;
     a.per_n = pl.per_n;
-    memcpy(a.split_base, pl.split_base, sizeof a.split_base);
-    memcpy(a.wg, pl.wg, sizeof a.wg);
+    // Work-group b runs launch position xcd_run(b) (the device's XCD
+    // mapping: XCD b % 8 takes a contiguous run of positions); position
+    // nt * per_n + i computes slice wg[i] & 255 of pixel tile wg[i] >> 8 of
+    // channel tile nt.
+    const int grid = (int)pl.grid, G8 = grid & ~7;
+    if (grid > kMaxVWG) return CONV3D_ERR_UNSUPPORTED;
+    for (int b = 0; b < grid; ++b) {
+      const int bid = b < G8 ? (b & 7) * (G8 >> 3) + (b >> 3) : b;
+      const int nt = bid / pl.per_n, i = bid - nt * pl.per_n;
+      const int mt = pl.wg[i] >> 8, sl = pl.wg[i] & 255;
+      const int ns = pl.split_base[mt + 1] - pl.split_base[mt];
+      const int slot = nt * pl.per_n + pl.split_base[mt] + sl;
+      a.vwg[b] = (uint64_t)mt | ((uint64_t)nt << 16) | ((uint64_t)sl << 32) | ((uint64_t)ns << 40) |
+                 ((uint64_t)slot << 48);
+    }
   }
   if (pl.grid > 0x7fffffffLL) return CONV3D_ERR_UNSUPPORTED;
   if (pl.persistent) {

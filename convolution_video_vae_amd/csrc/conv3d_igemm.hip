@@ -147,19 +147,16 @@ __device__ __forceinline__ TileCoord tile_coord(const IgemmArgs& a, int BM, int 
   t.slot = (t.split * a.m_tiles + m_tile) * a.n_tiles + rest % a.n_tiles;
   return t;
 }
-// The same for a live-balanced split (a.vsplit): the launch-order table
-// gives the pixel tile and slice of each work-group of a channel tile.
+// The same for a live-balanced split (a.vsplit): the host's table entry of
+// this work-group.
 __device__ __forceinline__ TileCoord tile_coord_live(const IgemmArgs& a, int BM, int BN) {
-  const int bid = xcd_run(blockIdx.x);
-  const int nt = bid / a.per_n, i = bid - nt * a.per_n;
-  const int e = a.wg[i];
-  const int mt = e >> 8;
+  const unsigned long long e = a.vwg[blockIdx.x];
   TileCoord t;
-  t.m0 = mt * BM;
-  t.co0 = nt * BN;
-  t.split = e & 255;
-  t.nsplit = a.split_base[mt + 1] - a.split_base[mt];
-  t.slot = nt * a.per_n + a.split_base[mt] + t.split;
+  t.m0 = (int)(e & 0xFFFFu) * BM;
+  t.co0 = (int)((e >> 16) & 0xFFFFu) * BN;
+  t.split = (int)((e >> 32) & 0xFFu);
+  t.nsplit = (int)((e >> 40) & 0xFFu);
+  t.slot = (int)(e >> 48);
   return t;
 }
 // Next tile of a persistent work-group (called by one thread): hand-out
@@ -1099,8 +1096,7 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
     return tile_sh;
   };
   const int rows_total = a.N * a.Do * a.Ho;
-  const float inv_wo = 1.0f / (float)a.Wo, inv_wo2 = 1.0f / (float)(a.Wo + 2);
-  const float inv_ho = 1.0f / (float)a.Ho, inv_do = 1.0f / (float)a.Do;
+  const float inv_wo = a.inv_wo, inv_wo2 = a.inv_wp, inv_ho = a.inv_ho, inv_do = a.inv_do;
   int tile_lin = a.queue ? fetch_tile() : 0;
   while (tile_lin >= 0) {
   // Recomputing the per-lane set-up each tile is cheaper than the registers

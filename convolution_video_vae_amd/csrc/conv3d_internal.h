@@ -53,16 +53,16 @@ struct IgemmArgs {
   // fp32 reciprocals of Ho, Do and Wo + 2 (row splits with one correction
   // step each way; uniform, so they stay in scalar registers).
   float inv_ho, inv_do, inv_wp;
-  // Live-balanced K split (halo kernel partials, vsplit != 0): pixel tile t
-  // is cut into split_base[t + 1] - split_base[t] slices of about equal
-  // live work (taps that read real input), so tiles of a causal layer's
-  // first frames, which see fewer taps, get fewer slices. Each channel tile
-  // has per_n work-groups; work-group i of a channel tile (in launch order)
-  // computes slice wg[i] & 255 of pixel tile wg[i] >> 8, and writes its
-  // partials to slot split_base[t] + slice of the channel tile's per_n.
+  // Live-balanced K split (halo kernel partials, vsplit != 0): a pixel
+  // tile is cut into slices of about equal live work (taps that read real
+  // input), so tiles of a causal layer's first frames, which see fewer
+  // taps, get fewer slices. vwg[b] describes work-group b (blockIdx.x): its
+  // pixel tile (bits 0-15), channel tile (16-31), slice (32-39), the
+  // slices of its pixel tile (40-47) and the partial slot it writes
+  // (48-63), all formed on the host so that the work-group's first scalar
+  // load is its last.
   int vsplit, per_n;
-  uint16_t split_base[kMaxVTiles + 1];
-  uint16_t wg[kMaxVWG];
+  uint64_t vwg[kMaxVWG];
   // Padded output (ypad != 0; slot kernels without a reduce): y is
   // [N][yDy][yHy][yWy][Cout] and output pixel (n, d, h, w) is stored at
   // (n, d + ypt, h + yph, w + ypw); residual and residual_out stay unpadded.
