@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # writes a known number of bytes (the --calibrate-copy pass). Valid only for
 # the kernel source it was taken on: reported as null once the source hash
 # differs.
-TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "999665d8f32f477b",
-           "bytes": 1603808960}   # 1313.8 MB fetched (FETCH_SIZE x 2.000) + 290.0 MB written
+TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "4b69f15090e8fc82",
+           "bytes": 1623583744}   # 1333.8 MB fetched (FETCH_SIZE x 2.000) + 289.8 MB written
 KERNEL_SOURCES = ("convolution_video_vae_amd/csrc/conv3d_igemm.hip",
                   "convolution_video_vae_amd/csrc/conv3d_device.h")
 
