@@ -40,7 +40,8 @@ EXPORTED = ("conv3d_packed_weight_bytes", "conv3d_pack_weight", "conv3d_output_d
             "conv3d_plan_describe", "conv3d_group_norm_workspace_bytes", "conv3d_group_norm",
             "conv3d_padded_workspace_bytes", "conv3d_fwd_padded", "conv3d_stream_pack_input",
             "conv3d_pack_weight_2d", "conv3d_norm_silu", "conv3d_packed_weight_bytes_fp8",
-            "conv3d_pack_weight_fp8", "conv3d_fwd_noalloc")
+            "conv3d_pack_weight_fp8", "conv3d_fwd_noalloc", "conv3d_gn_partials_bytes",
+            "conv3d_fwd_gn_stats", "conv3d_group_norm_from_partials")
 
 
 class Conv3dError(RuntimeError):
@@ -128,6 +129,12 @@ def lib():
         L.conv3d_group_norm_workspace_bytes.argtypes = [pg, ctypes.POINTER(sz)]
         L.conv3d_group_norm.restype = i
         L.conv3d_group_norm.argtypes = [pg, vp, vp, vp, vp, vp, sz, vp]
+        L.conv3d_gn_partials_bytes.restype = i
+        L.conv3d_gn_partials_bytes.argtypes = [pd, ctypes.POINTER(sz)]
+        L.conv3d_fwd_gn_stats.restype = i
+        L.conv3d_fwd_gn_stats.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
+        L.conv3d_group_norm_from_partials.restype = i
+        L.conv3d_group_norm_from_partials.argtypes = [pg, pd, vp, vp, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -320,6 +327,39 @@ def conv3d_group_norm(desc: conv3d_group_norm_desc, x, gamma, beta, y, workspace
     _check(lib().conv3d_group_norm(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
                                    _ptr(workspace), workspace_bytes, _stream(stream)),
            "conv3d_group_norm")
+
+
+def conv3d_gn_partials_bytes(desc: conv3d_desc) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().conv3d_gn_partials_bytes(ctypes.byref(desc), ctypes.byref(out)),
+           "conv3d_gn_partials_bytes")
+    return int(out.value)
+
+
+def conv3d_fwd_gn_stats(desc: conv3d_desc, x, w_packed, y, gn_partials, workspace=None,
+                        workspace_bytes: int = 0, stream=None) -> None:
+    """conv3d_fwd with no epilogue, plus the GroupNorm partial statistics of y."""
+    if workspace is not None and not workspace_bytes and not isinstance(workspace, int):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check_conv_buffers(desc, x, w_packed, None, y)
+    _check_workspace(workspace, workspace_bytes)
+    _check_buffer(gn_partials, conv3d_gn_partials_bytes(desc), "gn_partials", "fp32")
+    _check(lib().conv3d_fwd_gn_stats(ctypes.byref(desc), _ptr(x), _ptr(w_packed), _ptr(y),
+                                     _ptr(gn_partials), _ptr(workspace), workspace_bytes,
+                                     _stream(stream)), "conv3d_fwd_gn_stats")
+
+
+def conv3d_group_norm_from_partials(desc: conv3d_group_norm_desc, conv: conv3d_desc,
+                                    gn_partials, x, gamma, beta, y, workspace=None,
+                                    workspace_bytes: int = 0, stream=None) -> None:
+    """GroupNorm of a conv3d_fwd_gn_stats output from its partial statistics."""
+    if workspace is not None and not workspace_bytes and not isinstance(workspace, int):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().conv3d_group_norm_from_partials(ctypes.byref(desc), ctypes.byref(conv),
+                                                 _ptr(gn_partials), _ptr(x), _ptr(gamma),
+                                                 _ptr(beta), _ptr(y), _ptr(workspace),
+                                                 workspace_bytes, _stream(stream)),
+           "conv3d_group_norm_from_partials")
 
 
 def make_out_pad(pad_lo=(0, 0, 0), pad_hi=(0, 0, 0), history_frames: int = 0, cache=None,

@@ -110,6 +110,7 @@ size_t packed_bytes(const Problem& pr) {
 int k_chunks(const Problem& pr) { return pr.fp8 ? (pr.cin + 63) / 64 : (pr.cin + 31) / 32; }
 
 conv3d_status check_desc(const conv3d_desc* d, Problem* pr) {
+  *pr = Problem{};   // (flags stay 0 until check_epi sets them)
   if (!d) return CONV3D_ERR_NULL;
   if (d->n <= 0 || d->d <= 0 || d->h <= 0 || d->w <= 0 || d->cin <= 0 || d->cout <= 0)
     return CONV3D_ERR_SHAPE;
@@ -614,6 +615,18 @@ conv3d_status plan_group_norm(const conv3d_group_norm_desc* d, GnPlan* pl) {
   return CONV3D_OK;
 }
 
+// GroupNorm statistics from the conv's epilogue: the 512-slot x 128-channel
+// slot plan with its plain staged store (no post-operations, NDHWC in and
+// out, bf16, one pass, tiles in slot order) whose 510 stored slots span at
+// most two frames.
+bool gn_stats_ok(const Problem& pr, const Plan& pl) {
+  const TileCfg& c = pl.cfg;
+  return c.ns == -2 && c.wm == 2 && c.wn == 2 && c.pb == 8 && c.cb == 2 && pl.mode == EPI_STORE &&
+         !pl.reduce && pl.splits == 1 && !pl.frame_order && pr.flags == 0 && !pr.fp8 &&
+         pr.layout == CONV3D_NDHWC && pr.out_layout == CONV3D_NDHWC && pr.cout % 128 == 0 &&
+         pr.nb >= pr.n && (long long)pr.Ho * (pr.Wo + 2) >= c.bm() - 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -780,10 +793,37 @@ conv3d_status conv3d_fwd_noalloc(const conv3d_desc* desc, const void* x, const v
   return conv3d_fwd(desc, x, w_packed, epi, y, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
+static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                     const conv3d_epilogue* epi, const conv3d_out_pad* op, void* y,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     float* gn_partials);
+
+conv3d_status conv3d_gn_partials_bytes(const conv3d_desc* desc, size_t* bytes) {
+  if (!bytes) return CONV3D_ERR_NULL;
+  *bytes = 0;
+  Problem pr;
+  const conv3d_status st = check_desc(desc, &pr);
+  if (st != CONV3D_OK) return st;
+  Plan pl;
+  make_plan(pr, desc->split_k, &pl);
+  if (!gn_stats_ok(pr, pl)) return CONV3D_ERR_UNSUPPORTED;
+  *bytes = 512ull * pl.m_tiles * pl.n_tiles;
+  return CONV3D_OK;
+}
+
+conv3d_status conv3d_fwd_gn_stats(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                  void* y, void* gn_partials, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!gn_partials) return CONV3D_ERR_NULL;
+  return fwd_padded_pass(desc, x, w_packed, nullptr, nullptr, y, workspace, workspace_bytes, stream,
+                         (float*)gn_partials);
+}
+
 // One pass: every tensor within the 32-bit buffer range (nb == n).
 static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, const void* w_packed,
                                      const conv3d_epilogue* epi, const conv3d_out_pad* op, void* y,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     float* gn_partials) {
   Problem pr;
   conv3d_status st = check_desc(desc, &pr);
   if (st != CONV3D_OK) return st;
@@ -799,6 +839,8 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
   if (st != CONV3D_OK) return st;
   Plan pl;
   make_plan(pr, desc->split_k, &pl);
+  if (gn_partials && (pp.on || !gn_stats_ok(pr, pl))) return CONV3D_ERR_UNSUPPORTED;
+  if (gn_partials && ((uintptr_t)gn_partials & 15)) return CONV3D_ERR_ALIGN;
   const bool direct = direct_pad(pr, pl, pp);
   const size_t off_stage = pl.total;                     // staged unpadded output
   const size_t ws_total = pp.on && !direct ? off_stage + align256(pr.y_bytes) : pl.total;
@@ -820,13 +862,14 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
   const Range rg = (f & F_NORM) ? range_of(epi->gamma, 2LL * pr.cout) : Range();
   const Range ro = (f & F_RESIDUAL_OUT) ? range_of(epi->residual_out, pr.y_bytes) : Range();
   const Range rs = range_of(workspace, (long long)ws_total);
-  const Range outs[] = {ry, ro, rs, rcache};
+  const Range rgn = gn_partials ? range_of(gn_partials, 512LL * pl.m_tiles * pl.n_tiles) : Range();
+  const Range outs[] = {ry, ro, rs, rcache, rgn};
   const Range ins[] = {rx, rw, rb, rr, rg};
   for (const Range& o : outs)
     for (const Range& i : ins)
       if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
       if (overlaps(outs[i], outs[j])) return CONV3D_ERR_OVERLAP;
 
   char* ws = (char*)workspace;
@@ -923,7 +966,9 @@ static conv3d_status fwd_padded_pass(const conv3d_desc* desc, const void* x, con
     a.queue = (unsigned*)(ws + pl.off_queue);
     if (launch_queue_reset(a.queue, stream)) return CONV3D_ERR_HIP;
   }
-  const int rc = launch_igemm(pl.cfg, pl.mode, pr.reflect, pr.fp8, a, (int)pl.grid, stream);
+  a.gnp = gn_partials;
+  const int rc = launch_igemm(pl.cfg, gn_partials ? (int)EPI_STATS : pl.mode, pr.reflect, pr.fp8, a,
+                              (int)pl.grid, stream);
   if (rc) return rc < 0 ? CONV3D_ERR_UNSUPPORTED : CONV3D_ERR_HIP;
 
   if (pl.reduce) {
@@ -973,7 +1018,8 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
   if (st != CONV3D_OK) return st;
   const int nb = batch_chunk(pr, op);
   if (nb >= pr.n)
-    return fwd_padded_pass(desc, x, w_packed, epi, op, y, workspace, workspace_bytes, stream);
+    return fwd_padded_pass(desc, x, w_packed, epi, op, y, workspace, workspace_bytes, stream,
+                           nullptr);
 
   // A batch beyond the 32-bit buffer range: passes over nb consecutive
   // samples, in order on the stream, reusing the workspace. Each pass checks
@@ -1032,7 +1078,8 @@ conv3d_status conv3d_fwd_padded(const conv3d_desc* desc, const void* x, const vo
       if (op->cache) os.cache = (char*)op->cache + b0 * cs;
     }
     st = fwd_padded_pass(&ds, (const char*)x + b0 * xs, w_packed, epi ? &es : nullptr,
-                         op ? &os : nullptr, (char*)y + b0 * ys, workspace, workspace_bytes, stream);
+                         op ? &os : nullptr, (char*)y + b0 * ys, workspace, workspace_bytes, stream,
+                         nullptr);
     if (st != CONV3D_OK) return st;
   }
   return CONV3D_OK;
@@ -1193,6 +1240,57 @@ conv3d_status conv3d_group_norm(const conv3d_group_norm_desc* desc, const void* 
   a.partial = (double*)workspace;
   a.stats = (float*)((char*)workspace + pl.off_stats);
   return launch_group_norm(a, stream) ? CONV3D_ERR_HIP : CONV3D_OK;
+}
+
+conv3d_status conv3d_group_norm_from_partials(const conv3d_group_norm_desc* desc,
+                                             const conv3d_desc* conv, const void* gn_partials,
+                                             const void* x, const float* gamma, const float* beta,
+                                             void* y, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (!desc || !conv || !gn_partials || !x || !gamma || !beta || !y) return CONV3D_ERR_NULL;
+  GnPlan gp;
+  conv3d_status st = plan_group_norm(desc, &gp);
+  if (st != CONV3D_OK) return st;
+  Problem pr;
+  st = check_desc(conv, &pr);
+  if (st != CONV3D_OK) return st;
+  Plan pl;
+  make_plan(pr, conv->split_k, &pl);
+  if (!gn_stats_ok(pr, pl)) return CONV3D_ERR_UNSUPPORTED;
+  if (desc->n != pr.n || desc->d != pr.Do || desc->h != pr.Ho || desc->w != pr.Wo ||
+      desc->c != pr.cout)
+    return CONV3D_ERR_SHAPE;
+  const int cpg = desc->c / desc->groups;
+  if (cpg % 4 || 128 % cpg) return CONV3D_ERR_UNSUPPORTED;   // whole subgroups of one channel tile
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta) ||
+      !aligned16(gn_partials))
+    return CONV3D_ERR_ALIGN;
+  if (!workspace || workspace_bytes < gp.total) return CONV3D_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CONV3D_ERR_ALIGN;
+  const Range rx = range_of(x, gp.bytes), ry = range_of(y, gp.bytes);
+  const Range rg = range_of(gamma, (long long)desc->c * 4), rb = range_of(beta, (long long)desc->c * 4);
+  const Range rp = range_of(gn_partials, 512LL * pl.m_tiles * pl.n_tiles);
+  const Range rw = range_of(workspace, (long long)gp.total);
+  if (x != y && overlaps(rx, ry)) return CONV3D_ERR_OVERLAP;
+  for (const Range& o : {ry, rw})
+    for (const Range& i : {rg, rb, rp})
+      if (overlaps(o, i)) return CONV3D_ERR_OVERLAP;
+  if (overlaps(rw, rx) || overlaps(rw, ry)) return CONV3D_ERR_OVERLAP;
+  GroupNormArgs a = gp.a;
+  a.x = (const uint16_t*)x;
+  a.y = (uint16_t*)y;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.partial = nullptr;
+  a.stats = (float*)((char*)workspace + gp.off_stats);
+  GnTileArgs t;
+  t.part = (const float*)gn_partials;
+  t.n_ctiles = pl.n_tiles;
+  t.TS = pl.cfg.bm() - 2;
+  t.WP = pr.Wo + 2;
+  t.Ho = pr.Ho;
+  t.frames_per_unit = desc->t_isolated ? 1 : pr.Do;
+  return launch_group_norm_tiles(a, t, stream) ? CONV3D_ERR_HIP : CONV3D_OK;
 }
 
 conv3d_status conv3d_transpose(const void* src, int src_layout, void* dst, int n, int c, int d,

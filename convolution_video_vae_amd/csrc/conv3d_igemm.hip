@@ -1501,11 +1501,20 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 // PB * 4 stores, as the plain store does (dropped slots get out-of-range
 // offsets), which the caller's wait counts rely on. Barriers wait for LDS
 // operations only; the stores stay in flight.
-template <int PB>
+//
+// STATS (GroupNorm statistics of the stored values): each thread also sums
+// the bf16 values it stores, and their squares, per 4-channel subgroup and
+// per frame (the tile's stored slots span at most two frames; output rows
+// from rnext on are the second), in fp32 (v_dot2c_f32_bf16). After the
+// last round the 16 threads of each 8-channel block add their sums in
+// thread order and threads 0-127 write the tile's 128 floats to gnp:
+// [frame 0/1][subgroup 0-31 of the 128 channels][sum, sum of squares].
+template <int PB, bool STATS = false>
 __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t (&acc)[2][PB],
                                              u32x4_t* sbuf, int m0, int m_end, int WP,
                                              float inv_wp, int co0, int wave_m, int wave_n,
-                                             int lrow, int lgrp) {
+                                             int lrow, int lgrp, float* gnp = nullptr,
+                                             int rnext = 0) {
   constexpr int RBU = 16;                 // 16-byte units per slot row
   constexpr int UNITS = 32 * 2 * 2 * RBU; // per round: 64 lane rows x 2 pixel blocks
   static_assert(PB % 2 == 0 && UNITS % 256 == 0, "rounds of two pixel blocks");
@@ -1513,6 +1522,9 @@ __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t 
       __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
                                         0x00020000);
   const int tid = threadIdx.x;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  // [frame][subgroup][sum, sum of squares]
+  float st[2][2][2] = {{{0.f, 0.f}, {0.f, 0.f}}, {{0.f, 0.f}, {0.f, 0.f}}};
   static_for<PB / 2>([&](auto rc) {
     constexpr int rho = decltype(rc)::value;
 #pragma unroll
@@ -1539,14 +1551,42 @@ __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t 
       const int s = m0 + (r >> 1) * PB + 2 * rho + (r & 1);
       const int row = small_div(s, WP, inv_wp);
       const int col = s - row * WP;
-      const unsigned off = (s < m_end && col < a.Wo)
-                               ? (unsigned)((row * a.Wo + col) * a.Cout + co0 + pos * 8) * 2u
-                               : kOobOffset;
+      const bool ok = s < m_end && col < a.Wo;
+      const unsigned off =
+          ok ? (unsigned)((row * a.Wo + col) * a.Cout + co0 + pos * 8) * 2u : kOobOffset;
       __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)off, 0, 0);
+      if constexpr (STATS) {
+        const bool f1 = row >= rnext;
+        const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const bf16x2_t x0 = __builtin_bit_cast(bf16x2_t, (ok && !f1) ? v[w] : 0u);
+          const bf16x2_t x1 = __builtin_bit_cast(bf16x2_t, (ok && f1) ? v[w] : 0u);
+          st[0][w >> 1][0] = __builtin_amdgcn_fdot2_f32_bf16(x0, one, st[0][w >> 1][0], false);
+          st[0][w >> 1][1] = __builtin_amdgcn_fdot2_f32_bf16(x0, x0, st[0][w >> 1][1], false);
+          st[1][w >> 1][0] = __builtin_amdgcn_fdot2_f32_bf16(x1, one, st[1][w >> 1][0], false);
+          st[1][w >> 1][1] = __builtin_amdgcn_fdot2_f32_bf16(x1, x1, st[1][w >> 1][1], false);
+        }
+      }
     }
     // every wave has read this round's block before the next one overwrites it
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   });
+  if constexpr (STATS) {
+    // Thread t's sums at floats 8t .. 8t+7; thread t's 8-channel block is t % 16.
+    float* red = reinterpret_cast<float*>(sbuf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[tid * 8 + i] = st[i >> 2][(i >> 1) & 1][i & 1];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tid < 128) {
+      // output float t: frame t / 64, subgroup (t / 2) % 32 = 2 * block + half, sum t % 2
+      const int fr = tid >> 6, blk = (tid >> 2) & 15, idx = fr * 4 + (tid & 3);
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += red[(j * 16 + blk) * 8 + idx];
+      gnp[tid] = sum;
+    }
+  }
 }
 
 // The same for tiles whose waves each hold all BN = 32*CB channels of 32*PB
@@ -2009,7 +2049,16 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       }
     }
     const int cbase = pt.co0 + wave_n * R * CB + elgrp * RUN;
-    if (EPI == EPI_STORE && a.flags == 0 && !a.ypad) {
+    if constexpr (EPI == EPI_STATS) {
+      // The plain store with GroupNorm statistics per (tile, channel tile):
+      // the tile's first frame is that of its first slot's output row.
+      static_assert(PB == 8 && CB == 2 && WN == 2 && KW == 3 && !F8, "512 x 128 bf16 tiles");
+      const int mt = pt.m0 / S::TS;
+      const int f0 = small_div(small_div(pt.m0, WP, inv_wp), a.Ho, inv_ho);
+      store_staged<PB, true>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m, wave_n,
+                             elrow, elgrp, a.gnp + ((size_t)mt * a.n_tiles + pt.co0 / S::BN) * 128,
+                             (f0 + 1) * a.Ho);
+    } else if (EPI == EPI_STORE && a.flags == 0 && !a.ypad) {
       // 512 x 128 tiles store through the activation buffer the next tile
       // first fills in its main loop (its set-up has filled the other two).
       if constexpr (PB == 8 && CB == 2 && WN == 2)
@@ -2297,7 +2346,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     // Stage 0 of this tile has landed everywhere; the previous tile's plain
     // stores (issued after this tile's DMA) may still be in flight.
     // (The barrier also publishes wave 0's stage table.)
-    if (have_prev && EPI == EPI_STORE && a.flags == 0)
+    if (have_prev && (EPI == EPI_STATS || (EPI == EPI_STORE && a.flags == 0)))
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW1 + XJ + EPI_VM) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW1 + XJ) : "memory");
@@ -2483,6 +2532,9 @@ const Entry kEntries[] = {
     F32(4, 1, 1, 4, 1, 3, EPI_PARTIAL),
     F32(4, 1, 2, 3, 1, 3, EPI_PARTIAL),
     F32(4, 1, 2, 2, 1, 3, EPI_PARTIAL),
+    // The 512 x 128 slot tile's plain store with GroupNorm statistics.
+    C32(2, 2, 8, 2, 0, -2, EPI_STATS),
+    R32(2, 2, 8, 2, 0, -2, EPI_STATS),
 };
 #undef C32
 #undef C16

@@ -13,6 +13,7 @@ enum EpiMode : int {
   EPI_STORE = 0,    // bf16 out = value (bias / residual / residual_out per flags)
   EPI_NORM = 1,     // bf16 out = full contract with channel-row L2 norm + SiLU
   EPI_PARTIAL = 2,  // fp32 partial sums of one K slice (split-K)
+  EPI_STATS = 3,    // EPI_STORE without post-operations, plus GroupNorm partial statistics
 };
 
 // Epilogue flag bits (same values as the public CONV3D_EPI_* flags).
@@ -33,6 +34,9 @@ struct IgemmArgs {
   const uint16_t* wp;       // packed [27][CC][Cout][32]
   uint16_t* y;              // [M][Cout]
   float* partial;           // [splits][M][Cout] (EPI_PARTIAL)
+  // GroupNorm partial statistics (EPI_STATS): per pixel tile and channel tile,
+  // [frame 0/1][4-channel subgroup][sum, sum of squares] of the stored values.
+  float* gnp;
   const float* bias;        // [Cout]
   const uint16_t* residual; // [M][Cout]
   const uint16_t* gamma;    // [Cout]
@@ -136,6 +140,16 @@ struct GroupNormArgs {
   int silu;
 };
 
+// GroupNorm statistics from a conv's per-tile partial sums (IgemmArgs::gnp,
+// 512 x 128 slot tiles of TS stored slots, output rows of WP slots, Ho rows
+// per frame; a tile's slots span at most two frames).
+struct GnTileArgs {
+  const float* part;        // [m_tiles][n_ctiles][2][32][2]
+  int n_ctiles;             // 128-channel tiles
+  int TS, WP, Ho;
+  int frames_per_unit;      // 1 (per frame) or the frames of a sample
+};
+
 // Launchers (conv3d_kernels.hip, conv3d_norm.hip). Each returns 0 on success or the HIP
 // error code of the launch. `stream` is a hipStream_t.
 // taps = 27: an OIDHW weight; taps = 9: a [cout][cin][3][3] weight placed in
@@ -160,6 +174,9 @@ constexpr size_t kScratchBytes = (size_t)96 << 20;
 int scratch_address(void** ptr);
 int launch_queue_reset(unsigned* queue, void* stream);
 int launch_group_norm(const GroupNormArgs& args, void* stream);
+// The same with the statistics formed from a conv's partial sums (no pass
+// over x for them): a finalize work-group per unit, then the apply pass.
+int launch_group_norm_tiles(const GroupNormArgs& args, const GnTileArgs& t, void* stream);
 // Padded outputs: the unpadded output y0 [N][Do][Ho][Wo][Cout] placed into
 // y [N][Dy][Hy][Wy][Cout] at (pt, ph, pw); zeros elsewhere except the
 // interiors of the hist planes before pt; the last cache_k frames also into

@@ -236,6 +236,54 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_kernel(GroupNormArgs a) 
   }
 }
 
+// Finalize from a conv's per-tile partial sums. One work-group per unit;
+// thread (lane l, group g) adds, in fp64, the unit's tile entries (frame f
+// of the unit, then tile t of f: the tiles whose stored slots meet the
+// frame) with index congruent to l modulo L; the L lane sums of a group are
+// then added in lane order. Entry (f, t) is tile t's frame slot f - f0(t),
+// the cpg / 4 subgroups of the group in its channel tile.
+__global__ __launch_bounds__(kThreads) void gn_finalize_tiles_kernel(GroupNormArgs a, GnTileArgs t) {
+  __shared__ double r1[kThreads], r2[kThreads];
+  const int u = blockIdx.x;
+  const int L = kThreads / a.G;
+  const int tid = threadIdx.x;
+  const int g = tid % a.G, l = tid / a.G;
+  double S1 = 0.0, S2 = 0.0;
+  if (l < L) {
+    const int c0 = g * a.cpg, nt = c0 / 128, sg0 = (c0 % 128) / 4, nsg = a.cpg / 4;
+    const long long FS = (long long)t.Ho * t.WP;   // slots per frame
+    int e = 0;
+    for (int k = 0; k < t.frames_per_unit; ++k) {
+      const long long f = (long long)u * t.frames_per_unit + k;
+      const long long t_lo = f * FS / t.TS, t_hi = ((f + 1) * FS - 1) / t.TS;
+      for (long long m = t_lo; m <= t_hi; ++m, ++e) {
+        if (e % L != l) continue;
+        const long long f0 = (m * t.TS / t.WP) / t.Ho;
+        const float* q = t.part + ((m * t.n_ctiles + nt) * 2 + (f - f0)) * 64 + sg0 * 2;
+        for (int i = 0; i < nsg; ++i) {
+          S1 += (double)q[2 * i];
+          S2 += (double)q[2 * i + 1];
+        }
+      }
+    }
+  }
+  r1[tid] = S1;
+  r2[tid] = S2;
+  __syncthreads();
+  if (tid < a.G) {
+    double T1 = 0.0, T2 = 0.0;
+    for (int i = 0; i < L; ++i) {
+      T1 += r1[i * a.G + tid];
+      T2 += r2[i * a.G + tid];
+    }
+    const double n = (double)a.P * a.cpg;
+    const double m = T1 / n;
+    const double var = fmax(T2 / n - m * m, 0.0);
+    a.stats[((size_t)u * a.G + tid) * 2] = (float)m;
+    a.stats[((size_t)u * a.G + tid) * 2 + 1] = (float)(1.0 / sqrt(var + (double)a.eps));
+  }
+}
+
 template <bool SILU>
 __global__ __launch_bounds__(kThreads) void gn_apply_kernel(GroupNormArgs a) {
   const int item = gridDim.x - 1 - blockIdx.x;
@@ -273,6 +321,20 @@ __global__ __launch_bounds__(kThreads) void gn_apply_kernel(GroupNormArgs a) {
 }
 
 }  // namespace
+
+int launch_group_norm_tiles(const GroupNormArgs& args, const GnTileArgs& t, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(gn_finalize_tiles_kernel, dim3(args.units), dim3(kThreads), 0, s, args, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  const unsigned items = (unsigned)args.units * (unsigned)args.chunks;
+  if (args.silu)
+    hipLaunchKernelGGL(gn_apply_kernel<true>, dim3(items), dim3(kThreads), 0, s, args);
+  else
+    hipLaunchKernelGGL(gn_apply_kernel<false>, dim3(items), dim3(kThreads), 0, s, args);
+  e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;
+}
 
 int launch_group_norm(const GroupNormArgs& args, void* stream) {
   hipStream_t s = (hipStream_t)stream;

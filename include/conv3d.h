@@ -329,6 +329,43 @@ conv3d_status conv3d_group_norm(const conv3d_group_norm_desc* desc, const void* 
                                 const float* gamma, const float* beta, void* y,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* The conv and the GroupNorm after it, with the norm's statistics formed by
+ * the conv (FlyDSL issue page, MiniMax H3 comment: conv and norm move
+ * together; here the norm's read of x for its statistics is saved, the conv
+ * sums what it stores). Available for convs that conv3d_fwd runs on the
+ * 512-slot x 128-channel slot tile with a plain store: cout % 128 == 0, no
+ * epilogue flags, NDHWC in and out, bf16, one batch pass, tiles in slot order
+ * (conv3d_plan_describe shows "ns=-2 bm=512 bn=128" without "order=frame"),
+ * and output frames of at least 510 slots (Ho * (Wo + 2) >= 510); anything
+ * else is CONV3D_ERR_UNSUPPORTED.
+ *
+ * conv3d_gn_partials_bytes: bytes of the partial-statistics buffer for desc
+ *   (512 per pixel tile and 128-channel tile).
+ * conv3d_fwd_gn_stats: y = conv3d(x, w) exactly as conv3d_fwd with no
+ *   epilogue computes it (bit for bit), plus gn_partials: per pixel tile and
+ *   channel tile, fp32 sums and sums of squares of the stored bf16 values per
+ *   frame of the tile (at most two) and 4-channel subgroup. gn_partials (16-byte
+ *   aligned, conv3d_gn_partials_bytes) must not overlap any other tensor.
+ * conv3d_group_norm_from_partials: y = GroupNorm(x) (+ SiLU) as
+ *   conv3d_group_norm computes it, for x the y of a conv3d_fwd_gn_stats call
+ *   on `conv` and gn_partials its partial statistics; the mean and variance
+ *   come from the partials (summed in a fixed order in fp64), so they equal
+ *   conv3d_group_norm's up to fp32 rounding of the partial sums. desc must
+ *   describe the conv's output ([n][Do][Ho][Wo][cout]; else CONV3D_ERR_SHAPE),
+ *   and each group must be whole 4-channel subgroups of one 128-channel tile
+ *   (c / groups a multiple of 4 dividing 128; else CONV3D_ERR_UNSUPPORTED).
+ *   workspace: conv3d_group_norm_workspace_bytes(desc). Other rules as
+ *   conv3d_group_norm. The partials are only read. */
+conv3d_status conv3d_gn_partials_bytes(const conv3d_desc* desc, size_t* bytes);
+conv3d_status conv3d_fwd_gn_stats(const conv3d_desc* desc, const void* x, const void* w_packed,
+                                  void* y, void* gn_partials, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+conv3d_status conv3d_group_norm_from_partials(const conv3d_group_norm_desc* desc,
+                                             const conv3d_desc* conv, const void* gn_partials,
+                                             const void* x, const float* gamma, const float* beta,
+                                             void* y, void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* conv3d_status_str(conv3d_status status);
 

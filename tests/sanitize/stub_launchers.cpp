@@ -35,11 +35,13 @@ int launch_transpose(const uint16_t* src, uint16_t* dst, int n, int a, int b, vo
   return 0;
 }
 bool igemm_has_config(const TileCfg& cfg, int mode, bool, bool) {
-  return cfg.r > 0 && mode >= EPI_STORE && mode <= EPI_PARTIAL;
+  return cfg.r > 0 && mode >= EPI_STORE && mode <= EPI_STATS;
 }
 int launch_igemm(const TileCfg& cfg, int mode, bool, bool, const IgemmArgs& a, int grid, void*) {
   require(a.x && a.wp && a.y && grid > 0 && cfg.bm() > 0 && cfg.bn() > 0, "igemm args");
   require(mode != EPI_PARTIAL || a.partial, "partials need a workspace");
+  require(mode != EPI_STATS || (a.gnp && cfg.bm() == 512 && cfg.bn() == 128 && cfg.ns == -2),
+          "statistics need their buffer and the 512 x 128 slot tile");
   require(a.M > 0 && a.Cout > 0 && a.CC > 0 && a.steps_per_split > 0, "igemm sizes");
   ++g_launches;
   return 0;
@@ -56,6 +58,13 @@ int launch_queue_reset(unsigned* q, void*) {
 }
 int launch_group_norm(const GroupNormArgs& a, void*) {
   require(a.x && a.y && a.partial && a.stats && a.units > 0 && a.chunks > 0, "group norm args");
+  ++g_launches;
+  return 0;
+}
+int launch_group_norm_tiles(const GroupNormArgs& a, const GnTileArgs& t, void*) {
+  require(a.x && a.y && a.stats && a.units > 0 && a.chunks > 0 && t.part && t.n_ctiles > 0 &&
+              t.TS > 0 && t.WP > 0 && t.Ho > 0 && t.frames_per_unit > 0,
+          "group norm from partials args");
   ++g_launches;
   return 0;
 }

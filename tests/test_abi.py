@@ -437,3 +437,68 @@ def test_noalloc_rejects_before_touching_the_device():
     bad = cv.make_desc((1, 1, 4, 4, 64), 64)          # empty valid output
     assert lib.conv3d_fwd_noalloc(ctypes.byref(bad), X, X, None, X, None) == 2
     assert lib.conv3d_fwd_noalloc(None, X, X, None, X, None) == 1
+
+
+def test_gn_partials_plan_rules():
+    """conv3d_gn_partials_bytes: 512 bytes per pixel tile and 128-channel tile
+    for convs on the 512 x 128 slot plan with a plain store; every other plan
+    (split K, another tile, NCDHW, e4m3, the pixel-pair view, frames of fewer
+    than 510 slots) is CONV3D_ERR_UNSUPPORTED. Plan queries launch nothing."""
+    lib = cv.lib()
+    out = ctypes.c_size_t()
+    L = workloads.LAYERS["h3_l0_128"]
+    d = cv.make_desc(L.x_shape, L.cout, pad_lo=L.pad_lo, pad_hi=L.pad_hi)
+    assert lib.conv3d_gn_partials_bytes(ctypes.byref(d), ctypes.byref(out)) == 0
+    assert out.value == 512 * 2202
+    assert lib.conv3d_gn_partials_bytes(ctypes.byref(d), None) == 1
+    assert lib.conv3d_gn_partials_bytes(None, ctypes.byref(out)) == 1
+    two = cv.make_desc((1, 4, 24, 30, 128), 256, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=1)
+    assert lib.conv3d_gn_partials_bytes(ctypes.byref(two), ctypes.byref(out)) == 0
+    assert out.value == 512 * 7 * 2
+    unsupported = [
+        cv.make_desc((1, 3, 20, 40, 128), 128, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1)),   # split K
+        cv.make_desc((1, 3, 10, 16, 128), 128, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1),
+                     split_k=1),                                                     # 180-slot frames
+        cv.make_desc((1, 3, 20, 40, 128), 96, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=1),
+        cv.make_desc(L.x_shape, L.cout, pad_lo=L.pad_lo, pad_hi=L.pad_hi, dtype=cv.FP8_E4M3),
+        cv.make_desc(L.x_shape, L.cout, stride=(1, 2, 2), pad_lo=(2, 0, 0), pad_hi=(0, 1, 1)),
+    ]
+    n, dd, h, w, c = L.x_shape
+    unsupported.append(cv.make_desc((n, c, dd, h, w), L.cout, pad_lo=L.pad_lo, pad_hi=L.pad_hi,
+                                    layout=cv.NCDHW))
+    for u in unsupported:
+        assert lib.conv3d_gn_partials_bytes(ctypes.byref(u), ctypes.byref(out)) == 6, \
+            cv.conv3d_plan_describe(u)
+        assert out.value == 0
+
+
+def test_gn_stats_calls_reject_before_launching():
+    """conv3d_fwd_gn_stats and conv3d_group_norm_from_partials check pointers,
+    plans, shapes, group layout, alignment, workspace and overlaps on the host;
+    each failing call returns before anything is enqueued."""
+    lib = cv.lib()
+    X, W, Y, P, WS = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40   # never dereferenced
+    conv = cv.make_desc((1, 3, 20, 40, 128), 128, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1), split_k=1)
+    fwd = lib.conv3d_fwd_gn_stats
+    assert fwd(ctypes.byref(conv), X, W, Y, None, None, 0, None) == 1          # no partials
+    assert fwd(ctypes.byref(conv), X, W, Y, P + 4, None, 0, None) == 3         # misaligned
+    split = cv.make_desc((1, 3, 20, 40, 128), 128, pad_lo=(2, 1, 1), pad_hi=(0, 1, 1))
+    assert fwd(ctypes.byref(split), X, W, Y, P, WS, 1 << 30, None) == 6        # split plan
+    assert fwd(ctypes.byref(conv), X, W, Y, Y + 16, None, 0, None) == 4        # partials in y
+    gn = cv.make_group_norm_desc((1, 3, 20, 40, 128), 32, silu=True)
+    ws = ctypes.c_size_t()
+    assert lib.conv3d_group_norm_workspace_bytes(ctypes.byref(gn), ctypes.byref(ws)) == 0
+    G = 6 << 40
+    frm = lib.conv3d_group_norm_from_partials
+    args = lambda d, c, p, ws_bytes=ws.value: (ctypes.byref(d), ctypes.byref(c), p, Y, G, G + 512,
+                                               X, WS, ws_bytes, None)
+    assert frm(*args(gn, conv, None)) == 1
+    assert frm(*args(gn, split, P)) == 6                                         # not a stats plan
+    wrong = cv.make_group_norm_desc((1, 3, 20, 40, 256), 32)
+    assert frm(*args(wrong, conv, P)) == 2                                       # not the conv's output
+    g3 = cv.make_group_norm_desc((1, 3, 20, 40, 128), 16)                         # 8 channels: fine
+    assert frm(*args(g3, conv, P, 0)) == 5                                       # workspace too small
+    g_odd = cv.make_group_norm_desc((1, 3, 20, 40, 128), 64)                      # 2-channel groups
+    assert frm(*args(g_odd, conv, P)) == 6
+    assert frm(*args(gn, conv, P + 8)) == 3                                      # misaligned partials
+    assert frm(*args(gn, conv, WS)) == 4                                         # partials in workspace
