@@ -37,6 +37,9 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # differs.
 TRAFFIC = {"workload": "h3_l0_128", "kernel_hash": "4b69f15090e8fc82",
            "bytes": 1623583744}   # 1333.8 MB fetched (FETCH_SIZE x 2.000) + 289.8 MB written
+# conv layer -> the GroupNorm of its output, timed with and without the
+# statistics summed in the conv's epilogue
+CONV_GN_PAIRS = {"conv_gn_h3_l0_128": ("h3_l0_128", "gn_h3_l0_128")}
 KERNEL_SOURCES = ("convolution_video_vae_amd/csrc/conv3d_igemm.hip",
                   "convolution_video_vae_amd/csrc/conv3d_device.h")
 
@@ -457,6 +460,46 @@ def main():
                           f"{'per-frame' if N.t_isolated else 'per-sample'} statistics"
                           f"{', SiLU' if N.silu else ''}"}
             del x, y, gn
+            torch.cuda.empty_cache()
+        # a conv and the GroupNorm of its output: statistics in a separate
+        # pass over y against statistics summed in the conv's epilogue
+        for name, (lname, nname) in CONV_GN_PAIRS.items():
+            if wanted is not None and name not in wanted:
+                continue
+            L, N = workloads.LAYERS[lname], workloads.NORM_LAYERS[nname]
+            case = Case(L, torch, cv)
+            _, gamma, beta = workloads.norm_tensors(N)
+            gn = GroupNorm(N.x_shape, N.groups, gamma.cuda(), beta.cuda(), eps=N.eps,
+                           silu=N.silu, t_isolated=N.t_isolated)
+            assert tuple(case.y.shape) == tuple(N.x_shape)
+            part = torch.empty(cv.conv3d_gn_partials_bytes(case.layer.desc) // 4,
+                               dtype=torch.float32, device="cuda")
+            out = torch.empty_like(case.y)
+
+            def two_pass():
+                case()
+                gn(case.y, y=out)
+
+            def fused():
+                cv.conv3d_fwd_gn_stats(case.layer.desc, case.x, case.layer.w_packed, case.y,
+                                       part, case.layer.workspace)
+                cv.conv3d_group_norm_from_partials(gn.desc, case.layer.desc, part, case.y,
+                                                   gn.gamma, gn.beta, out, gn.workspace)
+            steps = max(5, args.steps)
+            tms, _ = time_case(two_pass, steps, 3, torch)
+            fms, _ = time_case(fused, steps, 3, torch)
+            assert torch.isfinite(out.float()).all().item()
+            flops = L.flops()
+            per_layer[name] = {
+                "us_two_pass": round(tms * 1e3, 2), "us_fused_stats": round(fms * 1e3, 2),
+                "saved_us": round((tms - fms) * 1e3, 2),
+                "tflops_fused_stats": round(flops / (fms * 1e-3) / 1e12, 2),
+                "config": f"{lname} conv, then {nname} ({N.groups} groups, "
+                          f"{'per-frame' if N.t_isolated else 'per-sample'} statistics"
+                          f"{', SiLU' if N.silu else ''}) of its output; "
+                          "two_pass = conv3d_fwd + conv3d_group_norm, fused_stats = "
+                          "conv3d_fwd_gn_stats + conv3d_group_norm_from_partials"}
+            del case, gn, part, out
             torch.cuda.empty_cache()
 
     if not args.no_layers:

@@ -39,10 +39,8 @@ __device__ __forceinline__ float lane_bf(const u32x4_t& v, int e) {
 // reciprocal. Each stays a few fp32 ulps from the exact value, far below the
 // bf16 rounding that follows, and the three kernels that finish the contract
 // share this code, so they agree bit for bit.
-__device__ __forceinline__ float norm_silu_value(float v, float rden, float sqrt_c, float g) {
-  const float nrm = rbf(v * rden);
-  const float scl = rbf(nrm * sqrt_c);
-  const float aff = rbf(scl * g);
+// aff / (1 + e^-aff) in fp32, before its final rounding.
+__device__ __forceinline__ float silu_f32(float aff) {
   constexpr float kLog2eHi = 1.44269502162933349609375f;   // fp32 nearest log2(e)
   constexpr float kLog2eLo = 1.925963033500011e-08f;       // log2(e) - kLog2eHi
   constexpr float kLn2 = 0.693147182464599609375f;
@@ -51,7 +49,28 @@ __device__ __forceinline__ float norm_silu_value(float v, float rden, float sqrt
   const float r = __builtin_fmaf(x, kLog2eLo, __builtin_fmaf(x, kLog2eHi, -t));
   const float e2 = __builtin_amdgcn_exp2f(t);
   const float ex = __builtin_fmaf(e2, r * kLn2, e2);
-  return rbf(aff * __builtin_amdgcn_rcpf(1.0f + ex));
+  return aff * __builtin_amdgcn_rcpf(1.0f + ex);
+}
+__device__ __forceinline__ float norm_silu_value(float v, float rden, float sqrt_c, float g) {
+  const float nrm = rbf(v * rden);
+  const float scl = rbf(nrm * sqrt_c);
+  const float aff = rbf(scl * g);
+  return rbf(silu_f32(aff));
+}
+
+// The low and high bf16 halves of a packed pair as fp32 (one shift / mask).
+__device__ __forceinline__ float bf_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+// norm_silu_value on both halves of a packed pair of values v with their
+// gammas g, as a packed pair: the same operations and roundings, two values
+// per conversion.
+__device__ __forceinline__ unsigned norm_silu_pair(unsigned v, unsigned g, float rden,
+                                                   float sqrt_c) {
+  const unsigned nrm = pack2(bf_lo(v) * rden, bf_hi(v) * rden);
+  const unsigned scl = pack2(bf_lo(nrm) * sqrt_c, bf_hi(nrm) * sqrt_c);
+  const unsigned aff = pack2(bf_lo(scl) * bf_lo(g), bf_hi(scl) * bf_hi(g));
+  return pack2(silu_f32(bf_lo(aff)), silu_f32(bf_hi(aff)));
 }
 
 }  // namespace conv3d

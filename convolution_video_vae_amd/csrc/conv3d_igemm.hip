@@ -1489,6 +1489,99 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 //   s2: stage i+1's fragments 2 .. PB-1, fragment f after the MFMAs of pixel
 //       block f-2 (its register's last reader), the rest of the weight DMA.
 // ----------------------------------------------------------------------------
+// EPI_NORM epilogue of the slot kernel (the work-group holds its pixels'
+// whole channel rows, BN == Cout). The arithmetic is the generic epilogue's,
+// with these differences in how it is carried out:
+//   - the tile's bias and gamma are staged once in LDS (sbuf: an activation
+//     buffer no wave reads during the epilogue), so the lanes read them
+//     without global-memory latency;
+//   - the residual reads of pixel block p+1 are in flight while block p is
+//     processed (for a pixel past the tile, pixel 0's row is read and its
+//     values are never stored);
+//   - values move as packed bf16 pairs: one conversion per two values, and
+//     each pair's squares added to the row sum by one v_dot2_f32_bf16.
+// HB / HR: bias / residual present (the caller dispatches on the flags).
+template <class T, int WM, int WN, int PB, int CB, bool HB, bool HR>
+__device__ __forceinline__ void epilogue_norm_slot(const IgemmArgs& a,
+                                                   typename T::acc_t (&acc)[CB][PB],
+                                                   const int (&mp)[PB], int co0, int cbase,
+                                                   int wave_m, int wave_n, int lrow, int lgrp,
+                                                   float* red, u32x4_t* sbuf) {
+  constexpr int R = T::R, NACC = T::NACC, RUN = NACC * CB, NQ = RUN / 8;
+  constexpr int BN = R * CB * WN, NT = 64 * WM * WN;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  float* sb = reinterpret_cast<float*>(sbuf);            // [BN] bias
+  uint16_t* sg = reinterpret_cast<uint16_t*>(sb + BN);   // [BN] gamma
+  for (int i = threadIdx.x; i < BN; i += NT) {
+    if (HB) sb[i] = a.bias[co0 + i];
+    sg[i] = a.gamma[co0 + i];
+  }
+  const bool out_res = a.flags & F_RESIDUAL_OUT;
+  u32x4_t rv[2][NQ];
+  auto load_res = [&](int p, u32x4_t (&d)[NQ]) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+        a.residual + (long long)(mp[p] >= 0 ? mp[p] : 0) * a.Cout + cbase);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) d[q] = src[q];
+  };
+  if (HR) load_res(0, rv[0]);
+  __syncthreads();   // the staged bias and gamma are visible
+  const float* lb = sb + (cbase - co0);
+  const u32x4_t* lg = reinterpret_cast<const u32x4_t*>(sg + (cbase - co0));
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    if (HR && p + 1 < PB) load_res(p + 1, rv[(p + 1) & 1]);
+    const int m = mp[p];
+    const bool ok = m >= 0;
+    const long long off = (long long)(ok ? m : 0) * a.Cout + cbase;
+    const long long yoff = (long long)y_pixel(a, ok ? m : 0) * a.Cout + cbase;
+    unsigned vpk[RUN / 2];
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      f32x4_t b[2];
+      if (HB) {
+        b[0] = *reinterpret_cast<const f32x4_t*>(lb + 8 * q);
+        b[1] = *reinterpret_cast<const f32x4_t*>(lb + 8 * q + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 8 * q + 2 * j;
+        unsigned pk = pack2(acc[c / NACC][p][c % NACC], acc[(c + 1) / NACC][p][(c + 1) % NACC]);
+        if (HB) pk = pack2(bf_lo(pk) + b[j >> 1][2 * (j & 1)], bf_hi(pk) + b[j >> 1][2 * (j & 1) + 1]);
+        if (HR) {
+          const unsigned r = rv[p & 1][q][j];
+          pk = pack2(bf_lo(pk) + bf_lo(r), bf_hi(pk) + bf_hi(r));
+        }
+        vpk[c / 2] = pk;
+        const bf16x2_t h = __builtin_bit_cast(bf16x2_t, pk);
+        t = __builtin_amdgcn_fdot2_f32_bf16(h, h, t, false);
+      }
+      if (out_res && ok)
+        *reinterpret_cast<u32x4_t*>(a.residual_out + off + 8 * q) =
+            u32x4_t{vpk[4 * q], vpk[4 * q + 1], vpk[4 * q + 2], vpk[4 * q + 3]};
+    }
+#pragma unroll
+    for (int o = R; o < 64; o <<= 1) t += __shfl_xor(t, o);  // lanes of the same pixel
+    if (WN > 1) {  // ... and the WN waves (a slot per pixel block: no reuse)
+      if (lgrp == 0) red[((wave_n * WM + wave_m) * PB + p) * R + lrow] = t;
+      __syncthreads();
+      t = 0.f;
+      for (int wn = 0; wn < WN; ++wn) t += red[((wn * WM + wave_m) * PB + p) * R + lrow];
+    }
+    const float rden = 1.0f / fmaxf(sqrtf(t), 1e-12f);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const u32x4_t gv = lg[q];
+      u32x4_t ov;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ov[j] = norm_silu_pair(vpk[4 * q + j], gv[j], rden, a.sqrt_c);
+      if (ok) *reinterpret_cast<u32x4_t*>(a.y + yoff + 8 * q) = ov;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Store of a 512-slot x 128-channel slot tile through LDS. The plain store's
 // instructions each write 16-byte pieces of 32 pixels PB slots apart, which
 // the store path absorbs about three times more slowly than whole lines. Here
@@ -1502,91 +1595,131 @@ __global__ __launch_bounds__(256) void igemm_halo_kernel(IgemmArgs a) {
 // offsets), which the caller's wait counts rely on. Barriers wait for LDS
 // operations only; the stores stay in flight.
 //
-// STATS (GroupNorm statistics of the stored values): each thread also sums
-// the bf16 values it stores, and their squares, per 4-channel subgroup and
-// per frame (the tile's stored slots span at most two frames; output rows
-// from rnext on are the second), in fp32 (v_dot2c_f32_bf16). After the
-// last round the 16 threads of each 8-channel block add their sums in
-// thread order and threads 0-127 write the tile's 128 floats to gnp:
+// STATS (GroupNorm statistics of the stored values): as each lane packs its
+// values for the LDS block it also adds them, and their squares, in fp32
+// (v_dot2_f32_bf16 on the packed pairs) per 4-channel subgroup and per frame
+// (the tile's stored slots span at most two frames; output rows from rnext
+// on are the second); slots that are not stored add zeros. After the last
+// round the lanes' sums go through LDS and threads 0-127 each add one
+// (frame, subgroup, sum / sum of squares) over the 64 pixel lanes (wave_m,
+// then lane row, ascending) and write the tile's 128 floats to gnp:
 // [frame 0/1][subgroup 0-31 of the 128 channels][sum, sum of squares].
+// A tile whose stored slots all precede row rnext (all but about one per
+// frame) keeps one frame's sums only.
 template <int PB, bool STATS = false>
 __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t (&acc)[2][PB],
                                              u32x4_t* sbuf, int m0, int m_end, int WP,
                                              float inv_wp, int co0, int wave_m, int wave_n,
-                                             int lrow, int lgrp, float* gnp = nullptr,
-                                             int rnext = 0) {
+                                             int lrow, int lgrp, const int* mp = nullptr,
+                                             float* gnp = nullptr, int rnext = 0) {
   constexpr int RBU = 16;                 // 16-byte units per slot row
   constexpr int UNITS = 32 * 2 * 2 * RBU; // per round: 64 lane rows x 2 pixel blocks
+  constexpr int WM = 2;
   static_assert(PB % 2 == 0 && UNITS % 256 == 0, "rounds of two pixel blocks");
   const __amdgpu_buffer_rsrc_t yr =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
                                         0x00020000);
-  const int tid = threadIdx.x;
+  // (The thread index passes through an empty asm so that the addresses
+  // formed from it are computed here, not hoisted to the kernel's start and
+  // kept in registers through the main loop.)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  // [frame][subgroup][sum, sum of squares]
-  float st[2][2][2] = {{{0.f, 0.f}, {0.f, 0.f}}, {{0.f, 0.f}, {0.f, 0.f}}};
-  static_for<PB / 2>([&](auto rc) {
-    constexpr int rho = decltype(rc)::value;
+  // (uniform: the output row of the tile's last stored slot)
+  const int rpx = rnext * a.Wo;
+  const bool two = STATS && small_div(min(m0 + PB * 64 - 2, m_end) - 1, WP, inv_wp) >= rnext;
+  auto rounds = [&](auto two_c) {
+    constexpr bool TWO = decltype(two_c)::value;
+    // [frame][lane subgroup 0-7][sum, sum of squares]
+    float st[TWO ? 2 : 1][8][2];
+    if constexpr (STATS) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = (wave_m * 32 + lrow) * 2 + j;
-      const int sw = (r >> 1) & 15;
+      for (int f = 0; f < (TWO ? 2 : 1); ++f)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        u32x4_t ov;
+        for (int g = 0; g < 8; ++g) st[f][g][0] = st[f][g][1] = 0.f;
+    }
+    static_for<PB / 2>([&](auto rc) {
+      constexpr int rho = decltype(rc)::value;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = 8 * k + 2 * q;   // lane channel 0 .. 31: acc[c / 16][p][c % 16]
-          ov[q] = pack2(acc[c / 16][2 * rho + j][c % 16], acc[(c + 1) / 16][2 * rho + j][(c + 1) % 16]);
+      for (int j = 0; j < 2; ++j) {
+        const int r = (wave_m * 32 + lrow) * 2 + j;
+        const int sw = (r >> 1) & 15;
+        bool ok = false, f1 = false;
+        if constexpr (STATS) {
+          ok = mp[2 * rho + j] >= 0;
+          f1 = TWO && mp[2 * rho + j] >= rpx;
         }
-        sbuf[r * RBU + ((wave_n * 8 + lgrp * 4 + k) ^ sw)] = ov;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          u32x4_t ov;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = 8 * k + 2 * q;   // lane channel 0 .. 31: acc[c / 16][p][c % 16]
+            ov[q] = pack2(acc[c / 16][2 * rho + j][c % 16], acc[(c + 1) / 16][2 * rho + j][(c + 1) % 16]);
+          }
+          sbuf[r * RBU + ((wave_n * 8 + lgrp * 4 + k) ^ sw)] = ov;
+          if constexpr (STATS) {
+            const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int g = 2 * k + (q >> 1);
+              if constexpr (TWO) {
+                const bf16x2_t x0 = __builtin_bit_cast(bf16x2_t, (ok && !f1) ? ov[q] : 0u);
+                const bf16x2_t x1 = __builtin_bit_cast(bf16x2_t, (ok && f1) ? ov[q] : 0u);
+                st[0][g][0] = __builtin_amdgcn_fdot2_f32_bf16(x0, one, st[0][g][0], false);
+                st[0][g][1] = __builtin_amdgcn_fdot2_f32_bf16(x0, x0, st[0][g][1], false);
+                st[TWO ? 1 : 0][g][0] = __builtin_amdgcn_fdot2_f32_bf16(x1, one, st[TWO ? 1 : 0][g][0], false);
+                st[TWO ? 1 : 0][g][1] = __builtin_amdgcn_fdot2_f32_bf16(x1, x1, st[TWO ? 1 : 0][g][1], false);
+              } else {
+                const bf16x2_t x = __builtin_bit_cast(bf16x2_t, ok ? ov[q] : 0u);
+                st[0][g][0] = __builtin_amdgcn_fdot2_f32_bf16(x, one, st[0][g][0], false);
+                st[0][g][1] = __builtin_amdgcn_fdot2_f32_bf16(x, x, st[0][g][1], false);
+              }
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < UNITS / 256; ++i) {
+        const int q = i * 256 + tid;
+        const int r = q >> 4, pos = q & 15;
+        const u32x4_t v = sbuf[r * RBU + (pos ^ ((r >> 1) & 15))];
+        const int s = m0 + (r >> 1) * PB + 2 * rho + (r & 1);
+        const int row = small_div(s, WP, inv_wp);
+        const int col = s - row * WP;
+        const bool ok = s < m_end && col < a.Wo;
+        const unsigned off =
+            ok ? (unsigned)((row * a.Wo + col) * a.Cout + co0 + pos * 8) * 2u : kOobOffset;
+        __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)off, 0, 0);
+      }
+      // every wave has read this round's block before the next one overwrites it
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    });
+    if constexpr (STATS) {
+      // Lane sums at floats NV*tid ..; thread t < 128 adds output float t:
+      // frame t / 64, subgroup sg = (t / 2) % 32 (wave column sg / 16, lane
+      // group (sg / 8) % 2, lane subgroup sg % 8), sum or square sum t % 2.
+      constexpr int NV = TWO ? 32 : 16;
+      float* red = reinterpret_cast<float*>(sbuf);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) red[tid * NV + i] = st[TWO ? (i >> 4) : 0][(i >> 1) & 7][i & 1];
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (tid < 128) {
+        const int fr = tid >> 6, sg = (tid >> 1) & 31;
+        const int i = (((sg & 7) << 1) | (tid & 1)) + 16 * fr;
+        const int lane0 = (((sg >> 4) * WM) * 64 + ((sg >> 3) & 1) * 32) * NV + i;
+        float sum = 0.f;
+        if (TWO || fr == 0) {
+          for (int wm = 0; wm < WM; ++wm)
+            for (int lr = 0; lr < 32; ++lr) sum += red[lane0 + (wm * 64 + lr) * NV];
+        }
+        gnp[tid] = sum;
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < UNITS / 256; ++i) {
-      const int q = i * 256 + tid;
-      const int r = q >> 4, pos = q & 15;
-      const u32x4_t v = sbuf[r * RBU + (pos ^ ((r >> 1) & 15))];
-      const int s = m0 + (r >> 1) * PB + 2 * rho + (r & 1);
-      const int row = small_div(s, WP, inv_wp);
-      const int col = s - row * WP;
-      const bool ok = s < m_end && col < a.Wo;
-      const unsigned off =
-          ok ? (unsigned)((row * a.Wo + col) * a.Cout + co0 + pos * 8) * 2u : kOobOffset;
-      __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)off, 0, 0);
-      if constexpr (STATS) {
-        const bool f1 = row >= rnext;
-        const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const bf16x2_t x0 = __builtin_bit_cast(bf16x2_t, (ok && !f1) ? v[w] : 0u);
-          const bf16x2_t x1 = __builtin_bit_cast(bf16x2_t, (ok && f1) ? v[w] : 0u);
-          st[0][w >> 1][0] = __builtin_amdgcn_fdot2_f32_bf16(x0, one, st[0][w >> 1][0], false);
-          st[0][w >> 1][1] = __builtin_amdgcn_fdot2_f32_bf16(x0, x0, st[0][w >> 1][1], false);
-          st[1][w >> 1][0] = __builtin_amdgcn_fdot2_f32_bf16(x1, one, st[1][w >> 1][0], false);
-          st[1][w >> 1][1] = __builtin_amdgcn_fdot2_f32_bf16(x1, x1, st[1][w >> 1][1], false);
-        }
-      }
-    }
-    // every wave has read this round's block before the next one overwrites it
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  });
-  if constexpr (STATS) {
-    // Thread t's sums at floats 8t .. 8t+7; thread t's 8-channel block is t % 16.
-    float* red = reinterpret_cast<float*>(sbuf);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[tid * 8 + i] = st[i >> 2][(i >> 1) & 1][i & 1];
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (tid < 128) {
-      // output float t: frame t / 64, subgroup (t / 2) % 32 = 2 * block + half, sum t % 2
-      const int fr = tid >> 6, blk = (tid >> 2) & 15, idx = fr * 4 + (tid & 3);
-      float sum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sum += red[(j * 16 + blk) * 8 + idx];
-      gnp[tid] = sum;
-    }
-  }
+  };
+  if (two) rounds(std::integral_constant<bool, true>{});
+  else rounds(std::integral_constant<bool, false>{});
 }
 
 // The same for tiles whose waves each hold all BN = 32*CB channels of 32*PB
@@ -1717,6 +1850,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   typedef typename T::acc_t acc_t;
   static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
   static_assert(EPI != EPI_NORM || WM * WN * PB * R * 4 <= 2048, "norm exchange area");
+  static_assert(EPI != EPI_NORM || 6 * R * CB * WN <= XU * 16, "norm bias / gamma staging");
   static_assert(NW + XJ + EPI_VM <= 63, "vmcnt range");
   static_assert(!(F8 && REF), "e4m3 operands take zero padding only");
   static_assert(!(PB == 8 && CB == 2 && WN == 2) || XU >= 2048, "staged store block");
@@ -1729,6 +1863,9 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   __shared__ float red[(EPI == EPI_NORM && WN > 1) ? WM * WN * PB * R : 1];
   // Stage table of the current tile (see start_tile).
   __shared__ u32x4_t stab[kSlotMaxStages];
+  // GroupNorm statistics: the partials' address, the tile count and the
+  // frame height, read back at each tile's end.
+  __shared__ unsigned long long epi_sh[EPI == EPI_STATS ? 2 : 1];
 
   const int tid = threadIdx.x;
   const int lane0 = tid & 63;
@@ -1737,6 +1874,11 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   const int wave_n = wave / WM;
   const int lrow = lane0 & 31;
   const int lgrp = lane0 >> 5;
+  if (EPI == EPI_STATS && tid == 0) {   // (visible after the first barrier)
+    epi_sh[0] = (unsigned long long)a.gnp;
+    epi_sh[EPI == EPI_STATS ? 1 : 0] =
+        (unsigned)a.n_tiles | ((unsigned long long)(unsigned)a.Ho << 32);
+  }
 
   // Tiles: one per work-group, or (a.queue set) a persistent work-group per
   // CU taking tiles from its XCD's queue, as in the halo kernel. The ticket
@@ -1863,18 +2005,28 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
                         (unsigned)__builtin_amdgcn_readfirstlane((int)t[2]),
                         (unsigned)__builtin_amdgcn_readfirstlane((int)t[3]), ok);
   };
+  // LDS destination of a DMA piece: the buffer's address plus a constant
+  // plus this wave's 1 KB slice. The slice offset passes through an empty asm
+  // at each use, so the compiler forms every destination with one scalar add
+  // instead of keeping dozens of them in registers through the main loop.
+  const unsigned wave_lds = (unsigned)wave * 1024u;
+  auto lds_dst = [&](const void* buf, unsigned cst) -> void* {
+    unsigned w = wave_lds;
+    asm volatile("" : "+s"(w));
+    return (void*)((const char*)buf + cst + w);
+  };
   // Weight DMA instruction k of a stage (tap kw = k / WJ, piece k % WJ).
   auto issue_w_one = [&](const StageDma& d, auto b_c, auto k_c) {
     constexpr int k = decltype(k_c)::value;
     constexpr int kw = k / WJ, j = k % WJ;
-    dma16(wrsrc, &wbuf(b_c)[kw * WUP + (j * 4 + wave) * 64], woff[j] | d.wor | d.wtap[kw],
+    dma16(wrsrc, lds_dst(wbuf(b_c), (kw * WUP + j * 256) * 16), woff[j] | d.wor | d.wtap[kw],
           d.wsoff[kw]);
   };
   auto issue_x_one = [&](const StageDma& d, auto b_c, auto j_c) {
     constexpr int j = decltype(j_c)::value;
     const int radj = (REF && (xmask[j] & d.rbit)) ? d.radj : 0;
     const unsigned off = (xmask[j] & d.pbit) ? (unsigned)(xbase[j] + d.delta + radj) : kOobOffset;
-    dma16(xrsrc, &xbuf(b_c)[(j * 4 + wave) * 64], off, 0u);
+    dma16(xrsrc, lds_dst(xbuf(b_c), j * 256 * 16), off, 0u);
   };
 
   // Set-up of tile t and the DMA of its first two stages.
@@ -2053,11 +2205,19 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       // The plain store with GroupNorm statistics per (tile, channel tile):
       // the tile's first frame is that of its first slot's output row.
       static_assert(PB == 8 && CB == 2 && WN == 2 && KW == 3 && !F8, "512 x 128 bf16 tiles");
+      // (The partials' address and the frame height come back from LDS:
+      // kept in registers they would stay live through the main loop.)
+      const unsigned long long gp = epi_sh[0], gq = epi_sh[1];
+      float* gnp = reinterpret_cast<float*>(
+          ((unsigned long long)__builtin_amdgcn_readfirstlane((int)(gp >> 32)) << 32) |
+          (unsigned)__builtin_amdgcn_readfirstlane((int)gp));
+      const int n_tiles = __builtin_amdgcn_readfirstlane((int)gq);
+      const int ho = __builtin_amdgcn_readfirstlane((int)(gq >> 32));
       const int mt = pt.m0 / S::TS;
-      const int f0 = small_div(small_div(pt.m0, WP, inv_wp), a.Ho, inv_ho);
+      const int f0 = small_div(small_div(pt.m0, WP, inv_wp), ho, inv_ho);
       store_staged<PB, true>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m, wave_n,
-                             elrow, elgrp, a.gnp + ((size_t)mt * a.n_tiles + pt.co0 / S::BN) * 128,
-                             (f0 + 1) * a.Ho);
+                             elrow, elgrp, mp, gnp + ((size_t)mt * n_tiles + pt.co0 / S::BN) * 128,
+                             (f0 + 1) * ho);
     } else if (EPI == EPI_STORE && a.flags == 0 && !a.ypad) {
       // 512 x 128 tiles store through the activation buffer the next tile
       // first fills in its main loop (its set-up has filled the other two).
@@ -2069,6 +2229,20 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
                                   elrow, elgrp);
       else
         store_plain<T, PB, CB>(a, acc, mp, cbase);
+    } else if constexpr (EPI == EPI_NORM) {
+      auto run = [&](auto hb, auto hr) {
+        epilogue_norm_slot<T, WM, WN, PB, CB, decltype(hb)::value, decltype(hr)::value>(
+            a, acc, mp, pt.co0, cbase, wave_m, wave_n, elrow, elgrp, red, xbuf2);
+      };
+      using B1 = std::integral_constant<bool, true>;
+      using B0 = std::integral_constant<bool, false>;
+      if (a.flags & F_BIAS) {
+        if (a.flags & F_RESIDUAL) run(B1{}, B1{});
+        else run(B1{}, B0{});
+      } else {
+        if (a.flags & F_RESIDUAL) run(B0{}, B1{});
+        else run(B0{}, B0{});
+      }
     } else {
       epilogue<T, WM, WN, PB, CB, EPI>(a, acc, mp, cbase, pt.split, wave_m, wave_n, elrow, elgrp,
                                        red);

@@ -236,35 +236,52 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_kernel(GroupNormArgs a) 
   }
 }
 
-// Finalize from a conv's per-tile partial sums. One work-group per unit;
-// thread (lane l, group g) adds, in fp64, the unit's tile entries (frame f
-// of the unit, then tile t of f: the tiles whose stored slots meet the
-// frame) with index congruent to l modulo L; the L lane sums of a group are
-// then added in lane order. Entry (f, t) is tile t's frame slot f - f0(t),
-// the cpg / 4 subgroups of the group in its channel tile.
+// Finalize from a conv's per-tile partial sums. One work-group per unit.
+// For each frame f of the unit, the tiles whose stored slots meet the frame
+// are taken in chunks: the threads first copy the chunk's 64-float rows
+// (tile t's frame slot f - f0(t), f0 the frame of its first slot, for every
+// channel tile) into LDS with independent 16-byte loads; then thread
+// (lane l, group g) adds, in fp64, the cpg / 4 subgroups of its group from
+// the rows of chunk tiles l, l + L, ... The L lane sums of a group are
+// finally added in lane order.
 __global__ __launch_bounds__(kThreads) void gn_finalize_tiles_kernel(GroupNormArgs a, GnTileArgs t) {
+  constexpr int kRows = 128;
   __shared__ double r1[kThreads], r2[kThreads];
+  __shared__ f32x4_t rows[kRows][16];
   const int u = blockIdx.x;
   const int L = kThreads / a.G;
   const int tid = threadIdx.x;
   const int g = tid % a.G, l = tid / a.G;
   double S1 = 0.0, S2 = 0.0;
-  if (l < L) {
-    const int c0 = g * a.cpg, nt = c0 / 128, sg0 = (c0 % 128) / 4, nsg = a.cpg / 4;
-    const long long FS = (long long)t.Ho * t.WP;   // slots per frame
-    int e = 0;
-    for (int k = 0; k < t.frames_per_unit; ++k) {
-      const long long f = (long long)u * t.frames_per_unit + k;
-      const long long t_lo = f * FS / t.TS, t_hi = ((f + 1) * FS - 1) / t.TS;
-      for (long long m = t_lo; m <= t_hi; ++m, ++e) {
-        if (e % L != l) continue;
-        const long long f0 = (m * t.TS / t.WP) / t.Ho;
-        const float* q = t.part + ((m * t.n_ctiles + nt) * 2 + (f - f0)) * 64 + sg0 * 2;
-        for (int i = 0; i < nsg; ++i) {
-          S1 += (double)q[2 * i];
-          S2 += (double)q[2 * i + 1];
+  const int c0 = g * a.cpg, nt = c0 / 128, sg0 = (c0 % 128) / 4, nsg = a.cpg / 4;
+  const int nct = t.n_ctiles, per_chunk = kRows / nct;
+  const long long FS = (long long)t.Ho * t.WP;   // slots per frame
+  for (int k = 0; k < t.frames_per_unit; ++k) {
+    const long long f = (long long)u * t.frames_per_unit + k;
+    const long long fs0 = f * FS;                 // the frame's first slot
+    const long long t_lo = fs0 / t.TS, t_hi = (fs0 + FS - 1) / t.TS;
+    const int nt_f = (int)(t_hi - t_lo + 1);
+    for (int ch = 0; ch < nt_f; ch += per_chunk) {
+      const int cn = min(per_chunk, nt_f - ch);
+      for (int idx = tid; idx < cn * nct * 16; idx += kThreads) {
+        const int row = idx >> 4, i = row / nct, ct = row - i * nct;
+        const long long m = t_lo + ch + i;
+        // tile m starts in frame f - 1 when its first slot precedes fs0
+        const int fslot = m * t.TS < fs0 ? 1 : 0;
+        rows[row][idx & 15] = reinterpret_cast<const f32x4_t*>(
+            t.part + ((m * nct + ct) * 2 + fslot) * 64)[idx & 15];
+      }
+      __syncthreads();
+      if (l < L) {
+        for (int i = l; i < cn; i += L) {
+          const float* q = reinterpret_cast<const float*>(rows[i * nct + nt]) + sg0 * 2;
+          for (int j = 0; j < nsg; ++j) {
+            S1 += (double)q[2 * j];
+            S2 += (double)q[2 * j + 1];
+          }
         }
       }
+      __syncthreads();
     }
   }
   r1[tid] = S1;
