@@ -1740,7 +1740,8 @@ __device__ __forceinline__ void store_staged_rows(const IgemmArgs& a, const f32x
   const __amdgpu_buffer_rsrc_t yr =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.y, (short)0, (int)((unsigned)a.M * (unsigned)a.Cout * 2u),
                                         0x00020000);
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;   // (kept from being hoisted, as in store_staged)
+  asm volatile("" : "+v"(tid));
   static_for<4>([&](auto rc) {
     constexpr int rho = decltype(rc)::value;
     if (wave == rho) {
