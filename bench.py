@@ -7,10 +7,12 @@ One step is one conv3d_fwd call on the headline layer (H3 L0: x NDHWC
 [1,17,256,256,128] bf16, w [128,128,3,3,3], causal time pad 2, spatial pad 1,
 about 1 TFLOP) with its inputs already resident in HBM and the weight packed
 once beforehand. The K timed steps run back to back on one stream between
-HIP events, bracketed by device synchronisation. `value` is TFLOP/s at the
-layer's algorithmic FLOP count 2*M*Cout*27*Cin (only live taps for the T=1
-layer). Every other layer shape is timed the same way and reported under
-"per_layer". One JSON line is printed on stdout.
+HIP events, bracketed by device synchronisation, after W untimed warm-up
+steps (default 60, about 45 ms of this layer: the chip's clocks settle over
+the first 40 or so back-to-back calls). `value` is TFLOP/s at the layer's
+algorithmic FLOP count 2*M*Cout*27*Cin (only live taps for the T=1 layer).
+Every other layer shape is timed the same way, after at least 50 ms of
+warm-up, and reported under "per_layer". One JSON line is printed on stdout.
 """
 from __future__ import annotations
 
@@ -57,7 +59,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=60)
     p.add_argument("--workload", default=None)
     p.add_argument("--no-layers", action="store_true", help="time only the headline layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -116,10 +118,37 @@ class Case:
         self.layer(self.x, residual=self.res, y=self.y)
 
 
-def time_case(case, steps, warmup, torch):
-    """Mean ms per call over `steps` back-to-back calls between two events."""
+# Per-layer entries warm up for at least this much GPU time: under sustained
+# launches the chip takes some tens of milliseconds to settle (the headline
+# layer's back-to-back time falls from about 850 to about 750 us over its
+# first 40 calls, then stays there for hundreds of calls).
+LAYER_WARM_MS = 50.0
+
+
+def warm_up(case, warmup, torch, warm_ms=0.0):
+    """`warmup` calls, then (warm_ms > 0) batches of 5 more until the
+    warm-up has taken at least warm_ms of GPU time."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
     for _ in range(warmup):
         case()
+    stop.record()
+    torch.cuda.synchronize()
+    spent = start.elapsed_time(stop)
+    while spent < warm_ms:
+        start.record()
+        for _ in range(5):
+            case()
+        stop.record()
+        torch.cuda.synchronize()
+        spent += start.elapsed_time(stop)
+
+
+def time_case(case, steps, warmup, torch, warm_ms=0.0):
+    """Mean ms per call over `steps` back-to-back calls between two events,
+    after warm_up(case, warmup, torch, warm_ms)."""
+    warm_up(case, warmup, torch, warm_ms)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -165,9 +194,10 @@ def time_each(case, n, torch, scrub=None):
 
 
 def time_layer(case, steps, warmup, torch, scrub):
-    """Back-to-back mean (the stepped figure), warm per-call median and cold
-    per-call median, all in ms."""
-    mean, wall = time_case(case, steps, warmup, torch)
+    """Back-to-back mean (the stepped figure, after a warm-up of at least
+    LAYER_WARM_MS), warm per-call median and cold per-call median, all in
+    ms."""
+    mean, wall = time_case(case, steps, warmup, torch, LAYER_WARM_MS)
     warm = time_each(case, max(50, steps), torch)
     cold = time_each(case, 20, torch, scrub)
     return mean, warm, cold, wall
@@ -274,7 +304,7 @@ def stream_cases(args, per_layer, wanted, torch, cv, workloads):
 
             def step():
                 cv.conv3d_norm_silu(x, n, d, h, w, c, epi, op, prev, y)
-            nms, _ = time_case(step, max(5, args.steps), 3, torch)
+            nms, _ = time_case(step, max(5, args.steps), 3, torch, LAYER_WARM_MS)
             moved = 2 * (3 * x.numel() + y.numel() + prev.numel() + cache.numel())
             per_layer[name] = {
                 "us": round(nms * 1e3, 2), "gbs": round(moved / (nms * 1e-3) / 1e9, 1),
@@ -338,7 +368,7 @@ def stream_cases(args, per_layer, wanted, torch, cv, workloads):
                       f"{list(S['pad_lo'])}/{list(S['pad_hi'])} into {list(conv.out_shape)}"
                       f"{', history ' + str(S['history']) if S.get('history') else ''}"
                       f"{', cache ' + str(S['cache']) if S.get('cache') else ''}")
-        sms, _ = time_case(step, max(5, args.steps), 3, torch)
+        sms, _ = time_case(step, max(5, args.steps), 3, torch, LAYER_WARM_MS)
         assert torch.isfinite(y.float()).all().item()
         tf = flops / (sms * 1e-3) / 1e12
         per_layer[name] = {"us": round(sms * 1e3, 2), "tflops": round(tf, 2),
@@ -486,8 +516,8 @@ def main():
                 cv.conv3d_group_norm_from_partials(gn.desc, case.layer.desc, part, case.y,
                                                    gn.gamma, gn.beta, out, gn.workspace)
             steps = max(5, args.steps)
-            tms, _ = time_case(two_pass, steps, 3, torch)
-            fms, _ = time_case(fused, steps, 3, torch)
+            tms, _ = time_case(two_pass, steps, 3, torch, LAYER_WARM_MS)
+            fms, _ = time_case(fused, steps, 3, torch, LAYER_WARM_MS)
             assert torch.isfinite(out.float()).all().item()
             flops = L.flops()
             per_layer[name] = {
