@@ -268,7 +268,9 @@ bool halo_ok(const Problem& pr, const TileCfg& c) {
 const TileCfg kSlotStore[] = {{32, 2, 2, 8, 2, 0, -2}, {32, 4, 1, 4, 3, 0, -2},
                                {32, 4, 1, 3, 5, 0, -2}};
 const TileCfg kHaloStore[] = {{32, 4, 1, 4, 4, 9, -1}, {32, 4, 1, 4, 3, 9, -1}};
-const TileCfg kPairStore[] = {{32, 2, 2, 8, 2, 0, -3}};
+// (512 x 128 tiles either way; one wave column across the 128 channels measured 4%
+// faster on H3 L0's stride-(1,2,2) layer: 250 against 260-263 us alternating.)
+const TileCfg kPairStore[] = {{32, 4, 1, 4, 4, 0, -3}, {32, 2, 2, 8, 2, 0, -3}};
 const TileCfg kHaloPartial[] = {{32, 2, 2, 4, 4, 5, -1}, {32, 2, 2, 4, 3, 5, -1},
                                 {32, 4, 1, 4, 4, 9, -1}};
 
