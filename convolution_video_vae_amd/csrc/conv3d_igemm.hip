@@ -1512,9 +1512,19 @@ __device__ __forceinline__ void epilogue_norm_slot(const IgemmArgs& a,
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   float* sb = reinterpret_cast<float*>(sbuf);            // [BN] bias
   uint16_t* sg = reinterpret_cast<uint16_t*>(sb + BN);   // [BN] gamma
-  for (int i = threadIdx.x; i < BN; i += NT) {
-    if (HB) sb[i] = a.bias[co0 + i];
-    sg[i] = a.gamma[co0 + i];
+  // Bias and gamma are read into registers before block 0's residual reads
+  // are issued, so waiting for them leaves the residual reads in flight; the
+  // barriers here wait for LDS operations only.
+  constexpr int NS = (BN + NT - 1) / NT;
+  float bv[NS];
+  uint16_t gv[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < BN) {
+      if (HB) bv[k] = a.bias[co0 + i];
+      gv[k] = a.gamma[co0 + i];
+    }
   }
   const bool out_res = a.flags & F_RESIDUAL_OUT;
   u32x4_t rv[2][NQ];
@@ -1525,7 +1535,15 @@ __device__ __forceinline__ void epilogue_norm_slot(const IgemmArgs& a,
     for (int q = 0; q < NQ; ++q) d[q] = src[q];
   };
   if (HR) load_res(0, rv[0]);
-  __syncthreads();   // the staged bias and gamma are visible
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < BN) {
+      if (HB) sb[i] = bv[k];
+      sg[i] = gv[k];
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // staged bias and gamma visible
   const float* lb = sb + (cbase - co0);
   const u32x4_t* lg = reinterpret_cast<const u32x4_t*>(sg + (cbase - co0));
 #pragma unroll
@@ -1565,7 +1583,7 @@ __device__ __forceinline__ void epilogue_norm_slot(const IgemmArgs& a,
     for (int o = R; o < 64; o <<= 1) t += __shfl_xor(t, o);  // lanes of the same pixel
     if (WN > 1) {  // ... and the WN waves (a slot per pixel block: no reuse)
       if (lgrp == 0) red[((wave_n * WM + wave_m) * PB + p) * R + lrow] = t;
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       t = 0.f;
       for (int wn = 0; wn < WN; ++wn) t += red[((wn * WM + wave_m) * PB + p) * R + lrow];
     }
