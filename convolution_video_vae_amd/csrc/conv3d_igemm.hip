@@ -1624,13 +1624,12 @@ __device__ __forceinline__ void epilogue_norm_slot(const IgemmArgs& a,
 // [frame 0/1][subgroup 0-31 of the 128 channels][sum, sum of squares].
 // A tile whose stored slots all precede row rnext (all but about one per
 // frame) keeps one frame's sums only.
-// after_first() runs once the first round's stores are issued.
-template <int PB, bool STATS, class Hook>
+template <int PB, bool STATS = false>
 __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t (&acc)[2][PB],
                                              u32x4_t* sbuf, int m0, int m_end, int WP,
                                              float inv_wp, int co0, int wave_m, int wave_n,
-                                             int lrow, int lgrp, const int* mp, float* gnp,
-                                             int rnext, Hook after_first) {
+                                             int lrow, int lgrp, const int* mp = nullptr,
+                                             float* gnp = nullptr, int rnext = 0) {
   constexpr int RBU = 16;                 // 16-byte units per slot row
   constexpr int UNITS = 32 * 2 * 2 * RBU; // per round: 64 lane rows x 2 pixel blocks
   constexpr int WM = 2;
@@ -1712,7 +1711,6 @@ __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t 
             ok ? (unsigned)((row * a.Wo + col) * a.Cout + co0 + pos * 8) * 2u : kOobOffset;
         __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)off, 0, 0);
       }
-      if constexpr (rho == 0) after_first();
       // every wave has read this round's block before the next one overwrites it
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     });
@@ -1749,11 +1747,11 @@ __device__ __forceinline__ void store_staged(const IgemmArgs& a, const f32x16_t 
 // hit distinct banks) and stored by all 256 threads in row order, i.e.
 // 32*PB consecutive slots of whole pixels. Each wave issues PB * CB * 2
 // stores, as the plain store does.
-template <int PB, int CB, class Hook>
+template <int PB, int CB>
 __device__ __forceinline__ void store_staged_rows(const IgemmArgs& a, const f32x16_t (&acc)[CB][PB],
                                                   u32x4_t* sbuf, int m0, int m_end, int WP,
                                                   float inv_wp, int co0, int wave, int lrow,
-                                                  int lgrp, Hook after_first) {
+                                                  int lgrp) {
   constexpr int ROWS = 32 * PB, USED = CB * 4;   // 16-byte units used per row
   constexpr int UNITS = ROWS * USED;
   static_assert(USED <= 16 && UNITS % 256 == 0, "rows of at most 16 units");
@@ -1794,7 +1792,6 @@ __device__ __forceinline__ void store_staged_rows(const IgemmArgs& a, const f32x
                                : kOobOffset;
       __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)off, 0, 0);
     }
-    if constexpr (rho == 0) after_first();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   });
 }
@@ -1869,6 +1866,8 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
   constexpr int NW1 = KW == 2 ? WJ : NW;
   constexpr int WTAP = WUP * 16;        // bytes
   constexpr int EPI_VM = PB * RUN / 8;  // stores of the plain epilogue per wave
+  // tiles whose plain epilogue is a staged store (store_staged, store_staged_rows)
+  constexpr bool STAGED = (PB == 8 && CB == 2 && WN == 2) || (PB == 4 && CB <= 4 && WN == 1);
   typedef typename T::acc_t acc_t;
   static_assert(RUN % 8 == 0, "each lane must hold whole 16-byte runs of channels");
   static_assert(EPI != EPI_NORM || WM * WN * PB * R * 4 <= 2048, "norm exchange area");
@@ -2051,10 +2050,7 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     dma16(xrsrc, lds_dst(xbuf(b_c), j * 256 * 16), off, 0u);
   };
 
-  StageDma d1_pending;
-  bool pending1 = false;
-  // Set-up of tile t and the DMA of its first stage (the second's is
-  // issue_stage1).
+  // Set-up of tile t and the DMA of its first two stages.
   auto start_tile = [&](int t) {
     // Recomputing the per-lane set-up each tile is cheaper than the registers
     // of keeping it.
@@ -2195,24 +2191,12 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       for (int c = 0; c < 4; ++c) t[c] = (unsigned)__builtin_amdgcn_readlane((int)ent[0][c], L);
       return t;
     };
-    const StageDma d0 = decode_uniform(lane_entry(0), 0 < nst);
-    d1_pending = decode_uniform(lane_entry(1), 1 < nst);
-    pending1 = true;
+    const StageDma d0 = decode_uniform(lane_entry(0), 0 < nst), d1 = decode_uniform(lane_entry(1), 1 < nst);
     tnext = lane_entry(2);
     static_for<NW>([&](auto k) { issue_w_one(d0, SlotC<0>{}, k); });
     static_for<XJ>([&](auto j) { issue_x_one(d0, SlotC<0>{}, j); });
-  };
-  // Stage 1's DMA of the tile set up last: issued once the previous tile's
-  // first store round is out (or at once when there is none), so the address
-  // unit works through it while the epilogue's other rounds go through LDS.
-  // The count of memory operations after stage 0's DMA is the same either
-  // way, which is what the wait before the main loop counts on.
-  auto issue_stage1 = [&]() {
-    if (pending1) {
-      static_for<NW1>([&](auto k) { issue_w_one(d1_pending, SlotC<1>{}, k); });
-      static_for<XJ>([&](auto j) { issue_x_one(d1_pending, SlotC<1>{}, j); });
-      pending1 = false;
-    }
+    static_for<NW1>([&](auto k) { issue_w_one(d1, SlotC<1>{}, k); });
+    static_for<XJ>([&](auto j) { issue_x_one(d1, SlotC<1>{}, j); });
   };
 
   acc_t acc[CB][PB];
@@ -2254,16 +2238,16 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       const int f0 = small_div(small_div(pt.m0, WP, inv_wp), ho, inv_ho);
       store_staged<PB, true>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m, wave_n,
                              elrow, elgrp, mp, gnp + ((size_t)mt * n_tiles + pt.co0 / S::BN) * 128,
-                             (f0 + 1) * ho, issue_stage1);
+                             (f0 + 1) * ho);
     } else if (EPI == EPI_STORE && a.flags == 0 && !a.ypad) {
       // 512 x 128 tiles store through the activation buffer the next tile
       // first fills in its main loop (its set-up has filled the other two).
       if constexpr (PB == 8 && CB == 2 && WN == 2)
-        store_staged<PB, false>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m,
-                                wave_n, elrow, elgrp, nullptr, nullptr, 0, issue_stage1);
+        store_staged<PB>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m, wave_n,
+                         elrow, elgrp);
       else if constexpr (PB == 4 && CB <= 4 && WN == 1)
         store_staged_rows<PB, CB>(a, acc, xbuf2, pt.m0, pt.m_end, WP, inv_wp, pt.co0, wave_m,
-                                  elrow, elgrp, issue_stage1);
+                                  elrow, elgrp);
       else
         store_plain<T, PB, CB>(a, acc, mp, cbase);
     } else if constexpr (EPI == EPI_NORM) {
@@ -2547,7 +2531,6 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
       start_tile(cur);
     }
     if (have_prev) finish_tile(prev);
-    issue_stage1();   // (no-op when the epilogue issued it)
     if (cur < 0) break;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
@@ -2558,7 +2541,11 @@ __global__ __launch_bounds__(256) void igemm_slot_kernel(IgemmArgs a) {
     // Stage 0 of this tile has landed everywhere; the previous tile's plain
     // stores (issued after this tile's DMA) may still be in flight.
     // (The barrier also publishes wave 0's stage table.)
-    if (have_prev && (EPI == EPI_STATS || (EPI == EPI_STORE && a.flags == 0)))
+    // The previous tile's stores follow this tile's first two stages' DMA.
+    // A staged epilogue issues exactly EPI_VM stores per wave (out-of-range
+    // ones included); any other may issue fewer, so the wait then covers its
+    // stores too.
+    if (have_prev && (EPI == EPI_STATS || (EPI == EPI_STORE && STAGED && a.flags == 0 && !a.ypad)))
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW1 + XJ + EPI_VM) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW1 + XJ) : "memory");
