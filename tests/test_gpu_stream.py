@@ -51,6 +51,11 @@ PAD_CASES = [
     ("in_place_slot_384x160_batch2", (2, 4, 9, 21, 64), 160, 1, 2, CAUSAL, 1, "ns=-2"),
     ("in_place_pair_view", (1, 4, 10, 24, 64), 128, 2, 2, ((1, 2, 2), (2, 0, 0), (0, 1, 1)), 1,
      "ns=-3"),
+    # 289 tiles on 256 persistent work-groups: tiles whose epilogue (the
+    # generic one, padded output, no post-operations) precedes the next
+    # tile's main loop
+    ("in_place_slot_persistent_nobias", (1, 9, 64, 254, 32), 128, 0, 1, CAUSAL, 1,
+     "persistent=1"),
 ]
 
 
